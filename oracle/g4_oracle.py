@@ -1,0 +1,327 @@
+"""Float64 CPU oracle for the Gemma-4 E-series decoder-layer forward.
+
+TEST INFRASTRUCTURE. Only the tests, the package entry's smoke check and the benchmark's CPU-baseline
+leg may import this module. The product path never calls it and shares no code with it.
+
+It is the plain definition of what the layer computes, written from the pages in their order:
+  * cortiq-engine `g4e.rs` (page 1): module doc (PLE, shared KV), `G4eGlobals` (inverse frequencies,
+    window "tokens, current included"), `rms`, `rms_plain`, `gelu_tanh`, `extend_embedding`,
+    `g4e_forward` (the layer body).
+  * ferrox-models `gemma4_engine.rs` (page 2): `Gemma4Hparams` (`is_swa`, `head_dim`, `has_kv`,
+    `rope_theta_for`), `project_per_layer_inputs`, `forward_token_on_worker` (embedding scale,
+    attention scale 1.0, V norm without weight, shared-KV head-dim assert).
+  * taconite-embeddinggemma2 `model.rs` (page 4): `rope_half` (NeoX half-split rotation), `rms_row`,
+    `text_attention` (GQA head map `kh = hh / group`).
+  * turbospark-runtime `gemma4/attn.rs` (page 5): `rotated_pairs = full_head_dim * partial_rotary / 2`,
+    sliding `kv_start = seq_len - sliding_window`.
+
+Readings where the pages are silent or disagree (each also listed in the design notes):
+  * Proportional RoPE: pair j of a full layer rotates by pos * theta^(-2j/hd_full) for j < R and is the
+    identity for R <= j < hd_full/2 (the "zero tail" of `G4eGlobals::inv_freq_global`).
+  * Shared-KV source: the last non-shared layer of the same attention type (page 1 module doc). A
+    shared layer with no such layer keeps its own K/V.
+  * Window: query at position i sees keys i-W < j <= i.
+  * Out-of-range token ids give a zero embedding row and a zero PLE table term.
+
+All arithmetic is numpy float64 on the given inputs (bf16 inputs are converted exactly).
+"""
+import math
+
+import numpy as np
+
+try:  # inputs may arrive as torch tensors (bf16 has no numpy dtype)
+    import torch
+except ImportError:  # pragma: no cover
+    torch = None
+
+
+def f64(x):
+    """Exact float64 copy of an array or tensor (bf16/f32 values are representable in f64)."""
+    if x is None:
+        return None
+    if torch is not None and isinstance(x, torch.Tensor):
+        return x.detach().to("cpu", torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _ints(x):
+    if torch is not None and isinstance(x, torch.Tensor):
+        return x.detach().to("cpu", torch.int64).numpy()
+    return np.asarray(x, dtype=np.int64)
+
+
+# --------------------------------------------------------------------------------------------
+# Primitives (page 1 `rms`, `rms_plain`, `gelu_tanh`; page 4 `rms_row`, `rope_half`)
+# --------------------------------------------------------------------------------------------
+
+def rms_norm(x, w=None, eps=1e-6):
+    """Plain x-hat times w over the last axis: x * (mean(x^2) + eps)^-1/2 * w.
+
+    eps sits inside the mean and the weight multiplies as is (no 1 + w) -- page 1, `rms` and the module
+    note that every norm is plain x-hat times w. With w None this is the scale-less norm of V (page 1,
+    `rms_plain`; page 2 applies a ones weight to V).
+    """
+    x = f64(x)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    y = x * (ms + eps) ** -0.5
+    if w is not None:
+        y = y * f64(w)
+    return y
+
+
+def gelu_tanh(x):
+    """0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) -- page 1, `gelu_tanh`."""
+    x = f64(x)
+    return 0.5 * x * (1.0 + np.tanh(0.7978845608028654 * (x + 0.044715 * x * x * x)))
+
+
+def rotated_pairs(cfg, sliding):
+    """Pairs that rotate: all hd/2 on sliding layers; floor(hd_full * p / 2) on full layers (page 5)."""
+    if sliding:
+        return cfg["head_dim_swa"] // 2
+    return int(cfg["head_dim_full"] * cfg["partial_rotary"] / 2.0)
+
+
+def inv_freq(hd, theta, n_rot):
+    """Inverse frequencies of the hd/2 NeoX pairs: theta^(-2j/hd) for j < n_rot, 0 beyond.
+
+    The zero tail makes those pairs the identity (page 1, `G4eGlobals` inverse-frequency note).
+    """
+    j = np.arange(hd // 2, dtype=np.float64)
+    inv = float(theta) ** (-2.0 * j / hd)
+    inv[n_rot:] = 0.0
+    return inv
+
+
+def rope(x, pos, inv):
+    """NeoX half-split rotation of the last axis (page 4, `rope_half`).
+
+    For pair j < hd/2: (x_j, x_{j+hd/2}) -> (x_j c - x_{j+hd/2} s, x_{j+hd/2} c + x_j s) with
+    (c, s) = (cos, sin)(pos * inv_j). `pos` broadcasts against x's leading axes.
+    """
+    x = f64(x)
+    h = x.shape[-1] // 2
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * inv
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = x[..., :h], x[..., h:]
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+
+
+# --------------------------------------------------------------------------------------------
+# Routing (page 1 module doc; page 2 `Gemma4Hparams`)
+# --------------------------------------------------------------------------------------------
+
+def kv_sources(layer_types, n_shared):
+    """Layer whose KV cache each layer attends over.
+
+    The first L - n_shared layers own their cache. A later (shared) layer reads the last non-shared
+    layer of its own attention type (page 1 module doc). If there is none, the layer keeps its own
+    cache (reading; the pages do not cover that case).
+    """
+    L = len(layer_types)
+    first_shared = L - n_shared
+    src = []
+    for l in range(L):
+        if l < first_shared:
+            src.append(l)
+            continue
+        cands = [j for j in range(first_shared) if layer_types[j] == layer_types[l]]
+        src.append(cands[-1] if cands else l)
+    return src
+
+
+def kv_sources_shortcut(layer_types, n_shared):
+    """The index shortcut of page 2 (`kv_reuse_layer`): sliding -> first_shared-2, full -> first_shared-1.
+
+    Kept only to pin the page's own fixture; it equals `kv_sources` only when the last two non-shared
+    layers are [sliding, full].
+    """
+    L = len(layer_types)
+    first_shared = L - n_shared
+    return [l if l < first_shared else first_shared - (2 if layer_types[l] == "S" else 1)
+            for l in range(L)]
+
+
+def layer_geometry(cfg, layer):
+    """(sliding, head_dim, theta, rotated pairs) of a layer (page 2 `head_dim`, `rope_theta_for`)."""
+    sliding = cfg["layer_types"][layer] == "S"
+    hd = cfg["head_dim_swa"] if sliding else cfg["head_dim_full"]
+    theta = cfg["theta_swa"] if sliding else cfg["theta_full"]
+    return sliding, hd, theta, rotated_pairs(cfg, sliding)
+
+
+# --------------------------------------------------------------------------------------------
+# Attention (page 1 `attend_all_heads(..., 1.0, window, ...)`; page 4 `text_attention`)
+# --------------------------------------------------------------------------------------------
+
+def attention(q, K, V, qpos, window=None, scale=1.0, chunk=256):
+    """Causal GQA softmax attention of one sequence against its cache.
+
+    q [T, nh, hd]; K, V [nkv, cap, hd]; qpos [T] absolute positions. Head h reads kv head
+    h // (nh / nkv). Query at position i sees keys j with lo <= j <= i, lo = 0 (full) or
+    i - W + 1 (sliding, W keys including itself). Score scale 1.0, no softcap.
+    """
+    q, K, V = f64(q), f64(K), f64(V)
+    qpos = _ints(qpos)
+    T, nh, hd = q.shape
+    nkv = K.shape[0]
+    grp = nh // nkv
+    out = np.zeros((T, nh, V.shape[-1]))
+    for t0 in range(0, T, chunk):
+        t1 = min(T, t0 + chunk)
+        p = qpos[t0:t1]
+        lo = 0 if window is None else max(0, int(p.min()) - window + 1)
+        hi = int(p.max()) + 1
+        j = np.arange(lo, hi)
+        vis = j[None, :] <= p[:, None]
+        if window is not None:
+            vis &= j[None, :] > p[:, None] - window
+        for h in range(nh):
+            g = h // grp
+            s = scale * (q[t0:t1, h, :] @ K[g, lo:hi, :].T)
+            s = np.where(vis, s, -np.inf)
+            s = s - s.max(axis=1, keepdims=True)
+            e = np.exp(s)
+            out[t0:t1, h, :] = (e / e.sum(axis=1, keepdims=True)) @ V[g, lo:hi, :]
+    return out
+
+
+# --------------------------------------------------------------------------------------------
+# Entry: embedding and per-layer inputs (page 1 `extend_embedding`; page 2 `project_per_layer_inputs`)
+# --------------------------------------------------------------------------------------------
+
+def _gather_rows(table, ids, n_rows):
+    """Rows of `table` for ids in [0, n_rows); out-of-range ids give zero rows."""
+    ids = _ints(ids)
+    ok = (ids >= 0) & (ids < n_rows)
+    safe = np.where(ok, ids, 0)
+    if torch is not None and isinstance(table, torch.Tensor):
+        rows = f64(table[torch.from_numpy(safe.reshape(-1))])
+    else:
+        rows = f64(table)[safe.reshape(-1)]
+    rows = rows.reshape(ids.shape + (rows.shape[-1],))
+    return rows * ok[..., None]
+
+
+def embed(ids, E, cfg):
+    """e = E[id] * sqrt(H) (page 2, token embedding times `(hidden as f32).sqrt()`)."""
+    return _gather_rows(E, ids, cfg["vocab"]) * math.sqrt(cfg["hidden"])
+
+
+def ple_inputs(ids, e, W_pm, ple_norm, Tab, cfg):
+    """Per-layer inputs [.., L, d] from the scaled embedding e and the token ids.
+
+    P = (W_pm e) * H^-1/2; chunk l of P is RMS-normed with ple_norm; the table row chunk times sqrt(d)
+    is added (zero when id >= ple_vocab); the sum is multiplied by 1/sqrt(2)
+    (page 1 `extend_embedding`, page 2 `project_per_layer_inputs`).
+    """
+    H, L, d, eps = cfg["hidden"], cfg["n_layers"], cfg["ple_dim"], cfg["eps"]
+    e = f64(e)
+    P = (e @ f64(W_pm).T) * (H ** -0.5)
+    P = P.reshape(e.shape[:-1] + (L, d))
+    pn = rms_norm(P, ple_norm, eps)
+    tab = _gather_rows(Tab, ids, cfg["ple_vocab"]).reshape(e.shape[:-1] + (L, d)) * math.sqrt(d)
+    return (pn + tab) * (1.0 / math.sqrt(2.0))
+
+
+# --------------------------------------------------------------------------------------------
+# One decoder layer (page 1 `g4e_forward` body; page 2 `forward_token_on_worker`)
+# --------------------------------------------------------------------------------------------
+
+def layer_forward(cfg, lw, layer, src, h, ple_l, pos, caches, trace=None):
+    """One layer over all tokens of a batch.
+
+    h [B, T, H] residual (f64, updated copy returned); ple_l [B, T, d] this layer's per-layer input;
+    pos [B, T] absolute positions; caches {layer: (K, V)} with K, V [B, nkv, cap, hd] float64 arrays,
+    modified in place when the layer owns its cache (src == layer). `trace`, if a dict, receives the
+    intermediates.
+    """
+    eps = cfg["eps"]
+    nh, nkv = cfg["n_heads"], cfg["n_kv_heads"]
+    sliding, hd, theta, n_rot = layer_geometry(cfg, layer)
+    inv = inv_freq(hd, theta, n_rot)
+    h = f64(h).copy()
+    B, T, H = h.shape
+    pos = _ints(pos)
+
+    # attention block
+    xn = rms_norm(h, lw["input_norm"], eps)
+    q = (xn @ f64(lw["wq"]).T).reshape(B, T, nh, hd)
+    q = rope(rms_norm(q, lw["q_norm"], eps), pos[:, :, None], inv)
+    if src == layer:
+        k = (xn @ f64(lw["wk"]).T).reshape(B, T, nkv, hd)
+        k = rope(rms_norm(k, lw["k_norm"], eps), pos[:, :, None], inv)
+        v = rms_norm((xn @ f64(lw["wv"]).T).reshape(B, T, nkv, hd), None, eps)
+        K, V = caches[layer]
+        for b in range(B):
+            for t in range(T):
+                K[b, :, pos[b, t], :] = k[b, t]
+                V[b, :, pos[b, t], :] = v[b, t]
+    K, V = caches[src]
+    if K.shape[-1] != hd:
+        raise ValueError(f"layer {layer}: source cache head_dim {K.shape[-1]} != {hd}")
+    window = cfg["window"] if sliding else None
+    o = np.stack([attention(q[b], K[b], V[b], pos[b], window) for b in range(B)])
+    a = o.reshape(B, T, nh * hd) @ f64(lw["wo"]).T
+    h = h + rms_norm(a, lw["post_attn_norm"], eps)
+
+    # gelu-tanh gated FFN
+    xn2 = rms_norm(h, lw["pre_ffn_norm"], eps)
+    act = gelu_tanh(xn2 @ f64(lw["w_gate"]).T) * (xn2 @ f64(lw["w_up"]).T)
+    ffn = act @ f64(lw["w_down"]).T
+    h = h + rms_norm(ffn, lw["post_ffn_norm"], eps)
+
+    # per-layer input injection: the gate reads the raw residual
+    g = gelu_tanh(h @ f64(lw["ple_gate"]).T) * f64(ple_l)
+    p = g @ f64(lw["ple_proj"]).T
+    h = h + rms_norm(p, lw["post_ple_norm"], eps)
+
+    h = h * float(lw.get("layer_scalar", 1.0))
+    if trace is not None:
+        trace.update(xn=xn, q=q, o=o, a=a, xn2=xn2, act=act, ffn=ffn, g=g, h=h)
+    return h
+
+
+# --------------------------------------------------------------------------------------------
+# Stack
+# --------------------------------------------------------------------------------------------
+
+def new_caches(cfg, B, cap, srcs=None):
+    """Zeroed float64 caches for every layer that owns one."""
+    srcs = srcs if srcs is not None else kv_sources(cfg["layer_types"], cfg["n_shared"])
+    out = {}
+    for l, s in enumerate(srcs):
+        if s == l:
+            _, hd, _, _ = layer_geometry(cfg, l)
+            out[l] = (np.zeros((B, cfg["n_kv_heads"], cap, hd)), np.zeros((B, cfg["n_kv_heads"], cap, hd)))
+    return out
+
+
+def entry(cfg, glob, ids):
+    """(h0, ple_in) from token ids: the scaled embedding and the per-layer inputs."""
+    e = embed(ids, glob["embed"], cfg)
+    ple = ple_inputs(ids, e, glob["ple_model_proj"], glob["ple_norm"], glob["ple_embed"], cfg)
+    return e, ple
+
+
+def forward(cfg, layers, h0, ple_in, pos, caches, srcs=None, layer_range=None, per_layer=None):
+    """Run layers over h0 [B, T, H] with per-layer inputs ple_in [B, T, L, d] at positions pos [B, T].
+
+    Returns the hidden state before the final norm (page 1: the caller applies the final norm, lm_head
+    and softcap). `layers` is a list (or a callable layer -> weights dict, for lazy loading).
+    """
+    srcs = srcs if srcs is not None else kv_sources(cfg["layer_types"], cfg["n_shared"])
+    h = f64(h0)
+    ple_in = f64(ple_in)
+    rng = layer_range if layer_range is not None else range(cfg["n_layers"])
+    for l in rng:
+        lw = layers(l) if callable(layers) else layers[l]
+        h = layer_forward(cfg, lw, l, srcs[l], h, ple_in[:, :, l, :], pos, caches)
+        if per_layer is not None:
+            per_layer.append(h)
+    return h
+
+
+def prefill_positions(pos0, T):
+    pos0 = _ints(pos0)
+    return pos0[:, None] + np.arange(T)[None, :]
