@@ -1,0 +1,171 @@
+"""Thin ctypes binding of libg4.so: the C structs of include/g4.h and one wrapper per export.
+
+Argument marshalling only: tensors are passed as raw device pointers (torch is used for device memory
+and streams), every computation runs in the library's HIP kernels. A missing library is an error.
+"""
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libg4.so")
+
+G4_OK, G4_EINVAL, G4_EGEOM, G4_ERANGE, G4_EHIP, G4_EUNSUP = range(6)
+G4_F32, G4_BF16 = 0, 1
+G4_PREFILL, G4_DECODE = 0, 1
+
+i32, i64, f32, vp, sz = C.c_int32, C.c_int64, C.c_float, C.c_void_p, C.c_size_t
+
+
+class ModelDesc(C.Structure):
+    _fields_ = [("hidden", i64), ("n_heads", i64), ("n_kv_heads", i64), ("head_dim_swa", i64),
+                ("head_dim_full", i64), ("ffn", i64), ("ple_dim", i64), ("n_layers", i64), ("window", i64),
+                ("vocab", i64), ("ple_vocab", i64), ("eps", f32), ("theta_swa", f32), ("theta_full", f32),
+                ("partial_rotary", f32), ("dtype", i32), ("reserved", i32)]
+
+
+LAYER_PTRS = ["input_norm", "wq", "wk", "wv", "wo", "q_norm", "k_norm", "post_attn_norm", "pre_ffn_norm",
+              "w_gate", "w_up", "w_down", "post_ffn_norm", "ple_gate", "ple_proj", "post_ple_norm"]
+
+
+class LayerDesc(C.Structure):
+    _fields_ = [("sliding", i32), ("kv_src", i32), ("layer_scalar", f32), ("reserved", i32)] + \
+               [(n, vp) for n in LAYER_PTRS]
+
+
+class KvEntry(C.Structure):
+    _fields_ = [("k", vp), ("v", vp), ("cap", i64), ("hd", i64), ("sliding", i32), ("reserved", i32)]
+
+
+_SIGS = {
+    "g4_status_str": (C.c_char_p, [C.c_int]),
+    "g4_last_error": (C.c_char_p, []),
+    "g4_version": (C.c_int, []),
+    "g4_kv_sources": (C.c_int, [C.POINTER(i32), i32, i32, C.POINTER(i32)]),
+    "g4_rmsnorm": (C.c_int, [vp, i32, i32, vp, vp, vp, f32, vp, vp, i64, i64, f32, i32, vp]),
+    "g4_qk_norm_rope": (C.c_int, [vp, i64, vp, vp, i64, i64, vp, i64, i64, i64, i64, f32, i64, f32, i32, vp]),
+    "g4_attn_prefill": (C.c_int, [vp, i64, vp, i32, i32, i32, i32, i64, vp, i64, i64, i64, i64, i64, f32, vp, i64,
+                                  i32, vp]),
+    "g4_attn_decode": (C.c_int, [vp, i64, vp, i32, i32, i32, i32, i64, vp, i64, i64, i64, i64, f32, vp, i64, vp, sz,
+                                 i32, vp]),
+    "g4_attn_decode_ws": (sz, [i64, i64, i64, i64]),
+    "g4_linear": (C.c_int, [vp, vp, vp, i64, i64, i64, i32, i32, vp, sz, vp]),
+    "g4_ffn_geglu_ws": (sz, [i64, i64, i64, i32]),
+    "g4_ffn_geglu": (C.c_int, [vp, vp, vp, vp, vp, i64, i64, i64, vp, sz, i32, vp]),
+    "g4_ple_inject_ws": (sz, [i64, i64, i64, i32]),
+    "g4_ple_inject": (C.c_int, [vp, vp, vp, i64, vp, vp, f32, i64, i64, i64, f32, vp, sz, i32, vp]),
+    "g4_embed_ple": (C.c_int, [vp, i64, vp, vp, vp, vp, C.POINTER(ModelDesc), vp, vp, vp, sz, vp]),
+    "g4_layer_forward": (C.c_int, [C.POINTER(ModelDesc), C.POINTER(LayerDesc), i32, vp, vp, C.POINTER(KvEntry), i32,
+                                   vp, i64, i64, i32, vp, sz, vp]),
+    "g4_stack_forward": (C.c_int, [C.POINTER(ModelDesc), C.POINTER(LayerDesc), vp, vp, C.POINTER(KvEntry), i32, vp,
+                                   i64, i64, i32, vp, sz, vp]),
+    "g4_workspace_size": (sz, [C.POINTER(ModelDesc), i64, i64, i64, i32]),
+}
+
+_lib = None
+
+
+class G4Error(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{_lib.g4_status_str(status).decode()}: {msg}")
+        self.status = status
+
+
+def lib():
+    """The loaded libg4.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m gemma_decoder_forward_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def exported_names():
+    return list(_SIGS)
+
+
+def check(status):
+    if status != G4_OK:
+        raise G4Error(status, lib().g4_last_error().decode())
+    return status
+
+
+def _call(name, *args):
+    return check(getattr(lib(), name)(*args))
+
+
+def g4_kv_sources(sliding, n_shared):
+    """kv_src list for a list of 0/1 sliding flags (host computation in the library)."""
+    n = len(sliding)
+    s_arr = (i32 * n)(*sliding)
+    out = (i32 * n)()
+    _call("g4_kv_sources", s_arr, n, n_shared, out)
+    return list(out)
+
+
+# ---- same-named wrappers (pointers are ints; stream is an int handle or None) -------------------
+def g4_rmsnorm(x, x_dtype, x_parts, w, y, res, res_scale, w_next, y_next, rows, dim, eps, dtype, stream=None):
+    return _call("g4_rmsnorm", x, x_dtype, x_parts, w, y, res, res_scale, w_next, y_next, rows, dim, eps, dtype, stream)
+
+
+def g4_qk_norm_rope(x, x_ld, w, y, y_ld, y_cap, pos, B, T, heads, hd, theta, rotated_pairs, eps, dtype, stream=None):
+    return _call("g4_qk_norm_rope", x, x_ld, w, y, y_ld, y_cap, pos, B, T, heads, hd, theta, rotated_pairs, eps, dtype,
+                 stream)
+
+
+def g4_attn_prefill(q, q_ld, kv, n_kv, layer, kv_src, sliding, window, pos0, B, T, nh, nkv, hd, scale, out, out_ld,
+                    dtype, stream=None):
+    return _call("g4_attn_prefill", q, q_ld, kv, n_kv, layer, kv_src, sliding, window, pos0, B, T, nh, nkv, hd, scale,
+                 out, out_ld, dtype, stream)
+
+
+def g4_attn_decode(q, q_ld, kv, n_kv, layer, kv_src, sliding, window, pos, B, nh, nkv, hd, scale, out, out_ld, ws,
+                   ws_bytes, dtype, stream=None):
+    return _call("g4_attn_decode", q, q_ld, kv, n_kv, layer, kv_src, sliding, window, pos, B, nh, nkv, hd, scale, out,
+                 out_ld, ws, ws_bytes, dtype, stream)
+
+
+def g4_attn_decode_ws(B, nh, hd, cap):
+    return lib().g4_attn_decode_ws(B, nh, hd, cap)
+
+
+def g4_linear(A, W, Cout, M, N, K, c_dtype, dtype, ws=None, ws_bytes=0, stream=None):
+    return _call("g4_linear", A, W, Cout, M, N, K, c_dtype, dtype, ws, ws_bytes, stream)
+
+
+def g4_ffn_geglu_ws(M, H, F, dtype):
+    return lib().g4_ffn_geglu_ws(M, H, F, dtype)
+
+
+def g4_ffn_geglu(x, w_gate, w_up, w_down, out, M, H, F, ws, ws_bytes, dtype, stream=None):
+    return _call("g4_ffn_geglu", x, w_gate, w_up, w_down, out, M, H, F, ws, ws_bytes, dtype, stream)
+
+
+def g4_ple_inject_ws(M, H, d, dtype):
+    return lib().g4_ple_inject_ws(M, H, d, dtype)
+
+
+def g4_ple_inject(h, w_gate, ple, ple_ld, w_proj, w_post, layer_scalar, M, H, d, eps, ws, ws_bytes, dtype, stream=None):
+    return _call("g4_ple_inject", h, w_gate, ple, ple_ld, w_proj, w_post, layer_scalar, M, H, d, eps, ws, ws_bytes,
+                 dtype, stream)
+
+
+def g4_embed_ple(ids, M, E, Tab, W_pm, ple_norm, model, h_out, ple_out, ws, ws_bytes, stream=None):
+    return _call("g4_embed_ple", ids, M, E, Tab, W_pm, ple_norm, C.byref(model), h_out, ple_out, ws, ws_bytes, stream)
+
+
+def g4_layer_forward(model, layer_desc, layer, h, ple_in, kv, n_kv, pos, B, T, mode, ws, ws_bytes, stream=None):
+    return _call("g4_layer_forward", C.byref(model), C.byref(layer_desc), layer, h, ple_in, kv, n_kv, pos, B, T, mode,
+                 ws, ws_bytes, stream)
+
+
+def g4_stack_forward(model, layers, h, ple_in, kv, n_kv, pos, B, T, mode, ws, ws_bytes, stream=None):
+    return _call("g4_stack_forward", C.byref(model), layers, h, ple_in, kv, n_kv, pos, B, T, mode, ws, ws_bytes, stream)
+
+
+def g4_workspace_size(model, B, T, cap, mode):
+    return lib().g4_workspace_size(C.byref(model), B, T, cap, mode)

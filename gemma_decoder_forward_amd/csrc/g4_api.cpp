@@ -1,0 +1,496 @@
+// The g4 C ABI: host-side validation of every argument, then asynchronous launches on the caller's
+// stream. The library owns no device memory; scratch comes from the caller's workspace.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "g4_internal.h"
+
+namespace g4 {
+
+static thread_local std::string g_last_error;
+
+g4_status fail(g4_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+g4_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(G4_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return G4_OK;
+}
+
+static bool dt_ok(int32_t dt) { return dt == G4_F32 || dt == G4_BF16; }
+
+#define G4_REQ(cond, st, ...)                 \
+  do {                                        \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+static g4_status check_model(const g4_model_desc* m) {
+  G4_REQ(m, G4_EINVAL, "model descriptor is NULL");
+  G4_REQ(dt_ok(m->dtype), G4_EINVAL, "model dtype %d is not G4_F32 or G4_BF16", m->dtype);
+  G4_REQ(m->hidden > 0 && m->n_heads > 0 && m->n_kv_heads > 0 && m->head_dim_swa > 0 && m->head_dim_full > 0 &&
+             m->ffn > 0 && m->ple_dim > 0 && m->n_layers > 0,
+         G4_EINVAL, "model sizes must be positive");
+  G4_REQ(m->n_heads % m->n_kv_heads == 0, G4_EGEOM, "n_heads %lld is not a multiple of n_kv_heads %lld",
+         (long long)m->n_heads, (long long)m->n_kv_heads);
+  G4_REQ(m->head_dim_swa % 2 == 0 && m->head_dim_full % 2 == 0, G4_EGEOM, "head dims must be even");
+  G4_REQ(m->head_dim_swa <= 512 && m->head_dim_full <= 512, G4_ERANGE, "head dims above 512 are not supported");
+  G4_REQ(m->window >= 1, G4_ERANGE, "window %lld < 1", (long long)m->window);
+  G4_REQ(m->partial_rotary >= 0.f && m->partial_rotary <= 1.f, G4_EINVAL, "partial_rotary %g outside [0,1]",
+         (double)m->partial_rotary);
+  G4_REQ(m->eps >= 0.f, G4_EINVAL, "eps < 0");
+  G4_REQ(m->theta_swa > 0.f && m->theta_full > 0.f, G4_EINVAL, "RoPE bases must be positive");
+  G4_REQ(m->hidden <= 16384, G4_ERANGE, "hidden %lld > 16384", (long long)m->hidden);
+  G4_REQ(m->ple_dim <= 512, G4_ERANGE, "ple_dim %lld > 512", (long long)m->ple_dim);
+  return G4_OK;
+}
+
+static int64_t rot_pairs(const g4_model_desc* m, int sliding) {
+  if (sliding) return m->head_dim_swa / 2;
+  return (int64_t)((double)m->head_dim_full * (double)m->partial_rotary / 2.0);
+}
+
+// Routing and cache checks shared by the attention entry points and the layer forward.
+static g4_status check_kv(const g4_kv_entry* kv, int32_t n_kv, int32_t layer, int32_t kv_src, int32_t sliding,
+                          int64_t hd, int64_t T, int32_t mode) {
+  G4_REQ(kv, G4_EINVAL, "kv table is NULL");
+  G4_REQ(n_kv > 0, G4_EINVAL, "n_kv %d <= 0", n_kv);
+  G4_REQ(layer >= 0 && layer < n_kv, G4_EINVAL, "layer %d outside the kv table [0,%d)", layer, n_kv);
+  G4_REQ(kv_src >= 0 && kv_src <= layer, G4_EGEOM, "kv_src %d must be in [0, layer %d]", kv_src, layer);
+  const g4_kv_entry& e = kv[kv_src];
+  G4_REQ(e.k && e.v, G4_EGEOM, "kv_src %d has no cache (a shared layer cannot be a source)", kv_src);
+  G4_REQ(e.hd == hd, G4_EGEOM, "layer %d head_dim %lld != kv_src %d cache head_dim %lld", layer, (long long)hd,
+         kv_src, (long long)e.hd);
+  G4_REQ(e.sliding == sliding, G4_EGEOM, "layer %d attention type differs from kv_src %d", layer, kv_src);
+  G4_REQ(e.cap > 0, G4_ERANGE, "cache capacity %lld <= 0", (long long)e.cap);
+  G4_REQ(T <= e.cap, G4_ERANGE, "T %lld exceeds cache capacity %lld", (long long)T, (long long)e.cap);
+  G4_REQ(mode == G4_PREFILL || T == 1, G4_EINVAL, "decode takes T == 1");
+  return G4_OK;
+}
+
+// ---- workspace plan of the layer forward -----------------------------------------------------
+struct Plan {
+  size_t xn, qkv, ao, f32buf, act, hb, gm, dec, emb_e, emb_p, total;
+  int64_t qkv_ld, splits;
+};
+
+static size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static Plan plan(const g4_model_desc* m, int64_t B, int64_t T, int64_t cap, int32_t mode) {
+  Plan p{};
+  const size_t E = dsize(m->dtype);
+  const int64_t M = B * T;
+  const int64_t hdm = m->head_dim_swa > m->head_dim_full ? m->head_dim_swa : m->head_dim_full;
+  p.qkv_ld = (m->n_heads + 2 * m->n_kv_heads) * hdm;
+  p.splits = 4;
+  size_t o = 0;
+  p.xn = o; o += al(M * m->hidden * E);
+  p.qkv = o; o += al(M * p.qkv_ld * E);
+  p.ao = o; o += al(M * m->n_heads * hdm * E);
+  p.f32buf = o; o += al((size_t)p.splits * M * m->hidden * 4);
+  p.act = o; o += al(M * m->ffn * E);
+  p.hb = o; o += al(M * m->hidden * E);
+  p.gm = o; o += al(M * m->ple_dim * E);
+  p.dec = o;
+  if (mode == G4_DECODE) o += al(attn_decode_ws(B, m->n_heads, hdm, cap > 0 ? cap : 1));
+  p.total = o;
+  // the entry (embedding + PLE) reuses the start of the workspace
+  p.emb_e = 0;
+  p.emb_p = al(M * m->hidden * E);
+  const size_t emb_total = p.emb_p + al(M * m->n_layers * m->ple_dim * 4);
+  if (emb_total > p.total) p.total = emb_total;
+  return p;
+}
+
+// GEMM with validation of the shapes it must see.
+static g4_status run_gemm(const void* A, int64_t lda, const void* B, const void* B2, int64_t ldb, void* C,
+                          int64_t ldc, int32_t c_dtype, int64_t M, int64_t N, int64_t K, int32_t epi,
+                          const float* aux, int64_t aux_ld, int32_t splits, int64_t split_stride, int32_t dt,
+                          hipStream_t s) {
+  GemmArgs a{};
+  a.A = A; a.lda = lda; a.B = B; a.B2 = B2; a.ldb = ldb; a.C = C; a.ldc = ldc; a.c_dtype = c_dtype;
+  a.aux = aux; a.aux_ld = aux_ld; a.M = M; a.N = N; a.K = K; a.epi = epi;
+  a.splits = splits < 1 ? 1 : splits; a.split_stride = split_stride;
+  return gemm(a, dt, s);
+}
+
+struct LayerCtx {
+  const g4_model_desc* m;
+  const g4_layer_desc* l;
+  int32_t layer;
+  float* h;
+  const float* ple_in;
+  const g4_kv_entry* kv;
+  int32_t n_kv;
+  const int32_t* pos;
+  int64_t B, T;
+  int32_t mode;
+  char* ws;
+  const Plan* p;
+  hipStream_t s;
+  bool xn_ready;                 // xn already holds rms(h) * input_norm (fused by the previous layer)
+  const void* next_input_norm;   // if set, the last tail also writes the next layer's xn
+};
+
+static g4_status check_layer(const g4_model_desc* m, const g4_layer_desc* l, int32_t layer, const g4_kv_entry* kv,
+                             int32_t n_kv, int64_t T, int32_t mode) {
+  G4_REQ(l, G4_EINVAL, "layer descriptor is NULL");
+  G4_REQ(layer >= 0 && layer < m->n_layers, G4_EINVAL, "layer %d outside [0, %lld)", layer, (long long)m->n_layers);
+  G4_REQ(n_kv == m->n_layers, G4_EINVAL, "n_kv %d != n_layers %lld", n_kv, (long long)m->n_layers);
+  G4_REQ(l->sliding == 0 || l->sliding == 1, G4_EINVAL, "layer %d: sliding must be 0 or 1", layer);
+  G4_REQ(l->input_norm && l->wq && l->wo && l->q_norm && l->post_attn_norm && l->pre_ffn_norm && l->w_gate &&
+             l->w_up && l->w_down && l->post_ffn_norm && l->ple_gate && l->ple_proj && l->post_ple_norm,
+         G4_EINVAL, "layer %d: a weight pointer is NULL", layer);
+  if (l->kv_src == layer) G4_REQ(l->wk && l->wv && l->k_norm, G4_EINVAL, "layer %d owns its cache but wk/wv/k_norm is NULL", layer);
+  else G4_REQ(l->kv_src < layer, G4_EGEOM, "layer %d: kv_src %d is not an earlier layer", layer, l->kv_src);
+  const int64_t hd = l->sliding ? m->head_dim_swa : m->head_dim_full;
+  return check_kv(kv, n_kv, layer, l->kv_src, l->sliding, hd, T, mode);
+}
+
+static g4_status layer_impl(const LayerCtx& c) {
+  const g4_model_desc* m = c.m;
+  const g4_layer_desc* l = c.l;
+  const int32_t dt = m->dtype;
+  const size_t E = dsize(dt);
+  const int64_t M = c.B * c.T, H = m->hidden, nh = m->n_heads, nkv = m->n_kv_heads, F = m->ffn, d = m->ple_dim;
+  const int sliding = l->sliding;
+  const int64_t hd = sliding ? m->head_dim_swa : m->head_dim_full;
+  const float theta = sliding ? m->theta_swa : m->theta_full;
+  const int64_t nrot = rot_pairs(m, sliding);
+  const bool own = l->kv_src == c.layer;
+  char* xn = c.ws + c.p->xn;
+  char* qkv = c.ws + c.p->qkv;
+  char* ao = c.ws + c.p->ao;
+  float* fb = (float*)(c.ws + c.p->f32buf);
+  char* act = c.ws + c.p->act;
+  char* hb = c.ws + c.p->hb;
+  char* gm = c.ws + c.p->gm;
+  const int64_t qld = c.p->qkv_ld;
+  g4_status st;
+#define G4_TRY(x)                 \
+  do {                            \
+    if ((st = (x)) != G4_OK) return st; \
+  } while (0)
+  if (M == 0) return G4_OK;
+  // 1. pre-attention norm
+  if (!c.xn_ready)
+    G4_TRY(rownorm(c.h, G4_F32, 1, 0, l->input_norm, xn, nullptr, 1.f, nullptr, nullptr, M, H, m->eps, dt, c.s));
+  // 2. projections: q, and k, v when the layer owns its cache
+  G4_TRY(run_gemm(xn, H, l->wq, nullptr, H, qkv, qld, dt, M, nh * hd, H, EPI_STORE, nullptr, 0, 1, 0, dt, c.s));
+  if (own) {
+    G4_TRY(run_gemm(xn, H, l->wk, nullptr, H, qkv + nh * hd * E, qld, dt, M, nkv * hd, H, EPI_STORE, nullptr, 0, 1,
+                    0, dt, c.s));
+    G4_TRY(run_gemm(xn, H, l->wv, nullptr, H, qkv + (nh + nkv) * hd * E, qld, dt, M, nkv * hd, H, EPI_STORE, nullptr,
+                    0, 1, 0, dt, c.s));
+  }
+  // 3. per-head norms + RoPE; k and v go straight into this layer's cache rows
+  HeadSeg segs[3];
+  int ns = 0;
+  segs[ns++] = HeadSeg{qkv, qld, l->q_norm, qkv, qld, 0, (int32_t)nh, 1};
+  if (own) {
+    const g4_kv_entry& e = c.kv[c.layer];
+    segs[ns++] = HeadSeg{qkv + nh * hd * E, qld, l->k_norm, e.k, 0, e.cap, (int32_t)nkv, 1};
+    segs[ns++] = HeadSeg{qkv + (nh + nkv) * hd * E, qld, nullptr, e.v, 0, e.cap, (int32_t)nkv, 0};
+  }
+  G4_TRY(qk_norm_rope(segs, ns, c.pos, c.B, c.T, hd, theta, nrot, m->eps, dt, c.s));
+  // 4. attention over the source layer's cache (no copy)
+  const g4_kv_entry& src = c.kv[l->kv_src];
+  AttnArgs aa{};
+  aa.q = qkv; aa.q_ld = qld; aa.k = src.k; aa.v = src.v; aa.cap = src.cap; aa.pos0 = c.pos;
+  aa.B = c.B; aa.T = c.T; aa.nh = nh; aa.nkv = nkv; aa.hd = hd; aa.sliding = sliding; aa.window = m->window;
+  aa.scale = 1.f; aa.out = ao; aa.out_ld = nh * hd;
+  if (c.mode == G4_DECODE) G4_TRY(attn_decode(aa, c.ws + c.p->dec, c.p->total - c.p->dec, dt, c.s));
+  else G4_TRY(attn_prefill(aa, dt, c.s));
+  // 5-6. o projection, then h += rms(a) * w_pa and xn2 = rms(h) * w_pf
+  const int32_t so = 1;
+  G4_TRY(run_gemm(ao, nh * hd, l->wo, nullptr, nh * hd, fb, H, G4_F32, M, H, nh * hd, EPI_STORE, nullptr, 0, so,
+                  M * H, dt, c.s));
+  G4_TRY(rownorm(fb, G4_F32, so, M * H, l->post_attn_norm, nullptr, c.h, 1.f, l->pre_ffn_norm, xn, M, H, m->eps, dt,
+                 c.s));
+  // 7. gate/up GEMM with the gelu-tanh product in its epilogue
+  G4_TRY(run_gemm(xn, H, l->w_gate, l->w_up, H, act, F, dt, M, F, H, EPI_GEGLU, nullptr, 0, 1, 0, dt, c.s));
+  // 8-9. down projection, then h += rms(ffn) * w_pff; hb = h in dtype for the PLE gate
+  const int32_t sd = 1;
+  G4_TRY(run_gemm(act, F, l->w_down, nullptr, F, fb, H, G4_F32, M, H, F, EPI_STORE, nullptr, 0, sd, M * H, dt, c.s));
+  G4_TRY(rownorm(fb, G4_F32, sd, M * H, l->post_ffn_norm, nullptr, c.h, 1.f, nullptr, hb, M, H, m->eps, dt, c.s));
+  // 10. PLE gate: gelu_tanh(h W_pg^T) * ple_in[:, layer]
+  const int64_t Ld = m->n_layers * d;
+  G4_TRY(run_gemm(hb, H, l->ple_gate, nullptr, H, gm, d, dt, M, d, H, EPI_GELU_MUL, c.ple_in + (int64_t)c.layer * d,
+                  Ld, 1, 0, dt, c.s));
+  // 11-12. PLE projection, h = (h + rms(p) * w_post_ple) * layer_scalar (+ next layer's xn)
+  G4_TRY(run_gemm(gm, d, l->ple_proj, nullptr, d, fb, H, G4_F32, M, H, d, EPI_STORE, nullptr, 0, 1, M * H, dt, c.s));
+  G4_TRY(rownorm(fb, G4_F32, 1, M * H, l->post_ple_norm, nullptr, c.h, l->layer_scalar, c.next_input_norm,
+                 c.next_input_norm ? xn : nullptr, M, H, m->eps, dt, c.s));
+#undef G4_TRY
+  return G4_OK;
+}
+
+}  // namespace g4
+
+using namespace g4;
+
+extern "C" {
+
+const char* g4_status_str(int status) {
+  switch (status) {
+    case G4_OK: return "G4_OK";
+    case G4_EINVAL: return "G4_EINVAL";
+    case G4_EGEOM: return "G4_EGEOM";
+    case G4_ERANGE: return "G4_ERANGE";
+    case G4_EHIP: return "G4_EHIP";
+    case G4_EUNSUP: return "G4_EUNSUP";
+    default: return "G4_UNKNOWN";
+  }
+}
+
+const char* g4_last_error(void) { return g_last_error.c_str(); }
+
+int g4_version(void) { return 100; }
+
+g4_status g4_kv_sources(const int32_t* sliding, int32_t n_layers, int32_t n_shared, int32_t* kv_src) {
+  G4_REQ(sliding && kv_src, G4_EINVAL, "sliding or kv_src is NULL");
+  G4_REQ(n_layers > 0 && n_shared >= 0 && n_shared <= n_layers, G4_EINVAL, "n_layers %d, n_shared %d", n_layers,
+         n_shared);
+  const int32_t first_shared = n_layers - n_shared;
+  for (int32_t l = 0; l < n_layers; ++l) {
+    G4_REQ(sliding[l] == 0 || sliding[l] == 1, G4_EINVAL, "sliding[%d] must be 0 or 1", l);
+    kv_src[l] = l;
+    if (l < first_shared) continue;
+    for (int32_t j = first_shared - 1; j >= 0; --j)
+      if (sliding[j] == sliding[l]) {
+        kv_src[l] = j;
+        break;
+      }
+  }
+  return G4_OK;
+}
+
+g4_status g4_rmsnorm(const void* x, int32_t x_dtype, int32_t x_parts, const void* w, void* y, float* res,
+                     float res_scale, const void* w_next, void* y_next, int64_t rows, int64_t dim, float eps,
+                     int32_t dtype, void* stream) {
+  G4_REQ(dt_ok(dtype), G4_EINVAL, "dtype %d", dtype);
+  G4_REQ(x_dtype == G4_F32 || x_dtype == dtype, G4_EINVAL, "x_dtype must be G4_F32 or dtype");
+  G4_REQ(rows >= 0 && dim > 0, G4_EINVAL, "rows %lld / dim %lld", (long long)rows, (long long)dim);
+  if (rows == 0) return G4_OK;
+  G4_REQ(x, G4_EINVAL, "x is NULL");
+  G4_REQ(dim <= 16384, G4_ERANGE, "dim %lld > 16384", (long long)dim);
+  G4_REQ(x_parts >= 1, G4_EINVAL, "x_parts %d < 1", x_parts);
+  G4_REQ(!y_next || res, G4_EINVAL, "y_next requires res");
+  G4_REQ(y || res, G4_EINVAL, "nothing to write: y and res are NULL");
+  G4_REQ(eps >= 0.f, G4_EINVAL, "eps < 0");
+  return rownorm(x, x_dtype, x_parts, rows * dim, w, y, res, res_scale, w_next, y_next, rows, dim, eps, dtype,
+                 (hipStream_t)stream);
+}
+
+g4_status g4_qk_norm_rope(const void* x, int64_t x_ld, const void* w, void* y, int64_t y_ld, int64_t y_cap,
+                          const int32_t* pos, int64_t B, int64_t T, int64_t heads, int64_t hd, float theta,
+                          int64_t rotated_pairs, float eps, int32_t dtype, void* stream) {
+  G4_REQ(dt_ok(dtype), G4_EINVAL, "dtype %d", dtype);
+  G4_REQ(B >= 0 && T >= 0 && heads > 0 && hd > 0, G4_EINVAL, "sizes must be positive");
+  if (B * T == 0) return G4_OK;
+  G4_REQ(x && y, G4_EINVAL, "x or y is NULL");
+  G4_REQ(hd % 2 == 0, G4_EGEOM, "head_dim %lld is odd", (long long)hd);
+  G4_REQ(hd <= 512, G4_ERANGE, "head_dim %lld > 512", (long long)hd);
+  G4_REQ(x_ld >= heads * hd, G4_EINVAL, "x_ld %lld < heads*hd", (long long)x_ld);
+  G4_REQ(y_cap > 0 || y_ld >= heads * hd, G4_EINVAL, "y_ld %lld < heads*hd", (long long)y_ld);
+  G4_REQ(y_cap >= 0, G4_EINVAL, "y_cap < 0");
+  G4_REQ(y_cap == 0 || T <= y_cap, G4_ERANGE, "T %lld > cache capacity %lld", (long long)T, (long long)y_cap);
+  G4_REQ(rotated_pairs >= 0 && rotated_pairs <= hd / 2, G4_ERANGE, "rotated_pairs %lld outside [0, hd/2]",
+         (long long)rotated_pairs);
+  G4_REQ(pos || (rotated_pairs == 0 && y_cap == 0), G4_EINVAL, "pos is NULL");
+  G4_REQ(rotated_pairs == 0 || theta > 0.f, G4_EINVAL, "theta <= 0");
+  HeadSeg sg{x, x_ld, w, y, y_ld, y_cap, (int32_t)heads, rotated_pairs > 0 ? 1 : 0};
+  return qk_norm_rope(&sg, 1, pos, B, T, hd, theta, rotated_pairs, eps, dtype, (hipStream_t)stream);
+}
+
+static g4_status check_attn(const void* q, int64_t q_ld, const g4_kv_entry* kv, int32_t n_kv, int32_t layer,
+                            int32_t kv_src, int32_t sliding, int64_t window, const int32_t* pos, int64_t B,
+                            int64_t T, int64_t nh, int64_t nkv, int64_t hd, void* out, int64_t out_ld,
+                            int32_t dtype, int32_t mode) {
+  G4_REQ(dt_ok(dtype), G4_EINVAL, "dtype %d", dtype);
+  G4_REQ(B >= 0 && T >= 0 && nh > 0 && nkv > 0 && hd > 0, G4_EINVAL, "sizes must be positive");
+  G4_REQ(B * T == 0 || (q && out && pos), G4_EINVAL, "q, out or pos is NULL");
+  G4_REQ(nh % nkv == 0, G4_EGEOM, "nh %lld is not a multiple of nkv %lld", (long long)nh, (long long)nkv);
+  G4_REQ(hd <= 512, G4_ERANGE, "head_dim %lld > 512", (long long)hd);
+  G4_REQ(q_ld >= nh * hd && out_ld >= nh * hd, G4_EINVAL, "q_ld/out_ld smaller than nh*hd");
+  G4_REQ(sliding == 0 || sliding == 1, G4_EINVAL, "sliding must be 0 or 1");
+  G4_REQ(!sliding || window >= 1, G4_ERANGE, "window %lld < 1", (long long)window);
+  return check_kv(kv, n_kv, layer, kv_src, sliding, hd, T, mode);
+}
+
+g4_status g4_attn_prefill(const void* q, int64_t q_ld, const g4_kv_entry* kv, int32_t n_kv, int32_t layer,
+                          int32_t kv_src, int32_t sliding, int64_t window, const int32_t* pos0, int64_t B,
+                          int64_t T, int64_t nh, int64_t nkv, int64_t hd, float scale, void* out, int64_t out_ld,
+                          int32_t dtype, void* stream) {
+  g4_status st = check_attn(q, q_ld, kv, n_kv, layer, kv_src, sliding, window, pos0, B, T, nh, nkv, hd, out,
+                            out_ld, dtype, G4_PREFILL);
+  if (st != G4_OK) return st;
+  AttnArgs a{};
+  a.q = q; a.q_ld = q_ld; a.k = kv[kv_src].k; a.v = kv[kv_src].v; a.cap = kv[kv_src].cap; a.pos0 = pos0;
+  a.B = B; a.T = T; a.nh = nh; a.nkv = nkv; a.hd = hd; a.sliding = sliding; a.window = window; a.scale = scale;
+  a.out = out; a.out_ld = out_ld;
+  if (B * T == 0) return G4_OK;
+  return attn_prefill(a, dtype, (hipStream_t)stream);
+}
+
+size_t g4_attn_decode_ws(int64_t B, int64_t nh, int64_t hd, int64_t cap) { return attn_decode_ws(B, nh, hd, cap); }
+
+g4_status g4_attn_decode(const void* q, int64_t q_ld, const g4_kv_entry* kv, int32_t n_kv, int32_t layer,
+                         int32_t kv_src, int32_t sliding, int64_t window, const int32_t* pos, int64_t B, int64_t nh,
+                         int64_t nkv, int64_t hd, float scale, void* out, int64_t out_ld, void* ws, size_t ws_bytes,
+                         int32_t dtype, void* stream) {
+  g4_status st = check_attn(q, q_ld, kv, n_kv, layer, kv_src, sliding, window, pos, B, 1, nh, nkv, hd, out, out_ld,
+                            dtype, G4_DECODE);
+  if (st != G4_OK) return st;
+  if (B == 0) return G4_OK;
+  G4_REQ(ws, G4_EINVAL, "workspace is NULL");
+  AttnArgs a{};
+  a.q = q; a.q_ld = q_ld; a.k = kv[kv_src].k; a.v = kv[kv_src].v; a.cap = kv[kv_src].cap; a.pos0 = pos;
+  a.B = B; a.T = 1; a.nh = nh; a.nkv = nkv; a.hd = hd; a.sliding = sliding; a.window = window; a.scale = scale;
+  a.out = out; a.out_ld = out_ld;
+  return attn_decode(a, ws, ws_bytes, dtype, (hipStream_t)stream);
+}
+
+g4_status g4_linear(const void* A, const void* W, void* C, int64_t M, int64_t N, int64_t K, int32_t c_dtype,
+                    int32_t dtype, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws; (void)ws_bytes;
+  G4_REQ(dt_ok(dtype), G4_EINVAL, "dtype %d", dtype);
+  G4_REQ(c_dtype == G4_F32 || c_dtype == dtype, G4_EINVAL, "c_dtype must be G4_F32 or dtype");
+  G4_REQ(M >= 0 && N > 0 && K > 0, G4_EINVAL, "M %lld N %lld K %lld", (long long)M, (long long)N, (long long)K);
+  if (M == 0) return G4_OK;
+  G4_REQ(A && W && C, G4_EINVAL, "A, W or C is NULL");
+  return run_gemm(A, K, W, nullptr, K, C, N, c_dtype, M, N, K, EPI_STORE, nullptr, 0, 1, 0, dtype, (hipStream_t)stream);
+}
+
+size_t g4_ffn_geglu_ws(int64_t M, int64_t H, int64_t F, int32_t dtype) {
+  (void)H;
+  return al((size_t)M * F * dsize(dtype));
+}
+
+g4_status g4_ffn_geglu(const void* x, const void* w_gate, const void* w_up, const void* w_down, float* out, int64_t M,
+                       int64_t H, int64_t F, void* ws, size_t ws_bytes, int32_t dtype, void* stream) {
+  G4_REQ(dt_ok(dtype), G4_EINVAL, "dtype %d", dtype);
+  G4_REQ(M >= 0 && H > 0 && F > 0, G4_EINVAL, "sizes");
+  if (M == 0) return G4_OK;
+  G4_REQ(x && w_gate && w_up && w_down && out, G4_EINVAL, "a pointer is NULL");
+  G4_REQ(ws && ws_bytes >= g4_ffn_geglu_ws(M, H, F, dtype), G4_EINVAL, "workspace too small (%zu < %zu)", ws_bytes,
+         g4_ffn_geglu_ws(M, H, F, dtype));
+  if (M == 0) return G4_OK;
+  hipStream_t s = (hipStream_t)stream;
+  g4_status st = run_gemm(x, H, w_gate, w_up, H, ws, F, dtype, M, F, H, EPI_GEGLU, nullptr, 0, 1, 0, dtype, s);
+  if (st != G4_OK) return st;
+  return run_gemm(ws, F, w_down, nullptr, F, out, H, G4_F32, M, H, F, EPI_STORE, nullptr, 0, 1, 0, dtype, s);
+}
+
+size_t g4_ple_inject_ws(int64_t M, int64_t H, int64_t d, int32_t dtype) {
+  return al((size_t)M * H * dsize(dtype)) + al((size_t)M * d * dsize(dtype)) + al((size_t)M * H * 4);
+}
+
+g4_status g4_ple_inject(float* h, const void* w_gate, const float* ple, int64_t ple_ld, const void* w_proj,
+                        const void* w_post, float layer_scalar, int64_t M, int64_t H, int64_t d, float eps, void* ws,
+                        size_t ws_bytes, int32_t dtype, void* stream) {
+  G4_REQ(dt_ok(dtype), G4_EINVAL, "dtype %d", dtype);
+  G4_REQ(M >= 0 && H > 0 && d > 0 && ple_ld >= d, G4_EINVAL, "sizes");
+  if (M == 0) return G4_OK;
+  G4_REQ(h && w_gate && ple && w_proj && w_post, G4_EINVAL, "a pointer is NULL");
+  G4_REQ(H <= 16384, G4_ERANGE, "H > 16384");
+  G4_REQ(ws && ws_bytes >= g4_ple_inject_ws(M, H, d, dtype), G4_EINVAL, "workspace too small");
+  if (M == 0) return G4_OK;
+  hipStream_t s = (hipStream_t)stream;
+  char* hb = (char*)ws;
+  char* gmb = hb + al((size_t)M * H * dsize(dtype));
+  float* pb = (float*)(gmb + al((size_t)M * d * dsize(dtype)));
+  g4_status st;
+  if ((st = cast_rows(h, hb, M * H, dtype, s)) != G4_OK) return st;
+  if ((st = run_gemm(hb, H, w_gate, nullptr, H, gmb, d, dtype, M, d, H, EPI_GELU_MUL, ple, ple_ld, 1, 0, dtype, s)) !=
+      G4_OK)
+    return st;
+  if ((st = run_gemm(gmb, d, w_proj, nullptr, d, pb, H, G4_F32, M, H, d, EPI_STORE, nullptr, 0, 1, 0, dtype, s)) != G4_OK)
+    return st;
+  return rownorm(pb, G4_F32, 1, M * H, w_post, nullptr, h, layer_scalar, nullptr, nullptr, M, H, eps, dtype, s);
+}
+
+g4_status g4_embed_ple(const int32_t* ids, int64_t M, const void* E, const void* Tab, const void* W_pm,
+                       const void* ple_norm, const g4_model_desc* model, float* h_out, float* ple_out, void* ws,
+                       size_t ws_bytes, void* stream) {
+  g4_status st = check_model(model);
+  if (st != G4_OK) return st;
+  G4_REQ(M >= 0, G4_EINVAL, "M < 0");
+  if (M == 0) return G4_OK;
+  G4_REQ(ids && E && Tab && W_pm && ple_norm && h_out && ple_out, G4_EINVAL, "a pointer is NULL");
+  G4_REQ(model->vocab > 0 && model->ple_vocab > 0, G4_EINVAL, "vocab sizes must be positive");
+  Plan p = plan(model, M, 1, 0, G4_PREFILL);
+  G4_REQ(ws && ws_bytes >= p.total, G4_EINVAL, "workspace too small (%zu < %zu)", ws_bytes, p.total);
+  if (M == 0) return G4_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const int32_t dt = model->dtype;
+  char* ecast = (char*)ws + p.emb_e;
+  float* P = (float*)((char*)ws + p.emb_p);
+  const int64_t Ld = model->n_layers * model->ple_dim;
+  if ((st = embed_rows(ids, M, E, model->vocab, model->hidden, h_out, ecast, dt, s)) != G4_OK) return st;
+  if ((st = run_gemm(ecast, model->hidden, W_pm, nullptr, model->hidden, P, Ld, G4_F32, M, Ld, model->hidden,
+                     EPI_STORE, nullptr, 0, 1, 0, dt, s)) != G4_OK)
+    return st;
+  return ple_combine(ids, M, P, Tab, model->ple_vocab, ple_norm, model->hidden, model->n_layers, model->ple_dim,
+                     model->eps, ple_out, dt, s);
+}
+
+size_t g4_workspace_size(const g4_model_desc* model, int64_t B, int64_t T, int64_t cap, int32_t mode) {
+  if (check_model(model) != G4_OK || B < 0 || T < 0) return 0;
+  return plan(model, B, T, cap, mode).total;
+}
+
+static g4_status layer_entry(const g4_model_desc* model, const g4_layer_desc* ld, int32_t layer, float* h,
+                             const float* ple_in, const g4_kv_entry* kv, int32_t n_kv, const int32_t* pos, int64_t B,
+                             int64_t T, int32_t mode, void* ws, size_t ws_bytes, void* stream, bool xn_ready,
+                             const void* next_norm) {
+  const int64_t cap = kv[ld->kv_src].cap;
+  Plan p = plan(model, B, T, cap, mode);
+  G4_REQ(ws && ws_bytes >= p.total, G4_EINVAL, "workspace too small (%zu < %zu)", ws_bytes, p.total);
+  LayerCtx c{model, ld, layer, h, ple_in, kv, n_kv, pos, B, T, mode, (char*)ws, &p, (hipStream_t)stream, xn_ready,
+             next_norm};
+  return layer_impl(c);
+}
+
+g4_status g4_layer_forward(const g4_model_desc* model, const g4_layer_desc* ld, int32_t layer, float* h,
+                           const float* ple_in, const g4_kv_entry* kv, int32_t n_kv, const int32_t* pos, int64_t B,
+                           int64_t T, int32_t mode, void* ws, size_t ws_bytes, void* stream) {
+  g4_status st = check_model(model);
+  if (st != G4_OK) return st;
+  G4_REQ(mode == G4_PREFILL || mode == G4_DECODE, G4_EINVAL, "mode %d", mode);
+  G4_REQ(h && ple_in && pos, G4_EINVAL, "h, ple_in or pos is NULL");
+  G4_REQ(B >= 0 && T >= 0, G4_EINVAL, "B, T");
+  if ((st = check_layer(model, ld, layer, kv, n_kv, T, mode)) != G4_OK) return st;
+  return layer_entry(model, ld, layer, h, ple_in, kv, n_kv, pos, B, T, mode, ws, ws_bytes, stream, false, nullptr);
+}
+
+g4_status g4_stack_forward(const g4_model_desc* model, const g4_layer_desc* layers, float* h, const float* ple_in,
+                           const g4_kv_entry* kv, int32_t n_kv, const int32_t* pos, int64_t B, int64_t T, int32_t mode,
+                           void* ws, size_t ws_bytes, void* stream) {
+  g4_status st = check_model(model);
+  if (st != G4_OK) return st;
+  G4_REQ(layers, G4_EINVAL, "layers is NULL");
+  G4_REQ(mode == G4_PREFILL || mode == G4_DECODE, G4_EINVAL, "mode %d", mode);
+  G4_REQ(h && ple_in && pos, G4_EINVAL, "h, ple_in or pos is NULL");
+  G4_REQ(B >= 0 && T >= 0, G4_EINVAL, "B, T");
+  for (int32_t l = 0; l < model->n_layers; ++l)
+    if ((st = check_layer(model, &layers[l], l, kv, n_kv, T, mode)) != G4_OK) return st;
+  for (int32_t l = 0; l < model->n_layers; ++l) {
+    const void* nn = l + 1 < model->n_layers ? layers[l + 1].input_norm : nullptr;
+    st = layer_entry(model, &layers[l], l, h, ple_in, kv, n_kv, pos, B, T, mode, ws, ws_bytes, stream, l > 0, nn);
+    if (st != G4_OK) return st;
+  }
+  return G4_OK;
+}
+
+}  // extern "C"

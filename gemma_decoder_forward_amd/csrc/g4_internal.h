@@ -1,0 +1,139 @@
+// Internal declarations of the g4 library: element types, wave/block reductions, launch helpers.
+// Every kernel of the library is written for gfx950 (CDNA4): 64-lane wavefronts.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/g4.h"
+
+namespace g4 {
+
+// bf16 stored as raw bits; arithmetic is always float32.
+typedef uint16_t bf16;
+
+__device__ __forceinline__ float bf2f(bf16 v) { return __uint_as_float((uint32_t)v << 16); }
+
+// Round to nearest even (NaN stays NaN).
+__device__ __forceinline__ bf16 f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16)0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16)(u >> 16);
+}
+
+template <typename T> struct io;
+template <> struct io<float> {
+  static __device__ __forceinline__ float ld(const float* p) { return *p; }
+  static __device__ __forceinline__ void st(float* p, float v) { *p = v; }
+};
+template <> struct io<bf16> {
+  static __device__ __forceinline__ float ld(const bf16* p) { return bf2f(*p); }
+  static __device__ __forceinline__ void st(bf16* p, float v) { *p = f2bf(v); }
+};
+template <typename T> __device__ __forceinline__ float ldf(const T* p) { return io<T>::ld(p); }
+template <typename T> __device__ __forceinline__ void stf(T* p, float v) { io<T>::st(p, v); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// Sum over a block of NT threads (NT multiple of 64, <= 1024). `sh` holds >= 17 floats.
+template <int NT>
+__device__ __forceinline__ float block_sum(float v, float* sh) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  if (l == 0) sh[w] = v;
+  __syncthreads();
+  if (w == 0) {
+    float t = (l < NT / 64) ? sh[l] : 0.f;
+    t = wave_sum(t);
+    if (l == 0) sh[16] = t;
+  }
+  __syncthreads();
+  float r = sh[16];
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ float gelu_tanh(float x) {
+  // 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))
+  const float u = 0.7978845608028654f * (x + 0.044715f * x * x * x);
+  return 0.5f * x * (1.f + tanhf(u));
+}
+
+inline size_t dsize(int32_t dt) { return dt == G4_BF16 ? 2 : 4; }
+
+// ---- error state (g4_api.cpp) ------------------------------------------------------------------
+g4_status fail(g4_status st, const char* fmt, ...);
+g4_status check_launch(const char* what);
+
+// ---- GEMM epilogues --------------------------------------------------------------------------
+enum Epi : int {
+  EPI_STORE = 0,     // C = acc (C in c_dtype)
+  EPI_GEGLU = 1,     // dual B (gate, up): C = gelu_tanh(acc_gate) * acc_up, C in dtype
+  EPI_GELU_MUL = 2,  // C = gelu_tanh(acc) * aux[m*aux_ld + n], aux float32, C in dtype
+};
+
+struct GemmArgs {
+  const void* A; int64_t lda;
+  const void* B; const void* B2; int64_t ldb;  // B2: the `up` matrix of EPI_GEGLU
+  void* C; int64_t ldc; int32_t c_dtype;
+  const float* aux; int64_t aux_ld;
+  int64_t M, N, K;
+  int32_t epi;
+  int32_t splits;        // split-K slices (EPI_STORE with f32 C only): slice s at C + s*split_stride
+  int64_t split_stride;  // elements between slices
+};
+
+// Launchers (return G4_OK or a failure with the message set).
+g4_status gemm(const GemmArgs& a, int32_t dtype, hipStream_t s);
+// Smallest ws bytes gemm() might use for these sizes (0 today: no internal scratch).
+size_t gemm_ws(int64_t M, int64_t N, int64_t K, int32_t dtype);
+
+struct HeadSeg {
+  const void* x; int64_t x_ld;
+  const void* w;           // per-head norm weight or nullptr
+  void* y; int64_t y_ld; int64_t y_cap;
+  int32_t heads; int32_t rope;
+};
+g4_status qk_norm_rope(const HeadSeg* segs, int nseg, const int32_t* pos, int64_t B, int64_t T,
+                       int64_t hd, float theta, int64_t n_rot, float eps, int32_t dtype,
+                       hipStream_t s);
+
+g4_status rownorm(const void* x, int32_t x_dtype, int32_t x_parts, int64_t part_stride,
+                  const void* w, void* y, float* res, float res_scale, const void* w_next,
+                  void* y_next, int64_t rows, int64_t dim, float eps, int32_t dtype,
+                  hipStream_t s);
+
+struct AttnArgs {
+  const void* q; int64_t q_ld;
+  const void* k; const void* v; int64_t cap;
+  const int32_t* pos0;
+  int64_t B, T, nh, nkv, hd;
+  int32_t sliding; int64_t window;
+  float scale;
+  void* out; int64_t out_ld;
+};
+g4_status attn_prefill(const AttnArgs& a, int32_t dtype, hipStream_t s);
+g4_status attn_decode(const AttnArgs& a, void* ws, size_t ws_bytes, int32_t dtype, hipStream_t s);
+size_t attn_decode_ws(int64_t B, int64_t nh, int64_t hd, int64_t cap);
+
+g4_status cast_rows(const float* x, void* y, int64_t n, int32_t dtype, hipStream_t s);
+g4_status gemm_simt(const GemmArgs& a, int32_t dtype, hipStream_t s);
+g4_status attn_rowwise(const AttnArgs& a, int32_t dtype, hipStream_t s);
+g4_status embed_rows(const int32_t* ids, int64_t M, const void* E, int64_t vocab, int64_t H,
+                     float* h_out, void* e_cast, int32_t dtype, hipStream_t s);
+g4_status ple_combine(const int32_t* ids, int64_t M, const float* P, const void* Tab,
+                      int64_t ple_vocab, const void* ple_norm, int64_t H, int64_t L, int64_t d,
+                      float eps, float* ple_out, int32_t dtype, hipStream_t s);
+
+}  // namespace g4

@@ -1,0 +1,310 @@
+// Row kernels: the fused RMSNorm residual tail, per-head norm + NeoX RoPE (into a cache slot or in
+// place), the scaled embedding gather and the per-layer-input combination.
+//
+// Every one is HBM-bound: one pass over its rows, 16-byte-friendly contiguous access along the row,
+// float32 arithmetic, block or wave reductions with cross-lane shuffles.
+#include "g4_internal.h"
+
+namespace g4 {
+
+// --------------------------------------------------------------------------------------------
+// Fused RMSNorm tail (cortiq-engine `rms`/`rms_plain` and the sandwich residual adds of `g4e_forward`).
+// One 256-thread block per row; values stay in registers between the two reductions.
+// --------------------------------------------------------------------------------------------
+template <typename TX, typename T, int VPT>
+__global__ __launch_bounds__(256) void k_rownorm(const TX* __restrict__ x, int parts, int64_t part_stride,
+                                                 const T* __restrict__ w, T* __restrict__ y,
+                                                 float* __restrict__ res, float res_scale,
+                                                 const T* __restrict__ w_next, T* __restrict__ y_next,
+                                                 int64_t dim, float eps) {
+  __shared__ float sh[32];
+  const int64_t row = blockIdx.x;
+  const TX* xr = x + row * dim;
+  float v[VPT];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int64_t c = threadIdx.x + (int64_t)i * 256;
+    float s = 0.f;
+    if (c < dim) {
+      for (int p = 0; p < parts; ++p) s += ldf(xr + p * part_stride + c);
+    }
+    v[i] = s;
+    ss += s * s;
+  }
+  ss = block_sum<256>(ss, sh);
+  const float inv = 1.f / sqrtf(ss / (float)dim + eps);
+  float ss2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int64_t c = threadIdx.x + (int64_t)i * 256;
+    if (c < dim) {
+      float n = v[i] * inv;
+      if (w) n *= ldf(w + c);
+      if (y) stf(y + row * dim + c, n);
+      if (res) {
+        const float r = (res[row * dim + c] + n) * res_scale;
+        res[row * dim + c] = r;
+        v[i] = r;
+        ss2 += r * r;
+      }
+    }
+  }
+  if (y_next) {
+    float inv2 = 1.f;
+    if (w_next) {
+      ss2 = block_sum<256>(ss2, sh);
+      inv2 = 1.f / sqrtf(ss2 / (float)dim + eps);
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int64_t c = threadIdx.x + (int64_t)i * 256;
+      if (c < dim) stf(y_next + row * dim + c, w_next ? v[i] * inv2 * ldf(w_next + c) : v[i]);
+    }
+  }
+}
+
+template <typename TX, typename T>
+static void launch_rownorm(int vpt, dim3 g, hipStream_t s, const TX* x, int parts, int64_t ps,
+                           const T* w, T* y, float* res, float rs, const T* wn, T* yn, int64_t dim,
+                           float eps) {
+#define G4_RN(V) \
+  hipLaunchKernelGGL((k_rownorm<TX, T, V>), g, dim3(256), 0, s, x, parts, ps, w, y, res, rs, wn, yn, dim, eps)
+  if (vpt <= 1) G4_RN(1);
+  else if (vpt <= 2) G4_RN(2);
+  else if (vpt <= 4) G4_RN(4);
+  else if (vpt <= 8) G4_RN(8);
+  else if (vpt <= 12) G4_RN(12);
+  else if (vpt <= 16) G4_RN(16);
+  else if (vpt <= 32) G4_RN(32);
+  else G4_RN(64);
+#undef G4_RN
+}
+
+g4_status rownorm(const void* x, int32_t x_dtype, int32_t x_parts, int64_t part_stride,
+                  const void* w, void* y, float* res, float res_scale, const void* w_next,
+                  void* y_next, int64_t rows, int64_t dim, float eps, int32_t dtype, hipStream_t s) {
+  if (rows == 0) return G4_OK;
+  if (dim > 64 * 256) return fail(G4_ERANGE, "rmsnorm: dim %lld exceeds 16384", (long long)dim);
+  const int vpt = (int)((dim + 255) / 256);
+  dim3 g((unsigned)rows);
+  if (dtype == G4_BF16) {
+    if (x_dtype == G4_F32)
+      launch_rownorm<float, bf16>(vpt, g, s, (const float*)x, x_parts, part_stride, (const bf16*)w, (bf16*)y,
+                                  res, res_scale, (const bf16*)w_next, (bf16*)y_next, dim, eps);
+    else
+      launch_rownorm<bf16, bf16>(vpt, g, s, (const bf16*)x, x_parts, part_stride, (const bf16*)w, (bf16*)y,
+                                 res, res_scale, (const bf16*)w_next, (bf16*)y_next, dim, eps);
+  } else {
+    launch_rownorm<float, float>(vpt, g, s, (const float*)x, x_parts, part_stride, (const float*)w, (float*)y,
+                                 res, res_scale, (const float*)w_next, (float*)y_next, dim, eps);
+  }
+  return check_launch("rmsnorm");
+}
+
+// --------------------------------------------------------------------------------------------
+// Per-head RMSNorm + NeoX RoPE (cortiq-engine q/k/v head loops; turbospark per-head norms and
+// `encode_rope_proportional_neox`; taconite `rope_half`). One block per token row; the cos/sin of the
+// row's position are computed once in float64 into LDS and shared by every head of every segment.
+// Pair j of a head pairs elements j and j + hd/2; pairs j >= n_rot are left untouched (zero frequency).
+// --------------------------------------------------------------------------------------------
+struct SegDev {
+  const void* x; int64_t x_ld;
+  const void* w;
+  void* y; int64_t y_ld; int64_t y_cap;
+  int32_t heads; int32_t rope;
+};
+struct SegPack { SegDev s[3]; int n; int total_heads; };
+
+template <typename T, int PPL>  // PPL: pairs per lane (hd/2 <= 64*PPL)
+__global__ __launch_bounds__(256) void k_qknr(SegPack pk, const int32_t* __restrict__ pos, int64_t T_,
+                                              int hd, float theta, int n_rot, float eps) {
+  __shared__ float cs[256], sn[256];
+  const int64_t m = blockIdx.x;
+  const int64_t b = m / T_, t = m % T_;
+  const int64_t p = pos ? (int64_t)pos[b] + t : 0;
+  const int half = hd >> 1;
+  for (int j = threadIdx.x; j < n_rot; j += 256) {
+    const double inv = pow((double)theta, -2.0 * (double)j / (double)hd);
+    double sv, cv;
+    sincos((double)p * inv, &sv, &cv);
+    cs[j] = (float)cv;
+    sn[j] = (float)sv;
+  }
+  __syncthreads();
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int gh = wave; gh < pk.total_heads; gh += 4) {
+    int si = 0, h = gh;
+    while (si < pk.n - 1 && h >= pk.s[si].heads) { h -= pk.s[si].heads; ++si; }
+    const SegDev& sg = pk.s[si];
+    const T* xh = (const T*)sg.x + m * sg.x_ld + (int64_t)h * hd;
+    float a[PPL], c[PPL];
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < PPL; ++i) {
+      const int j = lane + 64 * i;
+      a[i] = c[i] = 0.f;
+      if (j < half) { a[i] = ldf(xh + j); c[i] = ldf(xh + j + half); }
+      ss += a[i] * a[i] + c[i] * c[i];
+    }
+    ss = wave_sum(ss);
+    const float inv = 1.f / sqrtf(ss / (float)hd + eps);
+    T* yh;
+    if (sg.y_cap > 0) {
+      if (p < 0 || p >= sg.y_cap) continue;  // out-of-range position: no write
+      yh = (T*)sg.y + (((b * sg.heads + h) * sg.y_cap) + p) * hd;
+    } else {
+      yh = (T*)sg.y + m * sg.y_ld + (int64_t)h * hd;
+    }
+    const T* wv = (const T*)sg.w;
+#pragma unroll
+    for (int i = 0; i < PPL; ++i) {
+      const int j = lane + 64 * i;
+      if (j >= half) continue;
+      float u = a[i] * inv, v = c[i] * inv;
+      if (wv) { u *= ldf(wv + j); v *= ldf(wv + j + half); }
+      if (sg.rope && j < n_rot) {
+        const float co = cs[j], si2 = sn[j];
+        const float u2 = u * co - v * si2;
+        const float v2 = v * co + u * si2;
+        u = u2; v = v2;
+      }
+      stf(yh + j, u);
+      stf(yh + j + half, v);
+    }
+  }
+}
+
+g4_status qk_norm_rope(const HeadSeg* segs, int nseg, const int32_t* pos, int64_t B, int64_t T,
+                       int64_t hd, float theta, int64_t n_rot, float eps, int32_t dtype, hipStream_t s) {
+  if (B * T == 0) return G4_OK;
+  if (hd > 512 || hd < 2 || (hd & 1)) return fail(G4_ERANGE, "qk_norm_rope: head_dim %lld not in [2, 512]", (long long)hd);
+  SegPack pk{};
+  pk.n = nseg;
+  pk.total_heads = 0;
+  int any_rope = 0;
+  for (int i = 0; i < nseg; ++i) {
+    pk.s[i] = SegDev{segs[i].x, segs[i].x_ld, segs[i].w, segs[i].y, segs[i].y_ld, segs[i].y_cap,
+                     segs[i].heads, segs[i].rope};
+    pk.total_heads += segs[i].heads;
+    any_rope |= segs[i].rope;
+  }
+  const int nr = any_rope ? (int)n_rot : 0;
+  dim3 g((unsigned)(B * T));
+  const int ppl = (int)((hd / 2 + 63) / 64);
+#define G4_QK(TT, P) hipLaunchKernelGGL((k_qknr<TT, P>), g, dim3(256), 0, s, pk, pos, T, (int)hd, theta, nr, eps)
+  if (dtype == G4_BF16) {
+    if (ppl <= 1) G4_QK(bf16, 1); else if (ppl <= 2) G4_QK(bf16, 2); else G4_QK(bf16, 4);
+  } else {
+    if (ppl <= 1) G4_QK(float, 1); else if (ppl <= 2) G4_QK(float, 2); else G4_QK(float, 4);
+  }
+#undef G4_QK
+  return check_launch("qk_norm_rope");
+}
+
+// --------------------------------------------------------------------------------------------
+// Scaled embedding gather (ferrox `forward_token_on_worker`: row times sqrt(H)); ids outside
+// [0, vocab) give a zero row. Also writes the row in the model dtype for the PLE projection GEMM.
+// --------------------------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void k_embed(const int32_t* __restrict__ ids, const T* __restrict__ E,
+                                               int64_t vocab, int64_t H, float scale, float* __restrict__ h,
+                                               T* __restrict__ ecast) {
+  const int64_t m = blockIdx.x;
+  const int64_t id = ids[m];
+  const bool ok = id >= 0 && id < vocab;
+  for (int64_t c = threadIdx.x; c < H; c += 256) {
+    const float v = ok ? ldf(E + id * H + c) * scale : 0.f;
+    h[m * H + c] = v;
+    if (ecast) stf(ecast + m * H + c, v);
+  }
+}
+
+g4_status embed_rows(const int32_t* ids, int64_t M, const void* E, int64_t vocab, int64_t H,
+                     float* h_out, void* e_cast, int32_t dtype, hipStream_t s) {
+  if (M == 0) return G4_OK;
+  const float scale = sqrtf((float)H);
+  if (dtype == G4_BF16)
+    hipLaunchKernelGGL(k_embed<bf16>, dim3((unsigned)M), dim3(256), 0, s, ids, (const bf16*)E, vocab, H, scale,
+                       h_out, (bf16*)e_cast);
+  else
+    hipLaunchKernelGGL(k_embed<float>, dim3((unsigned)M), dim3(256), 0, s, ids, (const float*)E, vocab, H, scale,
+                       h_out, (float*)e_cast);
+  return check_launch("embed");
+}
+
+// --------------------------------------------------------------------------------------------
+// Per-layer inputs from the projected embedding (cortiq-engine `extend_embedding`, ferrox
+// `project_per_layer_inputs`): per (token, layer) chunk of d values,
+//   (rms(P * H^-1/2) * ple_norm + sqrt(d) * Tab[id, chunk]) / sqrt(2).
+// One wave per chunk, d <= 512.
+// --------------------------------------------------------------------------------------------
+template <typename T, int PER>
+__global__ __launch_bounds__(256) void k_ple_combine(const int32_t* __restrict__ ids, const float* __restrict__ P,
+                                                     const T* __restrict__ Tab, int64_t ple_vocab,
+                                                     const T* __restrict__ norm, int64_t L, int d,
+                                                     float pscale, float eps, float* __restrict__ out) {
+  const int64_t m = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t id = ids[m];
+  const bool ok = id >= 0 && id < ple_vocab;
+  const float tscale = sqrtf((float)d);
+  const float half = 0.70710678118654752f;
+  for (int64_t l = blockIdx.y * 4 + wave; l < L; l += (int64_t)gridDim.y * 4) {
+    const float* pr = P + (m * L + l) * d;
+    float v[PER];
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int j = lane + 64 * i;
+      v[i] = j < d ? pr[j] * pscale : 0.f;
+      ss += v[i] * v[i];
+    }
+    ss = wave_sum(ss);
+    const float inv = 1.f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int j = lane + 64 * i;
+      if (j >= d) continue;
+      float r = v[i] * inv * ldf(norm + j);
+      if (ok) r += ldf(Tab + id * (L * d) + l * d + j) * tscale;
+      out[(m * L + l) * d + j] = r * half;
+    }
+  }
+}
+
+g4_status ple_combine(const int32_t* ids, int64_t M, const float* P, const void* Tab, int64_t ple_vocab,
+                      const void* ple_norm, int64_t H, int64_t L, int64_t d, float eps, float* ple_out,
+                      int32_t dtype, hipStream_t s) {
+  if (M == 0) return G4_OK;
+  if (d > 512) return fail(G4_ERANGE, "ple_dim %lld exceeds 512", (long long)d);
+  const float pscale = 1.f / sqrtf((float)H);
+  dim3 g((unsigned)M, (unsigned)((L + 3) / 4));
+  const int per = (int)((d + 63) / 64);
+#define G4_PC(TT, P) hipLaunchKernelGGL((k_ple_combine<TT, P>), g, dim3(256), 0, s, ids, P_, (const TT*)Tab, ple_vocab, (const TT*)ple_norm, L, (int)d, pscale, eps, ple_out)
+  const float* P_ = P;
+  if (dtype == G4_BF16) {
+    if (per <= 1) G4_PC(bf16, 1); else if (per <= 4) G4_PC(bf16, 4); else G4_PC(bf16, 8);
+  } else {
+    if (per <= 1) G4_PC(float, 1); else if (per <= 4) G4_PC(float, 4); else G4_PC(float, 8);
+  }
+#undef G4_PC
+  return check_launch("ple_combine");
+}
+
+}  // namespace g4
+
+namespace g4 {
+template <typename T>
+__global__ __launch_bounds__(256) void k_cast(const float* __restrict__ x, T* __restrict__ y, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) stf(y + i, x[i]);
+}
+g4_status cast_rows(const float* x, void* y, int64_t n, int32_t dtype, hipStream_t s) {
+  if (n == 0) return G4_OK;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (dtype == G4_BF16) hipLaunchKernelGGL(k_cast<bf16>, dim3((unsigned)blocks), dim3(256), 0, s, x, (bf16*)y, n);
+  else hipLaunchKernelGGL(k_cast<float>, dim3((unsigned)blocks), dim3(256), 0, s, x, (float*)y, n);
+  return check_launch("cast");
+}
+}  // namespace g4

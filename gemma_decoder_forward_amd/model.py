@@ -1,0 +1,111 @@
+"""Model-level driver over libg4.so: descriptors, KV caches, workspace, prefill and decode calls.
+
+PyTorch supplies device memory and the stream; every step of the forward runs in the library.
+"""
+import ctypes as C
+
+import torch
+
+from . import binding as bd
+
+DTYPES = {"f32": (bd.G4_F32, torch.float32), "bf16": (bd.G4_BF16, torch.bfloat16)}
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+class G4Model:
+    """A Gemma-4 E-series text stack resident on one GPU.
+
+    cfg: a workload dict (hidden, n_heads, ..., layer_types "S"/"F" per layer, n_shared, dtype).
+    layers: list of per-layer dicts of device tensors (names as in g4_layer_desc).
+    glob: optional dict with embed, ple_embed, ple_model_proj, ple_norm (device tensors).
+    """
+
+    def __init__(self, cfg, layers, glob=None):
+        self.cfg = cfg
+        self.g4_dtype, self.torch_dtype = DTYPES[cfg["dtype"]]
+        L = len(cfg["layer_types"])
+        self.L = L
+        self.desc = bd.ModelDesc(
+            hidden=cfg["hidden"], n_heads=cfg["n_heads"], n_kv_heads=cfg["n_kv_heads"],
+            head_dim_swa=cfg["head_dim_swa"], head_dim_full=cfg["head_dim_full"], ffn=cfg["ffn"],
+            ple_dim=cfg["ple_dim"], n_layers=L, window=cfg["window"], vocab=cfg.get("vocab", 1),
+            ple_vocab=cfg.get("ple_vocab", 1), eps=cfg["eps"], theta_swa=cfg["theta_swa"],
+            theta_full=cfg["theta_full"], partial_rotary=cfg["partial_rotary"], dtype=self.g4_dtype)
+        self.sliding = [1 if t == "S" else 0 for t in cfg["layer_types"]]
+        self.kv_src = bd.g4_kv_sources(self.sliding, cfg["n_shared"])
+        self.layers = layers
+        self.glob = glob
+        self.descs = (bd.LayerDesc * L)()
+        for l, lw in enumerate(layers):
+            d = self.descs[l]
+            d.sliding = self.sliding[l]
+            d.kv_src = self.kv_src[l]
+            d.layer_scalar = float(lw.get("layer_scalar", 1.0))
+            own = self.kv_src[l] == l
+            for name in bd.LAYER_PTRS:
+                t = lw.get(name)
+                if name in ("wk", "wv", "k_norm") and not own:
+                    t = None
+                setattr(d, name, _ptr(t))
+        self._ws = None
+
+    def head_dim(self, l):
+        return self.cfg["head_dim_swa"] if self.sliding[l] else self.cfg["head_dim_full"]
+
+    def new_caches(self, B, cap, fill=None):
+        """Device K/V caches [B, nkv, cap, hd] for every owning layer, plus the C table."""
+        caches = {}
+        table = (bd.KvEntry * self.L)()
+        for l in range(self.L):
+            if self.kv_src[l] != l:
+                continue
+            hd = self.head_dim(l)
+            if fill is not None:
+                k, v = fill(l)
+            else:
+                k = torch.zeros((B, self.cfg["n_kv_heads"], cap, hd), dtype=self.torch_dtype, device="cuda")
+                v = torch.zeros_like(k)
+            caches[l] = (k, v)
+            table[l] = bd.KvEntry(k=k.data_ptr(), v=v.data_ptr(), cap=cap, hd=hd, sliding=self.sliding[l])
+        return caches, table
+
+    def workspace(self, B, T, cap, mode):
+        need = bd.g4_workspace_size(self.desc, B, T, cap, mode)
+        if need == 0:
+            raise RuntimeError("invalid model descriptor")
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        return self._ws
+
+    def embed(self, ids):
+        """ids int32 [B, T] (device) -> (h0 float32 [B, T, H], ple_in float32 [B, T, L, d])."""
+        B, T = ids.shape
+        M = B * T
+        H, L, d = self.cfg["hidden"], self.L, self.cfg["ple_dim"]
+        h = torch.empty((B, T, H), dtype=torch.float32, device="cuda")
+        ple = torch.empty((B, T, L, d), dtype=torch.float32, device="cuda")
+        ws = self.workspace(B, T, 1, bd.G4_PREFILL)
+        g = self.glob
+        bd.g4_embed_ple(ids.data_ptr(), M, g["embed"].data_ptr(), g["ple_embed"].data_ptr(),
+                        g["ple_model_proj"].data_ptr(), g["ple_norm"].data_ptr(), self.desc, h.data_ptr(),
+                        ple.data_ptr(), ws.data_ptr(), ws.numel(), _stream())
+        return h, ple
+
+    def forward(self, h, ple_in, pos, table, cap, mode=bd.G4_PREFILL, layer=None):
+        """Run all layers (or one, if `layer` is given) in place on h [B, T, H] float32."""
+        B, T = h.shape[0], h.shape[1]
+        ws = self.workspace(B, T, cap, mode)
+        if layer is None:
+            bd.g4_stack_forward(self.desc, self.descs, h.data_ptr(), ple_in.data_ptr(), table, self.L, pos.data_ptr(),
+                                B, T, mode, ws.data_ptr(), ws.numel(), _stream())
+        else:
+            bd.g4_layer_forward(self.desc, self.descs[layer], layer, h.data_ptr(), ple_in.data_ptr(), table, self.L,
+                                pos.data_ptr(), B, T, mode, ws.data_ptr(), ws.numel(), _stream())
+        return h

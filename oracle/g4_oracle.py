@@ -282,6 +282,46 @@ def layer_forward(cfg, lw, layer, src, h, ple_l, pos, caches, trace=None):
     return h
 
 
+def layer_forward_rows(cfg, lw, layer, h, ple_l, pos0, rows):
+    """Selected output rows of one cache-owning layer over a prefill of one sequence.
+
+    h [T, H] is the layer's input for tokens at positions pos0 .. pos0+T-1 (nothing cached before pos0),
+    ple_l [T, d]. Only the K/V rows the selected queries can see are formed, so a long sequence can be
+    checked at a few rows. Same formulas as `layer_forward`, restricted to rows.
+    """
+    eps = cfg["eps"]
+    nh, nkv = cfg["n_heads"], cfg["n_kv_heads"]
+    sliding, hd, theta, n_rot = layer_geometry(cfg, layer)
+    inv = inv_freq(hd, theta, n_rot)
+    h = f64(h)
+    rows = np.asarray(sorted(set(int(r) for r in rows)))
+    W = cfg["window"]
+    need = set()
+    for r in rows:
+        lo = max(0, r - W + 1) if sliding else 0
+        need.update(range(lo, r + 1))
+    need = np.asarray(sorted(need))
+    xk = rms_norm(h[need], lw["input_norm"], eps)
+    pk = (pos0 + need)[:, None]
+    k = rope(rms_norm((xk @ f64(lw["wk"]).T).reshape(len(need), nkv, hd), lw["k_norm"], eps), pk, inv)
+    v = rms_norm((xk @ f64(lw["wv"]).T).reshape(len(need), nkv, hd), None, eps)
+    cap = pos0 + int(rows.max()) + 1
+    K, V = np.zeros((nkv, cap, hd)), np.zeros((nkv, cap, hd))
+    K[:, pos0 + need, :] = k.transpose(1, 0, 2)
+    V[:, pos0 + need, :] = v.transpose(1, 0, 2)
+    hr = h[rows]
+    xn = rms_norm(hr, lw["input_norm"], eps)
+    q = rope(rms_norm((xn @ f64(lw["wq"]).T).reshape(len(rows), nh, hd), lw["q_norm"], eps), (pos0 + rows)[:, None], inv)
+    o = attention(q, K, V, pos0 + rows, W if sliding else None)
+    hr = hr + rms_norm(o.reshape(len(rows), nh * hd) @ f64(lw["wo"]).T, lw["post_attn_norm"], eps)
+    xn2 = rms_norm(hr, lw["pre_ffn_norm"], eps)
+    act = gelu_tanh(xn2 @ f64(lw["w_gate"]).T) * (xn2 @ f64(lw["w_up"]).T)
+    hr = hr + rms_norm(act @ f64(lw["w_down"]).T, lw["post_ffn_norm"], eps)
+    g = gelu_tanh(hr @ f64(lw["ple_gate"]).T) * f64(ple_l)[rows]
+    hr = hr + rms_norm(g @ f64(lw["ple_proj"]).T, lw["post_ple_norm"], eps)
+    return rows, hr * float(lw.get("layer_scalar", 1.0))
+
+
 # --------------------------------------------------------------------------------------------
 # Stack
 # --------------------------------------------------------------------------------------------

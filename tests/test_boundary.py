@@ -1,0 +1,134 @@
+"""C-ABI boundary on the host (no GPU): the library loads, exports every declared symbol, routes
+shared-KV layers exactly like the oracle, and rejects bad arguments before launching anything."""
+import ctypes as C
+import os
+import random
+import re
+
+import pytest
+
+import oracle as O
+from gemma_decoder_forward_amd import binding as bd
+from synth import configs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "g4.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(g4_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    L = bd.lib()
+    names = _declared()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in g4.h but not exported"
+    assert set(names) == set(bd.exported_names())
+
+
+def test_version_and_status_strings():
+    assert bd.lib().g4_version() >= 100
+    assert bd.lib().g4_status_str(bd.G4_EGEOM) == b"G4_EGEOM"
+
+
+@pytest.mark.parametrize("cid", [1, 3, 5])
+def test_routing_matches_oracle_on_configs(cid):
+    c = configs.get(cid)
+    sliding = [1 if t == "S" else 0 for t in c["layer_types"]]
+    assert bd.g4_kv_sources(sliding, c["n_shared"]) == O.kv_sources(c["layer_types"], c["n_shared"])
+
+
+def test_routing_matches_oracle_on_random_patterns():
+    rnd = random.Random(3)
+    for _ in range(300):
+        L = rnd.randint(1, 24)
+        types = "".join(rnd.choice("SF") for _ in range(L))
+        ns = rnd.randint(0, L)
+        assert bd.g4_kv_sources([1 if t == "S" else 0 for t in types], ns) == O.kv_sources(types, ns)
+
+
+def _model(**kw):
+    c = dict(configs.get(2), **kw)
+    return bd.ModelDesc(hidden=c["hidden"], n_heads=c["n_heads"], n_kv_heads=c["n_kv_heads"],
+                        head_dim_swa=c["head_dim_swa"], head_dim_full=c["head_dim_full"], ffn=c["ffn"],
+                        ple_dim=c["ple_dim"], n_layers=2, window=c["window"], vocab=c["vocab"],
+                        ple_vocab=c["ple_vocab"], eps=c["eps"], theta_swa=c["theta_swa"],
+                        theta_full=c["theta_full"], partial_rotary=c["partial_rotary"], dtype=bd.G4_BF16)
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation on the host
+
+
+def _table(entries):
+    t = (bd.KvEntry * len(entries))()
+    for i, e in enumerate(entries):
+        if e is not None:
+            t[i] = bd.KvEntry(k=FAKE, v=FAKE, cap=e[0], hd=e[1], sliding=e[2])
+    return t
+
+
+def _attn(table, layer, kv_src, sliding, hd, T=8, window=512, nh=8, nkv=2, q=FAKE):
+    return bd.lib().g4_attn_prefill(q, nh * hd, table, len(table), layer, kv_src, sliding, window, FAKE, 1, T, nh,
+                                    nkv, hd, 1.0, FAKE, nh * hd, bd.G4_BF16, None)
+
+
+def test_attention_validation_errors():
+    t = _table([(64, 256, 1), (64, 512, 0), None])
+    assert _attn(t, 2, 3, 1, 256) == bd.G4_EGEOM      # kv_src after the layer
+    assert _attn(t, 2, 2, 1, 256) == bd.G4_EGEOM      # source is a hole (shared layer)
+    assert _attn(t, 2, 1, 1, 512) == bd.G4_EGEOM      # sliding layer reading a full cache
+    assert _attn(t, 2, 0, 1, 512) == bd.G4_EGEOM      # head-dim mismatch
+    assert _attn(t, 2, 0, 1, 256, T=65) == bd.G4_ERANGE  # T beyond capacity
+    assert _attn(t, 2, 0, 1, 256, window=0) == bd.G4_ERANGE
+    assert _attn(t, 2, 0, 1, 256, nh=6, nkv=4) == bd.G4_EGEOM
+    assert _attn(t, 2, 0, 1, 256, q=None) == bd.G4_EINVAL
+    assert _attn(t, 7, 0, 1, 256) == bd.G4_EINVAL     # layer outside the table
+    assert b"head_dim" in bd.lib().g4_last_error() or bd.lib().g4_last_error()
+
+
+def test_layer_validation_errors():
+    m = _model()
+    ld = bd.LayerDesc(sliding=1, kv_src=0, layer_scalar=1.0)
+    for n in bd.LAYER_PTRS:
+        setattr(ld, n, FAKE)
+    t = _table([(64, 256, 1), (64, 512, 0)])
+    L = bd.lib()
+
+    def call(layer=0, T=8, B=1, mode=bd.G4_PREFILL, ws_bytes=1 << 40, model=m, desc=ld, table=t):
+        return L.g4_layer_forward(C.byref(model), C.byref(desc), layer, FAKE, FAKE, table, len(table), FAKE, B, T,
+                                  mode, FAKE, ws_bytes, None)
+
+    assert call(ws_bytes=10) == bd.G4_EINVAL          # workspace too small
+    assert call(T=2, mode=bd.G4_DECODE) == bd.G4_EINVAL
+    assert call(T=100) == bd.G4_ERANGE
+    bad = bd.LayerDesc.from_buffer_copy(ld)
+    bad.wk = None
+    assert call(desc=bad) == bd.G4_EINVAL             # owning layer without wk
+    bad2 = bd.LayerDesc.from_buffer_copy(ld)
+    bad2.kv_src = 1
+    assert call(desc=bad2) == bd.G4_EGEOM             # later layer as source
+    m2 = _model(n_kv_heads=3)
+    assert call(model=m2) == bd.G4_EGEOM
+    m3 = _model()
+    m3.dtype = 7
+    assert call(model=m3) == bd.G4_EINVAL
+    assert bd.g4_workspace_size(m, 1, 2048, 2048, bd.G4_PREFILL) > 0
+    assert bd.g4_workspace_size(m3, 1, 2048, 2048, bd.G4_PREFILL) == 0
+
+
+def test_row_op_validation_errors():
+    L = bd.lib()
+    assert L.g4_rmsnorm(None, 0, 1, None, FAKE, None, 1.0, None, None, 4, 16, 1e-6, 0, None) == bd.G4_EINVAL
+    assert L.g4_rmsnorm(FAKE, 0, 1, None, FAKE, None, 1.0, None, FAKE, 4, 16, 1e-6, 0, None) == bd.G4_EINVAL
+    assert L.g4_rmsnorm(FAKE, 0, 1, None, FAKE, None, 1.0, None, None, 4, 20000, 1e-6, 0, None) == bd.G4_ERANGE
+    assert L.g4_qk_norm_rope(FAKE, 256, None, FAKE, 256, 0, FAKE, 1, 4, 1, 257, 1e4, 0, 1e-6, 0, None) == bd.G4_EGEOM
+    assert L.g4_qk_norm_rope(FAKE, 256, None, FAKE, 256, 0, FAKE, 1, 4, 1, 256, 1e4, 129, 1e-6, 0, None) == bd.G4_ERANGE
+    assert L.g4_qk_norm_rope(FAKE, 256, None, FAKE, 256, 0, None, 1, 4, 1, 256, 1e4, 64, 1e-6, 0, None) == bd.G4_EINVAL
+    assert L.g4_qk_norm_rope(FAKE, 256, None, FAKE, 0, 3, FAKE, 1, 4, 1, 256, 1e4, 64, 1e-6, 0, None) == bd.G4_ERANGE
+    assert L.g4_linear(FAKE, FAKE, FAKE, 4, 0, 8, 0, 0, None, 0, None) == bd.G4_EINVAL
+    assert L.g4_linear(FAKE, FAKE, FAKE, 4, 8, 8, 1, 0, None, 0, None) == bd.G4_EINVAL
+    assert L.g4_ffn_geglu(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 8, FAKE, 1, 1, None) == bd.G4_EINVAL
+    assert L.g4_kv_sources(None, 3, 1, None) == bd.G4_EINVAL

@@ -1,0 +1,282 @@
+"""Per-export parity on the GPU: each g4_* entry point through the C ABI against the float64 oracle
+fed the same seeded inputs (bf16 inputs are compared as the exact bf16 values)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gemma_decoder_forward_amd import binding as bd
+from tests.gpu_util import DT, assert_close, log, max_rel, randn, rel_l2, stream
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------------------- rmsnorm
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("rows,dim,parts", [(37, 2560, 3), (5, 300, 1), (1, 64, 2), (0, 64, 1)])
+def test_rmsnorm_fused_tail(dt, rows, dim, parts):
+    log(f"rmsnorm {dt} rows={rows} dim={dim} parts={parts}")
+    gdt, tdt = DT[dt]
+    x = randn((parts, rows, dim), 1 + dim)
+    w = randn((dim,), 2, tdt, 0.1, 1.0)
+    wn = randn((dim,), 3, tdt, 0.1, 1.0)
+    res = randn((rows, dim), 4)
+    res0 = res.clone()
+    y = torch.empty((rows, dim), dtype=tdt, device="cuda")
+    yn = torch.empty_like(y)
+    bd.g4_rmsnorm(x.data_ptr(), bd.G4_F32, parts, w.data_ptr(), y.data_ptr(), res.data_ptr(), 0.75, wn.data_ptr(),
+                  yn.data_ptr(), rows, dim, 1e-6, gdt, stream())
+    torch.cuda.synchronize()
+    if rows == 0:  # empty input: a valid call that launches nothing, whatever the pointers
+        bd.g4_rmsnorm(None, bd.G4_F32, 1, None, None, None, 1.0, None, None, 0, dim, 1e-6, gdt, stream())
+        bd.g4_linear(None, None, None, 0, 8, 8, gdt, gdt, None, 0, stream())
+        return
+    n = O.rms_norm(O.f64(x).sum(0), w, 1e-6)
+    r = (O.f64(res0) + n) * 0.75
+    assert_close(y, n, dt, "y")
+    assert max_rel(res, r) <= 1e-5
+    assert_close(yn, O.rms_norm(r, wn, 1e-6), dt, "y_next")
+    # scale-less norm, copy-out of the residual
+    y2 = torch.empty((rows, dim), dtype=tdt, device="cuda")
+    res2 = res0.clone()
+    bd.g4_rmsnorm(x.data_ptr(), bd.G4_F32, parts, None, None, res2.data_ptr(), 1.0, None, y2.data_ptr(), rows, dim,
+                  1e-6, gdt, stream())
+    torch.cuda.synchronize()
+    r2 = O.f64(res0) + O.rms_norm(O.f64(x).sum(0), None, 1e-6)
+    assert max_rel(res2, r2) <= 1e-5
+    assert_close(y2, r2, dt, "copy")
+
+
+# ------------------------------------------------------------------------------- qk norm + rope
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("hd,theta,nrot", [(64, 1e4, 32), (128, 1e6, 16), (256, 1e4, 128), (512, 1e6, 64)])
+def test_qk_norm_rope_token_major_and_cache(dt, hd, theta, nrot):
+    log(f"qk_norm_rope {dt} hd={hd}")
+    gdt, tdt = DT[dt]
+    B, T, heads, cap = 2, 9, 3, 40
+    pos0 = torch.tensor([5, 23], dtype=torch.int32, device="cuda")
+    x = randn((B * T, heads * hd + 7), 10 + hd, tdt)  # padded leading dimension
+    ld = heads * hd + 7
+    w = randn((hd,), 11, tdt, 0.1, 1.0)
+    y = torch.empty((B * T, heads * hd), dtype=tdt, device="cuda")
+    bd.g4_qk_norm_rope(x.data_ptr(), ld, w.data_ptr(), y.data_ptr(), heads * hd, 0, pos0.data_ptr(), B, T, heads, hd,
+                       theta, nrot, 1e-6, gdt, stream())
+    sentinel = randn((B, heads, cap, hd), 12, tdt)
+    cache = sentinel.clone()
+    bd.g4_qk_norm_rope(x.data_ptr(), ld, w.data_ptr(), cache.data_ptr(), 0, cap, pos0.data_ptr(), B, T, heads, hd,
+                       theta, nrot, 1e-6, gdt, stream())
+    torch.cuda.synchronize()
+    xv = O.f64(x)[:, :heads * hd].reshape(B, T, heads, hd)
+    pos = O.prefill_positions([5, 23], T)
+    ref = O.rope(O.rms_norm(xv, w, 1e-6), pos[:, :, None], O.inv_freq(hd, theta, nrot))
+    assert_close(y.reshape(B, T, heads, hd), ref, dt, "token-major")
+    c = cache.cpu()
+    s = sentinel.cpu()
+    for b in range(B):
+        p0 = int(pos[b, 0])
+        written = c[b, :, p0:p0 + T, :]
+        assert_close(written.permute(1, 0, 2), ref[b], dt, "cache rows")
+        # every other row is bit-exactly untouched
+        assert torch.equal(c[b, :, :p0, :], s[b, :, :p0, :])
+        assert torch.equal(c[b, :, p0 + T:, :], s[b, :, p0 + T:, :])
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_rope_zero_frequency_tail_is_exact_identity(dt):
+    gdt, tdt = DT[dt]
+    hd, nrot, heads, T = 512, 64, 8, 33
+    pos0 = torch.tensor([31000], dtype=torch.int32, device="cuda")
+    x = randn((T, heads * hd), 20, tdt)
+    w = randn((hd,), 21, tdt, 0.1, 1.0)
+    a = torch.empty_like(x)
+    b = torch.empty_like(x)
+    bd.g4_qk_norm_rope(x.data_ptr(), heads * hd, w.data_ptr(), a.data_ptr(), heads * hd, 0, pos0.data_ptr(), 1, T,
+                       heads, hd, 1e6, nrot, 1e-6, gdt, stream())
+    bd.g4_qk_norm_rope(x.data_ptr(), heads * hd, w.data_ptr(), b.data_ptr(), heads * hd, 0, pos0.data_ptr(), 1, T,
+                       heads, hd, 1e6, 0, 1e-6, gdt, stream())
+    torch.cuda.synchronize()
+    a, b = a.view(T, heads, hd), b.view(T, heads, hd)
+    h = hd // 2
+    assert torch.equal(a[..., nrot:h], b[..., nrot:h]) and torch.equal(a[..., h + nrot:], b[..., h + nrot:])
+    assert not torch.equal(a[..., :nrot], b[..., :nrot])
+
+
+# ------------------------------------------------------------------------------- attention
+def _kv_table(entries):
+    t = (bd.KvEntry * len(entries))()
+    for i, e in enumerate(entries):
+        if e is not None:
+            k, v, sliding = e
+            t[i] = bd.KvEntry(k=k.data_ptr(), v=v.data_ptr(), cap=k.shape[2], hd=k.shape[3], sliding=sliding)
+    return t
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("hd,sliding,window,nh,nkv", [(64, 1, 32, 4, 1), (128, 0, 0, 4, 1), (256, 1, 512, 8, 2),
+                                                      (512, 0, 0, 8, 2), (256, 1, 7, 4, 2)])
+def test_attention_prefill_vs_oracle(dt, hd, sliding, window, nh, nkv):
+    log(f"attn_prefill {dt} hd={hd} sliding={sliding} W={window}")
+    gdt, tdt = DT[dt]
+    B, T, cap = 2, 77, 700
+    pos0_l = [0, 600]
+    pos0 = torch.tensor(pos0_l, dtype=torch.int32, device="cuda")
+    q = randn((B * T, nh * hd), 30 + hd, tdt)
+    K = randn((B, nkv, cap, hd), 31, tdt)
+    V = randn((B, nkv, cap, hd), 32, tdt)
+    out = torch.empty((B * T, nh * hd), dtype=tdt, device="cuda")
+    t = _kv_table([(K, V, sliding)])
+    bd.g4_attn_prefill(q.data_ptr(), nh * hd, t, 1, 0, 0, sliding, window, pos0.data_ptr(), B, T, nh, nkv, hd, 1.0,
+                       out.data_ptr(), nh * hd, gdt, stream())
+    torch.cuda.synchronize()
+    qv = O.f64(q).reshape(B, T, nh, hd)
+    pos = O.prefill_positions(pos0_l, T)
+    for b in range(B):
+        ref = O.attention(qv[b], O.f64(K[b]), O.f64(V[b]), pos[b], window if sliding else None)
+        assert_close(out.reshape(B, T, nh, hd)[b], ref, dt, f"seq {b}")
+
+
+@pytest.mark.parametrize("hd,sliding,window", [(64, 1, 7), (64, 0, 0), (256, 1, 33)])
+def test_attention_mask_probe_bit_exact(hd, sliding, window):
+    """q = 0 gives uniform weights; V_j = onehot(j mod hd) makes round(o * n) the mask row."""
+    T, nh, nkv = 64, 4, 1
+    q = torch.zeros((T, nh * hd), dtype=torch.bfloat16, device="cuda")
+    K = randn((1, nkv, T, hd), 40, torch.bfloat16)
+    Vh = torch.zeros((1, nkv, T, hd))
+    for j in range(T):
+        Vh[0, :, j, j % hd] = 1.0
+    V = Vh.to(torch.bfloat16).cuda()
+    pos0 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    t = _kv_table([(K, V, sliding)])
+    bd.g4_attn_prefill(q.data_ptr(), nh * hd, t, 1, 0, 0, sliding, window, pos0.data_ptr(), 1, T, nh, nkv, hd, 1.0,
+                       out.data_ptr(), nh * hd, bd.G4_BF16, stream())
+    torch.cuda.synchronize()
+    o = O.f64(out).reshape(T, nh, hd)
+    for i in range(T):
+        lo = max(0, i - window + 1) if sliding else 0
+        n = i - lo + 1
+        want = np.zeros(hd)
+        for j in range(lo, i + 1):
+            want[j % hd] += 1
+        for h in range(nh):
+            assert np.array_equal(np.rint(o[i, h] * n), want), (i, h)
+
+
+def test_attention_reads_kv_src_cache_without_copy():
+    """Caches filled with the constant layer+1: the output is exactly kv_src+1."""
+    hd, T, nh, nkv = 128, 16, 4, 1
+    caches = []
+    for l in range(4):
+        k = randn((1, nkv, 32, hd), 50 + l, torch.bfloat16)
+        v = torch.full((1, nkv, 32, hd), float(l + 1), dtype=torch.bfloat16, device="cuda")
+        caches.append((k, v, 0))
+    caches[2] = None  # a shared layer: a hole in the table
+    t = _kv_table(caches)
+    q = randn((T, nh * hd), 55, torch.bfloat16)
+    pos0 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for src in (0, 1, 3):
+        out = torch.empty_like(q)
+        bd.g4_attn_prefill(q.data_ptr(), nh * hd, t, 4, 3, src, 0, 0, pos0.data_ptr(), 1, T, nh, nkv, hd, 1.0,
+                           out.data_ptr(), nh * hd, bd.G4_BF16, stream())
+        torch.cuda.synchronize()
+        assert torch.all(out == float(src + 1))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("hd,sliding,window,nh,nkv", [(64, 1, 32, 4, 1), (512, 0, 0, 8, 2), (256, 1, 512, 8, 2),
+                                                      (128, 0, 0, 4, 2)])
+def test_attention_decode_vs_oracle(dt, hd, sliding, window, nh, nkv):
+    log(f"attn_decode {dt} hd={hd} sliding={sliding}")
+    gdt, tdt = DT[dt]
+    B, cap = 3, 1500
+    pos_l = [0, 700, 1499]
+    pos = torch.tensor(pos_l, dtype=torch.int32, device="cuda")
+    q = randn((B, nh * hd), 60 + hd, tdt)
+    K = randn((B, nkv, cap, hd), 61, tdt)
+    V = randn((B, nkv, cap, hd), 62, tdt)
+    out = torch.empty((B, nh * hd), dtype=tdt, device="cuda")
+    wsb = bd.g4_attn_decode_ws(B, nh, hd, cap)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    t = _kv_table([(K, V, sliding)])
+    bd.g4_attn_decode(q.data_ptr(), nh * hd, t, 1, 0, 0, sliding, window, pos.data_ptr(), B, nh, nkv, hd, 1.0,
+                      out.data_ptr(), nh * hd, ws.data_ptr(), wsb, gdt, stream())
+    torch.cuda.synchronize()
+    qv = O.f64(q).reshape(B, 1, nh, hd)
+    for b in range(B):
+        ref = O.attention(qv[b], O.f64(K[b]), O.f64(V[b]), [pos_l[b]], window if sliding else None)
+        assert_close(out.reshape(B, 1, nh, hd)[b], ref, dt, f"seq {b}")
+
+
+# ------------------------------------------------------------------------------- projections
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("M,N,K", [(77, 130, 200), (256, 512, 2560), (1, 256, 64), (300, 2560, 256)])
+def test_linear_vs_oracle(dt, M, N, K):
+    log(f"linear {dt} {M}x{N}x{K}")
+    gdt, tdt = DT[dt]
+    A = randn((M, K), 70, tdt)
+    W = randn((N, K), 71, tdt, 0.02)
+    C32 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    Cd = torch.empty((M, N), dtype=tdt, device="cuda")
+    bd.g4_linear(A.data_ptr(), W.data_ptr(), C32.data_ptr(), M, N, K, bd.G4_F32, gdt, None, 0, stream())
+    bd.g4_linear(A.data_ptr(), W.data_ptr(), Cd.data_ptr(), M, N, K, gdt, gdt, None, 0, stream())
+    torch.cuda.synchronize()
+    ref = O.f64(A) @ O.f64(W).T
+    assert max_rel(C32, ref) <= 1e-3
+    assert_close(Cd, ref, dt, "C in dtype")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_ffn_geglu_vs_oracle(dt):
+    gdt, tdt = DT[dt]
+    M, H, F = 33, 256, 1024
+    x = randn((M, H), 80, tdt)
+    wg, wu = randn((F, H), 81, tdt, 0.05), randn((F, H), 82, tdt, 0.05)
+    wd = randn((H, F), 83, tdt, 0.05)
+    out = torch.empty((M, H), dtype=torch.float32, device="cuda")
+    wsb = bd.g4_ffn_geglu_ws(M, H, F, gdt)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    bd.g4_ffn_geglu(x.data_ptr(), wg.data_ptr(), wu.data_ptr(), wd.data_ptr(), out.data_ptr(), M, H, F, ws.data_ptr(),
+                    wsb, gdt, stream())
+    torch.cuda.synchronize()
+    xv = O.f64(x)
+    ref = (O.gelu_tanh(xv @ O.f64(wg).T) * (xv @ O.f64(wu).T)) @ O.f64(wd).T
+    assert_close(out, ref, dt, "ffn")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("scalar", [1.0, 0.5])
+def test_ple_inject_vs_oracle(dt, scalar):
+    gdt, tdt = DT[dt]
+    M, H, d, L = 21, 256, 32, 3
+    h = randn((M, H), 90)
+    h0 = h.clone()
+    ple = randn((M, L * d), 91)
+    wg, wp = randn((d, H), 92, tdt, 0.05), randn((H, d), 93, tdt, 0.05)
+    wpost = randn((H,), 94, tdt, 0.1, 1.0)
+    wsb = bd.g4_ple_inject_ws(M, H, d, gdt)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    bd.g4_ple_inject(h.data_ptr(), wg.data_ptr(), ple[:, d:].data_ptr(), L * d, wp.data_ptr(), wpost.data_ptr(),
+                     scalar, M, H, d, 1e-6, ws.data_ptr(), wsb, gdt, stream())
+    torch.cuda.synchronize()
+    hv = O.f64(h0)
+    gmix = O.gelu_tanh(hv @ O.f64(wg).T) * O.f64(ple)[:, d:2 * d]
+    ref = (hv + O.rms_norm(gmix @ O.f64(wp).T, wpost, 1e-6)) * scalar
+    assert_close(h, ref, "f32" if dt == "f32" else "bf16", "h")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_embed_ple_vs_oracle(dt):
+    from synth import configs, gen
+    cfg = configs.get(1, dtype=dt)
+    glob = gen.model_globals(cfg, "cuda")
+    m_ids = [0, 5, 511, 300, 512, 7000, -3, 42]
+    ids = torch.tensor(m_ids, dtype=torch.int32, device="cuda")
+    from gemma_decoder_forward_amd.model import G4Model
+    layers = [gen.layer_weights(cfg, l, "cuda") for l in range(cfg["n_layers"])]
+    model = G4Model(cfg, layers, glob)
+    h, ple = model.embed(ids.view(1, -1))
+    torch.cuda.synchronize()
+    e_ref, p_ref = O.entry(cfg, {k: v.cpu() for k, v in glob.items()}, np.array([m_ids]))
+    assert_close(h, e_ref, "f32", "h0")
+    assert_close(ple, p_ref, "f32" if dt == "f32" else "bf16", "ple_in")
+    assert torch.all(h[0, 4:7] == 0)

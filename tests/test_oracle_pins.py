@@ -335,3 +335,14 @@ def test_batch_rows_are_independent():
     assert np.array_equal(out[0], out[2])
     one, _ = _run_oracle_stack(cfg, layers, h0[1:2], ple[1:2], O.prefill_positions([0], 5), srcs, 5)
     np.testing.assert_allclose(one[0], out[1], rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("types", ["SSF", "FSS"])
+def test_layer_rows_equal_whole_layer_rows(types):
+    cfg = configs.tiny(layer_types=types, T=13, window=4)
+    _, layers = _tiny_model(cfg)
+    h = rng.normal(size=(1, 13, cfg["hidden"]))
+    ple = rng.normal(size=(1, 13, cfg["ple_dim"]))
+    whole = O.layer_forward(cfg, layers[0], 0, 0, h, ple, O.prefill_positions([3], 13), O.new_caches(cfg, 1, 16))
+    rows, part = O.layer_forward_rows(cfg, layers[0], 0, h[0], ple[0], 3, [12, 0, 5, 9])
+    np.testing.assert_allclose(part, whole[0, rows], rtol=1e-13, atol=1e-13)
