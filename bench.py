@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Throughput of the Gemma-4 E-series decoder forward on one MI355X.
+
+Default workload: the E4B-shaped layer pair (one sliding layer, hd 256, W 512; one full layer, hd 512,
+25% proportional RoPE; H 2560, 8/2 heads, FFN 10240, PLE 256), bf16 weights, prefill of T = 2048
+tokens, batch 1. A step is one pass of the whole layer forward over that batch, inputs resident in HBM.
+Other workloads (--workload 3/4/5): the 42-layer prefill from token ids, decode at context 8192, and
+the 12-layer T = 32768 slice.
+
+Prints one JSON line. The dominant kernel's launches are timed inside the timed region with HIP events
+recorded by the library on its launch stream (g4_timer_*); `roofline` divides its algorithmic work per
+launch by that average duration. `cpu_baseline` times the float64 oracle on a bounded sample of the same
+workload on the host cores.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def workload(cid, batch):
+    from synth import configs
+    if cid == 4:
+        return configs.get(4, B=batch)
+    return configs.get(cid)
+
+
+def gemm_flops(cfg, M):
+    """Algorithmic GEMM flops of one layer-stack pass (2MNK), by kernel class."""
+    H, nh, nkv, F, d = cfg["hidden"], cfg["n_heads"], cfg["n_kv_heads"], cfg["ffn"], cfg["ple_dim"]
+    from gemma_decoder_forward_amd import binding as bd
+    srcs = bd.g4_kv_sources([1 if t == "S" else 0 for t in cfg["layer_types"]], cfg["n_shared"])
+    out = dict(qkv=0, o=0, gate_up=0, down=0, ple=0)
+    for l, t in enumerate(cfg["layer_types"]):
+        hd = cfg["head_dim_swa"] if t == "S" else cfg["head_dim_full"]
+        nq = nh * hd + (2 * nkv * hd if srcs[l] == l else 0)
+        out["qkv"] += 2 * M * nq * H
+        out["o"] += 2 * M * H * nh * hd
+        out["gate_up"] += 2 * M * 2 * F * H
+        out["down"] += 2 * M * H * F
+        out["ple"] += 2 * M * d * H * 2
+    return out
+
+
+def attn_flops(cfg, T):
+    """4 * nh * hd * (visible query-key pairs) over all layers of a prefill from position 0."""
+    tot = 0
+    W = cfg["window"]
+    for t in cfg["layer_types"]:
+        hd = cfg["head_dim_swa"] if t == "S" else cfg["head_dim_full"]
+        pairs = T * (T + 1) // 2 if t == "F" else sum(min(i + 1, W) for i in range(T))
+        tot += 4 * cfg["n_heads"] * hd * pairs * cfg["B"]
+    return tot
+
+
+def gate_up_weight_bytes(cfg):
+    return 2 * cfg["ffn"] * cfg["hidden"] * 2
+
+
+def run_gpu(cfg, steps, warmup, breakdown):
+    import torch
+    from gemma_decoder_forward_amd import binding as bd
+    from gemma_decoder_forward_amd.model import G4Model
+    from synth import gen
+
+    torch.cuda.set_device(0)
+    B, T = cfg["B"], cfg["T"]
+    layers = [gen.layer_weights(cfg, l, "cuda") for l in range(cfg["n_layers"])]
+    glob = gen.model_globals(cfg, "cuda") if cfg["embed"] else None
+    model = G4Model(cfg, layers, glob)
+    acts = gen.activations(cfg, "cuda")
+    decode = cfg["mode"] == "decode"
+    if decode:
+        cap = cfg["ctx"]
+        fills = {l: gen.decode_cache(cfg, l, "cuda") for l in range(cfg["n_layers"]) if model.kv_src[l] == l}
+        _, table = model.new_caches(B, cap, fill=lambda l: fills[l])
+        mode = bd.G4_DECODE
+    else:
+        cap = T
+        _, table = model.new_caches(B, cap)
+        mode = bd.G4_PREFILL
+    H = cfg["hidden"]
+    h = torch.empty((B, T, H), dtype=torch.float32, device="cuda")
+    ple = None if cfg["embed"] else acts["ple_in"]
+    model.workspace(B, T, cap, mode)
+
+    def step():
+        nonlocal ple
+        if cfg["embed"]:
+            e, p = model.embed(acts["ids"])
+            h.copy_(e)
+            ple = p
+        else:
+            h.copy_(acts["h0"])
+        model.forward(h, ple, acts["pos"], table, cap, mode)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    dom = "gate_up_gemm"
+    bd.g4_timer_enable(bd.KC[dom], steps * cfg["n_layers"] + 8)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dom_ms, dom_n = bd.g4_timer_read()
+    res = dict(ms_per_step=wall * 1e3 / steps, dom_ms=dom_ms, dom_n=dom_n)
+    if breakdown:
+        per = {}
+        for name, cls in bd.KC.items():
+            bd.g4_timer_enable(cls, 4 * cfg["n_layers"] * 3 + 8)
+            for _ in range(2):
+                step()
+            torch.cuda.synchronize()
+            ms, n = bd.g4_timer_read()
+            per[name] = round(ms / 2, 4)
+        res["breakdown_ms_per_step"] = per
+    assert torch.isfinite(h).all().item(), "non-finite output"
+    return res
+
+
+def cpu_baseline(cfg, budget_s):
+    """The float64 oracle, as it stands, on a bounded sample of the workload (host cores)."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    import oracle as O
+    from synth import gen
+
+    L = cfg["n_layers"]
+    layers = [{k: (O.f64(v) if isinstance(v, torch.Tensor) else v) for k, v in gen.layer_weights(cfg, l, "cuda").items()}
+              for l in range(L)]
+    acts = gen.activations(cfg, "cuda")
+    glob = None
+    if cfg["embed"]:
+        g = gen.model_globals(cfg, "cuda")
+        glob = g
+    srcs = O.kv_sources(cfg["layer_types"], cfg["n_shared"])
+
+    def run(Tp, nseq):
+        if cfg["mode"] == "decode":
+            sub = dict(cfg, B=nseq)
+            ids = acts["ids"][:nseq].cpu().numpy()
+            caches = {}
+            for l in range(L):
+                if srcs[l] == l:
+                    k, v = gen.decode_cache(sub, l, "cuda")
+                    caches[l] = (O.f64(k), O.f64(v))
+            pos = np.full((nseq, 1), cfg["ctx"] - 1)
+        else:
+            sub = dict(cfg, T=Tp)
+            ids = acts["ids"][:, :Tp].cpu().numpy() if cfg["embed"] else None
+            caches = O.new_caches(cfg, 1, Tp, srcs)
+            pos = O.prefill_positions([0], Tp)
+        if cfg["embed"]:
+            uniq, inv = np.unique(ids, return_inverse=True)
+            idx = torch.from_numpy(uniq).cuda()
+            gh = dict(embed=glob["embed"][idx].cpu(), ple_embed=glob["ple_embed"][idx].cpu(),
+                      ple_model_proj=O.f64(glob["ple_model_proj"]), ple_norm=glob["ple_norm"].cpu())
+            sub2 = dict(sub, vocab=len(uniq), ple_vocab=len(uniq))
+            idl = inv.reshape(ids.shape)
+        else:
+            h0 = O.f64(acts["h0"][:, :Tp])
+            ple = O.f64(acts["ple_in"][:, :Tp])
+        t0 = time.perf_counter()
+        if cfg["embed"]:
+            h0, ple = O.entry(sub2, gh, idl)
+        O.forward(sub, layers, h0, ple, pos, caches, srcs)
+        return time.perf_counter() - t0
+
+    if cfg["mode"] == "decode":
+        n = 1
+        t = run(0, n)
+        tokens, sample = n, f"decode step of {n} sequence at context {cfg['ctx']}"
+    else:
+        Tp = 128
+        t = run(Tp, 1)
+        target = int(Tp * budget_s / max(t, 1e-3)) // 64 * 64
+        target = min(cfg["T"], target)
+        if target > Tp:
+            Tp = target
+            t = run(Tp, 1)
+        tokens = Tp
+        sample = f"prefill of the first {Tp} of {cfg['T']} tokens (batch 1) through all {L} layers"
+    cores = sum(p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas") or 1
+    return dict(value=round(tokens / t, 3), unit="tokens/s", cores=cores, kind="oracle", sample=sample,
+                seconds=round(t, 2))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--batch", type=int, default=64, help="decode batch (workload 4)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): this build "
+              "measures the single-GPU forward; sharding is a design note, not implemented.", file=sys.stderr)
+        sys.exit(2)
+    cfg = workload(args.workload, args.batch)
+    r = run_gpu(cfg, args.steps, args.warmup, not args.no_breakdown)
+    B, T = cfg["B"], cfg["T"]
+    tokens = B * T
+    ms = r["ms_per_step"]
+    decode = cfg["mode"] == "decode"
+    dom_avg_s = r["dom_ms"] / max(r["dom_n"], 1) / 1e3
+    if decode:
+        per_launch = gate_up_weight_bytes(cfg) + 2 * B * cfg["hidden"] + 2 * B * cfg["ffn"]
+        achieved = per_launch / dom_avg_s / 1e9
+        roof = dict(bound="hbm", kernel="gate_up_gemm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(achieved / PEAK_HBM_GBS, 4), traffic=None, bytes_per_launch=per_launch,
+                    avg_launch_us=round(dom_avg_s * 1e6, 2))
+    else:
+        per_launch = 2 * tokens * 2 * cfg["ffn"] * cfg["hidden"]
+        achieved = per_launch / dom_avg_s / 1e12
+        roof = dict(bound="mfma", kernel="gate_up_gemm", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS,
+                    unit="TFLOP/s", frac=round(achieved / PEAK_BF16_TFLOPS, 4), traffic=None,
+                    flops_per_launch=per_launch, avg_launch_us=round(dom_avg_s * 1e6, 2))
+    gf = gemm_flops(cfg, tokens)
+    extra = dict(gemm_tflop_per_step=round(sum(gf.values()) / 1e12, 4))
+    if not decode:
+        af = attn_flops(cfg, T)
+        extra["attn_tflop_per_step"] = round(af / 1e12, 4)
+        extra["model_tflops"] = round((sum(gf.values()) + af) / (ms / 1e3) / 1e12, 2)
+    if "breakdown_ms_per_step" in r:
+        extra["breakdown_ms_per_step"] = r["breakdown_ms_per_step"]
+    names = {2: "e4b-layer-pair prefill", 3: "e4b-42-layer prefill from token ids", 4: "e4b-42-layer decode",
+             5: "e4b-12-layer long-context prefill"}
+    line = dict(
+        metric="prefill tokens/s" if not decode else "decode tokens/s",
+        value=round(tokens / (ms / 1e3), 2), unit="tokens/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+        ms_per_step=round(ms, 4), higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16",
+        data="synthetic (seeded N(0,0.02) weights, N(0,1) activations / uniform token ids)",
+        config=dict(workload=f"{names[args.workload]}: B={B} T={T}" + (f" ctx={cfg['ctx']}" if decode else ""),
+                    layers=cfg["n_layers"], layer_types=cfg["layer_types"], hidden=cfg["hidden"], ffn=cfg["ffn"],
+                    heads=f"{cfg['n_heads']}/{cfg['n_kv_heads']}",
+                    head_dim=f"{cfg['head_dim_swa']}/{cfg['head_dim_full']}", window=cfg["window"],
+                    global_batch=B, seq_len=T, parallelism="none (1 GPU)"),
+        roofline=roof, extra=extra,
+    )
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -58,6 +58,8 @@ _SIGS = {
                                    vp, i64, i64, i32, vp, sz, vp]),
     "g4_stack_forward": (C.c_int, [C.POINTER(ModelDesc), C.POINTER(LayerDesc), vp, vp, C.POINTER(KvEntry), i32, vp,
                                    i64, i64, i32, vp, sz, vp]),
+    "g4_timer_enable": (C.c_int, [i32, i32]),
+    "g4_timer_read": (C.c_int, [C.POINTER(C.c_double), C.POINTER(i32)]),
     "g4_workspace_size": (sz, [C.POINTER(ModelDesc), i64, i64, i64, i32]),
 }
 
@@ -169,3 +171,16 @@ def g4_stack_forward(model, layers, h, ple_in, kv, n_kv, pos, B, T, mode, ws, ws
 
 def g4_workspace_size(model, B, T, cap, mode):
     return lib().g4_workspace_size(C.byref(model), B, T, cap, mode)
+
+
+KC = dict(qkv_gemm=1, qk_norm_rope=2, attention=3, o_gemm=4, gate_up_gemm=5, down_gemm=6, ple_gemm=7, row_tail=8)
+
+
+def g4_timer_enable(cls, max_launches):
+    return _call("g4_timer_enable", cls, max_launches)
+
+
+def g4_timer_read():
+    ms, n = C.c_double(), i32()
+    _call("g4_timer_read", C.byref(ms), C.byref(n))
+    return ms.value, n.value

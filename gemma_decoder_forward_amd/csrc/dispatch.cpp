@@ -5,6 +5,8 @@ namespace g4 {
 
 g4_status gemm(const GemmArgs& a, int32_t dtype, hipStream_t s) {
   if (a.M == 0) return G4_OK;
+  g4_status st = G4_OK;
+  if (dtype == G4_BF16 && gemm_mfma(a, s, &st)) return st;
   return gemm_simt(a, dtype, s);
 }
 

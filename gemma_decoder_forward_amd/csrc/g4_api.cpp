@@ -28,6 +28,28 @@ g4_status check_launch(const char* what) {
   return G4_OK;
 }
 
+// ---- launch timer (g4_timer_enable / g4_timer_read) ----------------------------------------------
+struct Timer {
+  int32_t cls = 0;
+  int32_t cap = 0, n = 0;
+  hipEvent_t* ev = nullptr;
+};
+static Timer g_timer;
+
+struct TimedScope {  // records an event pair around the launches of one class
+  bool on;
+  hipStream_t s;
+  TimedScope(int32_t cls, hipStream_t st) : on(g_timer.cls == cls && g_timer.n < g_timer.cap), s(st) {
+    if (on) (void)hipEventRecord(g_timer.ev[2 * g_timer.n], s);
+  }
+  ~TimedScope() {
+    if (on) {
+      (void)hipEventRecord(g_timer.ev[2 * g_timer.n + 1], s);
+      ++g_timer.n;
+    }
+  }
+};
+
 static bool dt_ok(int32_t dt) { return dt == G4_F32 || dt == G4_BF16; }
 
 #define G4_REQ(cond, st, ...)                 \
@@ -186,12 +208,15 @@ static g4_status layer_impl(const LayerCtx& c) {
   if (!c.xn_ready)
     G4_TRY(rownorm(c.h, G4_F32, 1, 0, l->input_norm, xn, nullptr, 1.f, nullptr, nullptr, M, H, m->eps, dt, c.s));
   // 2. projections: q, and k, v when the layer owns its cache
+  {
+  TimedScope ts(G4_KC_QKV_GEMM, c.s);
   G4_TRY(run_gemm(xn, H, l->wq, nullptr, H, qkv, qld, dt, M, nh * hd, H, EPI_STORE, nullptr, 0, 1, 0, dt, c.s));
   if (own) {
     G4_TRY(run_gemm(xn, H, l->wk, nullptr, H, qkv + nh * hd * E, qld, dt, M, nkv * hd, H, EPI_STORE, nullptr, 0, 1,
                     0, dt, c.s));
     G4_TRY(run_gemm(xn, H, l->wv, nullptr, H, qkv + (nh + nkv) * hd * E, qld, dt, M, nkv * hd, H, EPI_STORE, nullptr,
                     0, 1, 0, dt, c.s));
+  }
   }
   // 3. per-head norms + RoPE; k and v go straight into this layer's cache rows
   HeadSeg segs[3];
@@ -202,35 +227,62 @@ static g4_status layer_impl(const LayerCtx& c) {
     segs[ns++] = HeadSeg{qkv + nh * hd * E, qld, l->k_norm, e.k, 0, e.cap, (int32_t)nkv, 1};
     segs[ns++] = HeadSeg{qkv + (nh + nkv) * hd * E, qld, nullptr, e.v, 0, e.cap, (int32_t)nkv, 0};
   }
-  G4_TRY(qk_norm_rope(segs, ns, c.pos, c.B, c.T, hd, theta, nrot, m->eps, dt, c.s));
+  {
+    TimedScope ts(G4_KC_QK_NORM_ROPE, c.s);
+    G4_TRY(qk_norm_rope(segs, ns, c.pos, c.B, c.T, hd, theta, nrot, m->eps, dt, c.s));
+  }
   // 4. attention over the source layer's cache (no copy)
   const g4_kv_entry& src = c.kv[l->kv_src];
   AttnArgs aa{};
   aa.q = qkv; aa.q_ld = qld; aa.k = src.k; aa.v = src.v; aa.cap = src.cap; aa.pos0 = c.pos;
   aa.B = c.B; aa.T = c.T; aa.nh = nh; aa.nkv = nkv; aa.hd = hd; aa.sliding = sliding; aa.window = m->window;
   aa.scale = 1.f; aa.out = ao; aa.out_ld = nh * hd;
-  if (c.mode == G4_DECODE) G4_TRY(attn_decode(aa, c.ws + c.p->dec, c.p->total - c.p->dec, dt, c.s));
-  else G4_TRY(attn_prefill(aa, dt, c.s));
+  {
+    TimedScope ts(G4_KC_ATTENTION, c.s);
+    if (c.mode == G4_DECODE) G4_TRY(attn_decode(aa, c.ws + c.p->dec, c.p->total - c.p->dec, dt, c.s));
+    else G4_TRY(attn_prefill(aa, dt, c.s));
+  }
   // 5-6. o projection, then h += rms(a) * w_pa and xn2 = rms(h) * w_pf
   const int32_t so = 1;
+  {
+  TimedScope ts(G4_KC_O_GEMM, c.s);
   G4_TRY(run_gemm(ao, nh * hd, l->wo, nullptr, nh * hd, fb, H, G4_F32, M, H, nh * hd, EPI_STORE, nullptr, 0, so,
                   M * H, dt, c.s));
+  }
+  {
+  TimedScope ts(G4_KC_ROW_TAIL, c.s);
   G4_TRY(rownorm(fb, G4_F32, so, M * H, l->post_attn_norm, nullptr, c.h, 1.f, l->pre_ffn_norm, xn, M, H, m->eps, dt,
                  c.s));
   // 7. gate/up GEMM with the gelu-tanh product in its epilogue
-  G4_TRY(run_gemm(xn, H, l->w_gate, l->w_up, H, act, F, dt, M, F, H, EPI_GEGLU, nullptr, 0, 1, 0, dt, c.s));
+  }
+  {
+    TimedScope ts(G4_KC_GATE_UP_GEMM, c.s);
+    G4_TRY(run_gemm(xn, H, l->w_gate, l->w_up, H, act, F, dt, M, F, H, EPI_GEGLU, nullptr, 0, 1, 0, dt, c.s));
+  }
   // 8-9. down projection, then h += rms(ffn) * w_pff; hb = h in dtype for the PLE gate
   const int32_t sd = 1;
+  {
+  TimedScope ts(G4_KC_DOWN_GEMM, c.s);
   G4_TRY(run_gemm(act, F, l->w_down, nullptr, F, fb, H, G4_F32, M, H, F, EPI_STORE, nullptr, 0, sd, M * H, dt, c.s));
+  }
+  {
+  TimedScope ts(G4_KC_ROW_TAIL, c.s);
   G4_TRY(rownorm(fb, G4_F32, sd, M * H, l->post_ffn_norm, nullptr, c.h, 1.f, nullptr, hb, M, H, m->eps, dt, c.s));
+  }
   // 10. PLE gate: gelu_tanh(h W_pg^T) * ple_in[:, layer]
   const int64_t Ld = m->n_layers * d;
+  {
+  TimedScope ts(G4_KC_PLE_GEMM, c.s);
   G4_TRY(run_gemm(hb, H, l->ple_gate, nullptr, H, gm, d, dt, M, d, H, EPI_GELU_MUL, c.ple_in + (int64_t)c.layer * d,
                   Ld, 1, 0, dt, c.s));
   // 11-12. PLE projection, h = (h + rms(p) * w_post_ple) * layer_scalar (+ next layer's xn)
   G4_TRY(run_gemm(gm, d, l->ple_proj, nullptr, d, fb, H, G4_F32, M, H, d, EPI_STORE, nullptr, 0, 1, M * H, dt, c.s));
+  }
+  {
+  TimedScope ts(G4_KC_ROW_TAIL, c.s);
   G4_TRY(rownorm(fb, G4_F32, 1, M * H, l->post_ple_norm, nullptr, c.h, l->layer_scalar, c.next_input_norm,
                  c.next_input_norm ? xn : nullptr, M, H, m->eps, dt, c.s));
+  }
 #undef G4_TRY
   return G4_OK;
 }
@@ -443,6 +495,44 @@ g4_status g4_embed_ple(const int32_t* ids, int64_t M, const void* E, const void*
     return st;
   return ple_combine(ids, M, P, Tab, model->ple_vocab, ple_norm, model->hidden, model->n_layers, model->ple_dim,
                      model->eps, ple_out, dt, s);
+}
+
+g4_status g4_timer_enable(int32_t cls, int32_t max_launches) {
+  G4_REQ(cls >= G4_KC_QKV_GEMM && cls <= G4_KC_ROW_TAIL, G4_EINVAL, "kernel class %d", cls);
+  G4_REQ(max_launches > 0 && max_launches <= 1 << 20, G4_EINVAL, "max_launches %d", max_launches);
+  if (g_timer.cap < max_launches) {
+    hipEvent_t* ev = new hipEvent_t[2 * (size_t)max_launches];
+    for (int32_t i = 0; i < 2 * max_launches; ++i) {
+      if (hipEventCreate(&ev[i]) != hipSuccess) {
+        for (int32_t j = 0; j < i; ++j) (void)hipEventDestroy(ev[j]);
+        delete[] ev;
+        return fail(G4_EHIP, "hipEventCreate failed");
+      }
+    }
+    for (int32_t i = 0; i < 2 * g_timer.cap; ++i) (void)hipEventDestroy(g_timer.ev[i]);
+    delete[] g_timer.ev;
+    g_timer.ev = ev;
+    g_timer.cap = max_launches;
+  }
+  g_timer.cls = cls;
+  g_timer.n = 0;
+  return G4_OK;
+}
+
+g4_status g4_timer_read(double* total_ms, int32_t* launches) {
+  G4_REQ(total_ms && launches, G4_EINVAL, "NULL output");
+  g_timer.cls = 0;
+  double t = 0;
+  for (int32_t i = 0; i < g_timer.n; ++i) {
+    float ms = 0;
+    if (hipEventSynchronize(g_timer.ev[2 * i + 1]) != hipSuccess ||
+        hipEventElapsedTime(&ms, g_timer.ev[2 * i], g_timer.ev[2 * i + 1]) != hipSuccess)
+      return fail(G4_EHIP, "event timing failed");
+    t += ms;
+  }
+  *total_ms = t;
+  *launches = g_timer.n;
+  return G4_OK;
 }
 
 size_t g4_workspace_size(const g4_model_desc* model, int64_t B, int64_t T, int64_t cap, int32_t mode) {

@@ -226,6 +226,29 @@ g4_status g4_stack_forward(const g4_model_desc* model, const g4_layer_desc* laye
                            const int32_t* pos, int64_t B, int64_t T, int32_t mode, void* ws,
                            size_t ws_bytes, void* stream);
 
+/* ---- timing instrumentation ------------------------------------------------------------------ */
+
+/* Kernel classes of the layer forward, for g4_timer_enable. */
+typedef enum g4_kernel_class {
+  G4_KC_QKV_GEMM = 1,   /* q/k/v projections */
+  G4_KC_QK_NORM_ROPE = 2,
+  G4_KC_ATTENTION = 3,
+  G4_KC_O_GEMM = 4,
+  G4_KC_GATE_UP_GEMM = 5, /* gate/up projection with the gelu-tanh product epilogue */
+  G4_KC_DOWN_GEMM = 6,
+  G4_KC_PLE_GEMM = 7,
+  G4_KC_ROW_TAIL = 8    /* fused RMSNorm residual tails */
+} g4_kernel_class;
+
+/* While enabled, every launch of kernel class `cls` made by g4_layer_forward / g4_stack_forward is
+ * bracketed by two HIP events recorded on the caller's stream (at most max_launches launches; later
+ * ones are not timed). Enabling creates the events (no device memory). Not thread-safe: one timer
+ * per process. */
+g4_status g4_timer_enable(int32_t cls, int32_t max_launches);
+/* Stops recording and returns the summed device time (ms) and the number of timed launches; waits for
+ * the recorded events to complete. */
+g4_status g4_timer_read(double* total_ms, int32_t* launches);
+
 /* Workspace bytes g4_layer_forward / g4_stack_forward / g4_embed_ple need for M = B*T rows over
  * caches of capacity `cap` (decode splits attention over key chunks of the cache). 0 if the model
  * descriptor is invalid. */
