@@ -14,6 +14,8 @@ size_t gemm_ws(int64_t, int64_t, int64_t, int32_t) { return 0; }
 
 g4_status attn_prefill(const AttnArgs& a, int32_t dtype, hipStream_t s) {
   if (a.B * a.T == 0) return G4_OK;
+  g4_status st = G4_OK;
+  if (dtype == G4_BF16 && attn_mfma(a, s, &st)) return st;
   return attn_rowwise(a, dtype, s);
 }
 

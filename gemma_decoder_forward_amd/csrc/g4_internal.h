@@ -131,6 +131,7 @@ g4_status cast_rows(const float* x, void* y, int64_t n, int32_t dtype, hipStream
 g4_status gemm_simt(const GemmArgs& a, int32_t dtype, hipStream_t s);
 bool gemm_mfma(const GemmArgs& a, hipStream_t s, g4_status* st);
 g4_status attn_rowwise(const AttnArgs& a, int32_t dtype, hipStream_t s);
+bool attn_mfma(const AttnArgs& a, hipStream_t s, g4_status* st);
 g4_status embed_rows(const int32_t* ids, int64_t M, const void* E, int64_t vocab, int64_t H,
                      float* h_out, void* e_cast, int32_t dtype, hipStream_t s);
 g4_status ple_combine(const int32_t* ids, int64_t M, const float* P, const void* Tab,

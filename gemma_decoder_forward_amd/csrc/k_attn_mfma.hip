@@ -1,0 +1,248 @@
+// Flash-style prefill attention on the CDNA4 matrix cores (bf16 operands, float32 softmax and
+// accumulation), causal with an optional sliding window, GQA groups sharing every K/V tile.
+//
+// Block = 4 waves. A "query group" is one head x 32 consecutive tokens; heads of a kv group share its K/V.
+// With HS = 1 each wave owns one query group (4 groups per block); with HS = 2 (head_dim 512, whose Q and
+// O do not fit one wave's registers) a pair of waves owns one group, each wave holding half of the head
+// dimension of Q and O: the pair adds its two partial score tiles through LDS, both run the identical
+// softmax, and each accumulates P V for its half. Keys advance in tiles of 32 staged in LDS (double
+// buffered, next tile prefetched into registers during the current tile's math):
+//   * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: A = K rows from LDS,
+//     B = the wave's Q held in registers for the whole key loop;
+//   * lane l then holds query (l % 32) and 16 of the tile's keys: 8*(j/4) + 4*(l/32) + j%4 for
+//     register j. The online softmax (exp2 form, max over the two lanes of a query) runs in place;
+//   * O^T = V^T P^T uses those probabilities directly as the B operand: for the 16-key MFMA step s,
+//     the lane's registers j = 8s..8s+7 are keys {16s + 4h + 0..3, 16s + 8 + 4h + 0..3} (h = l/32), and
+//     the A operand reads V^T at exactly those keys, so P never moves between lanes;
+//   * V is staged transposed (V^T[hd][key], key pairs packed in one dword, row stride 36 keys) so both
+//     the staging writes and the two 8-byte operand reads per MFMA are free of bank conflicts.
+// The O accumulator (HD/32 32x32 blocks per wave) lives in the accumulation registers.
+#include "g4_internal.h"
+
+namespace g4 {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+constexpr int AT_KB = 32;        // keys per tile
+constexpr int AT_VLD = 36;       // V^T row stride in bf16 (32 keys + 4)
+
+template <int HD>
+struct AttnLds {
+  static constexpr int KLD = HD + 8;  // K row stride in bf16
+  static constexpr int KSZ = AT_KB * KLD;
+  static constexpr int VSZ = HD * AT_VLD;
+  static constexpr int STAGE = KSZ + VSZ;
+};
+
+template <int HD, int HS>
+__global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float sl2) {
+  using L = AttnLds<HD>;
+  constexpr int HW = HD / HS;      // head elements owned by one wave
+  constexpr int NB = HW / 32;      // O blocks per wave
+  constexpr int KS = HW / 16;      // MFMA k-steps for S
+  constexpr int QG = 4 / HS;       // query groups per block
+  constexpr int KCH = AT_KB * HD / 8 / 256;   // 16-byte K chunks per thread
+  constexpr int VUN = 16 * (HD / 8) / 256;    // (key pair, hd chunk) units per thread
+  __shared__ __attribute__((aligned(16))) bf16 lds[2 * L::STAGE];
+  __shared__ float xch[HS == 2 ? 4 * 16 * 64 : 1];  // partial score tiles of the wave pairs
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, col = lane & 31;
+  const int half = wave % HS;
+  // query groups are numbered run * G + head_in_group; a block takes QG consecutive ones
+  const int nruns = (int)((a.T + 31) / 32);
+  const int ngroups = nruns * G;
+  const int nblk = (ngroups + QG - 1) / QG;
+  const int blk = nblk - 1 - (int)blockIdx.x;  // heaviest (latest) groups first
+  const int gi = blk * QG + wave / HS;
+  const int64_t g = blockIdx.y, b = blockIdx.z;
+  const int run = gi / G;
+  const int64_t head = g * G + gi % G;
+  const int64_t tq = (int64_t)run * 32 + col;  // this lane's query token
+  const int64_t p0 = a.pos0[b];
+  const bool qvalid = gi < ngroups && tq < a.T;
+  const int64_t qi = p0 + tq;                  // absolute position of the query
+
+  // block key range (union over its groups)
+  const int g_first = blk * QG, g_last = (blk * QG + QG - 1) < ngroups - 1 ? blk * QG + QG - 1 : ngroups - 1;
+  int64_t tlast = (int64_t)(g_last / G) * 32 + 31;
+  if (tlast > a.T - 1) tlast = a.T - 1;
+  const int64_t imin = p0 + (int64_t)(g_first / G) * 32, imax = p0 + tlast;
+  int64_t lob = a.sliding ? imin - a.window + 1 : 0;
+  if (lob < 0) lob = 0;
+  int64_t hib = imax < a.cap - 1 ? imax : a.cap - 1;
+  const int64_t kstart = lob & ~(int64_t)(AT_KB - 1);
+  const int ntiles = hib >= lob ? (int)((hib - kstart) / AT_KB + 1) : 0;
+  int64_t qlo = a.sliding ? qi - a.window + 1 : 0;
+  if (qlo < 0) qlo = 0;
+
+  // Q fragments (B operand of S^T): query col, hd 16s + 8h .. +7
+  bf16x8_t qf[KS];
+  {
+    const bf16* qrow = (const bf16*)a.q + (b * a.T + (qvalid ? tq : 0)) * a.q_ld + (qvalid ? head : 0) * HD +
+                       half * HW + 8 * h;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      uint4 v = qvalid ? *(const uint4*)(qrow + 16 * s) : make_uint4(0, 0, 0, 0);
+      qf[s] = *(bf16x8_t*)&v;
+    }
+  }
+
+  const bf16* Kb = (const bf16*)a.k + (b * a.nkv + g) * a.cap * HD;
+  const bf16* Vb = (const bf16*)a.v + (b * a.nkv + g) * a.cap * HD;
+  uint4 rk[KCH], rv[2 * VUN];
+  auto gload = [&](int it) {
+    const int64_t k0 = kstart + (int64_t)it * AT_KB;
+#pragma unroll
+    for (int j = 0; j < KCH; ++j) {
+      const int u = tid + 256 * j, r = u / (HD / 8), c = u % (HD / 8);
+      const int64_t key = k0 + r;
+      rk[j] = (key >= lob && key <= hib) ? *(const uint4*)(Kb + key * HD + 8 * c) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < VUN; ++j) {
+      const int u = tid + 256 * j, p = u & 15, c = u >> 4;
+      const int64_t key = k0 + 2 * p;
+      rv[2 * j] = (key >= lob && key <= hib) ? *(const uint4*)(Vb + key * HD + 8 * c) : make_uint4(0, 0, 0, 0);
+      rv[2 * j + 1] =
+          (key + 1 >= lob && key + 1 <= hib) ? *(const uint4*)(Vb + (key + 1) * HD + 8 * c) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto lstore = [&](int buf) {
+    bf16* ks = lds + buf * L::STAGE;
+    bf16* vs = ks + L::KSZ;
+#pragma unroll
+    for (int j = 0; j < KCH; ++j) {
+      const int u = tid + 256 * j, r = u / (HD / 8), c = u % (HD / 8);
+      *(uint4*)(ks + r * L::KLD + 8 * c) = rk[j];
+    }
+#pragma unroll
+    for (int j = 0; j < VUN; ++j) {
+      const int u = tid + 256 * j, p = u & 15, c = u >> 4;
+      const uint32_t* lo = (const uint32_t*)&rv[2 * j];
+      const uint32_t* hi = (const uint32_t*)&rv[2 * j + 1];
+      uint32_t* dst = (uint32_t*)(vs + (8 * c) * AT_VLD) + p;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // element 2i and 2i+1 of the chunk: (key 2p, key 2p+1) pairs for hd rows 8c+2i and 8c+2i+1
+        dst[(2 * i) * (AT_VLD / 2)] = (lo[i] & 0xffffu) | (hi[i] << 16);
+        dst[(2 * i + 1) * (AT_VLD / 2)] = (lo[i] >> 16) | (hi[i] & 0xffff0000u);
+      }
+    }
+  };
+
+  f32x16_t o[NB];
+#pragma unroll
+  for (int d = 0; d < NB; ++d)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  if (ntiles > 0) {
+    gload(0);
+    lstore(0);
+    __syncthreads();
+  }
+  for (int it = 0; it < ntiles; ++it) {
+    const int cur = it & 1;
+    if (it + 1 < ntiles) gload(it + 1);
+    const bf16* ks = lds + cur * L::STAGE;
+    const bf16* vs = ks + L::KSZ;
+    const int64_t k0 = kstart + (int64_t)it * AT_KB;
+    // S^T = K Q^T
+    f32x16_t s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+    const bf16* kf = ks + col * L::KLD + half * HW + 8 * h;
+#pragma unroll
+    for (int st = 0; st < KS; ++st)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t*)(kf + 16 * st), qf[st], s, 0, 0, 0);
+    if (HS == 2) {  // add the partner wave's partial scores (the other half of the head dimension)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xch[(wave * 16 + r) * 64 + lane] = s[r];
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] += xch[((wave ^ 1) * 16 + r) * 64 + lane];
+    }
+    // mask, scale to the exp2 domain, online softmax
+    float mt = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t key = k0 + 8 * (r >> 2) + 4 * h + (r & 3);
+      const bool vis = qvalid && key <= qi && key >= qlo && key <= hib;
+      const float v = vis ? s[r] * sl2 : -INFINITY;
+      s[r] = v;
+      mt = fmaxf(mt, v);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float m_new = fmaxf(m_run, mt);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    float psum = 0.f;
+    bf16x8_t pb[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(s[r] - m_use);
+      psum += p;
+      pb[r >> 3][r & 7] = (__bf16)p;
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int d = 0; d < NB; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+    // O^T += V^T P^T
+    const bf16* vf = vs + (half * HW + col) * AT_VLD + 4 * h;
+#pragma unroll
+    for (int d = 0; d < NB; ++d) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const bf16* vp = vf + d * 32 * AT_VLD + 16 * st;
+        bf16x4_t lo4 = *(const bf16x4_t*)vp;
+        bf16x4_t hi4 = *(const bf16x4_t*)(vp + 8);
+        bf16x8_t va = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[st], o[d], 0, 0, 0);
+      }
+    }
+    if (it + 1 < ntiles) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (!qvalid) return;
+  const float il = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  bf16* orow = (bf16*)a.out + (b * a.T + tq) * a.out_ld + head * HD + half * HW;
+#pragma unroll
+  for (int d = 0; d < NB; ++d)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int hd0 = 32 * d + 8 * r4 + 4 * h;
+      uint2 pk;
+      pk.x = (uint32_t)f2bf(o[d][4 * r4] * il) | ((uint32_t)f2bf(o[d][4 * r4 + 1] * il) << 16);
+      pk.y = (uint32_t)f2bf(o[d][4 * r4 + 2] * il) | ((uint32_t)f2bf(o[d][4 * r4 + 3] * il) << 16);
+      *(uint2*)(orow + hd0) = pk;
+    }
+}
+
+// bf16, head_dim 128/256/512, groups of 1, 2 or 4 query heads per kv head, 16-byte aligned rows.
+bool attn_mfma(const AttnArgs& a, hipStream_t s, g4_status* st) {
+  const int64_t G = a.nh / a.nkv;
+  if (!(G == 1 || G == 2 || G == 4)) return false;
+  if (!(a.hd == 128 || a.hd == 256 || a.hd == 512)) return false;
+  if ((a.q_ld | a.out_ld) & 7) return false;
+  if (((uintptr_t)a.q | (uintptr_t)a.k | (uintptr_t)a.v | (uintptr_t)a.out) & 15) return false;
+  const int HS = a.hd == 512 ? 2 : 1, QG = 4 / HS;
+  const int64_t ngroups = ((a.T + 31) / 32) * G;
+  dim3 grid((unsigned)((ngroups + QG - 1) / QG), (unsigned)a.nkv, (unsigned)a.B);
+  const float sl2 = a.scale * 1.4426950408889634f;
+  if (a.hd == 128) hipLaunchKernelGGL((k_attn_mfma<128, 1>), grid, dim3(256), 0, s, a, (int)G, sl2);
+  else if (a.hd == 256) hipLaunchKernelGGL((k_attn_mfma<256, 1>), grid, dim3(256), 0, s, a, (int)G, sl2);
+  else hipLaunchKernelGGL((k_attn_mfma<512, 2>), grid, dim3(256), 0, s, a, (int)G, sl2);
+  *st = check_launch("attn_mfma");
+  return true;
+}
+
+}  // namespace g4

@@ -113,7 +113,8 @@ def _kv_table(entries):
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("hd,sliding,window,nh,nkv", [(64, 1, 32, 4, 1), (128, 0, 0, 4, 1), (256, 1, 512, 8, 2),
-                                                      (512, 0, 0, 8, 2), (256, 1, 7, 4, 2)])
+                                                      (512, 0, 0, 8, 2), (256, 1, 7, 4, 2), (128, 1, 40, 2, 2),
+                                                      (512, 1, 100, 4, 2)])
 def test_attention_prefill_vs_oracle(dt, hd, sliding, window, nh, nkv):
     log(f"attn_prefill {dt} hd={hd} sliding={sliding} W={window}")
     gdt, tdt = DT[dt]
@@ -135,7 +136,7 @@ def test_attention_prefill_vs_oracle(dt, hd, sliding, window, nh, nkv):
         assert_close(out.reshape(B, T, nh, hd)[b], ref, dt, f"seq {b}")
 
 
-@pytest.mark.parametrize("hd,sliding,window", [(64, 1, 7), (64, 0, 0), (256, 1, 33)])
+@pytest.mark.parametrize("hd,sliding,window", [(64, 1, 7), (64, 0, 0), (256, 1, 33), (128, 0, 0), (512, 1, 21)])
 def test_attention_mask_probe_bit_exact(hd, sliding, window):
     """q = 0 gives uniform weights; V_j = onehot(j mod hd) makes round(o * n) the mask row."""
     T, nh, nkv = 64, 4, 1
@@ -180,6 +181,24 @@ def test_attention_reads_kv_src_cache_without_copy():
                            out.data_ptr(), nh * hd, bd.G4_BF16, stream())
         torch.cuda.synchronize()
         assert torch.all(out == float(src + 1))
+
+
+@pytest.mark.parametrize("hd,sliding,W", [(256, 1, 512), (512, 0, 0)])
+def test_attention_prefill_long_e4b_shapes(hd, sliding, W):
+    """E4B heads (8 q / 2 kv) over T = 2048 from position 0, the layer pair's attention call."""
+    log(f"attn_prefill long hd={hd}")
+    B, T, nh, nkv = 1, 2048, 8, 2
+    q = randn((T, nh * hd), 35 + hd, torch.bfloat16)
+    K = randn((1, nkv, T, hd), 36, torch.bfloat16)
+    V = randn((1, nkv, T, hd), 37, torch.bfloat16)
+    out = torch.empty_like(q)
+    pos0 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    t = _kv_table([(K, V, sliding)])
+    bd.g4_attn_prefill(q.data_ptr(), nh * hd, t, 1, 0, 0, sliding, W, pos0.data_ptr(), B, T, nh, nkv, hd, 1.0,
+                       out.data_ptr(), nh * hd, bd.G4_BF16, stream())
+    torch.cuda.synchronize()
+    ref = O.attention(O.f64(q).reshape(T, nh, hd), O.f64(K[0]), O.f64(V[0]), np.arange(T), W if sliding else None)
+    assert_close(out.reshape(T, nh, hd), ref, "bf16", "long")
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
