@@ -102,7 +102,7 @@ static g4_status check_kv(const g4_kv_entry* kv, int32_t n_kv, int32_t layer, in
 
 // ---- workspace plan of the layer forward -----------------------------------------------------
 struct Plan {
-  size_t xn, qkv, ao, f32buf, act, hb, gm, dec, emb_e, emb_p, total;
+  size_t xn, qkv, ao, f32buf, act, hb, gm, dec, gws, gws_bytes, emb_e, emb_p, total;
   int64_t qkv_ld, splits;
 };
 
@@ -125,6 +125,19 @@ static Plan plan(const g4_model_desc* m, int64_t B, int64_t T, int64_t cap, int3
   p.gm = o; o += al(M * m->ple_dim * E);
   p.dec = o;
   if (mode == G4_DECODE) o += al(attn_decode_ws(B, m->n_heads, hdm, cap > 0 ? cap : 1));
+  p.gws = o;
+  p.gws_bytes = 0;
+  if (M <= 64 && m->dtype == G4_BF16) {  // partial sums of the few-row GEMM
+    const int64_t H = m->hidden, nh = m->n_heads, nkv = m->n_kv_heads, hs = m->head_dim_swa, hf = m->head_dim_full;
+    const int64_t shapes[10][2] = {{nh * hs, H}, {(nh + 2 * nkv) * hs, H}, {nh * hf, H}, {(nh + 2 * nkv) * hf, H},
+                                   {2 * m->ffn, H}, {H, m->ffn}, {H, nh * hs}, {H, nh * hf},
+                                   {m->ple_dim, H}, {H, m->ple_dim}};
+    for (auto& sh : shapes) {
+      const size_t b = gemm_skinny_ws(M, (sh[0] + 63) / 64 * 64, (sh[1] + 127) / 128 * 128);
+      if (b > p.gws_bytes) p.gws_bytes = b;
+    }
+    o += al(p.gws_bytes);
+  }
   p.total = o;
   // the entry (embedding + PLE) reuses the start of the workspace
   p.emb_e = 0;
@@ -135,15 +148,35 @@ static Plan plan(const g4_model_desc* m, int64_t B, int64_t T, int64_t cap, int3
 }
 
 // GEMM with validation of the shapes it must see.
+static thread_local void* g_gws = nullptr;  // scratch of the current layer call for the few-row GEMM
+static thread_local size_t g_gws_bytes = 0;
+
 static g4_status run_gemm(const void* A, int64_t lda, const void* B, const void* B2, int64_t ldb, void* C,
                           int64_t ldc, int32_t c_dtype, int64_t M, int64_t N, int64_t K, int32_t epi,
                           const float* aux, int64_t aux_ld, int32_t splits, int64_t split_stride, int32_t dt,
                           hipStream_t s) {
   GemmArgs a{};
+  a.ws = g_gws; a.ws_bytes = g_gws_bytes;
   a.A = A; a.lda = lda; a.B = B; a.B2 = B2; a.ldb = ldb; a.C = C; a.ldc = ldc; a.c_dtype = c_dtype;
   a.aux = aux; a.aux_ld = aux_ld; a.M = M; a.N = N; a.K = K; a.epi = epi;
   a.splits = splits < 1 ? 1 : splits; a.split_stride = split_stride;
   return gemm(a, dt, s);
+}
+
+// Split-K slices for a float32-output projection whose consumer (the row tail) sums the slices:
+// minimise rounds-of-256x256-tiles / splits over 1..4.
+static int32_t pick_splits(int64_t M, int64_t N, int64_t K) {
+  if (M < 128 || N % 256 || K % 256) return 1;
+  const int64_t tiles = ((M + 255) / 256) * (N / 256);
+  int32_t best = 1;
+  double best_cost = 1e30;
+  for (int32_t s = 1; s <= 4; ++s) {
+    if (K / s < 512) break;
+    const double rounds = (double)((tiles * s + 255) / 256);
+    const double cost = rounds / s * (1.0 + 0.03 * (s - 1));  // extra slices cost a little traffic
+    if (cost < best_cost - 1e-9) { best_cost = cost; best = s; }
+  }
+  return best;
 }
 
 struct LayerCtx {
@@ -204,19 +237,25 @@ static g4_status layer_impl(const LayerCtx& c) {
     if ((st = (x)) != G4_OK) return st; \
   } while (0)
   if (M == 0) return G4_OK;
+  g_gws = c.ws + c.p->gws;
+  g_gws_bytes = c.p->gws_bytes;
+  struct ClearGws { ~ClearGws() { g_gws = nullptr; g_gws_bytes = 0; } } clear_gws;
   // 1. pre-attention norm
   if (!c.xn_ready)
     G4_TRY(rownorm(c.h, G4_F32, 1, 0, l->input_norm, xn, nullptr, 1.f, nullptr, nullptr, M, H, m->eps, dt, c.s));
   // 2. projections: q, and k, v when the layer owns its cache
   {
-  TimedScope ts(G4_KC_QKV_GEMM, c.s);
-  G4_TRY(run_gemm(xn, H, l->wq, nullptr, H, qkv, qld, dt, M, nh * hd, H, EPI_STORE, nullptr, 0, 1, 0, dt, c.s));
-  if (own) {
-    G4_TRY(run_gemm(xn, H, l->wk, nullptr, H, qkv + nh * hd * E, qld, dt, M, nkv * hd, H, EPI_STORE, nullptr, 0, 1,
-                    0, dt, c.s));
-    G4_TRY(run_gemm(xn, H, l->wv, nullptr, H, qkv + (nh + nkv) * hd * E, qld, dt, M, nkv * hd, H, EPI_STORE, nullptr,
-                    0, 1, 0, dt, c.s));
-  }
+    TimedScope ts(G4_KC_QKV_GEMM, c.s);
+    GemmArgs ga{};
+    ga.A = xn; ga.lda = H; ga.ldb = H; ga.C = qkv; ga.ldc = qld; ga.c_dtype = dt; ga.M = M; ga.K = H;
+    ga.epi = EPI_STORE; ga.splits = 1; ga.ws = g_gws; ga.ws_bytes = g_gws_bytes;
+    ga.nseg = own ? 3 : 1;
+    ga.segB[0] = l->wq; ga.seg_rows[0] = nh * hd;
+    ga.segB[1] = l->wk; ga.seg_rows[1] = nkv * hd;
+    ga.segB[2] = l->wv; ga.seg_rows[2] = nkv * hd;
+    ga.N = nh * hd + (own ? 2 * nkv * hd : 0);
+    ga.B = l->wq;
+    G4_TRY(gemm(ga, dt, c.s));
   }
   // 3. per-head norms + RoPE; k and v go straight into this layer's cache rows
   HeadSeg segs[3];
@@ -243,7 +282,7 @@ static g4_status layer_impl(const LayerCtx& c) {
     else G4_TRY(attn_prefill(aa, dt, c.s));
   }
   // 5-6. o projection, then h += rms(a) * w_pa and xn2 = rms(h) * w_pf
-  const int32_t so = 1;
+  const int32_t so = pick_splits(M, H, nh * hd);
   {
   TimedScope ts(G4_KC_O_GEMM, c.s);
   G4_TRY(run_gemm(ao, nh * hd, l->wo, nullptr, nh * hd, fb, H, G4_F32, M, H, nh * hd, EPI_STORE, nullptr, 0, so,
@@ -260,7 +299,7 @@ static g4_status layer_impl(const LayerCtx& c) {
     G4_TRY(run_gemm(xn, H, l->w_gate, l->w_up, H, act, F, dt, M, F, H, EPI_GEGLU, nullptr, 0, 1, 0, dt, c.s));
   }
   // 8-9. down projection, then h += rms(ffn) * w_pff; hb = h in dtype for the PLE gate
-  const int32_t sd = 1;
+  const int32_t sd = pick_splits(M, H, F);
   {
   TimedScope ts(G4_KC_DOWN_GEMM, c.s);
   G4_TRY(run_gemm(act, F, l->w_down, nullptr, F, fb, H, G4_F32, M, H, F, EPI_STORE, nullptr, 0, sd, M * H, dt, c.s));
@@ -421,12 +460,23 @@ g4_status g4_linear(const void* A, const void* W, void* C, int64_t M, int64_t N,
   G4_REQ(M >= 0 && N > 0 && K > 0, G4_EINVAL, "M %lld N %lld K %lld", (long long)M, (long long)N, (long long)K);
   if (M == 0) return G4_OK;
   G4_REQ(A && W && C, G4_EINVAL, "A, W or C is NULL");
-  return run_gemm(A, K, W, nullptr, K, C, N, c_dtype, M, N, K, EPI_STORE, nullptr, 0, 1, 0, dtype, (hipStream_t)stream);
+  g_gws = ws;  // optional scratch for the few-row kernel
+  g_gws_bytes = ws ? ws_bytes : 0;
+  const g4_status st =
+      run_gemm(A, K, W, nullptr, K, C, N, c_dtype, M, N, K, EPI_STORE, nullptr, 0, 1, 0, dtype, (hipStream_t)stream);
+  g_gws = nullptr;
+  g_gws_bytes = 0;
+  return st;
 }
 
 size_t g4_ffn_geglu_ws(int64_t M, int64_t H, int64_t F, int32_t dtype) {
-  (void)H;
-  return al((size_t)M * F * dsize(dtype));
+  size_t sk = 0;
+  if (M <= 64 && dtype == G4_BF16) {
+    const size_t a = gemm_skinny_ws(M, (2 * F + 63) / 64 * 64, (H + 127) / 128 * 128);
+    const size_t b = gemm_skinny_ws(M, (H + 63) / 64 * 64, (F + 127) / 128 * 128);
+    sk = a > b ? a : b;
+  }
+  return al((size_t)M * F * dsize(dtype)) + al(sk);
 }
 
 g4_status g4_ffn_geglu(const void* x, const void* w_gate, const void* w_up, const void* w_down, float* out, int64_t M,
@@ -439,9 +489,13 @@ g4_status g4_ffn_geglu(const void* x, const void* w_gate, const void* w_up, cons
          g4_ffn_geglu_ws(M, H, F, dtype));
   if (M == 0) return G4_OK;
   hipStream_t s = (hipStream_t)stream;
+  g_gws = (char*)ws + al((size_t)M * F * dsize(dtype));
+  g_gws_bytes = ws_bytes - al((size_t)M * F * dsize(dtype));
   g4_status st = run_gemm(x, H, w_gate, w_up, H, ws, F, dtype, M, F, H, EPI_GEGLU, nullptr, 0, 1, 0, dtype, s);
-  if (st != G4_OK) return st;
-  return run_gemm(ws, F, w_down, nullptr, F, out, H, G4_F32, M, H, F, EPI_STORE, nullptr, 0, 1, 0, dtype, s);
+  if (st == G4_OK) st = run_gemm(ws, F, w_down, nullptr, F, out, H, G4_F32, M, H, F, EPI_STORE, nullptr, 0, 1, 0, dtype, s);
+  g_gws = nullptr;
+  g_gws_bytes = 0;
+  return st;
 }
 
 size_t g4_ple_inject_ws(int64_t M, int64_t H, int64_t d, int32_t dtype) {

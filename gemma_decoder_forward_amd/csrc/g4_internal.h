@@ -92,6 +92,12 @@ struct GemmArgs {
   int32_t epi;
   int32_t splits;        // split-K slices (EPI_STORE with f32 C only): slice s at C + s*split_stride
   int64_t split_stride;  // elements between slices
+  // EPI_STORE only: B rows (= C columns) are the concatenation of nseg (1..3) matrices segB[i] with
+  // seg_rows[i] rows each (nseg == 0 means one matrix, B, of N rows)
+  int32_t nseg;
+  const void* segB[3];
+  int64_t seg_rows[3];
+  void* ws; size_t ws_bytes;  // scratch for the few-row kernel's partial sums (may be null)
 };
 
 // Launchers (return G4_OK or a failure with the message set).
@@ -130,6 +136,9 @@ size_t attn_decode_ws(int64_t B, int64_t nh, int64_t hd, int64_t cap);
 g4_status cast_rows(const float* x, void* y, int64_t n, int32_t dtype, hipStream_t s);
 g4_status gemm_simt(const GemmArgs& a, int32_t dtype, hipStream_t s);
 bool gemm_mfma(const GemmArgs& a, hipStream_t s, g4_status* st);
+bool gemm_skinny(const GemmArgs& a, const void* const* segs, const int64_t* seg_rows, int nseg, void* ws,
+                 size_t ws_bytes, hipStream_t s, g4_status* st);
+size_t gemm_skinny_ws(int64_t M, int64_t Nt, int64_t K);
 g4_status attn_rowwise(const AttnArgs& a, int32_t dtype, hipStream_t s);
 bool attn_mfma(const AttnArgs& a, hipStream_t s, g4_status* st);
 g4_status embed_rows(const int32_t* ids, int64_t M, const void* E, int64_t vocab, int64_t H,

@@ -246,7 +246,7 @@ static g4_status launch_mfma(const GemmArgs& a, hipStream_t s) {
 // Picks a tile that gives enough blocks for 256 CUs; false if the shape does not suit the MFMA path.
 bool gemm_mfma(const GemmArgs& a, hipStream_t s, g4_status* st) {
   const int64_t tiles256 = ((a.M + 255) / 256) * (a.N / (a.epi == EPI_GEGLU ? 128 : 256)) * a.splits;
-  if (mfma_ok(a, 256) && tiles256 >= 256) {
+  if (mfma_ok(a, 256) && tiles256 >= 192) {
     *st = launch_mfma<256, 256>(a, s);
     return true;
   }

@@ -244,6 +244,26 @@ def test_linear_vs_oracle(dt, M, N, K):
     assert_close(Cd, ref, dt, "C in dtype")
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 256, 2560), (8, 3072, 2560), (33, 512, 10240), (64, 2560, 10240),
+                                   (17, 20480, 2560)])
+def test_linear_few_rows_weight_streaming(M, N, K):
+    """Decode-shaped projections (M = batch): the weight-streaming split-K path, given a workspace."""
+    log(f"linear few rows {M}x{N}x{K}")
+    A = randn((M, K), 72, torch.bfloat16)
+    W = randn((N, K), 73, torch.bfloat16, 0.02)
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    bd.g4_linear(A.data_ptr(), W.data_ptr(), C.data_ptr(), M, N, K, bd.G4_F32, bd.G4_BF16, ws.data_ptr(), ws.numel(),
+                 stream())
+    Cb = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    bd.g4_linear(A.data_ptr(), W.data_ptr(), Cb.data_ptr(), M, N, K, bd.G4_BF16, bd.G4_BF16, ws.data_ptr(),
+                 ws.numel(), stream())
+    torch.cuda.synchronize()
+    ref = O.f64(A) @ O.f64(W).T
+    assert max_rel(C, ref) <= 1e-3
+    assert_close(Cb, ref, "bf16", "bf16 out")
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_ffn_geglu_vs_oracle(dt):
     gdt, tdt = DT[dt]
