@@ -35,6 +35,11 @@ template <> struct io<bf16> {
 template <typename T> __device__ __forceinline__ float ldf(const T* p) { return io<T>::ld(p); }
 template <typename T> __device__ __forceinline__ void stf(T* p, float v) { io<T>::st(p, v); }
 
+// Lane 0's value of a float, broadcast (the builtin is int -> int: pass the bits, not the value).
+__device__ __forceinline__ float first_lane_f(float v) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
@@ -132,6 +137,8 @@ struct AttnArgs {
 g4_status attn_prefill(const AttnArgs& a, int32_t dtype, hipStream_t s);
 g4_status attn_decode(const AttnArgs& a, void* ws, size_t ws_bytes, int32_t dtype, hipStream_t s);
 size_t attn_decode_ws(int64_t B, int64_t nh, int64_t hd, int64_t cap);
+bool attn_decode_mfma(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t s, g4_status* st);
+size_t attn_decode_mfma_ws(int64_t B, int64_t nh, int64_t hd, int64_t cap);
 
 g4_status cast_rows(const float* x, void* y, int64_t n, int32_t dtype, hipStream_t s);
 g4_status gemm_simt(const GemmArgs& a, int32_t dtype, hipStream_t s);

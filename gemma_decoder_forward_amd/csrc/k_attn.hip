@@ -215,11 +215,15 @@ static void dec_plan(int64_t B, int64_t nkv, int64_t max_keys, int& chunk, int& 
 size_t attn_decode_ws(int64_t B, int64_t nh, int64_t hd, int64_t cap) {
   int chunk, nchunk;
   dec_plan(B, 1, cap, chunk, nchunk);  // nkv = 1 gives the largest chunk count
-  return (size_t)B * nh * nchunk * (hd + 2) * sizeof(float);
+  const size_t a = (size_t)B * nh * nchunk * (hd + 2) * sizeof(float);
+  const size_t b = attn_decode_mfma_ws(B, nh, hd, cap);
+  return a > b ? a : b;
 }
 
 g4_status attn_decode(const AttnArgs& a, void* ws, size_t ws_bytes, int32_t dtype, hipStream_t s) {
   if (a.B == 0) return G4_OK;
+  g4_status mst = G4_OK;
+  if (dtype == G4_BF16 && attn_decode_mfma(a, ws, ws_bytes, s, &mst)) return mst;
   const int64_t G = a.nh / a.nkv;
   if (G > DEC_GMAX) return fail(G4_EUNSUP, "attn_decode: %lld query heads per kv head (max %d)", (long long)G, DEC_GMAX);
   if (a.hd > 512) return fail(G4_ERANGE, "attn_decode: head_dim %lld > 512", (long long)a.hd);

@@ -226,6 +226,33 @@ def test_attention_decode_vs_oracle(dt, hd, sliding, window, nh, nkv):
         assert_close(out.reshape(B, 1, nh, hd)[b], ref, dt, f"seq {b}")
 
 
+@pytest.mark.parametrize("hd,sliding,window,nh,nkv", [(256, 1, 512, 2, 2), (512, 0, 0, 8, 2), (128, 1, 100, 8, 2)])
+def test_attention_decode_many_sequences_long_chunks(hd, sliding, window, nh, nkv):
+    """64 sequences: the key chunks grow to 256 keys (several 16-key steps per wave), ragged ends."""
+    log(f"attn_decode bf16 B=64 hd={hd} sliding={sliding} G={nh // nkv}")
+    gdt, tdt = DT["bf16"]
+    B, cap = 64, 1500
+    g = torch.Generator().manual_seed(70 + hd)
+    pos_l = torch.randint(0, cap, (B,), generator=g).tolist()
+    pos_l[0], pos_l[1], pos_l[2] = 0, cap - 1, 255
+    pos = torch.tensor(pos_l, dtype=torch.int32, device="cuda")
+    q = randn((B, nh * hd), 71 + hd, tdt)
+    K = randn((B, nkv, cap, hd), 72, tdt)
+    V = randn((B, nkv, cap, hd), 73, tdt)
+    out = torch.empty((B, nh * hd), dtype=tdt, device="cuda")
+    wsb = bd.g4_attn_decode_ws(B, nh, hd, cap)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    t = _kv_table([(K, V, sliding)])
+    bd.g4_attn_decode(q.data_ptr(), nh * hd, t, 1, 0, 0, sliding, window, pos.data_ptr(), B, nh, nkv, hd, 0.5,
+                      out.data_ptr(), nh * hd, ws.data_ptr(), wsb, gdt, stream())
+    torch.cuda.synchronize()
+    qv = O.f64(q).reshape(B, 1, nh, hd)
+    Kc, Vc, oc = K.cpu(), V.cpu(), out.reshape(B, 1, nh, hd)
+    for b in range(B):
+        ref = O.attention(qv[b], O.f64(Kc[b]), O.f64(Vc[b]), [pos_l[b]], window if sliding else None, scale=0.5)
+        assert_close(oc[b], ref, "bf16", f"seq {b} pos {pos_l[b]}")
+
+
 # ------------------------------------------------------------------------------- projections
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("M,N,K", [(77, 130, 200), (256, 512, 2560), (1, 256, 64), (300, 2560, 256)])
