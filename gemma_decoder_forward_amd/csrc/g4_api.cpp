@@ -102,7 +102,7 @@ static g4_status check_kv(const g4_kv_entry* kv, int32_t n_kv, int32_t layer, in
 
 // ---- workspace plan of the layer forward -----------------------------------------------------
 struct Plan {
-  size_t xn, qkv, ao, f32buf, act, hb, gm, dec, gws, gws_bytes, emb_e, emb_p, total;
+  size_t xn, qkv, ao, f32buf, act, hb, gm, dec, gws, gws_bytes, fx, fx_bytes, fy, fy_bytes, emb_e, emb_p, total;
   int64_t qkv_ld, splits;
 };
 
@@ -137,6 +137,18 @@ static Plan plan(const g4_model_desc* m, int64_t B, int64_t T, int64_t cap, int3
       if (b > p.gws_bytes) p.gws_bytes = b;
     }
     o += al(p.gws_bytes);
+    // the few-row layer path: split-K partials of q/k/v, gate/up and the PLE gate (fx) and of the
+    // projections back to H (fy); a GEMM reading one region writes the other
+    for (const int64_t rows : {(nh + 2 * nkv) * hs, (nh + 2 * nkv) * hf, 2 * m->ffn, m->ple_dim}) {
+      const size_t b = gemm_skinny_ws(M, (rows + 63) / 64 * 64, (H + 127) / 128 * 128);
+      if (b > p.fx_bytes) p.fx_bytes = b;
+    }
+    for (const int64_t k : {m->ffn, nh * hs, nh * hf, m->ple_dim}) {
+      const size_t b = gemm_skinny_ws(M, (H + 63) / 64 * 64, (k + 127) / 128 * 128);
+      if (b > p.fy_bytes) p.fy_bytes = b;
+    }
+    p.fx = o; o += al(p.fx_bytes);
+    p.fy = o; o += al(p.fy_bytes);
   }
   p.total = o;
   // the entry (embedding + PLE) reuses the start of the workspace
@@ -212,7 +224,180 @@ static g4_status check_layer(const g4_model_desc* m, const g4_layer_desc* l, int
   return check_kv(kv, n_kv, layer, l->kv_src, l->sliding, hd, T, mode);
 }
 
+// The layer for few token rows (decode batches, M <= 64, bf16): every projection streams its weights
+// once through the few-row GEMM and leaves float32 split-K partials, and the next step sums them as it
+// reads them -- the per-head norm/RoPE kernel for q/k/v, the row tails for the projections back to H,
+// and the staging of the next GEMM's A operand for the gelu-tanh products (gate * up, PLE gate * input).
+// Same arithmetic as the general path; fewer launches and no intermediate finishing passes.
+static bool few_row_ok(const LayerCtx& c) {
+  const g4_model_desc* m = c.m;
+  const g4_layer_desc* l = c.l;
+  const int64_t M = c.B * c.T, H = m->hidden, nh = m->n_heads, nkv = m->n_kv_heads;
+  const int64_t hd = l->sliding ? m->head_dim_swa : m->head_dim_full;
+  if (m->dtype != G4_BF16 || M > 64 || c.p->fx_bytes == 0) return false;
+  const void* q3[3] = {l->wq, l->wk, l->wv};
+  const int64_t r3[3] = {nh * hd, nkv * hd, nkv * hd};
+  const void* gu[2] = {l->w_gate, l->w_up};
+  const int64_t rgu[2] = {m->ffn, m->ffn};
+  const void* wo[1] = {l->wo};
+  const void* wd[1] = {l->w_down};
+  const void* pg[1] = {l->ple_gate};
+  const void* pp[1] = {l->ple_proj};
+  const int64_t rH[1] = {H}, rd[1] = {m->ple_dim};
+  return skinny_ok(M, H, q3, r3, l->kv_src == c.layer ? 3 : 1, H) && skinny_ok(M, nh * hd, wo, rH, 1, nh * hd) &&
+         skinny_ok(M, H, gu, rgu, 2, H) && skinny_ok(M, m->ffn, wd, rH, 1, m->ffn) &&
+         skinny_ok(M, H, pg, rd, 1, H) && skinny_ok(M, m->ple_dim, pp, rH, 1, m->ple_dim) &&
+         (m->ffn % 4) == 0 && (m->ple_dim % 4) == 0 && ((uintptr_t)c.ple_in & 15) == 0;
+}
+
+// Whether the consumer GEMM (K x Nc weights) should form its A operand from `parts` float32 slices while
+// staging it (each of its blocks re-reads its slice of the partials from L2), rather than after a
+// separate finishing pass writes A once in bf16: fused while the re-reads stay within a few MB.
+static bool stage_from_parts(int64_t M, int64_t Kc, int64_t Nc, int parts, int reads_per_value) {
+  int rows = 0, kc = 0, sp = 0;
+  skinny_plan(M, Kc, Nc, &rows, &kc, &sp);
+  const double bytes = (double)(Nc / rows) * sp * M * kc * parts * 4.0 * reads_per_value;
+  return bytes <= 16e6;
+}
+
+static g4_status few_row_layer(const LayerCtx& c) {
+  const g4_model_desc* m = c.m;
+  const g4_layer_desc* l = c.l;
+  const int32_t dt = m->dtype;
+  const size_t E = dsize(dt);
+  const int64_t M = c.B * c.T, H = m->hidden, nh = m->n_heads, nkv = m->n_kv_heads, F = m->ffn, d = m->ple_dim;
+  const int sliding = l->sliding;
+  const int64_t hd = sliding ? m->head_dim_swa : m->head_dim_full;
+  const bool own = l->kv_src == c.layer;
+  char* xn = c.ws + c.p->xn;
+  char* qkv = c.ws + c.p->qkv;
+  char* ao = c.ws + c.p->ao;
+  char* hb = c.ws + c.p->hb;
+  char* act = c.ws + c.p->act;
+  char* gm = c.ws + c.p->gm;
+  float* X = (float*)(c.ws + c.p->fx);
+  float* Y = (float*)(c.ws + c.p->fy);
+  const size_t XB = c.p->fx_bytes, YB = c.p->fy_bytes;
+  const int64_t qld = c.p->qkv_ld;
+  g4_status st;
+#define G4_TRY(x)                 \
+  do {                            \
+    if ((st = (x)) != G4_OK) return st; \
+  } while (0)
+  if (!c.xn_ready)
+    G4_TRY(rownorm(c.h, G4_F32, 1, 0, l->input_norm, xn, nullptr, 1.f, nullptr, nullptr, M, H, m->eps, dt, c.s));
+  // q, k, v partials, then per-head norms + RoPE from their sums; k and v land in the cache
+  const int64_t Nq = nh * hd + (own ? 2 * nkv * hd : 0);
+  int s1 = 0;
+  {
+    TimedScope ts(G4_KC_QKV_GEMM, c.s);
+    const void* segs[3] = {l->wq, l->wk, l->wv};
+    const int64_t rows[3] = {nh * hd, nkv * hd, nkv * hd};
+    SkA sa{};
+    sa.a = xn; sa.lda = H; sa.kind = SKA_BF16;
+    G4_TRY(gemm_skinny_part(sa, M, H, segs, rows, own ? 3 : 1, H, X, XB, &s1, c.s));
+  }
+  {
+    TimedScope ts(G4_KC_QK_NORM_ROPE, c.s);
+    HeadSeg segs[3];
+    int ns = 0;
+    segs[ns++] = HeadSeg{X, Nq, l->q_norm, qkv, qld, 0, (int32_t)nh, 1};
+    if (own) {
+      const g4_kv_entry& e = c.kv[c.layer];
+      segs[ns++] = HeadSeg{X + nh * hd, Nq, l->k_norm, e.k, 0, e.cap, (int32_t)nkv, 1};
+      segs[ns++] = HeadSeg{X + (nh + nkv) * hd, Nq, nullptr, e.v, 0, e.cap, (int32_t)nkv, 0};
+    }
+    G4_TRY(qk_norm_rope_parts(segs, ns, s1, M * Nq, c.pos, c.B, c.T, hd, sliding ? m->theta_swa : m->theta_full,
+                              rot_pairs(m, sliding), m->eps, dt, c.s));
+  }
+  {
+    const g4_kv_entry& src = c.kv[l->kv_src];
+    AttnArgs aa{};
+    aa.q = qkv; aa.q_ld = qld; aa.k = src.k; aa.v = src.v; aa.cap = src.cap; aa.pos0 = c.pos;
+    aa.B = c.B; aa.T = c.T; aa.nh = nh; aa.nkv = nkv; aa.hd = hd; aa.sliding = sliding; aa.window = m->window;
+    aa.scale = 1.f; aa.out = ao; aa.out_ld = nh * hd;
+    TimedScope ts(G4_KC_ATTENTION, c.s);
+    if (c.mode == G4_DECODE) G4_TRY(attn_decode(aa, c.ws + c.p->dec, c.p->fx - c.p->dec, dt, c.s));
+    else G4_TRY(attn_prefill(aa, dt, c.s));
+  }
+  const void* wo[1] = {l->wo};
+  const void* wd[1] = {l->w_down};
+  const void* wpg[1] = {l->ple_gate};
+  const void* wpp[1] = {l->ple_proj};
+  const int64_t rH[1] = {H}, rd[1] = {d};
+  // o projection; h += rms(a) * w_pa; xn2 = rms(h) * w_pf
+  int s2 = 0;
+  {
+    TimedScope ts(G4_KC_O_GEMM, c.s);
+    SkA sa{};
+    sa.a = ao; sa.lda = nh * hd; sa.kind = SKA_BF16;
+    G4_TRY(gemm_skinny_part(sa, M, nh * hd, wo, rH, 1, nh * hd, Y, YB, &s2, c.s));
+  }
+  {
+    TimedScope ts(G4_KC_ROW_TAIL, c.s);
+    G4_TRY(rownorm(Y, G4_F32, s2, M * H, l->post_attn_norm, nullptr, c.h, 1.f, l->pre_ffn_norm, xn, M, H, m->eps,
+                   dt, c.s));
+  }
+  // gate/up partials; the down projection forms gelu_tanh(gate) * up while staging its A operand
+  int s3 = 0, s4 = 0;
+  {
+    TimedScope ts(G4_KC_GATE_UP_GEMM, c.s);
+    const void* segs[2] = {l->w_gate, l->w_up};
+    const int64_t rows[2] = {F, F};
+    SkA sa{};
+    sa.a = xn; sa.lda = H; sa.kind = SKA_BF16;
+    G4_TRY(gemm_skinny_part(sa, M, H, segs, rows, 2, H, X, XB, &s3, c.s));
+  }
+  {
+    TimedScope ts(G4_KC_DOWN_GEMM, c.s);
+    SkA sa{};
+    if (stage_from_parts(M, F, H, s3, 2)) {
+      sa.a = X; sa.lda = 2 * F; sa.kind = SKA_GEGLU; sa.parts = s3; sa.part_stride = M * 2 * F; sa.up_off = F;
+    } else {
+      GemmArgs ga{};
+      ga.M = M; ga.N = F; ga.C = act; ga.ldc = F; ga.c_dtype = dt; ga.epi = EPI_GEGLU;
+      G4_TRY(gemm_skinny_finish(ga, X, s3, 2 * F, c.s));
+      sa.a = act; sa.lda = F; sa.kind = SKA_BF16;
+    }
+    G4_TRY(gemm_skinny_part(sa, M, F, wd, rH, 1, F, Y, YB, &s4, c.s));
+  }
+  {
+    TimedScope ts(G4_KC_ROW_TAIL, c.s);
+    G4_TRY(rownorm(Y, G4_F32, s4, M * H, l->post_ffn_norm, nullptr, c.h, 1.f, nullptr, hb, M, H, m->eps, dt, c.s));
+  }
+  // PLE: gate partials from the raw residual; the projection forms gelu_tanh(gate) * ple_in while staging
+  int s5 = 0, s6 = 0;
+  {
+    TimedScope ts(G4_KC_PLE_GEMM, c.s);
+    SkA sa{};
+    sa.a = hb; sa.lda = H; sa.kind = SKA_BF16;
+    G4_TRY(gemm_skinny_part(sa, M, H, wpg, rd, 1, H, X, XB, &s5, c.s));
+    const float* ple_l = c.ple_in + (int64_t)c.layer * d;
+    SkA sb{};
+    if (stage_from_parts(M, d, H, s5, 1)) {
+      sb.a = X; sb.lda = d; sb.kind = SKA_GELU_MUL; sb.parts = s5; sb.part_stride = M * d;
+      sb.aux = ple_l; sb.aux_ld = m->n_layers * d;
+    } else {
+      GemmArgs ga{};
+      ga.M = M; ga.N = d; ga.C = gm; ga.ldc = d; ga.c_dtype = dt; ga.epi = EPI_GELU_MUL;
+      ga.aux = ple_l; ga.aux_ld = m->n_layers * d;
+      G4_TRY(gemm_skinny_finish(ga, X, s5, d, c.s));
+      sb.a = gm; sb.lda = d; sb.kind = SKA_BF16;
+    }
+    G4_TRY(gemm_skinny_part(sb, M, d, wpp, rH, 1, d, Y, YB, &s6, c.s));
+  }
+  {
+    TimedScope ts(G4_KC_ROW_TAIL, c.s);
+    G4_TRY(rownorm(Y, G4_F32, s6, M * H, l->post_ple_norm, nullptr, c.h, l->layer_scalar, c.next_input_norm,
+                   c.next_input_norm ? xn : nullptr, M, H, m->eps, dt, c.s));
+  }
+#undef G4_TRY
+  (void)E;
+  return G4_OK;
+}
+
 static g4_status layer_impl(const LayerCtx& c) {
+  if (c.B * c.T > 0 && few_row_ok(c)) return few_row_layer(c);
   const g4_model_desc* m = c.m;
   const g4_layer_desc* l = c.l;
   const int32_t dt = m->dtype;

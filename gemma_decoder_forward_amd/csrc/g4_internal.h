@@ -119,6 +119,11 @@ struct HeadSeg {
 g4_status qk_norm_rope(const HeadSeg* segs, int nseg, const int32_t* pos, int64_t B, int64_t T,
                        int64_t hd, float theta, int64_t n_rot, float eps, int32_t dtype,
                        hipStream_t s);
+// The same with every input segment read as the sum of `parts` float32 slices part_stride apart (the
+// split-K partials of the projection); outputs in dtype.
+g4_status qk_norm_rope_parts(const HeadSeg* segs, int nseg, int parts, int64_t part_stride, const int32_t* pos,
+                             int64_t B, int64_t T, int64_t hd, float theta, int64_t n_rot, float eps, int32_t dtype,
+                             hipStream_t s);
 
 g4_status rownorm(const void* x, int32_t x_dtype, int32_t x_parts, int64_t part_stride,
                   const void* w, void* y, float* res, float res_scale, const void* w_next,
@@ -146,6 +151,29 @@ bool gemm_mfma(const GemmArgs& a, hipStream_t s, g4_status* st);
 bool gemm_skinny(const GemmArgs& a, const void* const* segs, const int64_t* seg_rows, int nseg, void* ws,
                  size_t ws_bytes, hipStream_t s, g4_status* st);
 size_t gemm_skinny_ws(int64_t M, int64_t Nt, int64_t K);
+
+// Few-row GEMM writing float32 split-K partials [splits][M][Nt] (Nt = sum of the segment rows), for a
+// consumer that sums the slices itself. The A operand is bf16 rows, or is formed while it is staged from
+// float32 partial slices of an earlier few-row GEMM:
+enum SkAKind : int {
+  SKA_BF16 = 0,      // A[m][k] = a[m*lda + k] (bf16)
+  SKA_GEGLU = 1,     // A[m][k] = bf16(gelu_tanh(sum_p P[m*lda + k]) * sum_p P[m*lda + up_off + k])
+  SKA_GELU_MUL = 2,  // A[m][k] = bf16(gelu_tanh(sum_p P[m*lda + k]) * aux[m*aux_ld + k])
+};
+struct SkA {
+  const void* a; int64_t lda;
+  int32_t kind; int32_t parts; int64_t part_stride;  // partial slices: `parts` slices part_stride floats apart
+  int64_t up_off;
+  const float* aux; int64_t aux_ld;
+};
+// True if the few-row kernel takes these shapes (M <= 64, K % 128 == 0, segments of 64-row multiples,
+// 16-byte aligned rows).
+bool skinny_ok(int64_t M, int64_t K, const void* const* segs, const int64_t* seg_rows, int nseg, int64_t ldb);
+void skinny_plan(int64_t M, int64_t K, int64_t Nt, int* rows_per_block, int* kc, int* splits);
+// Sums `splits` partial slices [splits][M][Nt] and applies a's epilogue into a.C (a.M, a.N, a.ldc, ...).
+g4_status gemm_skinny_finish(const GemmArgs& a, const float* part, int splits, int64_t Nt, hipStream_t s);
+g4_status gemm_skinny_part(const SkA& sa, int64_t M, int64_t K, const void* const* segs, const int64_t* seg_rows,
+                           int nseg, int64_t ldb, float* part, size_t part_bytes, int* splits, hipStream_t s);
 g4_status attn_rowwise(const AttnArgs& a, int32_t dtype, hipStream_t s);
 bool attn_mfma(const AttnArgs& a, hipStream_t s, g4_status* st);
 g4_status embed_rows(const int32_t* ids, int64_t M, const void* E, int64_t vocab, int64_t H,

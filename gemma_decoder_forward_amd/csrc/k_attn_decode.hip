@@ -3,10 +3,10 @@
 // the group share it).
 //
 // Scores: v_mfma_f32_16x16x32_bf16 with the group's query heads as rows (padded to 16) and 16 keys as
-// columns. Lane l supplies key (l % 16) and head elements 128c + 32*(l/16) + 8t .. +7 for MFMA t of
-// 128-element chunk c, i.e. 64 contiguous bytes of a K row per lane per chunk straight from memory; the
-// queries sit in registers in the same element order. Lanes 0..15 then hold the scores of heads 0..3
-// for key (l % 16).
+// columns. Lane l supplies key (l % 16) and head elements 128c + 32t + 8*(l/16) .. +7 for MFMA t of
+// 128-element chunk c, straight from memory: the four lanes of a key read 64 contiguous bytes per load.
+// The queries sit in registers in the same element order. Lanes 0..15 then hold the scores of heads
+// 0..3 for key (l % 16).
 // P V: each lane owns HD/64 consecutive head elements for all heads of the group; V rows are read
 // coalesced and each probability is broadcast from the lane that holds it (readlane), so the
 // accumulation is plain FMAs. Online softmax in the exp2 domain.
@@ -47,12 +47,12 @@ __global__ __launch_bounds__(256) void k_attn_dec_mfma(AttnArgs a, int chunk, in
   bf16x8_t qf[NC][4];
   {
     const bool real = col < G;
-    const bf16* qr = (const bf16*)a.q + b * a.q_ld + (g * G + (real ? col : 0)) * HD + 32 * q4;
+    const bf16* qr = (const bf16*)a.q + b * a.q_ld + (g * G + (real ? col : 0)) * HD + 8 * q4;
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc)
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        uint4 v = real ? *(const uint4*)(qr + 128 * cc + 8 * t) : make_uint4(0, 0, 0, 0);
+        uint4 v = real ? *(const uint4*)(qr + 128 * cc + 32 * t) : make_uint4(0, 0, 0, 0);
         qf[cc][t] = *(bf16x8_t*)&v;
       }
   }
@@ -73,12 +73,12 @@ __global__ __launch_bounds__(256) void k_attn_dec_mfma(AttnArgs a, int chunk, in
     const bool kv = key < k1;
     // scores S[head][key] for 16 keys
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-    const bf16* kr = Kb + (kv ? key : kt) * HD + 32 * q4;
+    const bf16* kr = Kb + (kv ? key : kt) * HD + 8 * q4;
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
       uint4 kw[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) kw[t] = *(const uint4*)(kr + 128 * cc + 8 * t);
+      for (int t = 0; t < 4; ++t) kw[t] = *(const uint4*)(kr + 128 * cc + 32 * t);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[cc][t], *(bf16x8_t*)&kw[t], s, 0, 0, 0);
@@ -162,30 +162,53 @@ __global__ __launch_bounds__(256) void k_attn_dec_mfma(AttnArgs a, int chunk, in
   }
 }
 
-// Combines the key-chunk partials (m in the exp2 domain) of each (sequence, head).
+// Combines the key-chunk partials (m in the exp2 domain) of one (sequence, head) and 256 head elements
+// (grid.y covers the head). The chunk weights exp2(m_c - M) are formed once in LDS; every thread then
+// adds its element over the chunks with independent loads.
+constexpr int DM_MAX_CHUNKS = 2048;
+
 __global__ __launch_bounds__(256) void k_attn_dec_merge2(AttnArgs a, int nchunk, const float* __restrict__ ws) {
+  __shared__ float wgt[DM_MAX_CHUNKS];
+  __shared__ float sh[32];
   const int64_t bh = blockIdx.x;
   const int64_t b = bh / a.nh, h = bh % a.nh;
   const int hd = (int)a.hd;
+  const int tid = threadIdx.x;
   const float* src = ws + bh * nchunk * (int64_t)(hd + 2);
-  float M = -INFINITY;
-  for (int c = 0; c < nchunk; ++c) M = fmaxf(M, src[c * (hd + 2) + hd]);
-  float L = 0.f;
-  if (M > -INFINITY)
-    for (int c = 0; c < nchunk; ++c) L += src[c * (hd + 2) + hd + 1] * __builtin_amdgcn_exp2f(src[c * (hd + 2) + hd] - M);
-  const float il = L > 0.f ? 1.f / L : 0.f;
-  for (int d = threadIdx.x; d < hd; d += 256) {
-    float o = 0.f;
-    if (M > -INFINITY)
-      for (int c = 0; c < nchunk; ++c) o += src[c * (hd + 2) + d] * __builtin_amdgcn_exp2f(src[c * (hd + 2) + hd] - M);
-    stf((bf16*)a.out + b * a.out_ld + h * hd + d, o * il);
+  float mloc = -INFINITY;
+  for (int c = tid; c < nchunk; c += 256) mloc = fmaxf(mloc, src[c * (hd + 2) + hd]);
+  mloc = wave_max(mloc);
+  if ((tid & 63) == 0) sh[tid >> 6] = mloc;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+  float lloc = 0.f;
+  for (int c = tid; c < nchunk; c += 256) {
+    const float w = M > -INFINITY ? __builtin_amdgcn_exp2f(src[c * (hd + 2) + hd] - M) : 0.f;
+    wgt[c] = w;
+    lloc += src[c * (hd + 2) + hd + 1] * w;
   }
+  lloc = wave_sum(lloc);
+  __syncthreads();
+  if ((tid & 63) == 0) sh[4 + (tid >> 6)] = lloc;
+  __syncthreads();
+  const float L = sh[4] + sh[5] + sh[6] + sh[7];
+  const float il = L > 0.f ? 1.f / L : 0.f;
+  const int d = blockIdx.y * 256 + tid;
+  if (d >= hd) return;
+  float o = 0.f;
+#pragma unroll 8
+  for (int c = 0; c < nchunk; ++c) o += wgt[c] * src[c * (hd + 2) + d];
+  stf((bf16*)a.out + b * a.out_ld + h * hd + d, o * il);
 }
 
 static void dm_plan(int64_t B, int64_t nkv, int64_t max_keys, int& chunk, int& nchunk) {
   chunk = 1024;
   while (chunk > 64 && B * nkv * ((max_keys + chunk - 1) / chunk) < 512) chunk >>= 1;
   nchunk = (int)((max_keys + chunk - 1) / chunk);
+  while (nchunk > DM_MAX_CHUNKS) {  // the merge keeps one weight per chunk in LDS
+    chunk *= 2;
+    nchunk = (int)((max_keys + chunk - 1) / chunk);
+  }
   if (nchunk < 1) nchunk = 1;
 }
 
@@ -212,7 +235,8 @@ bool attn_decode_mfma(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t 
   else if (a.hd == 256) hipLaunchKernelGGL(k_attn_dec_mfma<256>, g, dim3(256), 0, s, a, chunk, nchunk, sl2, (float*)ws);
   else hipLaunchKernelGGL(k_attn_dec_mfma<512>, g, dim3(256), 0, s, a, chunk, nchunk, sl2, (float*)ws);
   if ((*st = check_launch("attn_decode_mfma")) != G4_OK) return true;
-  hipLaunchKernelGGL(k_attn_dec_merge2, dim3((unsigned)(a.B * a.nh)), dim3(256), 0, s, a, nchunk, (const float*)ws);
+  hipLaunchKernelGGL(k_attn_dec_merge2, dim3((unsigned)(a.B * a.nh), (unsigned)((a.hd + 255) / 256)), dim3(256), 0, s, a,
+                     nchunk, (const float*)ws);
   *st = check_launch("attn_decode_merge");
   return true;
 }

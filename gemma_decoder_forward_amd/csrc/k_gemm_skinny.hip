@@ -1,11 +1,11 @@
 // Weight-streaming GEMM for few token rows (decode: M = batch <= 64): C = A B^T with B the weights.
 //
 // HBM-bound: every weight byte is read once. A block owns 64 weight rows (one 16-row MFMA block per wave)
-// and a K range of kc; the activation slice A[0:M, k-range] is staged once in LDS and shared by the four
-// waves. Per 128-k step a lane reads 64 contiguous bytes of its weight row (4 lanes cover 256 bytes of
-// a row), the next step's weights are prefetched into registers, and v_mfma_f32_16x16x32_bf16 forms
-// the products: lane l supplies row (l % 16) and k values 32*(l/16) + 8t .. +7 for MFMA t of the step,
-// for the activations and the weights alike, so both operands see the same k order.
+// or 16 rows (see RW below) and a K range of kc; the activation slice A[0:M, k-range] is staged once in
+// LDS. Per 128-k step a lane reads four 16-byte pieces of its weight row; load t of a step covers
+// k = 32t .. 32t+31 of 16 rows, the four lanes of a row reading 64 contiguous bytes, and
+// v_mfma_f32_16x16x32_bf16 t takes exactly those: lane l supplies row (l % 16) and k = 32t + 8(l/16)
+// .. +7, for the activations and the weights alike.
 // Blocks over K write float32 partials [split][M][rows]; k_gemm_finish sums them and applies the
 // epilogue (store, gelu-tanh gate*up, gelu*aux).
 //
@@ -30,51 +30,135 @@ __device__ __forceinline__ const bf16* sk_row(const SkSeg& s, int64_t r) {
   return s.b[2] + (r - s.end[1]) * s.ldb;
 }
 
-template <int MB>
-__global__ __launch_bounds__(256) void k_gemm_skinny(const bf16* __restrict__ A, int64_t lda, int64_t M, SkSeg sg,
-                                                     int64_t K, int kc, float* __restrict__ part, int64_t Nt) {
+constexpr int SK_D = 4;  // 128-k steps per batch of weight loads
+
+// 8 consecutive A values formed from float32 partial slices (see SkAKind), rounded to bf16.
+template <int AK>
+__device__ __forceinline__ uint4 sk_a_from_parts(const SkA& sa, int64_t m, int64_t k) {
+  const float* pr = (const float*)sa.a + m * sa.lda + k;
+  float g[8], u[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) g[e] = u[e] = 0.f;
+  for (int p = 0; p < sa.parts; ++p) {
+    const float4 x0 = *(const float4*)(pr + p * sa.part_stride), x1 = *(const float4*)(pr + p * sa.part_stride + 4);
+    g[0] += x0.x; g[1] += x0.y; g[2] += x0.z; g[3] += x0.w; g[4] += x1.x; g[5] += x1.y; g[6] += x1.z; g[7] += x1.w;
+    if (AK == SKA_GEGLU) {
+      const float* ur = pr + p * sa.part_stride + sa.up_off;
+      const float4 y0 = *(const float4*)ur, y1 = *(const float4*)(ur + 4);
+      u[0] += y0.x; u[1] += y0.y; u[2] += y0.z; u[3] += y0.w; u[4] += y1.x; u[5] += y1.y; u[6] += y1.z; u[7] += y1.w;
+    }
+  }
+  if (AK == SKA_GELU_MUL) {
+    const float* ar = sa.aux + m * sa.aux_ld + k;
+    const float4 y0 = *(const float4*)ar, y1 = *(const float4*)(ar + 4);
+    u[0] = y0.x; u[1] = y0.y; u[2] = y0.z; u[3] = y0.w; u[4] = y1.x; u[5] = y1.y; u[6] = y1.z; u[7] = y1.w;
+  }
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    w[e] = (uint32_t)f2bf(gelu_tanh(g[2 * e]) * u[2 * e]) | ((uint32_t)f2bf(gelu_tanh(g[2 * e + 1]) * u[2 * e + 1]) << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// RW = 4: each wave owns 16 weight rows over the block's whole K range (64 rows per block, A shared by
+// the four waves). RW = 1: the four waves share 16 rows and split the block's K range between them,
+// adding their sums through LDS at the end -- for matrices with few rows, so that the grid fills the
+// chip with fewer K splits (fewer partial slices for the consumer to add).
+template <int MB, int AK, int RW>
+__global__ __launch_bounds__(256) void k_gemm_skinny(SkA sa, int64_t M, SkSeg sg, int64_t K, int kc,
+                                                     float* __restrict__ part, int64_t Nt) {
   extern __shared__ __attribute__((aligned(16))) bf16 As[];
+  constexpr int BR = 16 * RW;  // weight rows per block
   const int ald = kc + 8;  // LDS row stride (bf16); (kc + 8) * 2 bytes = 4 (mod 64) words -> conflict-free rows
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t k0 = (int64_t)blockIdx.y * kc;
   const int kn = (int)((K - k0) < kc ? (K - k0) : kc);
-  // stage A[0:16*MB, k0:k0+kn] (rows >= M are zero)
+  const int nst = kn >> 7;  // 128-k steps of this block
+  const int q = lane >> 4;
+  const int wrow0 = RW == 4 ? wave * 16 : 0;
+  const int spw = RW == 4 ? nst : (nst + 3) / 4;  // steps of each wave: [sbeg, send)
+  const int sbeg = RW == 4 ? 0 : wave * spw;
+  const int send = sbeg + spw < nst ? sbeg + spw : nst;
+  const int nmine = send > sbeg ? send - sbeg : 0;
+
+  // Weights through a buffer descriptor that starts at the block's first row (a block never straddles
+  // two matrices of the concatenation): a step past this wave's K range gets an offset beyond the
+  // descriptor's size, reads as zero and costs no memory traffic. So every load below is issued
+  // unconditionally, the compiler's wait counts stay exact, and batches are double-buffered in
+  // registers: the loads of batch i+1 are in flight while batch i is multiplied.
+  const bf16* wblk = sk_row(sg, (int64_t)blockIdx.x * BR) + k0;
+  const int64_t wbytes = ((BR - 1) * sg.ldb + kn) * 2;
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)wblk, (short)0, (int)wbytes, 0x00020000);
+  const uint32_t lrow = (uint32_t)((wrow0 + (lane & 15)) * sg.ldb + 8 * q) * 2;
+  auto load_batch = [&](uint4 (&w)[SK_D][4], int s0) {
+#pragma unroll
+    for (int s = 0; s < SK_D; ++s) {
+      const int st = sbeg + s0 + s;
+      const uint32_t off = st < send ? lrow + (uint32_t)st * 256 : 0x80000000u;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(off + 64 * t), 0, 0);
+        w[s][t] = *(const uint4*)&v;
+      }
+    }
+  };
+  uint4 wa[SK_D][4], wb[SK_D][4];
+  load_batch(wa, 0);
+
+  // stage A[0:16*MB, k0:k0+kn] (rows >= M are zero) while the first weights arrive
   const int cpr = kn / 8;
   for (int idx = tid; idx < 16 * MB * cpr; idx += 256) {
     const int m = idx / cpr, c = idx - m * cpr;
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (m < M) v = *(const uint4*)(A + m * lda + k0 + 8 * c);
+    if (m < M) {
+      if (AK == SKA_BF16) v = *(const uint4*)((const bf16*)sa.a + m * sa.lda + k0 + 8 * c);
+      else v = sk_a_from_parts<AK>(sa, m, k0 + 8 * c);
+    }
     *(uint4*)(As + m * ald + 8 * c) = v;
   }
   __syncthreads();
 
-  const int64_t r = (int64_t)blockIdx.x * 64 + wave * 16 + (lane & 15);
-  const int q = lane >> 4;
-  const bf16* wrow = sk_row(sg, r) + k0 + 32 * q;
-  const bf16* arow = As + (lane & 15) * ald + 32 * q;
+  const bf16* arow = As + (lane & 15) * ald + 8 * q;
   f32x4_t acc[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc[mb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  uint4 wcur[4], wnxt[4];
+  auto mul_batch = [&](const uint4 (&w)[SK_D][4], int s0) {
 #pragma unroll
-  for (int t = 0; t < 4; ++t) wcur[t] = *(const uint4*)(wrow + 8 * t);
-  for (int kk = 0; kk < kn; kk += 128) {
-    const bool more = kk + 128 < kn;
+    for (int s = 0; s < SK_D; ++s)
+      if (s0 + s < nmine) {  // uniform; the LDS slice of A ends at this block's K range
+        const int kk = (sbeg + s0 + s) * 128;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) wnxt[t] = more ? *(const uint4*)(wrow + kk + 128 + 8 * t) : wcur[t];
+        for (int t = 0; t < 4; ++t) {
+          const bf16x8_t bw = *(const bf16x8_t*)&w[s][t];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const bf16x8_t bw = *(const bf16x8_t*)&wcur[t];
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const bf16x8_t af = *(const bf16x8_t*)(arow + mb * 16 * ald + kk + 8 * t);
-        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bw, acc[mb], 0, 0, 0);
+          for (int mb = 0; mb < MB; ++mb) {
+            const bf16x8_t af = *(const bf16x8_t*)(arow + mb * 16 * ald + kk + 32 * t);
+            acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bw, acc[mb], 0, 0, 0);
+          }
+        }
       }
-    }
+  };
+  // two register batches alternate roles (no copies between them, so no waits for data in flight)
+  for (int s0 = 0; s0 < nmine; s0 += 2 * SK_D) {
+    load_batch(wb, s0 + SK_D);
+    mul_batch(wa, s0);
+    load_batch(wa, s0 + 2 * SK_D);
+    mul_batch(wb, s0 + SK_D);
+  }
+  if (RW == 1) {  // add the four waves' sums
+    __shared__ f32x4_t red[3][MB][64];
+    if (wave > 0)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) wcur[t] = wnxt[t];
+      for (int mb = 0; mb < MB; ++mb) red[wave - 1][mb][lane] = acc[mb];
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int w = 0; w < 3; ++w) acc[mb] += red[w][mb][lane];
   }
   // C[m][r]: lane holds column (lane % 16) and rows 4*(lane/16) + i of each 16-row block
+  const int64_t r = (int64_t)blockIdx.x * BR + wrow0 + (lane & 15);
   float* pb = part + (int64_t)blockIdx.y * M * Nt;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -108,28 +192,71 @@ __global__ __launch_bounds__(256) void k_gemm_finish(GemmArgs a, const float* __
   }
 }
 
-static int sk_kc(int mb, int64_t K, int64_t rowblocks) {
-  int kc = mb >= 4 ? 1024 : 2048;                    // LDS: 16*mb rows x (kc + 8) bf16 <= ~132 KB
-  while (kc > 128 && rowblocks * ((K + kc - 1) / kc) < 512) kc >>= 1;  // enough blocks for 256 CUs
-  if (kc > K) kc = (int)((K + 127) / 128 * 128);
-  return kc;
+// Rows per block: 64 (four waves on separate rows) when the matrix has enough rows, else 16 (four waves
+// splitting K). With more than 16 token rows every block stages a large A slice, so 64-row blocks
+// (which share it four ways) are preferred down to 2048-row matrices. Then the K range per block (kc, a multiple of 128) and the number of K splits: about
+// three blocks per CU, each wave with at least one 128-k step, and the LDS slice of A, 16*mb rows x
+// (kc + 8) bf16, within 66 KB (mb 1, 2) or 132 KB (mb 4, one block per CU with deep weight loads).
+static void sk_plan(int mb, int64_t K, int64_t Nt, int& rw, int& kc, int& splits) {
+  rw = Nt / 64 >= (mb == 1 ? 192 : 32) ? 4 : 1;  // with more token rows, A staging favours 64-row blocks
+  const int64_t rowblocks = Nt / (16 * rw);
+  const int64_t steps = K / 128;
+  const int64_t max_steps = mb == 1 ? 16 : 8;
+  int64_t s = (768 + rowblocks - 1) / rowblocks;
+  if (rw == 1 && s > steps / 4) s = steps / 4;  // at least one step per wave
+  const int64_t smin = (steps + max_steps - 1) / max_steps;
+  if (s < smin) s = smin;
+  if (s > steps) s = steps;
+  if (s < 1) s = 1;
+  const int64_t per = (steps + s - 1) / s;
+  kc = (int)(per * 128);
+  splits = (int)((steps + per - 1) / per);
 }
 
 size_t gemm_skinny_ws(int64_t M, int64_t Nt, int64_t K) {
   const int mb = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-  const int kc = sk_kc(mb, K, Nt / 64);
-  return (size_t)((K + kc - 1) / kc) * M * Nt * sizeof(float);
+  int rw, kc, splits;
+  sk_plan(mb, K, Nt, rw, kc, splits);
+  return (size_t)splits * M * Nt * sizeof(float);
 }
 
-// M <= 64 rows, bf16, K % 128 == 0, every B segment a multiple of 64 rows. Returns false if not taken.
-bool gemm_skinny(const GemmArgs& a, const void* const* segs, const int64_t* seg_rows, int nseg, void* ws,
-                 size_t ws_bytes, hipStream_t s, g4_status* st) {
-  if (a.M > 64 || a.M <= 0 || a.K % 128 || a.lda % 8 || a.ldb % 8) return false;
+bool skinny_ok(int64_t M, int64_t K, const void* const* segs, const int64_t* seg_rows, int nseg, int64_t ldb) {
+  if (M > 64 || M <= 0 || K % 128 || ldb % 8 || nseg < 1 || nseg > 3) return false;
+  for (int i = 0; i < nseg; ++i)
+    if (seg_rows[i] % 64 || ((uintptr_t)segs[i] & 15)) return false;
+  return true;
+}
+
+template <int MB, int RW>
+static void sk_launch(const SkA& sa, dim3 g, size_t lds, hipStream_t s, int64_t M, const SkSeg& sg, int64_t K,
+                      int kc, float* part, int64_t Nt) {
+  static bool lds_set = false;  // allow > 64 KB of dynamic LDS (gfx950 has 160 KB per CU)
+  if (!lds_set) {
+    (void)hipFuncSetAttribute((const void*)k_gemm_skinny<MB, SKA_BF16, RW>, hipFuncAttributeMaxDynamicSharedMemorySize, 140 * 1024);
+    (void)hipFuncSetAttribute((const void*)k_gemm_skinny<MB, SKA_GEGLU, RW>, hipFuncAttributeMaxDynamicSharedMemorySize, 140 * 1024);
+    (void)hipFuncSetAttribute((const void*)k_gemm_skinny<MB, SKA_GELU_MUL, RW>, hipFuncAttributeMaxDynamicSharedMemorySize, 140 * 1024);
+    lds_set = true;
+  }
+  if (sa.kind == SKA_GEGLU)
+    hipLaunchKernelGGL((k_gemm_skinny<MB, SKA_GEGLU, RW>), g, dim3(256), lds, s, sa, M, sg, K, kc, part, Nt);
+  else if (sa.kind == SKA_GELU_MUL)
+    hipLaunchKernelGGL((k_gemm_skinny<MB, SKA_GELU_MUL, RW>), g, dim3(256), lds, s, sa, M, sg, K, kc, part, Nt);
+  else
+    hipLaunchKernelGGL((k_gemm_skinny<MB, SKA_BF16, RW>), g, dim3(256), lds, s, sa, M, sg, K, kc, part, Nt);
+}
+
+g4_status gemm_skinny_part(const SkA& sa, int64_t M, int64_t K, const void* const* segs, const int64_t* seg_rows,
+                           int nseg, int64_t ldb, float* part, size_t part_bytes, int* splits_out, hipStream_t s) {
+  if (!skinny_ok(M, K, segs, seg_rows, nseg, ldb))
+    return fail(G4_EUNSUP, "few-row GEMM: unsupported shape M=%lld K=%lld", (long long)M, (long long)K);
+  if (sa.kind == SKA_BF16 ? (sa.lda % 8 || ((uintptr_t)sa.a & 15))
+                          : (sa.lda % 4 || sa.part_stride % 4 || sa.up_off % 4 || sa.parts < 1 || ((uintptr_t)sa.a & 15) ||
+                             (sa.kind == SKA_GELU_MUL && (sa.aux_ld % 4 || ((uintptr_t)sa.aux & 15)))))
+    return fail(G4_EUNSUP, "few-row GEMM: A operand rows not 16-byte aligned");
   SkSeg sg{};
   int64_t Nt = 0;
   for (int i = 0; i < 3; ++i) {
     if (i < nseg) {
-      if (seg_rows[i] % 64 || ((uintptr_t)segs[i] & 15)) return false;
       Nt += seg_rows[i];
       sg.b[i] = (const bf16*)segs[i];
     } else {
@@ -137,33 +264,57 @@ bool gemm_skinny(const GemmArgs& a, const void* const* segs, const int64_t* seg_
     }
     sg.end[i] = Nt;
   }
-  sg.ldb = a.ldb;
-  if (((uintptr_t)a.A & 15)) return false;
-  const int mb = a.M <= 16 ? 1 : (a.M <= 32 ? 2 : 4);
-  const int kc = sk_kc(mb, a.K, Nt / 64);
-  const int splits = (int)((a.K + kc - 1) / kc);
-  const size_t need = (size_t)splits * a.M * Nt * sizeof(float);
-  if (!ws || ws_bytes < need) return false;
-  dim3 g((unsigned)(Nt / 64), (unsigned)splits);
+  sg.ldb = ldb;
+  const int mb = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  int rw, kc, splits;
+  sk_plan(mb, K, Nt, rw, kc, splits);
+  if ((size_t)splits * M * Nt * sizeof(float) > part_bytes)
+    return fail(G4_EINVAL, "few-row GEMM: partial buffer too small");
+  dim3 g((unsigned)(Nt / (16 * rw)), (unsigned)splits);
   const size_t lds = (size_t)16 * mb * (kc + 8) * sizeof(bf16);
-  static bool lds_set = false;  // allow > 64 KB of dynamic LDS (gfx950 has 160 KB per CU)
-  if (!lds_set) {
-    (void)hipFuncSetAttribute((const void*)k_gemm_skinny<1>, hipFuncAttributeMaxDynamicSharedMemorySize, 150 * 1024);
-    (void)hipFuncSetAttribute((const void*)k_gemm_skinny<2>, hipFuncAttributeMaxDynamicSharedMemorySize, 150 * 1024);
-    (void)hipFuncSetAttribute((const void*)k_gemm_skinny<4>, hipFuncAttributeMaxDynamicSharedMemorySize, 150 * 1024);
-    lds_set = true;
+  if (rw == 4) {
+    if (mb == 1) sk_launch<1, 4>(sa, g, lds, s, M, sg, K, kc, part, Nt);
+    else if (mb == 2) sk_launch<2, 4>(sa, g, lds, s, M, sg, K, kc, part, Nt);
+    else sk_launch<4, 4>(sa, g, lds, s, M, sg, K, kc, part, Nt);
+  } else {
+    if (mb == 1) sk_launch<1, 1>(sa, g, lds, s, M, sg, K, kc, part, Nt);
+    else if (mb == 2) sk_launch<2, 1>(sa, g, lds, s, M, sg, K, kc, part, Nt);
+    else sk_launch<4, 1>(sa, g, lds, s, M, sg, K, kc, part, Nt);
   }
-  float* part = (float*)ws;
-  if (mb == 1) hipLaunchKernelGGL(k_gemm_skinny<1>, g, dim3(256), lds, s, (const bf16*)a.A, a.lda, a.M, sg, a.K, kc, part, Nt);
-  else if (mb == 2) hipLaunchKernelGGL(k_gemm_skinny<2>, g, dim3(256), lds, s, (const bf16*)a.A, a.lda, a.M, sg, a.K, kc, part, Nt);
-  else hipLaunchKernelGGL(k_gemm_skinny<4>, g, dim3(256), lds, s, (const bf16*)a.A, a.lda, a.M, sg, a.K, kc, part, Nt);
-  if ((*st = check_launch("gemm_skinny")) != G4_OK) return true;
+  *splits_out = splits;
+  return check_launch("gemm_skinny");
+}
+
+void skinny_plan(int64_t M, int64_t K, int64_t Nt, int* rows_per_block, int* kc, int* splits) {
+  int rw = 0;
+  sk_plan(M <= 16 ? 1 : (M <= 32 ? 2 : 4), K, Nt, rw, *kc, *splits);
+  *rows_per_block = 16 * rw;
+}
+
+g4_status gemm_skinny_finish(const GemmArgs& a, const float* part, int splits, int64_t Nt, hipStream_t s) {
+  if (a.M * a.N == 0) return G4_OK;
   dim3 gf((unsigned)((a.M * a.N + 255) / 256));
   if (a.epi == EPI_GEGLU) hipLaunchKernelGGL((k_gemm_finish<EPI_GEGLU, false>), gf, dim3(256), 0, s, a, part, splits, Nt);
   else if (a.epi == EPI_GELU_MUL) hipLaunchKernelGGL((k_gemm_finish<EPI_GELU_MUL, false>), gf, dim3(256), 0, s, a, part, splits, Nt);
   else if (a.c_dtype == G4_F32) hipLaunchKernelGGL((k_gemm_finish<EPI_STORE, true>), gf, dim3(256), 0, s, a, part, splits, Nt);
   else hipLaunchKernelGGL((k_gemm_finish<EPI_STORE, false>), gf, dim3(256), 0, s, a, part, splits, Nt);
-  *st = check_launch("gemm_finish");
+  return check_launch("gemm_finish");
+}
+
+// M <= 64 rows, bf16, K % 128 == 0, every B segment a multiple of 64 rows. Returns false if not taken.
+bool gemm_skinny(const GemmArgs& a, const void* const* segs, const int64_t* seg_rows, int nseg, void* ws,
+                 size_t ws_bytes, hipStream_t s, g4_status* st) {
+  if (!skinny_ok(a.M, a.K, segs, seg_rows, nseg, a.ldb) || a.lda % 8 || ((uintptr_t)a.A & 15)) return false;
+  int64_t Nt = 0;
+  for (int i = 0; i < nseg; ++i) Nt += seg_rows[i];
+  if (!ws || ws_bytes < gemm_skinny_ws(a.M, Nt, a.K)) return false;
+  SkA sa{};
+  sa.a = a.A; sa.lda = a.lda; sa.kind = SKA_BF16;
+  float* part = (float*)ws;
+  int splits = 0;
+  if ((*st = gemm_skinny_part(sa, a.M, a.K, segs, seg_rows, nseg, a.ldb, part, ws_bytes, &splits, s)) != G4_OK)
+    return true;
+  *st = gemm_skinny_finish(a, part, splits, Nt, s);
   return true;
 }
 

@@ -20,14 +20,20 @@ __global__ __launch_bounds__(256) void k_rownorm(const TX* __restrict__ x, int p
   __shared__ float sh[32];
   const int64_t row = blockIdx.x;
   const TX* xr = x + row * dim;
-  float v[VPT];
+  // Every operand of the row is loaded up front, so the row costs one memory round trip, not three.
+  float v[VPT], rv[VPT], wv[VPT], wn[VPT];
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
     const int64_t c = threadIdx.x + (int64_t)i * 256;
     float s = 0.f;
+    rv[i] = 0.f;
+    wv[i] = wn[i] = 1.f;
     if (c < dim) {
       for (int p = 0; p < parts; ++p) s += ldf(xr + p * part_stride + c);
+      if (res) rv[i] = res[row * dim + c];
+      if (w) wv[i] = ldf(w + c);
+      if (w_next) wn[i] = ldf(w_next + c);
     }
     v[i] = s;
     ss += s * s;
@@ -39,11 +45,10 @@ __global__ __launch_bounds__(256) void k_rownorm(const TX* __restrict__ x, int p
   for (int i = 0; i < VPT; ++i) {
     const int64_t c = threadIdx.x + (int64_t)i * 256;
     if (c < dim) {
-      float n = v[i] * inv;
-      if (w) n *= ldf(w + c);
+      const float n = v[i] * inv * wv[i];
       if (y) stf(y + row * dim + c, n);
       if (res) {
-        const float r = (res[row * dim + c] + n) * res_scale;
+        const float r = (rv[i] + n) * res_scale;
         res[row * dim + c] = r;
         v[i] = r;
         ss2 += r * r;
@@ -59,7 +64,102 @@ __global__ __launch_bounds__(256) void k_rownorm(const TX* __restrict__ x, int p
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int64_t c = threadIdx.x + (int64_t)i * 256;
-      if (c < dim) stf(y_next + row * dim + c, w_next ? v[i] * inv2 * ldf(w_next + c) : v[i]);
+      if (c < dim) stf(y_next + row * dim + c, w_next ? v[i] * inv2 * wn[i] : v[i]);
+    }
+  }
+}
+
+// 4 consecutive values as float (16-byte float or 8-byte bf16 loads) and back.
+__device__ __forceinline__ float4 ld4(const float* p) { return *(const float4*)p; }
+__device__ __forceinline__ float4 ld4(const bf16* p) {
+  const uint2 u = *(const uint2*)p;
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xffff0000u));
+}
+__device__ __forceinline__ void st4(float* p, float4 v) { *(float4*)p = v; }
+__device__ __forceinline__ void st4(bf16* p, float4 v) {
+  *(uint2*)p = make_uint2((uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16), (uint32_t)f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16));
+}
+__device__ __forceinline__ float4 operator+(float4 a, float4 b) { return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w); }
+__device__ __forceinline__ float4 operator*(float4 a, float4 b) { return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w); }
+__device__ __forceinline__ float4 operator*(float4 a, float s) { return make_float4(a.x * s, a.y * s, a.z * s, a.w * s); }
+__device__ __forceinline__ float dot4(float4 a) { return a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w; }
+
+// The same tail for dim % 4 == 0 with 4-wide loads; the split-K slices are read 8 at a time so that a
+// row with many slices still costs few memory round trips. Slices are added in slice order.
+template <typename TX, typename T, int V4>
+__global__ __launch_bounds__(256) void k_rownorm4(const TX* __restrict__ x, int parts, int64_t part_stride,
+                                                  const T* __restrict__ w, T* __restrict__ y,
+                                                  float* __restrict__ res, float res_scale,
+                                                  const T* __restrict__ w_next, T* __restrict__ y_next,
+                                                  int64_t dim, float eps) {
+  __shared__ float sh[32];
+  const int64_t row = blockIdx.x;
+  const TX* xr = x + row * dim;
+  const float4 one = make_float4(1.f, 1.f, 1.f, 1.f), zero = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 v[V4], rv[V4], wv[V4], wn[V4];
+#pragma unroll
+  for (int i = 0; i < V4; ++i) {
+    const int64_t c = 4 * (threadIdx.x + (int64_t)i * 256);
+    v[i] = rv[i] = zero;
+    wv[i] = wn[i] = one;
+    if (c < dim) {
+      if (res) rv[i] = ld4(res + row * dim + c);
+      if (w) wv[i] = ld4(w + c);
+      if (w_next) wn[i] = ld4(w_next + c);
+    }
+  }
+  int p = 0;
+  for (; p + 8 <= parts; p += 8) {
+#pragma unroll
+    for (int i = 0; i < V4; ++i) {
+      const int64_t c = 4 * (threadIdx.x + (int64_t)i * 256);
+      if (c < dim) {
+        float4 t[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) t[j] = ld4(xr + (p + j) * part_stride + c);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[i] = v[i] + t[j];
+      }
+    }
+  }
+  for (; p < parts; ++p) {
+#pragma unroll
+    for (int i = 0; i < V4; ++i) {
+      const int64_t c = 4 * (threadIdx.x + (int64_t)i * 256);
+      if (c < dim) v[i] = v[i] + ld4(xr + p * part_stride + c);
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < V4; ++i) ss += dot4(v[i]);
+  ss = block_sum<256>(ss, sh);
+  const float inv = 1.f / sqrtf(ss / (float)dim + eps);
+  float ss2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < V4; ++i) {
+    const int64_t c = 4 * (threadIdx.x + (int64_t)i * 256);
+    if (c < dim) {
+      const float4 n = v[i] * inv * wv[i];
+      if (y) st4(y + row * dim + c, n);
+      if (res) {
+        const float4 r = (rv[i] + n) * res_scale;
+        st4(res + row * dim + c, r);
+        v[i] = r;
+        ss2 += dot4(r);
+      }
+    }
+  }
+  if (y_next) {
+    float inv2 = 1.f;
+    if (w_next) {
+      ss2 = block_sum<256>(ss2, sh);
+      inv2 = 1.f / sqrtf(ss2 / (float)dim + eps);
+    }
+#pragma unroll
+    for (int i = 0; i < V4; ++i) {
+      const int64_t c = 4 * (threadIdx.x + (int64_t)i * 256);
+      if (c < dim) st4(y_next + row * dim + c, w_next ? v[i] * inv2 * wn[i] : v[i]);
     }
   }
 }
@@ -68,6 +168,20 @@ template <typename TX, typename T>
 static void launch_rownorm(int vpt, dim3 g, hipStream_t s, const TX* x, int parts, int64_t ps,
                            const T* w, T* y, float* res, float rs, const T* wn, T* yn, int64_t dim,
                            float eps) {
+  const bool vec = (dim % 4) == 0 && (ps % 4) == 0 && dim <= 4096 &&
+                   (((uintptr_t)x | (uintptr_t)w | (uintptr_t)y | (uintptr_t)res | (uintptr_t)wn | (uintptr_t)yn) &
+                    15) == 0;
+  if (vec) {
+    const int v4 = (int)((dim / 4 + 255) / 256);
+#define G4_RN4(V) \
+  hipLaunchKernelGGL((k_rownorm4<TX, T, V>), g, dim3(256), 0, s, x, parts, ps, w, y, res, rs, wn, yn, dim, eps)
+    if (v4 <= 1) G4_RN4(1);
+    else if (v4 <= 2) G4_RN4(2);
+    else if (v4 <= 3) G4_RN4(3);
+    else G4_RN4(4);
+#undef G4_RN4
+    return;
+  }
 #define G4_RN(V) \
   hipLaunchKernelGGL((k_rownorm<TX, T, V>), g, dim3(256), 0, s, x, parts, ps, w, y, res, rs, wn, yn, dim, eps)
   if (vpt <= 1) G4_RN(1);
@@ -104,8 +218,8 @@ g4_status rownorm(const void* x, int32_t x_dtype, int32_t x_parts, int64_t part_
 
 // --------------------------------------------------------------------------------------------
 // Per-head RMSNorm + NeoX RoPE (cortiq-engine q/k/v head loops; turbospark per-head norms and
-// `encode_rope_proportional_neox`; taconite `rope_half`). One block per token row; the cos/sin of the
-// row's position are computed once in float64 into LDS and shared by every head of every segment.
+// `encode_rope_proportional_neox`; taconite `rope_half`). One block per (token row, four heads), one
+// wave per head; each block puts the cos/sin of the row's position in LDS for its heads.
 // Pair j of a head pairs elements j and j + hd/2; pairs j >= n_rot are left untouched (zero frequency).
 // --------------------------------------------------------------------------------------------
 struct SegDev {
@@ -114,37 +228,54 @@ struct SegDev {
   void* y; int64_t y_ld; int64_t y_cap;
   int32_t heads; int32_t rope;
 };
-struct SegPack { SegDev s[3]; int n; int total_heads; };
+struct SegPack { SegDev s[3]; int n; int total_heads; int parts; int64_t part_stride; };
 
-template <typename T, int PPL>  // PPL: pairs per lane (hd/2 <= 64*PPL)
+// TI: input element type (float for summed split-K slices); T: output type. PPL: pairs per lane
+// (hd/2 <= 64*PPL).
+template <typename TI, typename T, int PPL>
 __global__ __launch_bounds__(256) void k_qknr(SegPack pk, const int32_t* __restrict__ pos, int64_t T_,
-                                              int hd, float theta, int n_rot, float eps) {
+                                              int hd, double rstep, int n_rot, float eps) {
   __shared__ float cs[256], sn[256];
   const int64_t m = blockIdx.x;
   const int64_t b = m / T_, t = m % T_;
   const int64_t p = pos ? (int64_t)pos[b] + t : 0;
   const int half = hd >> 1;
+  // angle of pair j: p * theta^(-2j/hd) = p * rstep^j, in float64 (rstep^j by binary powering), reduced
+  // to [-pi, pi] in float64 with 2*pi split into two doubles, then cos/sin in float32
   for (int j = threadIdx.x; j < n_rot; j += 256) {
-    const double inv = pow((double)theta, -2.0 * (double)j / (double)hd);
-    double sv, cv;
-    sincos((double)p * inv, &sv, &cv);
-    cs[j] = (float)cv;
-    sn[j] = (float)sv;
+    double inv = 1.0, base = rstep;
+    for (int e = j; e; e >>= 1) {
+      if (e & 1) inv *= base;
+      base *= base;
+    }
+    const double ang = (double)p * inv;
+    const double k = rint(ang * 0.15915494309189535);
+    double r = fma(-k, 6.283185307179586, ang);
+    r = fma(-k, 2.4492935982947064e-16, r);
+    float sv, cv;
+    sincosf((float)r, &sv, &cv);
+    cs[j] = cv;
+    sn[j] = sv;
   }
   __syncthreads();
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int gh = wave; gh < pk.total_heads; gh += 4) {
+  for (int gh = blockIdx.y * 4 + wave; gh < pk.total_heads; gh += 4 * gridDim.y) {
     int si = 0, h = gh;
     while (si < pk.n - 1 && h >= pk.s[si].heads) { h -= pk.s[si].heads; ++si; }
     const SegDev& sg = pk.s[si];
-    const T* xh = (const T*)sg.x + m * sg.x_ld + (int64_t)h * hd;
+    const TI* xh = (const TI*)sg.x + m * sg.x_ld + (int64_t)h * hd;
     float a[PPL], c[PPL];
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < PPL; ++i) {
       const int j = lane + 64 * i;
       a[i] = c[i] = 0.f;
-      if (j < half) { a[i] = ldf(xh + j); c[i] = ldf(xh + j + half); }
+      if (j < half)
+#pragma unroll 4
+        for (int pp = 0; pp < pk.parts; ++pp) {
+          a[i] += ldf(xh + pp * pk.part_stride + j);
+          c[i] += ldf(xh + pp * pk.part_stride + j + half);
+        }
       ss += a[i] * a[i] + c[i] * c[i];
     }
     ss = wave_sum(ss);
@@ -175,13 +306,16 @@ __global__ __launch_bounds__(256) void k_qknr(SegPack pk, const int32_t* __restr
   }
 }
 
-g4_status qk_norm_rope(const HeadSeg* segs, int nseg, const int32_t* pos, int64_t B, int64_t T,
-                       int64_t hd, float theta, int64_t n_rot, float eps, int32_t dtype, hipStream_t s) {
+static g4_status qknr_launch(const HeadSeg* segs, int nseg, int parts, int64_t part_stride, bool f32_in,
+                             const int32_t* pos, int64_t B, int64_t T, int64_t hd, float theta, int64_t n_rot,
+                             float eps, int32_t dtype, hipStream_t s) {
   if (B * T == 0) return G4_OK;
   if (hd > 512 || hd < 2 || (hd & 1)) return fail(G4_ERANGE, "qk_norm_rope: head_dim %lld not in [2, 512]", (long long)hd);
   SegPack pk{};
   pk.n = nseg;
   pk.total_heads = 0;
+  pk.parts = parts;
+  pk.part_stride = part_stride;
   int any_rope = 0;
   for (int i = 0; i < nseg; ++i) {
     pk.s[i] = SegDev{segs[i].x, segs[i].x_ld, segs[i].w, segs[i].y, segs[i].y_ld, segs[i].y_cap,
@@ -190,16 +324,32 @@ g4_status qk_norm_rope(const HeadSeg* segs, int nseg, const int32_t* pos, int64_
     any_rope |= segs[i].rope;
   }
   const int nr = any_rope ? (int)n_rot : 0;
-  dim3 g((unsigned)(B * T));
+  const double rstep = pow((double)theta, -2.0 / (double)hd);
+  // one wave per head: blocks of four heads, so a token's heads run in parallel
+  dim3 g((unsigned)(B * T), (unsigned)((pk.total_heads + 3) / 4));
   const int ppl = (int)((hd / 2 + 63) / 64);
-#define G4_QK(TT, P) hipLaunchKernelGGL((k_qknr<TT, P>), g, dim3(256), 0, s, pk, pos, T, (int)hd, theta, nr, eps)
-  if (dtype == G4_BF16) {
-    if (ppl <= 1) G4_QK(bf16, 1); else if (ppl <= 2) G4_QK(bf16, 2); else G4_QK(bf16, 4);
+#define G4_QK(TI, TT, P) \
+  hipLaunchKernelGGL((k_qknr<TI, TT, P>), g, dim3(256), 0, s, pk, pos, T, (int)hd, rstep, nr, eps)
+  if (dtype == G4_BF16 && f32_in) {
+    if (ppl <= 1) G4_QK(float, bf16, 1); else if (ppl <= 2) G4_QK(float, bf16, 2); else G4_QK(float, bf16, 4);
+  } else if (dtype == G4_BF16) {
+    if (ppl <= 1) G4_QK(bf16, bf16, 1); else if (ppl <= 2) G4_QK(bf16, bf16, 2); else G4_QK(bf16, bf16, 4);
   } else {
-    if (ppl <= 1) G4_QK(float, 1); else if (ppl <= 2) G4_QK(float, 2); else G4_QK(float, 4);
+    if (ppl <= 1) G4_QK(float, float, 1); else if (ppl <= 2) G4_QK(float, float, 2); else G4_QK(float, float, 4);
   }
 #undef G4_QK
   return check_launch("qk_norm_rope");
+}
+
+g4_status qk_norm_rope(const HeadSeg* segs, int nseg, const int32_t* pos, int64_t B, int64_t T,
+                       int64_t hd, float theta, int64_t n_rot, float eps, int32_t dtype, hipStream_t s) {
+  return qknr_launch(segs, nseg, 1, 0, false, pos, B, T, hd, theta, n_rot, eps, dtype, s);
+}
+
+g4_status qk_norm_rope_parts(const HeadSeg* segs, int nseg, int parts, int64_t part_stride, const int32_t* pos,
+                             int64_t B, int64_t T, int64_t hd, float theta, int64_t n_rot, float eps, int32_t dtype,
+                             hipStream_t s) {
+  return qknr_launch(segs, nseg, parts, part_stride, true, pos, B, T, hd, theta, n_rot, eps, dtype, s);
 }
 
 // --------------------------------------------------------------------------------------------

@@ -180,6 +180,21 @@ def test_bf16_stack_per_layer_parity(cid, T):
     assert max(errs) <= TOL_BF16_RELL2, f"layer {int(np.argmax(errs))}: {max(errs):.3e}"
 
 
+@pytest.mark.parametrize("T", [1, 24, 48])
+def test_bf16_few_row_prefill_per_layer(T):
+    """Prefills of at most 64 token rows take the few-row layer path (fused partial sums); E4B layer pair."""
+    cfg = configs.get(2, T=T)
+    model, layers, glob = build_model(cfg)
+    acts = gen.activations(cfg, "cuda")
+    h0, ple = _oracle_inputs(cfg, glob, acts, T)
+    hs = [h0]
+    O.forward(cfg, host_layer(layers), h0, ple, O.prefill_positions([0], T), O.new_caches(cfg, 1, T), per_layer=hs)
+    caches, table = model.new_caches(1, T)
+    errs = _per_layer(model, hs, ple, acts["pos"], table, T, bd.G4_PREFILL)
+    log(f"T={T} per-layer rel L2: " + " ".join(f"{e:.1e}" for e in errs))
+    assert max(errs) <= TOL_BF16_RELL2
+
+
 # ------------------------------------------------------------------------------- full sizes, sampled rows
 def _rows_case(cfg, layer, h0_host, ple_host, model, T, extra):
     rows = list(range(32)) + extra + list(range(T - 32, T))
