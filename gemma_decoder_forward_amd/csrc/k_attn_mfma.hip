@@ -77,6 +77,16 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
   const int ntiles = hib >= lob ? (int)((hib - kstart) / AT_KB + 1) : 0;
   int64_t qlo = a.sliding ? qi - a.window + 1 : 0;
   if (qlo < 0) qlo = 0;
+  const int64_t qhi = qi < hib ? qi : hib;  // this query's last visible key
+  // keys visible to every query of the wave: [wlo_all, whi_all] (empty for a wave with invalid queries)
+  int64_t wlo_all, whi_all;
+  {
+    const int64_t first = p0 + (int64_t)run * 32, last = p0 + (int64_t)run * 32 + 31;
+    wlo_all = a.sliding ? last - a.window + 1 : 0;
+    if (wlo_all < lob) wlo_all = lob;
+    whi_all = first < hib ? first : hib;
+    if (!(gi < ngroups && (int64_t)run * 32 + 31 < a.T)) { wlo_all = 1; whi_all = 0; }
+  }
 
   // Q fragments (B operand of S^T): query col, hd 16s + 8h .. +7
   bf16x8_t qf[KS];
@@ -166,20 +176,34 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] += xch[((wave ^ 1) * 16 + r) * 64 + lane];
     }
-    // mask, scale to the exp2 domain, online softmax
+    // mask (only on tiles that cut the causal edge, the window start or the block's key range), scale
+    // to the exp2 domain, online softmax
     float mt = -INFINITY;
+    if (k0 >= wlo_all && k0 + AT_KB - 1 <= whi_all) {  // every key of the tile visible to every query
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t key = k0 + 8 * (r >> 2) + 4 * h + (r & 3);
-      const bool vis = qvalid && key <= qi && key >= qlo && key <= hib;
-      const float v = vis ? s[r] * sl2 : -INFINITY;
-      s[r] = v;
-      mt = fmaxf(mt, v);
+      for (int r = 0; r < 16; ++r) {
+        s[r] *= sl2;
+        mt = fmaxf(mt, s[r]);
+      }
+    } else {
+      const int rel = (int)(k0 - qlo), lim = (int)(qhi - k0);  // visible keys: rel + key' >= 0, key' <= lim
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kk = 8 * (r >> 2) + 4 * h + (r & 3);
+        const bool vis = qvalid && kk + rel >= 0 && kk <= lim;
+        const float v = vis ? s[r] * sl2 : -INFINITY;
+        s[r] = v;
+        mt = fmaxf(mt, v);
+      }
     }
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float m_new = fmaxf(m_run, mt);
+    // The reference maximum is raised only when the tile's maximum exceeds it by more than 8 (log2
+    // domain): probabilities then stay below 2^8, which float32 sums and bf16 P hold exactly as well,
+    // and the accumulator rescale -- a multiply of every O register -- is skipped on almost all tiles.
+    // The result is the same softmax (every term and the normaliser use one reference).
+    const bool raise = mt > m_run + 8.f;
+    const float m_new = raise ? mt : m_run;
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     float psum = 0.f;
     bf16x8_t pb[2];
 #pragma unroll
@@ -188,12 +212,16 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
       psum += p;
       pb[r >> 3][r & 7] = (__bf16)p;
     }
-    l_run = l_run * alpha + psum;
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // some query of the wave moved its reference
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < NB; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+    }
+    l_run += psum;
     m_run = m_new;
-#pragma unroll
-    for (int d = 0; d < NB; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
     // O^T += V^T P^T
     const bf16* vf = vs + (half * HW + col) * AT_VLD + 4 * h;
 #pragma unroll
