@@ -340,18 +340,25 @@ static g4_status few_row_layer(const LayerCtx& c) {
   }
   // gate/up partials; the down projection forms gelu_tanh(gate) * up while staging its A operand
   int s3 = 0, s4 = 0;
+  const bool gated = skinny_gated_ok(M, H, F);  // one pass writes the bf16 product directly
   {
     TimedScope ts(G4_KC_GATE_UP_GEMM, c.s);
-    const void* segs[2] = {l->w_gate, l->w_up};
-    const int64_t rows[2] = {F, F};
     SkA sa{};
     sa.a = xn; sa.lda = H; sa.kind = SKA_BF16;
-    G4_TRY(gemm_skinny_part(sa, M, H, segs, rows, 2, H, X, XB, &s3, c.s));
+    if (gated) {
+      G4_TRY(gemm_skinny_gated(sa, M, H, l->w_gate, l->w_up, F, H, act, F, c.s));
+    } else {
+      const void* segs[2] = {l->w_gate, l->w_up};
+      const int64_t rows[2] = {F, F};
+      G4_TRY(gemm_skinny_part(sa, M, H, segs, rows, 2, H, X, XB, &s3, c.s));
+    }
   }
   {
     TimedScope ts(G4_KC_DOWN_GEMM, c.s);
     SkA sa{};
-    if (stage_from_parts(M, F, H, s3, 2)) {
+    if (gated) {
+      sa.a = act; sa.lda = F; sa.kind = SKA_BF16;
+    } else if (stage_from_parts(M, F, H, s3, 2)) {
       sa.a = X; sa.lda = 2 * F; sa.kind = SKA_GEGLU; sa.parts = s3; sa.part_stride = M * 2 * F; sa.up_off = F;
     } else {
       GemmArgs ga{};

@@ -170,6 +170,10 @@ struct SkA {
 // 16-byte aligned rows).
 bool skinny_ok(int64_t M, int64_t K, const void* const* segs, const int64_t* seg_rows, int nseg, int64_t ldb);
 void skinny_plan(int64_t M, int64_t K, int64_t Nt, int* rows_per_block, int* kc, int* splits);
+// C[M, F] (bf16, row stride ldc) = bf16(gelu_tanh(A w_gate^T) * (A w_up^T)) in one pass, for M <= 16.
+bool skinny_gated_ok(int64_t M, int64_t K, int64_t F);
+g4_status gemm_skinny_gated(const SkA& sa, int64_t M, int64_t K, const void* w_gate, const void* w_up, int64_t F,
+                            int64_t ldb, void* C, int64_t ldc, hipStream_t s);
 // Sums `splits` partial slices [splits][M][Nt] and applies a's epilogue into a.C (a.M, a.N, a.ldc, ...).
 g4_status gemm_skinny_finish(const GemmArgs& a, const float* part, int splits, int64_t Nt, hipStream_t s);
 g4_status gemm_skinny_part(const SkA& sa, int64_t M, int64_t K, const void* const* segs, const int64_t* seg_rows,

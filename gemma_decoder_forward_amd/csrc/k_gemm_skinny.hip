@@ -32,6 +32,9 @@ __device__ __forceinline__ const bf16* sk_row(const SkSeg& s, int64_t r) {
 
 constexpr int SK_D = 4;  // 128-k steps per batch of weight loads
 
+// LDS rows of the staged A slice: the M token rows, plus a zero row when the MFMA blocks have more rows.
+__host__ __device__ inline int sk_lds_rows(int mb, int64_t M) { return M < 16 * mb ? (int)M + 1 : 16 * mb; }
+
 // 8 consecutive A values formed from float32 partial slices (see SkAKind), rounded to bf16.
 template <int AK>
 __device__ __forceinline__ uint4 sk_a_from_parts(const SkA& sa, int64_t m, int64_t k) {
@@ -64,7 +67,11 @@ __device__ __forceinline__ uint4 sk_a_from_parts(const SkA& sa, int64_t m, int64
 // the four waves). RW = 1: the four waves share 16 rows and split the block's K range between them,
 // adding their sums through LDS at the end -- for matrices with few rows, so that the grid fills the
 // chip with fewer K splits (fewer partial slices for the consumer to add).
-template <int MB, int AK, int RW>
+// GATED: the gelu-tanh gated product of two matrices in one pass (one K split): block b owns output
+// columns 16b .. 16b+15; waves 0, 1 take those gate rows and waves 2, 3 the same up rows, each pair
+// splitting K in halves. The four sums meet in LDS and wave 0 stores bf16(gelu_tanh(gate) * up) to
+// C[m][16b + ...] (ldc = Nt).
+template <int MB, int AK, int RW, bool GATED = false>
 __global__ __launch_bounds__(256) void k_gemm_skinny(SkA sa, int64_t M, SkSeg sg, int64_t K, int kc,
                                                      float* __restrict__ part, int64_t Nt) {
   extern __shared__ __attribute__((aligned(16))) bf16 As[];
@@ -75,9 +82,10 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(SkA sa, int64_t M, SkSeg sg
   const int kn = (int)((K - k0) < kc ? (K - k0) : kc);
   const int nst = kn >> 7;  // 128-k steps of this block
   const int q = lane >> 4;
-  const int wrow0 = RW == 4 ? wave * 16 : 0;
-  const int spw = RW == 4 ? nst : (nst + 3) / 4;  // steps of each wave: [sbeg, send)
-  const int sbeg = RW == 4 ? 0 : wave * spw;
+  const int wrow0 = RW == 4 && !GATED ? wave * 16 : 0;
+  // steps of each wave: [sbeg, send)
+  const int spw = GATED ? (nst + 1) / 2 : (RW == 4 ? nst : (nst + 3) / 4);
+  const int sbeg = GATED ? (wave & 1) * spw : (RW == 4 ? 0 : wave * spw);
   const int send = sbeg + spw < nst ? sbeg + spw : nst;
   const int nmine = send > sbeg ? send - sbeg : 0;
 
@@ -86,10 +94,11 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(SkA sa, int64_t M, SkSeg sg
   // descriptor's size, reads as zero and costs no memory traffic. So every load below is issued
   // unconditionally, the compiler's wait counts stay exact, and batches are double-buffered in
   // registers: the loads of batch i+1 are in flight while batch i is multiplied.
-  const bf16* wblk = sk_row(sg, (int64_t)blockIdx.x * BR) + k0;
-  const int64_t wbytes = ((BR - 1) * sg.ldb + kn) * 2;
+  const bf16* wblk = GATED ? sg.b[__builtin_amdgcn_readfirstlane(wave) >> 1] + (int64_t)blockIdx.x * 16 * sg.ldb + k0
+                           : sk_row(sg, (int64_t)blockIdx.x * BR) + k0;
+  const int64_t wbytes = ((GATED ? 15 : BR - 1) * sg.ldb + kn) * 2;
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)wblk, (short)0, (int)wbytes, 0x00020000);
-  const uint32_t lrow = (uint32_t)((wrow0 + (lane & 15)) * sg.ldb + 8 * q) * 2;
+  const uint32_t lrow = (uint32_t)(((GATED ? 0 : wrow0) + (lane & 15)) * sg.ldb + 8 * q) * 2;
   auto load_batch = [&](uint4 (&w)[SK_D][4], int s0) {
 #pragma unroll
     for (int s = 0; s < SK_D; ++s) {
@@ -105,9 +114,11 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(SkA sa, int64_t M, SkSeg sg
   uint4 wa[SK_D][4], wb[SK_D][4];
   load_batch(wa, 0);
 
-  // stage A[0:16*MB, k0:k0+kn] (rows >= M are zero) while the first weights arrive
+  // stage A[0:M, k0:k0+kn] while the first weights arrive, plus one zero row that stands in for every
+  // MFMA row >= M (so the LDS slice and its staging scale with M, not with the 16-row MFMA blocks)
+  const int nrow = sk_lds_rows(MB, M);
   const int cpr = kn / 8;
-  for (int idx = tid; idx < 16 * MB * cpr; idx += 256) {
+  for (int idx = tid; idx < nrow * cpr; idx += 256) {
     const int m = idx / cpr, c = idx - m * cpr;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (m < M) {
@@ -118,7 +129,12 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(SkA sa, int64_t M, SkSeg sg
   }
   __syncthreads();
 
-  const bf16* arow = As + (lane & 15) * ald + 8 * q;
+  int aoff[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int m = mb * 16 + (lane & 15);
+    aoff[mb] = (m < M ? m : nrow - 1) * ald + 8 * q;
+  }
   f32x4_t acc[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc[mb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
@@ -132,7 +148,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(SkA sa, int64_t M, SkSeg sg
           const bf16x8_t bw = *(const bf16x8_t*)&w[s][t];
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
-            const bf16x8_t af = *(const bf16x8_t*)(arow + mb * 16 * ald + kk + 32 * t);
+            const bf16x8_t af = *(const bf16x8_t*)(As + aoff[mb] + kk + 32 * t);
             acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bw, acc[mb], 0, 0, 0);
           }
         }
@@ -144,6 +160,26 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(SkA sa, int64_t M, SkSeg sg
     mul_batch(wa, s0);
     load_batch(wa, s0 + 2 * SK_D);
     mul_batch(wb, s0 + SK_D);
+  }
+  if (GATED) {
+    __shared__ f32x4_t xs[3][MB][64];
+    if (wave > 0)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) xs[wave - 1][mb][lane] = acc[mb];
+    __syncthreads();
+    if (wave > 0) return;
+    bf16* C = (bf16*)part;
+    const int64_t n = (int64_t)blockIdx.x * 16 + (lane & 15);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const f32x4_t g = acc[mb] + xs[0][mb][lane], u = xs[1][mb][lane] + xs[2][mb][lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t m = mb * 16 + 4 * q + i;
+        if (m < M) C[m * Nt + n] = f2bf(gelu_tanh(g[i]) * u[i]);
+      }
+    }
+    return;
   }
   if (RW == 1) {  // add the four waves' sums
     __shared__ f32x4_t red[3][MB][64];
@@ -271,7 +307,7 @@ g4_status gemm_skinny_part(const SkA& sa, int64_t M, int64_t K, const void* cons
   if ((size_t)splits * M * Nt * sizeof(float) > part_bytes)
     return fail(G4_EINVAL, "few-row GEMM: partial buffer too small");
   dim3 g((unsigned)(Nt / (16 * rw)), (unsigned)splits);
-  const size_t lds = (size_t)16 * mb * (kc + 8) * sizeof(bf16);
+  const size_t lds = (size_t)sk_lds_rows(mb, M) * (kc + 8) * sizeof(bf16);
   if (rw == 4) {
     if (mb == 1) sk_launch<1, 4>(sa, g, lds, s, M, sg, K, kc, part, Nt);
     else if (mb == 2) sk_launch<2, 4>(sa, g, lds, s, M, sg, K, kc, part, Nt);
@@ -299,6 +335,35 @@ g4_status gemm_skinny_finish(const GemmArgs& a, const float* part, int splits, i
   else if (a.c_dtype == G4_F32) hipLaunchKernelGGL((k_gemm_finish<EPI_STORE, true>), gf, dim3(256), 0, s, a, part, splits, Nt);
   else hipLaunchKernelGGL((k_gemm_finish<EPI_STORE, false>), gf, dim3(256), 0, s, a, part, splits, Nt);
   return check_launch("gemm_finish");
+}
+
+bool skinny_gated_ok(int64_t M, int64_t K, int64_t F) {
+  return M >= 1 && M <= 16 && K % 256 == 0 && F % 16 == 0 && (size_t)sk_lds_rows(1, M) * (K + 8) * sizeof(bf16) <= 96 * 1024;
+}
+
+g4_status gemm_skinny_gated(const SkA& sa, int64_t M, int64_t K, const void* w_gate, const void* w_up, int64_t F,
+                            int64_t ldb, void* C, int64_t ldc, hipStream_t s) {
+  if (!skinny_gated_ok(M, K, F) || sa.kind != SKA_BF16 || ldb % 8 || ((uintptr_t)w_gate & 15) || ((uintptr_t)w_up & 15) ||
+      sa.lda % 8 || ((uintptr_t)sa.a & 15))
+    return fail(G4_EUNSUP, "gated few-row GEMM: unsupported shape M=%lld K=%lld F=%lld", (long long)M, (long long)K,
+                (long long)F);
+  SkSeg sg{};
+  sg.b[0] = (const bf16*)w_gate;
+  sg.b[1] = (const bf16*)w_up;
+  sg.b[2] = (const bf16*)w_up;
+  sg.end[0] = F; sg.end[1] = 2 * F; sg.end[2] = 2 * F;
+  sg.ldb = ldb;
+  const int kc = (int)K;
+  const size_t lds = (size_t)sk_lds_rows(1, M) * (kc + 8) * sizeof(bf16);
+  static bool lds_set = false;
+  if (!lds_set) {
+    (void)hipFuncSetAttribute((const void*)k_gemm_skinny<1, SKA_BF16, 4, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              96 * 1024);
+    lds_set = true;
+  }
+  hipLaunchKernelGGL((k_gemm_skinny<1, SKA_BF16, 4, true>), dim3((unsigned)(F / 16), 1), dim3(256), lds, s, sa, M, sg, K,
+                     kc, (float*)C, ldc);
+  return check_launch("gemm_skinny_gated");
 }
 
 // M <= 64 rows, bf16, K % 128 == 0, every B segment a multiple of 64 rows. Returns false if not taken.
