@@ -109,3 +109,25 @@ class G4Model:
             bd.g4_layer_forward(self.desc, self.descs[layer], layer, h.data_ptr(), ple_in.data_ptr(), table, self.L,
                                 pos.data_ptr(), B, T, mode, ws.data_ptr(), ws.numel(), _stream())
         return h
+
+
+def capture(step, warmup=1):
+    """Record `step` (a function issuing library calls on the current stream) as one HIP graph.
+
+    The step runs `warmup` times first on a side stream, so that every buffer it needs (workspace,
+    outputs) is allocated before capture; a replay then re-issues all of its kernels with one launch.
+    Inputs and outputs are the same device buffers on every replay. Returns the torch CUDAGraph.
+    """
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(warmup):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    return g
+
