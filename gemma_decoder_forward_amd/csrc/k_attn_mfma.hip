@@ -28,13 +28,40 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 constexpr int AT_KB = 32;        // keys per tile
 constexpr int AT_VLD = 36;       // V^T row stride in bf16 (32 keys + 4)
 
+typedef __attribute__((address_space(3))) void at_lds_void;
+typedef short at_v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) at_v4s at_lds_v4s;
+typedef __attribute__((ext_vector_type(4))) uint32_t at_rsrc;
+
+// Head dim 512 stages K and V by direct buffer-to-LDS loads (one 1 KB instruction per row) and keeps V
+// row-major; the V^T operand then comes from the LDS transpose read. Smaller heads stage through
+// registers and store V transposed.
 template <int HD>
 struct AttnLds {
-  static constexpr int KLD = HD + 8;  // K row stride in bf16
+  static constexpr bool DMA = HD == 512;
+  static constexpr int KLD = HD + 8;   // K row stride in bf16 (16-lane chunk reads hit every bank once)
+  static constexpr int VROW = HD + 16; // row-major V stride (a transpose read's four row pieces on distinct banks)
   static constexpr int KSZ = AT_KB * KLD;
-  static constexpr int VSZ = HD * AT_VLD;
+  static constexpr int VSZ = DMA ? AT_KB * VROW : HD * AT_VLD;
   static constexpr int STAGE = KSZ + VSZ;
 };
+
+__device__ __forceinline__ at_rsrc at_make_rsrc(const void* base, int64_t bytes) {
+  const uint64_t p = (uint64_t)base;
+  const uint32_t n = bytes > 0x7fffffff ? 0x7fffffffu : (bytes < 0 ? 0u : (uint32_t)bytes);
+  at_rsrc r;
+  r.x = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  r.y = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32) & 0xffffu);
+  r.z = __builtin_amdgcn_readfirstlane(n);
+  r.w = 0x00020000u;
+  return r;
+}
+
+// 16 bytes per lane from voff + soff straight into LDS at m0 + 16 * lane (inline assembly: the
+// completion is awaited with an explicit vmcnt before the barrier that precedes the reads).
+__device__ __forceinline__ void at_dma16(const at_rsrc& r, uint32_t voff, uint32_t soff, uint32_t m0) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" : : "v"(voff), "s"(r), "s"(soff), "{m0}"(m0) : "memory");
+}
 
 template <int HD, int HS>
 __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float sl2) {
@@ -102,7 +129,8 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
 
   const bf16* Kb = (const bf16*)a.k + (b * a.nkv + g) * a.cap * HD;
   const bf16* Vb = (const bf16*)a.v + (b * a.nkv + g) * a.cap * HD;
-  uint4 rk[KCH], rv[2 * VUN];
+  constexpr bool DMA = L::DMA;
+  uint4 rk[DMA ? 1 : KCH], rv[DMA ? 1 : 2 * VUN];
   auto gload = [&](int it) {
     const int64_t k0 = kstart + (int64_t)it * AT_KB;
 #pragma unroll
@@ -142,6 +170,38 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
       }
     }
   };
+  // DMA staging (head dim 512): rows 8w .. 8w+7 of the tile from wave w, K and V. Keys past the cache
+  // clamp to its last row (they are masked); V rows whose keys lie outside [lob, hib] are zeroed after
+  // they land (a masked probability times a stale value must stay zero, not NaN).
+  const at_rsrc rks = at_make_rsrc(Kb, a.cap * HD * 2), rvs = at_make_rsrc(Vb, a.cap * HD * 2);
+  auto dma = [&](int it, int buf) {
+    const int64_t k0 = kstart + (int64_t)it * AT_KB;
+    const uint32_t kb0 = (uint32_t)(uintptr_t)(at_lds_void*)(lds + buf * L::STAGE);
+    const uint32_t vb0 = kb0 + L::KSZ * 2;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform: offsets and M0 live in SGPRs
+#pragma unroll
+    for (int r = 0; r < AT_KB / 4; ++r) {
+      const int row = (AT_KB / 4) * wv + r;
+      int64_t key = k0 + row;
+      if (key > a.cap - 1) key = a.cap - 1;
+      const uint32_t src = __builtin_amdgcn_readfirstlane((uint32_t)(key * HD * 2));
+      at_dma16(rks, (uint32_t)lane * 16, src, kb0 + (uint32_t)(row * L::KLD * 2));
+      at_dma16(rvs, (uint32_t)lane * 16, src, vb0 + (uint32_t)(row * L::VROW * 2));
+    }
+  };
+  auto edge_tile = [&](int it) {
+    const int64_t k0 = kstart + (int64_t)it * AT_KB;
+    return !(k0 >= lob && k0 + AT_KB - 1 <= hib);
+  };
+  auto vclean = [&](int it, int buf) {
+    const int64_t k0 = kstart + (int64_t)it * AT_KB;
+    bf16* vs = lds + buf * L::STAGE + L::KSZ;
+    for (int u = tid; u < AT_KB * (HD / 8); u += 256) {
+      const int row = u / (HD / 8);
+      const int64_t key = k0 + row;
+      if (key < lob || key > hib) *(uint4*)(vs + row * L::VROW + 8 * (u % (HD / 8))) = make_uint4(0, 0, 0, 0);
+    }
+  };
 
   f32x16_t o[NB];
 #pragma unroll
@@ -151,13 +211,26 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
   float m_run = -INFINITY, l_run = 0.f;
 
   if (ntiles > 0) {
-    gload(0);
-    lstore(0);
-    __syncthreads();
+    if constexpr (DMA) {
+      dma(0, 0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (edge_tile(0)) {
+        vclean(0, 0);
+        __syncthreads();
+      }
+    } else {
+      gload(0);
+      lstore(0);
+      __syncthreads();
+    }
   }
   for (int it = 0; it < ntiles; ++it) {
     const int cur = it & 1;
-    if (it + 1 < ntiles) gload(it + 1);
+    if (it + 1 < ntiles) {
+      if constexpr (DMA) dma(it + 1, cur ^ 1);
+      else gload(it + 1);
+    }
     const bf16* ks = lds + cur * L::STAGE;
     const bf16* vs = ks + L::KSZ;
     const int64_t k0 = kstart + (int64_t)it * AT_KB;
@@ -222,21 +295,51 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
     }
     l_run += psum;
     m_run = m_new;
-    // O^T += V^T P^T
-    const bf16* vf = vs + (half * HW + col) * AT_VLD + 4 * h;
+    // O^T += V^T P^T. MFMA step st takes keys 16st + 4h + (0..3) and 16st + 8 + 4h + (0..3) for lane half
+    // h (the order of the score registers).
+    if constexpr (DMA) {
+      // LDS transpose read (ds_read_b64_tr_b16): within a 16-lane group lane i receives element i % 4 of
+      // the 8 bytes addressed by lane 4j + i/4, j = 0..3. Lane a of group q addresses key row
+      // kb + a/4 at head elements 32d + 16(q % 2) + 4(a % 4), so lane i gets keys kb .. kb+3 of head
+      // element 32d + 16(q % 2) + i: the A operand row of lane 16(q % 2) + i.
+      const int a16 = lane & 15, grp = lane >> 4;
+      const bf16* vb = vs + (4 * (grp >> 1) + (a16 >> 2)) * L::VROW + half * HW + 16 * (grp & 1) + 4 * (a16 & 3);
 #pragma unroll
-    for (int d = 0; d < NB; ++d) {
+      for (int d = 0; d < NB; ++d) {
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const bf16* vp = vf + d * 32 * AT_VLD + 16 * st;
-        bf16x4_t lo4 = *(const bf16x4_t*)vp;
-        bf16x4_t hi4 = *(const bf16x4_t*)(vp + 8);
-        bf16x8_t va = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[st], o[d], 0, 0, 0);
+        for (int st = 0; st < 2; ++st) {
+          bf16x4_t part[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const bf16* addr = vb + (16 * st + 8 * e) * L::VROW + 32 * d;
+            part[e] = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((at_lds_v4s*)(at_lds_void*)addr));
+          }
+          const bf16x8_t va = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+          o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[st], o[d], 0, 0, 0);
+        }
       }
+      __builtin_amdgcn_s_waitcnt(0);  // the next tile's direct-to-LDS loads
+      __syncthreads();
+      if (it + 1 < ntiles && edge_tile(it + 1)) {
+        vclean(it + 1, cur ^ 1);
+        __syncthreads();
+      }
+    } else {
+      const bf16* vf = vs + (half * HW + col) * AT_VLD + 4 * h;
+#pragma unroll
+      for (int d = 0; d < NB; ++d) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const bf16* vp = vf + d * 32 * AT_VLD + 16 * st;
+          bf16x4_t lo4 = *(const bf16x4_t*)vp;
+          bf16x4_t hi4 = *(const bf16x4_t*)(vp + 8);
+          bf16x8_t va = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+          o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[st], o[d], 0, 0, 0);
+        }
+      }
+      if (it + 1 < ntiles) lstore(cur ^ 1);
+      __syncthreads();
     }
-    if (it + 1 < ntiles) lstore(cur ^ 1);
-    __syncthreads();
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
