@@ -5,8 +5,9 @@
 // With HS = 1 each wave owns one query group (4 groups per block); with HS = 2 (head_dim 512, whose Q and
 // O do not fit one wave's registers) a pair of waves owns one group, each wave holding half of the head
 // dimension of Q and O: the pair adds its two partial score tiles through LDS, both run the identical
-// softmax, and each accumulates P V for its half. Keys advance in tiles of 32 staged in LDS (double
-// buffered, next tile prefetched into registers during the current tile's math):
+// softmax, and each accumulates P V for its half. Keys advance in tiles of 32 staged in LDS, double
+// buffered: the next tile's rows are loaded straight into LDS (buffer_load ... lds, one instruction per
+// row) while the current tile is multiplied.
 //   * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: A = K rows from LDS,
 //     B = the wave's Q held in registers for the whole key loop;
 //   * lane l then holds query (l % 32) and 16 of the tile's keys: 8*(j/4) + 4*(l/32) + j%4 for
@@ -14,8 +15,8 @@
 //   * O^T = V^T P^T uses those probabilities directly as the B operand: for the 16-key MFMA step s,
 //     the lane's registers j = 8s..8s+7 are keys {16s + 4h + 0..3, 16s + 8 + 4h + 0..3} (h = l/32), and
 //     the A operand reads V^T at exactly those keys, so P never moves between lanes;
-//   * V is staged transposed (V^T[hd][key], key pairs packed in one dword, row stride 36 keys) so both
-//     the staging writes and the two 8-byte operand reads per MFMA are free of bank conflicts.
+//   * V stays row-major in LDS and the V^T operand comes from the LDS transpose read; K and V rows are
+//     padded (strides of 16 and 32 bytes mod 256) so both operand reads are free of bank conflicts.
 // The O accumulator (HD/32 32x32 blocks per wave) lives in the accumulation registers.
 #include "g4_internal.h"
 
@@ -26,23 +27,21 @@ typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 
 constexpr int AT_KB = 32;        // keys per tile
-constexpr int AT_VLD = 36;       // V^T row stride in bf16 (32 keys + 4)
 
 typedef __attribute__((address_space(3))) void at_lds_void;
 typedef short at_v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) at_v4s at_lds_v4s;
 typedef __attribute__((ext_vector_type(4))) uint32_t at_rsrc;
 
-// Head dim 512 stages K and V by direct buffer-to-LDS loads (one 1 KB instruction per row) and keeps V
-// row-major; the V^T operand then comes from the LDS transpose read. Smaller heads stage through
-// registers and store V transposed.
+// K and V are staged by direct buffer-to-LDS loads (one instruction per row: 64, 32 or 16 lanes of
+// 16 bytes for head dim 512, 256, 128) and V stays row-major; the V^T operand then comes from the LDS
+// transpose read.
 template <int HD>
 struct AttnLds {
-  static constexpr bool DMA = HD == 512;
   static constexpr int KLD = HD + 8;   // K row stride in bf16 (16-lane chunk reads hit every bank once)
   static constexpr int VROW = HD + 16; // row-major V stride (a transpose read's four row pieces on distinct banks)
   static constexpr int KSZ = AT_KB * KLD;
-  static constexpr int VSZ = DMA ? AT_KB * VROW : HD * AT_VLD;
+  static constexpr int VSZ = AT_KB * VROW;
   static constexpr int STAGE = KSZ + VSZ;
 };
 
@@ -70,8 +69,6 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
   constexpr int NB = HW / 32;      // O blocks per wave
   constexpr int KS = HW / 16;      // MFMA k-steps for S
   constexpr int QG = 4 / HS;       // query groups per block
-  constexpr int KCH = AT_KB * HD / 8 / 256;   // 16-byte K chunks per thread
-  constexpr int VUN = 16 * (HD / 8) / 256;    // (key pair, hd chunk) units per thread
   __shared__ __attribute__((aligned(16))) bf16 lds[2 * L::STAGE];
   __shared__ float xch[HS == 2 ? 4 * 16 * 64 : 1];  // partial score tiles of the wave pairs
 
@@ -129,48 +126,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
 
   const bf16* Kb = (const bf16*)a.k + (b * a.nkv + g) * a.cap * HD;
   const bf16* Vb = (const bf16*)a.v + (b * a.nkv + g) * a.cap * HD;
-  constexpr bool DMA = L::DMA;
-  uint4 rk[DMA ? 1 : KCH], rv[DMA ? 1 : 2 * VUN];
-  auto gload = [&](int it) {
-    const int64_t k0 = kstart + (int64_t)it * AT_KB;
-#pragma unroll
-    for (int j = 0; j < KCH; ++j) {
-      const int u = tid + 256 * j, r = u / (HD / 8), c = u % (HD / 8);
-      const int64_t key = k0 + r;
-      rk[j] = (key >= lob && key <= hib) ? *(const uint4*)(Kb + key * HD + 8 * c) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < VUN; ++j) {
-      const int u = tid + 256 * j, p = u & 15, c = u >> 4;
-      const int64_t key = k0 + 2 * p;
-      rv[2 * j] = (key >= lob && key <= hib) ? *(const uint4*)(Vb + key * HD + 8 * c) : make_uint4(0, 0, 0, 0);
-      rv[2 * j + 1] =
-          (key + 1 >= lob && key + 1 <= hib) ? *(const uint4*)(Vb + (key + 1) * HD + 8 * c) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto lstore = [&](int buf) {
-    bf16* ks = lds + buf * L::STAGE;
-    bf16* vs = ks + L::KSZ;
-#pragma unroll
-    for (int j = 0; j < KCH; ++j) {
-      const int u = tid + 256 * j, r = u / (HD / 8), c = u % (HD / 8);
-      *(uint4*)(ks + r * L::KLD + 8 * c) = rk[j];
-    }
-#pragma unroll
-    for (int j = 0; j < VUN; ++j) {
-      const int u = tid + 256 * j, p = u & 15, c = u >> 4;
-      const uint32_t* lo = (const uint32_t*)&rv[2 * j];
-      const uint32_t* hi = (const uint32_t*)&rv[2 * j + 1];
-      uint32_t* dst = (uint32_t*)(vs + (8 * c) * AT_VLD) + p;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // element 2i and 2i+1 of the chunk: (key 2p, key 2p+1) pairs for hd rows 8c+2i and 8c+2i+1
-        dst[(2 * i) * (AT_VLD / 2)] = (lo[i] & 0xffffu) | (hi[i] << 16);
-        dst[(2 * i + 1) * (AT_VLD / 2)] = (lo[i] >> 16) | (hi[i] & 0xffff0000u);
-      }
-    }
-  };
-  // DMA staging (head dim 512): rows 8w .. 8w+7 of the tile from wave w, K and V. Keys past the cache
+  // Staging: rows 8w .. 8w+7 of the tile from wave w, K and V. Keys past the cache
   // clamp to its last row (they are masked); V rows whose keys lie outside [lob, hib] are zeroed after
   // they land (a masked probability times a stale value must stay zero, not NaN).
   const at_rsrc rks = at_make_rsrc(Kb, a.cap * HD * 2), rvs = at_make_rsrc(Vb, a.cap * HD * 2);
@@ -185,8 +141,10 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
       int64_t key = k0 + row;
       if (key > a.cap - 1) key = a.cap - 1;
       const uint32_t src = __builtin_amdgcn_readfirstlane((uint32_t)(key * HD * 2));
-      at_dma16(rks, (uint32_t)lane * 16, src, kb0 + (uint32_t)(row * L::KLD * 2));
-      at_dma16(rvs, (uint32_t)lane * 16, src, vb0 + (uint32_t)(row * L::VROW * 2));
+      if (lane < HD / 8) {  // a row is HD / 8 lanes of 16 bytes
+        at_dma16(rks, (uint32_t)lane * 16, src, kb0 + (uint32_t)(row * L::KLD * 2));
+        at_dma16(rvs, (uint32_t)lane * 16, src, vb0 + (uint32_t)(row * L::VROW * 2));
+      }
     }
   };
   auto edge_tile = [&](int it) {
@@ -211,26 +169,17 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
   float m_run = -INFINITY, l_run = 0.f;
 
   if (ntiles > 0) {
-    if constexpr (DMA) {
-      dma(0, 0);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (edge_tile(0)) {
-        vclean(0, 0);
-        __syncthreads();
-      }
-    } else {
-      gload(0);
-      lstore(0);
+    dma(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (edge_tile(0)) {
+      vclean(0, 0);
       __syncthreads();
     }
   }
   for (int it = 0; it < ntiles; ++it) {
     const int cur = it & 1;
-    if (it + 1 < ntiles) {
-      if constexpr (DMA) dma(it + 1, cur ^ 1);
-      else gload(it + 1);
-    }
+    if (it + 1 < ntiles) dma(it + 1, cur ^ 1);
     const bf16* ks = lds + cur * L::STAGE;
     const bf16* vs = ks + L::KSZ;
     const int64_t k0 = kstart + (int64_t)it * AT_KB;
@@ -297,7 +246,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
     m_run = m_new;
     // O^T += V^T P^T. MFMA step st takes keys 16st + 4h + (0..3) and 16st + 8 + 4h + (0..3) for lane half
     // h (the order of the score registers).
-    if constexpr (DMA) {
+    {
       // LDS transpose read (ds_read_b64_tr_b16): within a 16-lane group lane i receives element i % 4 of
       // the 8 bytes addressed by lane 4j + i/4, j = 0..3. Lane a of group q addresses key row
       // kb + a/4 at head elements 32d + 16(q % 2) + 4(a % 4), so lane i gets keys kb .. kb+3 of head
@@ -324,21 +273,6 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
         vclean(it + 1, cur ^ 1);
         __syncthreads();
       }
-    } else {
-      const bf16* vf = vs + (half * HW + col) * AT_VLD + 4 * h;
-#pragma unroll
-      for (int d = 0; d < NB; ++d) {
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const bf16* vp = vf + d * 32 * AT_VLD + 16 * st;
-          bf16x4_t lo4 = *(const bf16x4_t*)vp;
-          bf16x4_t hi4 = *(const bf16x4_t*)(vp + 8);
-          bf16x8_t va = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[st], o[d], 0, 0, 0);
-        }
-      }
-      if (it + 1 < ntiles) lstore(cur ^ 1);
-      __syncthreads();
     }
   }
 
