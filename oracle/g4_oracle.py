@@ -14,6 +14,8 @@ It is the plain definition of what the layer computes, written from the pages in
     `text_attention` (GQA head map `kh = hh / group`).
   * turbospark-runtime `gemma4/attn.rs` (page 5): `rotated_pairs = full_head_dim * partial_rotary / 2`,
     sliding `kv_start = seq_len - sliding_window`.
+  * the output head after the stack (page 2 `forward_token_on_worker`, page 1 module doc): final RMSNorm,
+    output projection, final-logit softcap.
 
 Readings where the pages are silent or disagree (each also listed in the design notes):
   * Proportional RoPE: pair j of a full layer rotates by pos * theta^(-2j/hd_full) for j < R and is the
@@ -365,3 +367,22 @@ def forward(cfg, layers, h0, ple_in, pos, caches, srcs=None, layer_range=None, p
 def prefill_positions(pos0, T):
     pos0 = _ints(pos0)
     return pos0[:, None] + np.arange(T)[None, :]
+
+
+# --------------------------------------------------------------------------------------------
+# Output head (ferrox-models `forward_token_on_worker` tail; page 1 module doc: final norm + lm_head +
+# final-logit softcap)
+# --------------------------------------------------------------------------------------------
+
+def softcap(x, cap):
+    """cap * tanh(x / cap); cap <= 0 leaves x unchanged (no softcap configured)."""
+    x = f64(x)
+    if cap is None or cap <= 0:
+        return x
+    return cap * np.tanh(x / cap)
+
+
+def logits(h, out_norm, w_out, cap, eps=1e-6):
+    """Logits of hidden rows h [M, H]: W_out rms(h) * out_norm (W_out [vocab, H]), then the softcap."""
+    return softcap(rms_norm(h, out_norm, eps) @ f64(w_out).T, cap)
+

@@ -35,6 +35,9 @@ MUTATIONS = {
     "embedding_unscaled": ('* math.sqrt(cfg["hidden"])', ""),
     "ple_table_unscaled": ("* math.sqrt(d)\n", "\n"),
     "route_first_same_type": ("src.append(cands[-1] if cands else l)", "src.append(cands[0] if cands else l)"),
+    "softcap_unscaled": ("return cap * np.tanh(x / cap)", "return np.tanh(x / cap)"),
+    "logits_without_final_norm": ("return softcap(rms_norm(h, out_norm, eps) @ f64(w_out).T, cap)",
+                                  "return softcap(f64(h) @ f64(w_out).T, cap)"),
 }
 
 pytestmark = pytest.mark.skipif(os.environ.get("G4_MUTATIONS") != "1", reason="opt-in: set G4_MUTATIONS=1")

@@ -346,3 +346,34 @@ def test_layer_rows_equal_whole_layer_rows(types):
     whole = O.layer_forward(cfg, layers[0], 0, 0, h, ple, O.prefill_positions([3], 13), O.new_caches(cfg, 1, 16))
     rows, part = O.layer_forward_rows(cfg, layers[0], 0, h[0], ple[0], 3, [12, 0, 5, 9])
     np.testing.assert_allclose(part, whole[0, rows], rtol=1e-13, atol=1e-13)
+
+
+# ---------------------------------------------------------------- output head
+def test_softcap_bounds_taylor_and_identity():
+    """Pins of cap * tanh(x / cap): odd, strictly inside (-cap, cap), slope 1 at 0, third-order Taylor
+    term -x^3 / (3 cap^2), saturation at +-cap, and no cap -> identity."""
+    cap = json.load(open(os.path.join(GOLD, "constants.json")))["final_logit_softcap"]
+    x = rng.normal(size=2000) * 50
+    y = O.softcap(x, cap)
+    assert np.all(np.abs(y) < cap) and np.allclose(O.softcap(-x, cap), -y, rtol=0, atol=0)
+    small = np.array([1e-3, 0.05, 0.3])
+    np.testing.assert_allclose(O.softcap(small, cap), small - small ** 3 / (3 * cap ** 2), rtol=0, atol=1e-8)
+    assert abs(O.softcap(np.array([1e4]), cap)[0] - cap) < 1e-12
+    np.testing.assert_array_equal(O.softcap(x, 0.0), x)
+
+
+def test_logits_brute_force():
+    """Final norm + output projection + softcap against pure-Python loops on tiny sizes."""
+    M, H, V, cap = 3, 8, 11, 30.0
+    h = rng.normal(size=(M, H)) * 3
+    wn = 1 + 0.1 * rng.normal(size=H)
+    W = rng.normal(size=(V, H)) * 2
+    got = O.logits(h, wn, W, cap)
+    for m in range(M):
+        ms = sum(float(v) * float(v) for v in h[m]) / H
+        inv = 1.0 / math.sqrt(ms + 1e-6)
+        xn = [float(h[m][k]) * inv * float(wn[k]) for k in range(H)]
+        for v in range(V):
+            z = sum(xn[k] * float(W[v][k]) for k in range(H))
+            assert abs(got[m, v] - cap * math.tanh(z / cap)) < 1e-12
+
