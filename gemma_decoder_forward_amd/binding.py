@@ -54,6 +54,8 @@ _SIGS = {
     "g4_ple_inject_ws": (sz, [i64, i64, i64, i32]),
     "g4_ple_inject": (C.c_int, [vp, vp, vp, i64, vp, vp, f32, i64, i64, i64, f32, vp, sz, i32, vp]),
     "g4_embed_ple": (C.c_int, [vp, i64, vp, vp, vp, vp, C.POINTER(ModelDesc), vp, vp, vp, sz, vp]),
+    "g4_logits_ws": (sz, [i64, i64, i64, i32]),
+    "g4_logits": (C.c_int, [vp, i64, i64, vp, vp, i64, f32, f32, vp, vp, sz, i32, vp]),
     "g4_layer_forward": (C.c_int, [C.POINTER(ModelDesc), C.POINTER(LayerDesc), i32, vp, vp, C.POINTER(KvEntry), i32,
                                    vp, i64, i64, i32, vp, sz, vp]),
     "g4_stack_forward": (C.c_int, [C.POINTER(ModelDesc), C.POINTER(LayerDesc), vp, vp, C.POINTER(KvEntry), i32, vp,
@@ -158,6 +160,14 @@ def g4_ple_inject(h, w_gate, ple, ple_ld, w_proj, w_post, layer_scalar, M, H, d,
 
 def g4_embed_ple(ids, M, E, Tab, W_pm, ple_norm, model, h_out, ple_out, ws, ws_bytes, stream=None):
     return _call("g4_embed_ple", ids, M, E, Tab, W_pm, ple_norm, C.byref(model), h_out, ple_out, ws, ws_bytes, stream)
+
+
+def g4_logits_ws(M, H, vocab, dtype):
+    return lib().g4_logits_ws(M, H, vocab, dtype)
+
+
+def g4_logits(h, M, H, out_norm, w_out, vocab, eps, softcap, logits, ws, ws_bytes, dtype, stream=None):
+    return _call("g4_logits", h, M, H, out_norm, w_out, vocab, eps, softcap, logits, ws, ws_bytes, dtype, stream)
 
 
 def g4_layer_forward(model, layer_desc, layer, h, ple_in, kv, n_kv, pos, B, T, mode, ws, ws_bytes, stream=None):

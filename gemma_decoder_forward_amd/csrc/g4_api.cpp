@@ -661,6 +661,35 @@ g4_status g4_linear(const void* A, const void* W, void* C, int64_t M, int64_t N,
   return st;
 }
 
+size_t g4_logits_ws(int64_t M, int64_t H, int64_t vocab, int32_t dtype) {
+  if (M <= 0 || H <= 0 || vocab <= 0) return 0;
+  size_t sk = 0;
+  if (M <= 64 && dtype == G4_BF16) sk = gemm_skinny_ws(M, (vocab + 63) / 64 * 64, (H + 127) / 128 * 128);
+  return al((size_t)M * H * dsize(dtype)) + al(sk);
+}
+
+g4_status g4_logits(const float* h, int64_t M, int64_t H, const void* out_norm, const void* w_out, int64_t vocab,
+                    float eps, float softcap, float* logits, void* ws, size_t ws_bytes, int32_t dtype, void* stream) {
+  G4_REQ(dt_ok(dtype), G4_EINVAL, "dtype %d", dtype);
+  G4_REQ(M >= 0 && H > 0 && vocab > 0, G4_EINVAL, "M %lld H %lld vocab %lld", (long long)M, (long long)H,
+         (long long)vocab);
+  G4_REQ(softcap >= 0.f, G4_EINVAL, "softcap %g < 0", (double)softcap);
+  if (M == 0) return G4_OK;
+  G4_REQ(h && out_norm && w_out && logits, G4_EINVAL, "h, out_norm, w_out or logits is NULL");
+  const size_t need = g4_logits_ws(M, H, vocab, dtype);
+  G4_REQ(ws && ws_bytes >= need, G4_EINVAL, "workspace too small (%zu < %zu)", ws_bytes, need);
+  hipStream_t s = (hipStream_t)stream;
+  char* xn = (char*)ws;
+  g_gws = (char*)ws + al((size_t)M * H * dsize(dtype));
+  g_gws_bytes = ws_bytes - al((size_t)M * H * dsize(dtype));
+  struct ClearGws { ~ClearGws() { g_gws = nullptr; g_gws_bytes = 0; } } clear_gws;
+  g4_status st = rownorm(h, G4_F32, 1, 0, out_norm, xn, nullptr, 1.f, nullptr, nullptr, M, H, eps, dtype, s);
+  if (st != G4_OK) return st;
+  st = run_gemm(xn, H, w_out, nullptr, H, logits, vocab, G4_F32, M, vocab, H, EPI_STORE, nullptr, 0, 1, 0, dtype, s);
+  if (st != G4_OK) return st;
+  return softcap_inplace(logits, M * vocab, softcap, s);
+}
+
 size_t g4_ffn_geglu_ws(int64_t M, int64_t H, int64_t F, int32_t dtype) {
   size_t sk = 0;
   if (M <= 64 && dtype == G4_BF16) {

@@ -146,6 +146,7 @@ bool attn_decode_mfma(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t 
 size_t attn_decode_mfma_ws(int64_t B, int64_t nh, int64_t hd, int64_t cap);
 
 g4_status cast_rows(const float* x, void* y, int64_t n, int32_t dtype, hipStream_t s);
+g4_status softcap_inplace(float* x, int64_t n, float cap, hipStream_t s);
 g4_status gemm_simt(const GemmArgs& a, int32_t dtype, hipStream_t s);
 bool gemm_mfma(const GemmArgs& a, hipStream_t s, g4_status* st);
 bool gemm_skinny(const GemmArgs& a, const void* const* segs, const int64_t* seg_rows, int nseg, void* ws,

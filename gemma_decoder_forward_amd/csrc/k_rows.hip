@@ -457,4 +457,22 @@ g4_status cast_rows(const float* x, void* y, int64_t n, int32_t dtype, hipStream
   else hipLaunchKernelGGL(k_cast<float>, dim3((unsigned)blocks), dim3(256), 0, s, x, (float*)y, n);
   return check_launch("cast");
 }
+// --------------------------------------------------------------------------------------------
+// Final-logit softcap in place (ferrox-models `forward_token_on_worker`: softcap after the output
+// head): x <- cap * tanh(x / cap).
+// --------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_softcap(float* __restrict__ x, int64_t n, float cap) {
+  const float inv = 1.f / cap;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    x[i] = cap * tanhf(x[i] * inv);
+}
+
+g4_status softcap_inplace(float* x, int64_t n, float cap, hipStream_t s) {
+  if (n == 0 || cap <= 0.f) return G4_OK;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(k_softcap, dim3((unsigned)blocks), dim3(256), 0, s, x, n, cap);
+  return check_launch("softcap");
+}
+
 }  // namespace g4

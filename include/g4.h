@@ -195,6 +195,17 @@ g4_status g4_ple_inject(float* h, const void* w_gate, const float* ple, int64_t 
                         int64_t H, int64_t d, float eps, void* ws, size_t ws_bytes, int32_t dtype,
                         void* stream);
 
+/* Output head after the stack (ferrox-models `forward_token_on_worker` tail; cortiq-engine module doc:
+ * final norm + lm_head + final-logit softcap):
+ *   logits[m, :] = cap * tanh((W_out * (rms(h[m]) * out_norm)) / cap)      (no tanh when softcap == 0)
+ * h float32 [M, H] (contiguous rows: pass the rows whose logits are wanted, e.g. each sequence's last
+ * token); out_norm [H] and W_out [vocab, H] in dtype (W_out may be the token embedding table);
+ * logits float32 [M, vocab]. Workspace: g4_logits_ws bytes. softcap < 0 is G4_EINVAL. */
+size_t g4_logits_ws(int64_t M, int64_t H, int64_t vocab, int32_t dtype);
+g4_status g4_logits(const float* h, int64_t M, int64_t H, const void* out_norm, const void* w_out, int64_t vocab,
+                    float eps, float softcap, float* logits, void* ws, size_t ws_bytes, int32_t dtype,
+                    void* stream);
+
 /* Token embedding and per-layer inputs (cortiq-engine `extend_embedding`; ferrox
  * `project_per_layer_inputs` and the embedding scale of `forward_token_on_worker`):
  *   h_out[m]        = E[id] * sqrt(H)                              (zero row if id outside [0,vocab))

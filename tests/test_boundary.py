@@ -132,3 +132,15 @@ def test_row_op_validation_errors():
     assert L.g4_linear(FAKE, FAKE, FAKE, 4, 8, 8, 1, 0, None, 0, None) == bd.G4_EINVAL
     assert L.g4_ffn_geglu(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 8, FAKE, 1, 1, None) == bd.G4_EINVAL
     assert L.g4_kv_sources(None, 3, 1, None) == bd.G4_EINVAL
+
+
+def test_logits_validation_errors():
+    L = bd.lib()
+    ws = bd.g4_logits_ws(4, 64, 128, bd.G4_BF16)
+    assert ws > 0 and bd.g4_logits_ws(0, 64, 128, bd.G4_BF16) == 0
+    assert L.g4_logits(None, 0, 64, None, None, 128, 1e-6, 30.0, None, None, 0, 1, None) == bd.G4_OK  # empty
+    assert L.g4_logits(FAKE, 4, 64, FAKE, FAKE, 128, 1e-6, -1.0, FAKE, FAKE, ws, 1, None) == bd.G4_EINVAL
+    assert L.g4_logits(FAKE, 4, 64, FAKE, FAKE, 128, 1e-6, 30.0, FAKE, FAKE, ws - 1, 1, None) == bd.G4_EINVAL
+    assert L.g4_logits(FAKE, 4, 64, None, FAKE, 128, 1e-6, 30.0, FAKE, FAKE, ws, 1, None) == bd.G4_EINVAL
+    assert L.g4_logits(FAKE, 4, 64, FAKE, FAKE, 0, 1e-6, 30.0, FAKE, FAKE, ws, 1, None) == bd.G4_EINVAL
+    assert L.g4_logits(FAKE, 4, 64, FAKE, FAKE, 128, 1e-6, 30.0, FAKE, FAKE, ws, 5, None) == bd.G4_EINVAL

@@ -346,3 +346,27 @@ def test_embed_ple_vs_oracle(dt):
     assert_close(h, e_ref, "f32", "h0")
     assert_close(ple, p_ref, "f32" if dt == "f32" else "bf16", "ple_in")
     assert torch.all(h[0, 4:7] == 0)
+
+
+# ------------------------------------------------------------------------------- output head
+@pytest.mark.parametrize("dt,M,H,V,cap", [("f32", 5, 256, 512, 30.0), ("f32", 70, 64, 200, 0.0),
+                                          ("bf16", 1, 2560, 262144, 30.0), ("bf16", 7, 2560, 262144, 30.0),
+                                          ("bf16", 300, 256, 4096, 30.0), ("bf16", 33, 256, 960, 0.0)])
+def test_logits_vs_oracle(dt, M, H, V, cap):
+    """Final norm + output projection + softcap; the E4B vocabulary at decode batch sizes (few-row path)."""
+    log(f"logits {dt} M={M} H={H} V={V} cap={cap}")
+    gdt, tdt = DT[dt]
+    h = randn((M, H), 90 + M, torch.float32, 2.0)
+    wn = randn((H,), 91, tdt, 0.1, 1.0)
+    W = randn((V, H), 92, tdt, 0.5)  # large enough that many logits reach the softcap's curved part
+    out = torch.empty((M, V), dtype=torch.float32, device="cuda")
+    wsb = bd.g4_logits_ws(M, H, V, gdt)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    bd.g4_logits(h.data_ptr(), M, H, wn.data_ptr(), W.data_ptr(), V, 1e-6, cap, out.data_ptr(), ws.data_ptr(), wsb,
+                 gdt, stream())
+    torch.cuda.synchronize()
+    ref = O.logits(O.f64(h), O.f64(wn), O.f64(W), cap)
+    assert_close(out, ref, dt, "logits")
+    if cap > 0:
+        assert float(out.abs().max()) < cap
+
