@@ -33,7 +33,7 @@ class LayerDesc(C.Structure):
 
 
 class KvEntry(C.Structure):
-    _fields_ = [("k", vp), ("v", vp), ("cap", i64), ("hd", i64), ("sliding", i32), ("reserved", i32)]
+    _fields_ = [("k", vp), ("v", vp), ("cap", i64), ("hd", i64), ("sliding", i32), ("ring", i32)]
 
 
 _SIGS = {

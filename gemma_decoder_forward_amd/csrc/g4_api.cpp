@@ -84,7 +84,7 @@ static int64_t rot_pairs(const g4_model_desc* m, int sliding) {
 
 // Routing and cache checks shared by the attention entry points and the layer forward.
 static g4_status check_kv(const g4_kv_entry* kv, int32_t n_kv, int32_t layer, int32_t kv_src, int32_t sliding,
-                          int64_t hd, int64_t T, int32_t mode) {
+                          int64_t hd, int64_t T, int32_t mode, int64_t window) {
   G4_REQ(kv, G4_EINVAL, "kv table is NULL");
   G4_REQ(n_kv > 0, G4_EINVAL, "n_kv %d <= 0", n_kv);
   G4_REQ(layer >= 0 && layer < n_kv, G4_EINVAL, "layer %d outside the kv table [0,%d)", layer, n_kv);
@@ -95,7 +95,17 @@ static g4_status check_kv(const g4_kv_entry* kv, int32_t n_kv, int32_t layer, in
          kv_src, (long long)e.hd);
   G4_REQ(e.sliding == sliding, G4_EGEOM, "layer %d attention type differs from kv_src %d", layer, kv_src);
   G4_REQ(e.cap > 0, G4_ERANGE, "cache capacity %lld <= 0", (long long)e.cap);
-  G4_REQ(T <= e.cap, G4_ERANGE, "T %lld exceeds cache capacity %lld", (long long)T, (long long)e.cap);
+  G4_REQ(e.ring == 0 || e.ring == 1, G4_EINVAL, "kv entry %d: ring must be 0 or 1", kv_src);
+  if (e.ring) {
+    G4_REQ(e.sliding, G4_EGEOM, "kv entry %d: only a sliding-window cache can be a ring", kv_src);
+    G4_REQ(e.cap >= window, G4_ERANGE, "ring of %lld rows is shorter than the window %lld", (long long)e.cap,
+           (long long)window);
+    G4_REQ(T <= e.cap - window + 1, G4_ERANGE,
+           "T %lld > ring rows %lld - window %lld + 1 (prefill longer prompts in chunks)", (long long)T,
+           (long long)e.cap, (long long)window);
+  } else {
+    G4_REQ(T <= e.cap, G4_ERANGE, "T %lld exceeds cache capacity %lld", (long long)T, (long long)e.cap);
+  }
   G4_REQ(mode == G4_PREFILL || T == 1, G4_EINVAL, "decode takes T == 1");
   return G4_OK;
 }
@@ -221,7 +231,7 @@ static g4_status check_layer(const g4_model_desc* m, const g4_layer_desc* l, int
   if (l->kv_src == layer) G4_REQ(l->wk && l->wv && l->k_norm, G4_EINVAL, "layer %d owns its cache but wk/wv/k_norm is NULL", layer);
   else G4_REQ(l->kv_src < layer, G4_EGEOM, "layer %d: kv_src %d is not an earlier layer", layer, l->kv_src);
   const int64_t hd = l->sliding ? m->head_dim_swa : m->head_dim_full;
-  return check_kv(kv, n_kv, layer, l->kv_src, l->sliding, hd, T, mode);
+  return check_kv(kv, n_kv, layer, l->kv_src, l->sliding, hd, T, mode, m->window);
 }
 
 // The layer for few token rows (decode batches, M <= 64, bf16): every projection streams its weights
@@ -304,8 +314,8 @@ static g4_status few_row_layer(const LayerCtx& c) {
     segs[ns++] = HeadSeg{X, Nq, l->q_norm, qkv, qld, 0, (int32_t)nh, 1};
     if (own) {
       const g4_kv_entry& e = c.kv[c.layer];
-      segs[ns++] = HeadSeg{X + nh * hd, Nq, l->k_norm, e.k, 0, e.cap, (int32_t)nkv, 1};
-      segs[ns++] = HeadSeg{X + (nh + nkv) * hd, Nq, nullptr, e.v, 0, e.cap, (int32_t)nkv, 0};
+      segs[ns++] = HeadSeg{X + nh * hd, Nq, l->k_norm, e.k, 0, e.cap, (int32_t)nkv, 1, e.ring};
+      segs[ns++] = HeadSeg{X + (nh + nkv) * hd, Nq, nullptr, e.v, 0, e.cap, (int32_t)nkv, 0, e.ring};
     }
     G4_TRY(qk_norm_rope_parts(segs, ns, s1, M * Nq, c.pos, c.B, c.T, hd, sliding ? m->theta_swa : m->theta_full,
                               rot_pairs(m, sliding), m->eps, dt, c.s));
@@ -315,7 +325,7 @@ static g4_status few_row_layer(const LayerCtx& c) {
     AttnArgs aa{};
     aa.q = qkv; aa.q_ld = qld; aa.k = src.k; aa.v = src.v; aa.cap = src.cap; aa.pos0 = c.pos;
     aa.B = c.B; aa.T = c.T; aa.nh = nh; aa.nkv = nkv; aa.hd = hd; aa.sliding = sliding; aa.window = m->window;
-    aa.scale = 1.f; aa.out = ao; aa.out_ld = nh * hd;
+    aa.scale = 1.f; aa.out = ao; aa.out_ld = nh * hd; aa.ring = src.ring;
     TimedScope ts(G4_KC_ATTENTION, c.s);
     if (c.mode == G4_DECODE) G4_TRY(attn_decode(aa, c.ws + c.p->dec, c.p->fx - c.p->dec, dt, c.s));
     else G4_TRY(attn_prefill(aa, dt, c.s));
@@ -455,8 +465,8 @@ static g4_status layer_impl(const LayerCtx& c) {
   segs[ns++] = HeadSeg{qkv, qld, l->q_norm, qkv, qld, 0, (int32_t)nh, 1};
   if (own) {
     const g4_kv_entry& e = c.kv[c.layer];
-    segs[ns++] = HeadSeg{qkv + nh * hd * E, qld, l->k_norm, e.k, 0, e.cap, (int32_t)nkv, 1};
-    segs[ns++] = HeadSeg{qkv + (nh + nkv) * hd * E, qld, nullptr, e.v, 0, e.cap, (int32_t)nkv, 0};
+    segs[ns++] = HeadSeg{qkv + nh * hd * E, qld, l->k_norm, e.k, 0, e.cap, (int32_t)nkv, 1, e.ring};
+    segs[ns++] = HeadSeg{qkv + (nh + nkv) * hd * E, qld, nullptr, e.v, 0, e.cap, (int32_t)nkv, 0, e.ring};
   }
   {
     TimedScope ts(G4_KC_QK_NORM_ROPE, c.s);
@@ -467,7 +477,7 @@ static g4_status layer_impl(const LayerCtx& c) {
   AttnArgs aa{};
   aa.q = qkv; aa.q_ld = qld; aa.k = src.k; aa.v = src.v; aa.cap = src.cap; aa.pos0 = c.pos;
   aa.B = c.B; aa.T = c.T; aa.nh = nh; aa.nkv = nkv; aa.hd = hd; aa.sliding = sliding; aa.window = m->window;
-  aa.scale = 1.f; aa.out = ao; aa.out_ld = nh * hd;
+  aa.scale = 1.f; aa.out = ao; aa.out_ld = nh * hd; aa.ring = src.ring;
   {
     TimedScope ts(G4_KC_ATTENTION, c.s);
     if (c.mode == G4_DECODE) G4_TRY(attn_decode(aa, c.ws + c.p->dec, c.p->total - c.p->dec, dt, c.s));
@@ -608,7 +618,7 @@ static g4_status check_attn(const void* q, int64_t q_ld, const g4_kv_entry* kv, 
   G4_REQ(q_ld >= nh * hd && out_ld >= nh * hd, G4_EINVAL, "q_ld/out_ld smaller than nh*hd");
   G4_REQ(sliding == 0 || sliding == 1, G4_EINVAL, "sliding must be 0 or 1");
   G4_REQ(!sliding || window >= 1, G4_ERANGE, "window %lld < 1", (long long)window);
-  return check_kv(kv, n_kv, layer, kv_src, sliding, hd, T, mode);
+  return check_kv(kv, n_kv, layer, kv_src, sliding, hd, T, mode, window);
 }
 
 g4_status g4_attn_prefill(const void* q, int64_t q_ld, const g4_kv_entry* kv, int32_t n_kv, int32_t layer,
@@ -621,7 +631,7 @@ g4_status g4_attn_prefill(const void* q, int64_t q_ld, const g4_kv_entry* kv, in
   AttnArgs a{};
   a.q = q; a.q_ld = q_ld; a.k = kv[kv_src].k; a.v = kv[kv_src].v; a.cap = kv[kv_src].cap; a.pos0 = pos0;
   a.B = B; a.T = T; a.nh = nh; a.nkv = nkv; a.hd = hd; a.sliding = sliding; a.window = window; a.scale = scale;
-  a.out = out; a.out_ld = out_ld;
+  a.out = out; a.out_ld = out_ld; a.ring = kv[kv_src].ring;
   if (B * T == 0) return G4_OK;
   return attn_prefill(a, dtype, (hipStream_t)stream);
 }
@@ -640,7 +650,7 @@ g4_status g4_attn_decode(const void* q, int64_t q_ld, const g4_kv_entry* kv, int
   AttnArgs a{};
   a.q = q; a.q_ld = q_ld; a.k = kv[kv_src].k; a.v = kv[kv_src].v; a.cap = kv[kv_src].cap; a.pos0 = pos;
   a.B = B; a.T = 1; a.nh = nh; a.nkv = nkv; a.hd = hd; a.sliding = sliding; a.window = window; a.scale = scale;
-  a.out = out; a.out_ld = out_ld;
+  a.out = out; a.out_ld = out_ld; a.ring = kv[kv_src].ring;
   return attn_decode(a, ws, ws_bytes, dtype, (hipStream_t)stream);
 }
 

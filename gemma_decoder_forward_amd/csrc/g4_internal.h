@@ -113,8 +113,9 @@ size_t gemm_ws(int64_t M, int64_t N, int64_t K, int32_t dtype);
 struct HeadSeg {
   const void* x; int64_t x_ld;
   const void* w;           // per-head norm weight or nullptr
-  void* y; int64_t y_ld; int64_t y_cap;
+  void* y; int64_t y_ld; int64_t y_cap;  // y_cap > 0: y is a cache [B, heads, y_cap, hd]
   int32_t heads; int32_t rope;
+  int32_t ring;            // the cache is a ring: position p lives in row p mod y_cap
 };
 g4_status qk_norm_rope(const HeadSeg* segs, int nseg, const int32_t* pos, int64_t B, int64_t T,
                        int64_t hd, float theta, int64_t n_rot, float eps, int32_t dtype,
@@ -138,7 +139,16 @@ struct AttnArgs {
   int32_t sliding; int64_t window;
   float scale;
   void* out; int64_t out_ld;
+  int32_t ring;  // the cache is a ring of cap rows: key j lives in row j mod cap
 };
+
+// Cache row of key position j, and the last key a query at position i can see in the cache.
+__device__ __forceinline__ int64_t kv_row(int64_t j, int64_t cap, int32_t ring) {
+  return ring ? (int64_t)((uint64_t)j % (uint64_t)cap) : j;
+}
+__device__ __forceinline__ int64_t kv_last(int64_t i, int64_t cap, int32_t ring) {
+  return ring || i < cap - 1 ? i : cap - 1;
+}
 g4_status attn_prefill(const AttnArgs& a, int32_t dtype, hipStream_t s);
 g4_status attn_decode(const AttnArgs& a, void* ws, size_t ws_bytes, int32_t dtype, hipStream_t s);
 size_t attn_decode_ws(int64_t B, int64_t nh, int64_t hd, int64_t cap);

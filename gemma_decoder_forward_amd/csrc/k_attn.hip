@@ -11,11 +11,11 @@
 
 namespace g4 {
 
-__device__ __forceinline__ void key_range(int64_t i, int sliding, int64_t window, int64_t cap, int64_t& lo,
-                                          int64_t& hi) {
+__device__ __forceinline__ void key_range(int64_t i, int sliding, int64_t window, int64_t cap, int32_t ring,
+                                          int64_t& lo, int64_t& hi) {
   lo = sliding ? i - window + 1 : 0;
   if (lo < 0) lo = 0;
-  hi = i < cap - 1 ? i : cap - 1;  // keys beyond the cache do not exist
+  hi = kv_last(i, cap, ring);  // keys beyond a linear cache do not exist
 }
 
 // --------------------------------------------------------------------------------------------
@@ -29,7 +29,7 @@ __global__ __launch_bounds__(256) void k_attn_rowwise(AttnArgs a) {
   const int hd = (int)a.hd;
   const int64_t i = (int64_t)a.pos0[b] + t;
   int64_t lo, hi;
-  key_range(i, a.sliding, a.window, a.cap, lo, hi);
+  key_range(i, a.sliding, a.window, a.cap, a.ring, lo, hi);
   const T* qr = (const T*)a.q + (b * a.T + t) * a.q_ld + h * hd;
   const T* Kb = (const T*)a.k + (b * a.nkv + g) * a.cap * hd;
   const T* Vb = (const T*)a.v + (b * a.nkv + g) * a.cap * hd;
@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void k_attn_rowwise(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
       const int d = lane + 64 * e;
-      if (d < hd) s += q[e] * ldf(Kb + j * hd + d);
+      if (d < hd) s += q[e] * ldf(Kb + kv_row(j, a.cap, a.ring) * hd + d);
     }
     s = wave_sum(s);
     const float mn = fmaxf(m, s);
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void k_attn_rowwise(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
       const int d = lane + 64 * e;
-      acc[e] = acc[e] * c + (d < hd ? p * ldf(Vb + j * hd + d) : 0.f);
+      acc[e] = acc[e] * c + (d < hd ? p * ldf(Vb + kv_row(j, a.cap, a.ring) * hd + d) : 0.f);
     }
     m = mn;
   }
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(256) void k_attn_dec_part(AttnArgs a, int chunk, in
   const int hd = (int)a.hd;
   const int64_t i = a.pos0[b];
   int64_t lo, hi;
-  key_range(i, a.sliding, a.window, a.cap, lo, hi);
+  key_range(i, a.sliding, a.window, a.cap, a.ring, lo, hi);
   const int64_t k0 = lo + (int64_t)c * chunk;
   int64_t k1 = k0 + chunk - 1;
   if (k1 > hi) k1 = hi;
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256) void k_attn_dec_part(AttnArgs a, int chunk, in
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
       const int d = lane * EPL + e;
-      kv[e] = d < hd ? ldf(Kb + (k0 + kk) * hd + d) : 0.f;
+      kv[e] = d < hd ? ldf(Kb + kv_row(k0 + kk, a.cap, a.ring) * hd + d) : 0.f;
     }
     for (int hh = 0; hh < G; ++hh) {
       float s = 0.f;
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void k_attn_dec_part(AttnArgs a, int chunk, in
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
         const int d = lane * EPL + e;
-        if (d < hd) acc[e] += p * ldf(Vb + (k0 + kk) * hd + d);
+        if (d < hd) acc[e] += p * ldf(Vb + kv_row(k0 + kk, a.cap, a.ring) * hd + d);
       }
     }
 #pragma unroll

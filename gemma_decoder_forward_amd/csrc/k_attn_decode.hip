@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void k_attn_dec_mfma(AttnArgs a, int chunk, in
   const int64_t i = a.pos0[b];
   int64_t lo = a.sliding ? i - a.window + 1 : 0;
   if (lo < 0) lo = 0;
-  const int64_t hi = i < a.cap - 1 ? i : a.cap - 1;
+  const int64_t hi = kv_last(i, a.cap, a.ring);
   // this wave's keys: [k0, k1)
   const int64_t cb = lo + (int64_t)c * chunk;
   const int wch = chunk / 4;
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void k_attn_dec_mfma(AttnArgs a, int chunk, in
     const bool kv = key < k1;
     // scores S[head][key] for 16 keys
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-    const bf16* kr = Kb + (kv ? key : kt) * HD + 8 * q4;
+    const bf16* kr = Kb + kv_row(kv ? key : kt, a.cap, a.ring) * HD + 8 * q4;
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
       uint4 kw[4];
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256) void k_attn_dec_mfma(AttnArgs a, int chunk, in
     // P V over the 16 keys
     const int nkeys = (int)((k1 - kt) < 16 ? (k1 - kt) : 16);
     for (int j = 0; j < nkeys; ++j) {
-      const bf16* vr = Vb + (kt + j) * HD + lane * EPL;
+      const bf16* vr = Vb + kv_row(kt + j, a.cap, a.ring) * HD + lane * EPL;
       float vv[EPL];
       if (EPL == 8) {
         const uint4 w = *(const uint4*)vr;

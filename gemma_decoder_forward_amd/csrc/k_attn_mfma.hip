@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
   const int64_t imin = p0 + (int64_t)(g_first / G) * 32, imax = p0 + tlast;
   int64_t lob = a.sliding ? imin - a.window + 1 : 0;
   if (lob < 0) lob = 0;
-  int64_t hib = imax < a.cap - 1 ? imax : a.cap - 1;
+  int64_t hib = kv_last(imax, a.cap, a.ring);
   const int64_t kstart = lob & ~(int64_t)(AT_KB - 1);
   const int ntiles = hib >= lob ? (int)((hib - kstart) / AT_KB + 1) : 0;
   int64_t qlo = a.sliding ? qi - a.window + 1 : 0;
@@ -139,8 +139,8 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
     for (int r = 0; r < AT_KB / 4; ++r) {
       const int row = (AT_KB / 4) * wv + r;
       int64_t key = k0 + row;
-      if (key > a.cap - 1) key = a.cap - 1;
-      const uint32_t src = __builtin_amdgcn_readfirstlane((uint32_t)(key * HD * 2));
+      if (!a.ring && key > a.cap - 1) key = a.cap - 1;
+      const uint32_t src = __builtin_amdgcn_readfirstlane((uint32_t)(kv_row(key, a.cap, a.ring) * HD * 2));
       if (lane < HD / 8) {  // a row is HD / 8 lanes of 16 bytes
         at_dma16(rks, (uint32_t)lane * 16, src, kb0 + (uint32_t)(row * L::KLD * 2));
         at_dma16(rvs, (uint32_t)lane * 16, src, vb0 + (uint32_t)(row * L::VROW * 2));

@@ -226,7 +226,7 @@ struct SegDev {
   const void* x; int64_t x_ld;
   const void* w;
   void* y; int64_t y_ld; int64_t y_cap;
-  int32_t heads; int32_t rope;
+  int32_t heads; int32_t rope; int32_t ring;
 };
 struct SegPack { SegDev s[3]; int n; int total_heads; int parts; int64_t part_stride; };
 
@@ -282,8 +282,9 @@ __global__ __launch_bounds__(256) void k_qknr(SegPack pk, const int32_t* __restr
     const float inv = 1.f / sqrtf(ss / (float)hd + eps);
     T* yh;
     if (sg.y_cap > 0) {
-      if (p < 0 || p >= sg.y_cap) continue;  // out-of-range position: no write
-      yh = (T*)sg.y + (((b * sg.heads + h) * sg.y_cap) + p) * hd;
+      if (p < 0 || (!sg.ring && p >= sg.y_cap)) continue;  // out-of-range position: no write
+      const int64_t row = sg.ring ? p % sg.y_cap : p;
+      yh = (T*)sg.y + (((b * sg.heads + h) * sg.y_cap) + row) * hd;
     } else {
       yh = (T*)sg.y + m * sg.y_ld + (int64_t)h * hd;
     }
@@ -319,7 +320,7 @@ static g4_status qknr_launch(const HeadSeg* segs, int nseg, int parts, int64_t p
   int any_rope = 0;
   for (int i = 0; i < nseg; ++i) {
     pk.s[i] = SegDev{segs[i].x, segs[i].x_ld, segs[i].w, segs[i].y, segs[i].y_ld, segs[i].y_cap,
-                     segs[i].heads, segs[i].rope};
+                     segs[i].heads, segs[i].rope, segs[i].ring};
     pk.total_heads += segs[i].heads;
     any_rope |= segs[i].rope;
   }

@@ -59,21 +59,28 @@ class G4Model:
     def head_dim(self, l):
         return self.cfg["head_dim_swa"] if self.sliding[l] else self.cfg["head_dim_full"]
 
-    def new_caches(self, B, cap, fill=None):
-        """Device K/V caches [B, nkv, cap, hd] for every owning layer, plus the C table."""
+    def new_caches(self, B, cap, fill=None, ring=0):
+        """Device K/V caches [B, nkv, rows, hd] for every owning layer, plus the C table.
+
+        rows = cap, position p in row p; with ring > 0 the sliding layers' caches are rings of `ring` rows
+        (position p in row p mod ring, ring >= window), which bounds their memory by the window instead of
+        the context; a call then takes at most ring - window + 1 tokens per sequence."""
         caches = {}
         table = (bd.KvEntry * self.L)()
         for l in range(self.L):
             if self.kv_src[l] != l:
                 continue
             hd = self.head_dim(l)
+            is_ring = 1 if (ring and self.sliding[l]) else 0
+            rows = ring if is_ring else cap
             if fill is not None:
                 k, v = fill(l)
             else:
-                k = torch.zeros((B, self.cfg["n_kv_heads"], cap, hd), dtype=self.torch_dtype, device="cuda")
+                k = torch.zeros((B, self.cfg["n_kv_heads"], rows, hd), dtype=self.torch_dtype, device="cuda")
                 v = torch.zeros_like(k)
             caches[l] = (k, v)
-            table[l] = bd.KvEntry(k=k.data_ptr(), v=v.data_ptr(), cap=cap, hd=hd, sliding=self.sliding[l])
+            table[l] = bd.KvEntry(k=k.data_ptr(), v=v.data_ptr(), cap=rows, hd=hd, sliding=self.sliding[l],
+                                  ring=is_ring)
         return caches, table
 
     def workspace(self, B, T, cap, mode):

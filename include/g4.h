@@ -96,7 +96,11 @@ typedef struct g4_kv_entry {
   int64_t cap;     /* rows per (sequence, kv head) */
   int64_t hd;      /* head width of the rows */
   int32_t sliding; /* attention type of the layer that owns the cache */
-  int32_t reserved;
+  int32_t ring;    /* 0: position p lives in row p (p < cap). 1 (sliding layers only): a ring of cap >= window
+                      rows, position p lives in row p mod cap (the ring capacity of a sliding layer's cache in turbospark-runtime,
+                      families/gemma4/attn.rs, encode_gemma4_layer_attn_and_router); a call of T tokens
+                      per sequence then needs T <= cap - window + 1, so that no key a query of the call can
+                      see is overwritten by the call's own writes (longer prompts are prefilled in chunks) */
 } g4_kv_entry;
 
 /* ---- helpers ---------------------------------------------------------------------------------- */

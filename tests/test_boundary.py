@@ -66,7 +66,7 @@ def _table(entries):
     t = (bd.KvEntry * len(entries))()
     for i, e in enumerate(entries):
         if e is not None:
-            t[i] = bd.KvEntry(k=FAKE, v=FAKE, cap=e[0], hd=e[1], sliding=e[2])
+            t[i] = bd.KvEntry(k=FAKE, v=FAKE, cap=e[0], hd=e[1], sliding=e[2], ring=e[3] if len(e) > 3 else 0)
     return t
 
 
@@ -87,6 +87,18 @@ def test_attention_validation_errors():
     assert _attn(t, 2, 0, 1, 256, q=None) == bd.G4_EINVAL
     assert _attn(t, 7, 0, 1, 256) == bd.G4_EINVAL     # layer outside the table
     assert b"head_dim" in bd.lib().g4_last_error() or bd.lib().g4_last_error()
+
+
+def test_ring_cache_validation_errors():
+    """A ring cache: sliding layers only, at least a window of rows, and at most rows - window + 1 tokens a call."""
+    t = _table([(640, 256, 1, 1), (640, 512, 0, 1), (512, 256, 1, 1), (640, 256, 1, 2)])
+    L = bd.lib()
+    # every case fails on the host before any launch
+    assert _attn(t, 1, 1, 0, 512, T=8) == bd.G4_EGEOM      # full-attention cache marked as a ring
+    assert _attn(t, 2, 2, 1, 256, T=8, window=600) == bd.G4_ERANGE  # ring shorter than the window
+    assert _attn(t, 0, 0, 1, 256, T=130) == bd.G4_ERANGE   # 130 > 640 - 512 + 1
+    assert _attn(t, 3, 3, 1, 256, T=8) == bd.G4_EINVAL     # ring flag neither 0 nor 1
+    assert b"ring" in L.g4_last_error()
 
 
 def test_layer_validation_errors():
