@@ -15,12 +15,16 @@ typedef uint16_t bf16;
 
 __device__ __forceinline__ float bf2f(bf16 v) { return __uint_as_float((uint32_t)v << 16); }
 
-// Round to nearest even (NaN stays NaN).
-__device__ __forceinline__ bf16 f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16)0x7fc0;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16)(u >> 16);
+// Round to nearest even (NaN stays NaN): the hardware conversion (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16 f2bf(float f) { return __builtin_bit_cast(bf16, (__bf16)f); }
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_hw;
+// Four floats rounded to bf16 and packed for one 8-byte store.
+__device__ __forceinline__ uint2 pack_bf16x4(const float* v) {
+  bf16x2_hw lo, hi;
+  lo[0] = (__bf16)v[0]; lo[1] = (__bf16)v[1];
+  hi[0] = (__bf16)v[2]; hi[1] = (__bf16)v[3];
+  return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
 }
 
 template <typename T> struct io;
@@ -69,10 +73,12 @@ __device__ __forceinline__ float block_sum(float v, float* sh) {
   return r;
 }
 
+// gelu, tanh form: 0.5 x (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3). Evaluated as the equal
+// x / (1 + exp(-2u)), with exp(-2u) = 2^t, t = -2 log2(e) u, through the hardware base-2 exponential
+// and reciprocal (about 1 ulp each): large |u| saturate to x or to 0 without overflow trouble.
 __device__ __forceinline__ float gelu_tanh(float x) {
-  // 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))
-  const float u = 0.7978845608028654f * (x + 0.044715f * x * x * x);
-  return 0.5f * x * (1.f + tanhf(u));
+  const float t = x * (-2.302208198144325f - 0.1029432395800235f * x * x);
+  return x * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(t));
 }
 
 inline size_t dsize(int32_t dt) { return dt == G4_BF16 ? 2 : 4; }

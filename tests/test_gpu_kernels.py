@@ -271,6 +271,20 @@ def test_linear_vs_oracle(dt, M, N, K):
     assert_close(Cd, ref, dt, "C in dtype")
 
 
+@pytest.mark.parametrize("M,N,K", [(1000, 12288, 544), (520, 24576, 96), (600, 24576, 32), (300, 24576, 2560)])
+def test_linear_large_tiles_pipeline_depths(M, N, K):
+    """The 256x256-tile MFMA path (at least 192 tiles): ragged M, and K steps fewer than, equal to and
+    more than the LDS stages (K = 32, 96, 544, 2560 in steps of 32)."""
+    log(f"linear large tiles {M}x{N}x{K}")
+    A = randn((M, K), 74, torch.bfloat16)
+    W = randn((N, K), 75, torch.bfloat16, 0.02)
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    bd.g4_linear(A.data_ptr(), W.data_ptr(), C.data_ptr(), M, N, K, bd.G4_F32, bd.G4_BF16, None, 0, stream())
+    torch.cuda.synchronize()
+    ref = O.f64(A) @ O.f64(W).T
+    assert max_rel(C, ref) <= 1e-3
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 256, 2560), (8, 3072, 2560), (33, 512, 10240), (64, 2560, 10240),
                                    (17, 20480, 2560)])
 def test_linear_few_rows_weight_streaming(M, N, K):
