@@ -1,26 +1,33 @@
 // bf16 GEMM on the CDNA4 matrix cores: C = A B^T, A [M,K] and B [N,K] row-major (K contiguous),
 // float32 accumulation with v_mfma_f32_32x32x16_bf16.
 //
-// Block: 256 threads = 4 waves in a 2x2 grid; a wave owns a (BM/2) x (BN/2) sub-tile made of 32x32
-// MFMA blocks. K advances in steps of 32 (one 64-byte row segment per tile row, two MFMA k-slices).
+// Block: NW waves in an (NW/2) x 2 grid; a wave owns a (BM/(NW/2)) x (BN/2) sub-tile made of 32x32
+// MFMA blocks. The 256x256 tile runs 8 waves (two per SIMD, 64x128 each), so one wave's MFMAs cover
+// the other's waits; the 128x128 tile runs 4. K advances in steps of BK (one BK*2-byte row segment
+// per tile row, BK/16 MFMA k-slices).
 //
 // Operand staging: buffer loads write straight into LDS (buffer_load_dwordx4 ... lds), so no registers
-// hold staged data and the accumulators keep the whole accumulation-register file. One wave load
-// instruction fills 1 KB = 16 tile rows; inside a row the 4 16-byte chunks are XOR-permuted with
-// ((row >> 1) ^ (row >> 2)) & 3, which keeps the 16-byte fragment reads free of bank conflicts. NS stages in a ring: the loads of step k + NS are issued as soon as every wave has finished
-// reading step k's stage, so global loads have NS - 1 steps of MFMA work to land in.
+// hold staged data. One wave load instruction fills 1 KB of a stage: 1024 / (2 BK) tile rows. Global
+// reads move through the vector L1, which can keep only a bounded number of line requests in flight
+// per CU; BK = 64 makes every request a whole 128-byte line, twice the bytes per request of BK = 32,
+// and that doubles what the L1 can pull from L2 per unit of latency. Inside a row the 16-byte chunks
+// are XOR-permuted so that the fragment reads of any 8 (and any 16) consecutive rows fall on distinct
+// bank groups. NS stages form a ring: the loads for step k + NS are issued as soon as every wave has
+// finished reading step k's stage.
 //
-// Latency hiding without a second wave per SIMD (a 128x128 wave tile needs the whole accumulation
-// file): the operand fragments of the next k-slice are read from LDS while the MFMAs of the current
-// one run (two register sets, A/B ping-pong), and the block meets once per step, between the two
-// k-slices, where the waits for the next stage and for the freed stage coincide.
+// Schedule: two fragment register sets alternate between k-slices; the reads of the next slice and
+// the global loads ride between the MFMAs of the current one. The block meets once per step, before
+// the last k-slice, where the wait for the next stage and the release of the current one coincide.
+// Loads of steps past the K range use a scalar offset beyond the buffer; the range check turns them
+// into zeros without memory traffic, so every step keeps the same loads in flight.
 //
 // Buffer descriptors start at the tile's first row, so rows past the matrix read as zero (ragged M)
-// and every per-row offset fits 32 bits; the per-load row step and the K step ride in the scalar offset.
+// and every per-row offset fits 32 bits.
 //
 // MFMA operand layout (32x32x16 bf16): lane l supplies row (l % 32) and the 8 consecutive k values
 // starting at 8 * (l / 32), for A and for B alike (B is stored [N, K], so its rows are the output
-// columns). Accumulator register j of lane l holds C[8*(j/4) + 4*(l/32) + j%4][l % 32].
+// columns). B goes in as the first operand, so register r of lane l holds C[m][n] with m = l % 32 and
+// n = 8 (r / 4) + 4 (l / 32) + r % 4: four consecutive output columns per register group.
 //
 // Epilogues: float32 or bf16 store, split-K float32 slices, the gelu-tanh gated product of two weight
 // matrices (gate and up rows interleaved in 32-row blocks of the B tile, so a lane holds matching gate
@@ -33,8 +40,16 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int MF_BK = 32;  // K per step
-constexpr int MF_NS = 4;   // LDS stages
+#ifndef G4_GEMM_BK
+#define G4_GEMM_BK 64
+#endif
+#ifndef G4_GEMM_NS
+#define G4_GEMM_NS 2
+#endif
+#ifndef G4_GEMM_NW
+#define G4_GEMM_NW 8
+#endif
+constexpr int MF_KMIN = 64;  // K granularity the MFMA path accepts (every configuration's BK divides it)
 
 // Linear block id -> (tile_m, tile_n). Blocks are dispatched round-robin over the 8 XCDs; renumber so
 // each XCD walks a contiguous range, then walk that range in groups of 8 tile rows so neighbouring
@@ -52,9 +67,13 @@ __device__ __forceinline__ void tile_of(int bid, int tm, int tn, int& im, int& i
   in_ = r / gm;
 }
 
-// chunk permutation of a 64-byte LDS row: the fragment reads of any 8 consecutive rows (one 128-byte
-// bank line per cycle) and of any 16 consecutive rows land on distinct 16-byte bank groups
-__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+// Chunk permutation of an LDS row of BK bf16 (BK/8 chunks of 16 bytes). 128-byte rows: row ^ (row >> 3)
+// permutes the 8 chunks of 8 consecutive rows, and pairs of 8-row groups differ in row parity.
+// 64-byte rows: ((row >> 1) ^ (row >> 2)) covers the 4 chunks twice over 8 rows, once per row parity.
+template <int BK>
+__device__ __forceinline__ int swz(int row) {
+  return BK == 64 ? (row ^ (row >> 3)) & 7 : ((row >> 1) ^ (row >> 2)) & 3;
+}
 
 typedef __attribute__((ext_vector_type(4))) uint32_t rsrc_t;
 
@@ -80,19 +99,24 @@ __device__ __forceinline__ void lds_dma16(const rsrc_t& r, uint32_t voff, uint32
 // vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt[3:0] and [15:14]).
 #define G4_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
 
-template <int BM, int BN, int EPI, bool CF32>
-__global__ __launch_bounds__(256, 1) void k_gemm_mfma(GemmArgs a, int tiles_m, int tiles_n) {
-  constexpr int WM = BM / 2, WN = BN / 2;
+template <int BM, int BN, int NW, int BK, int NS, int EPI, bool CF32>
+__global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a, int tiles_m, int tiles_n) {
+  constexpr int WM = BM / (NW / 2), WN = BN / 2;  // waves in a (NW/2) x 2 grid
   constexpr int FM = WM / 32, FN = WN / 32;
-  constexpr int NMF = FM * FN;                // MFMAs per wave per k-slice
-  constexpr int NRD = FM + FN;                // fragment reads per wave per k-slice
-  constexpr int AJ = BM / 64, BJ = BN / 64;  // 1 KB load instructions per wave per K step
-  constexpr int LG = AJ + BJ;                 // load instructions per wave per stage
-  constexpr int ASZ = BM * MF_BK, STAGE = (BM + BN) * MF_BK;  // in bf16 elements
+  constexpr int NMF = FM * FN;                  // MFMAs per wave per k-slice
+  constexpr int NRD = FM + FN;                  // fragment reads per wave per k-slice
+  constexpr int KS = BK / 16;                   // k-slices per step
+  constexpr int CPR = BK / 8, RPI = 64 / CPR;   // 16-byte chunks per LDS row, rows per load instruction
+  constexpr int AJ = BM / (RPI * NW), BJ = BN / (RPI * NW);  // load instructions per wave per step
+  constexpr int LG = AJ + BJ;
+  constexpr int ASZ = BM * BK, STAGE = (BM + BN) * BK;  // in bf16 elements
   static_assert(EPI != EPI_GEGLU || (FN % 2) == 0, "gate/up pairs must sit in one wave");
+  static_assert((NW == 4 || NW == 8) && AJ * RPI * NW == BM && BJ * RPI * NW == BN, "loader covers the tile");
+  static_assert(KS % 2 == 0 && MF_KMIN % BK == 0, "k-slices alternate two register sets");
   static_assert(NRD <= NMF && LG <= NMF, "every read and load rides behind an MFMA");
-  static_assert((MF_NS - 1) * LG <= 63, "vmcnt range");
-  __shared__ __attribute__((aligned(1024))) bf16 lds[MF_NS * STAGE];
+  static_assert((NS - 1) * LG <= 63 && NS >= 2, "vmcnt range");
+  static_assert(NS * STAGE * 2 <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) bf16 lds[NS * STAGE];
 
   int im, in_;
   tile_of(blockIdx.x, tiles_m, tiles_n, im, in_);
@@ -106,34 +130,45 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mfma(GemmArgs a, int tiles_m, i
   const int wm = wave >> 1, wn = wave & 1;
 
   // split-K range
-  const int64_t kper = ((a.K + a.splits - 1) / a.splits + MF_BK - 1) / MF_BK * MF_BK;
+  const int64_t kper = ((a.K + a.splits - 1) / a.splits + BK - 1) / BK * BK;
   const int64_t kb = (int64_t)blockIdx.z * kper;
   int64_t ke = kb + kper;
   if (ke > a.K) ke = a.K;
-  const int nk = ke > kb ? (int)((ke - kb) / MF_BK) : 0;
+  const int nk = ke > kb ? (int)((ke - kb) / BK) : 0;
 
-  // Loader geometry. Instruction j of wave w fills LDS rows 16(w + 4j) .. +15; lane i loads row
-  // 16(w + 4j) + i/4 into LDS chunk i%4, which holds global chunk (i%4) ^ swz(row); swz(row) depends
-  // on the lane only. GEGLU: B tile row block b (32 rows) holds gate rows (b even) or up rows (b odd)
-  // 32(b/2) .. +31, so wave w's instructions all read gate (w < 2) or up (w >= 2) rows 32j + 16(w&1) + i/4.
-  const int lr = lane >> 2, lc = (lane & 3) ^ swz(lane >> 2);
+  // Loader geometry. Load instruction q covers the RPI LDS rows of group g = wave + NW q (A rows for
+  // q < AJ, B rows after): lane i fills LDS row RPI g + i / CPR, chunk i % CPR, from global chunk
+  // (i % CPR) ^ swz(row). GEGLU: B tile row block b = RPI g / 32 (32 rows) holds gate rows (b even) or
+  // up rows (b odd) 32 (b / 2) + (RPI g) % 32 + ...; every row of one instruction sits in one block.
+  const int lr = lane / CPR, lcp = lane % CPR;
   const rsrc_t ra = make_rsrc((const bf16*)a.A + m0 * a.lda + kb, (a.M - m0) * a.lda * 2 - kb * 2);
-  const bf16* bsrc = (EPI == EPI_GEGLU && (wave >> 1)) ? (const bf16*)a.B2 : (const bf16*)a.B;
-  const rsrc_t rb = make_rsrc(bsrc + n0 * a.ldb + kb, (a.N - n0) * a.ldb * 2 - kb * 2);
-  const uint32_t avoff = (uint32_t)(((int64_t)(16 * wave + lr) * a.lda + 8 * lc) * 2);
-  const int brow0 = EPI == EPI_GEGLU ? 16 * (wave & 1) : 16 * wave;
-  const uint32_t bvoff = (uint32_t)(((int64_t)(brow0 + lr) * a.ldb + 8 * lc) * 2);
-  const uint32_t astep = (uint32_t)(64 * a.lda * 2);
-  const uint32_t bstep = (uint32_t)((EPI == EPI_GEGLU ? 32 : 64) * a.ldb * 2);
+  const rsrc_t rg = make_rsrc((const bf16*)a.B + n0 * a.ldb + kb, (a.N - n0) * a.ldb * 2 - kb * 2);
+  const rsrc_t ru = EPI == EPI_GEGLU ? make_rsrc((const bf16*)a.B2 + n0 * a.ldb + kb, (a.N - n0) * a.ldb * 2 - kb * 2) : rg;
+  uint32_t voff[LG];
+  bool use_up[LG];
+#pragma unroll
+  for (int q = 0; q < LG; ++q) {
+    const bool isa = q < AJ;
+    const int g = wave + NW * (isa ? q : q - AJ);
+    const int row = RPI * g + lr;  // LDS row within the A or B part of the stage
+    const int chunk = lcp ^ swz<BK>(row);
+    int src = row;
+    use_up[q] = false;
+    if (!isa && EPI == EPI_GEGLU) {
+      const int b = (RPI * g) / 32;
+      use_up[q] = b & 1;
+      src = 32 * (b >> 1) + (RPI * g) % 32 + lr;
+    }
+    voff[q] = (uint32_t)(((int64_t)src * (isa ? a.lda : a.ldb) + 8 * chunk) * 2);
+  }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)lds;
-  // Load instruction q (A rows first, then B rows) of step kt. A step past the range (the ring keeps
-  // issuing one stage per step) gets a scalar offset beyond the buffer, which the range check turns
-  // into zeros without moving data, so every step keeps the same number of loads in flight.
+  // Load instruction q of step kt. A step past the range gets an offset beyond the buffer (zeros, no
+  // traffic), so every step keeps the same number of loads in flight.
   auto dma = [&](int kt, int q) {
-    const uint32_t koff = kt < nk ? (uint32_t)kt * MF_BK * 2 : 0x80000000u;
-    const uint32_t lbase = lds0 + (uint32_t)(kt % MF_NS) * STAGE * 2;
-    if (q < AJ) lds_dma16(ra, avoff, q * astep + koff, lbase + (wave + 4 * q) * 1024);
-    else lds_dma16(rb, bvoff, (q - AJ) * bstep + koff, lbase + ASZ * 2 + (wave + 4 * (q - AJ)) * 1024);
+    const uint32_t koff = kt < nk ? (uint32_t)kt * BK * 2 : 0x80000000u;
+    const uint32_t lbase = lds0 + (uint32_t)(kt % NS) * STAGE * 2;
+    if (q < AJ) lds_dma16(ra, voff[q], koff, lbase + (wave + NW * q) * 1024);
+    else lds_dma16(use_up[q] ? ru : rg, voff[q], koff, lbase + ASZ * 2 + (wave + NW * (q - AJ)) * 1024);
   };
 
   f32x16_t acc[FM][FN];
@@ -146,23 +181,22 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mfma(GemmArgs a, int tiles_m, i
 
   // fragment addresses (elements within a stage): row r, k chunk 2ks + h at chunk (2ks + h) ^ swz(r)
   const int frow = lane & 31, fh = lane >> 5;
-  int aoff[2][FM], boff[2][FN];
+  int aoff[KS][FM], boff[KS][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int row = wm * WM + 32 * i + frow;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) aoff[ks][i] = row * MF_BK + (((2 * ks + fh) ^ swz(row)) << 3);
+    for (int ks = 0; ks < KS; ++ks) aoff[ks][i] = row * BK + (((2 * ks + fh) ^ swz<BK>(row)) << 3);
   }
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     const int row = wn * WN + 32 * j + frow;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) boff[ks][j] = ASZ + row * MF_BK + (((2 * ks + fh) ^ swz(row)) << 3);
+    for (int ks = 0; ks < KS; ++ks) boff[ks][j] = ASZ + row * BK + (((2 * ks + fh) ^ swz<BK>(row)) << 3);
   }
 
   // Two fragment sets. Read q of a k-slice comes in the order the MFMAs consume them: A0, B0..B(FN-1),
-  // A1..A(FM-1); MFMA q multiplies A fragment q / FN with B fragment q % FN. Operands are swapped
-  // (B first) so that a lane's accumulator registers run along output columns.
+  // A1..A(FM-1); MFMA q multiplies A fragment q / FN with B fragment q % FN.
   bf16x8_t fa[2][FM], fb[2][FN];
   auto rd = [&](int set, int ks, const bf16* st, int q) {
     if (q == 0) fa[set][0] = *(const bf16x8_t*)(st + aoff[ks][0]);
@@ -176,33 +210,36 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mfma(GemmArgs a, int tiles_m, i
 
   if (nk > 0) {
 #pragma unroll
-    for (int kt = 0; kt < MF_NS; ++kt)
+    for (int kt = 0; kt < NS; ++kt)
 #pragma unroll
       for (int q = 0; q < LG; ++q) dma(kt, q);
-    G4_WAIT_VMCNT((MF_NS - 1) * LG);  // step 0 landed
+    G4_WAIT_VMCNT((NS - 1) * LG);  // step 0 landed
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < NRD; ++q) rd(0, 0, lds, q);
     for (int kt = 0; kt < nk; ++kt) {
-      const bf16* st = lds + (kt % MF_NS) * STAGE;
-      const bf16* st1 = lds + ((kt + 1) % MF_NS) * STAGE;
-      // k-slice 0: MFMAs on set 0, with the reads of slice 1 into set 1 riding behind them
+      const bf16* st = lds + (kt % NS) * STAGE;
+      const bf16* st1 = lds + ((kt + 1) % NS) * STAGE;
+      // k-slices 0 .. KS-2: MFMAs on one set while the next slice's fragments load into the other
 #pragma unroll
-      for (int q = 0; q < NMF; ++q) {
-        mf(0, q);
-        if (q < NRD) rd(1, 1, st, q);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int ks = 0; ks < KS - 1; ++ks) {
+#pragma unroll
+        for (int q = 0; q < NMF; ++q) {
+          mf(ks & 1, q);
+          if (q < NRD) rd((ks + 1) & 1, ks + 1, st, q);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-      // step kt + 1 landed in every wave, and every wave is done reading step kt's stage
-      G4_WAIT_VMCNT((MF_NS - 2) * LG);
+      // step kt + 1 landed in every wave, and every wave has read all of step kt's stage
+      G4_WAIT_VMCNT((NS - 2) * LG);
       __syncthreads();
-      // k-slice 1: MFMAs on set 1; behind them the reads of the next step's slice 0, then the loads
-      // that refill the stage just consumed with step kt + NS
+      // last k-slice; behind its MFMAs the next step's first fragments, then the loads that refill the
+      // stage just released with step kt + NS
 #pragma unroll
       for (int q = 0; q < NMF; ++q) {
         mf(1, q);
         if (q < NRD) rd(0, 0, st1, q);
-        if (q >= NMF - LG) dma(kt + MF_NS, q - (NMF - LG));
+        if (q >= NMF - LG) dma(kt + NS, q - (NMF - LG));
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -254,12 +291,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mfma(GemmArgs a, int tiles_m, i
   }
 }
 
-// Shapes the MFMA kernel takes: bf16, K a multiple of 32, output columns a multiple of the tile,
+// Shapes the MFMA kernel takes: bf16, K a multiple of 64, output columns a multiple of the tile,
 // 16-byte aligned rows, operands small enough for 32-bit buffer offsets, and outputs (and the
 // GELU_MUL factor) whose rows take 4-column vector stores.
 static bool mfma_ok(const GemmArgs& a, int BN) {
   const int ncols = a.epi == EPI_GEGLU ? BN / 2 : BN;
-  if (a.K % MF_BK || a.N % ncols) return false;
+  if (a.K % MF_KMIN || a.N % ncols) return false;
   if ((a.lda | a.ldb) & 7) return false;
   if (((uintptr_t)a.A | (uintptr_t)a.B | (uintptr_t)(a.B2 ? a.B2 : a.B)) & 15) return false;
   if (a.M * a.lda * 2 > 0x7fffffffLL || a.N * a.ldb * 2 > 0x7fffffffLL) return false;
@@ -270,15 +307,15 @@ static bool mfma_ok(const GemmArgs& a, int BN) {
   return true;
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int NW, int BK, int NS>
 static g4_status launch_mfma(const GemmArgs& a, hipStream_t s) {
   const int ncols = a.epi == EPI_GEGLU ? BN / 2 : BN;
   const int tm = (int)((a.M + BM - 1) / BM), tn = (int)(a.N / ncols);
-  dim3 g((unsigned)(tm * tn), 1, (unsigned)a.splits);
-  if (a.epi == EPI_GEGLU) hipLaunchKernelGGL((k_gemm_mfma<BM, BN, EPI_GEGLU, false>), g, dim3(256), 0, s, a, tm, tn);
-  else if (a.epi == EPI_GELU_MUL) hipLaunchKernelGGL((k_gemm_mfma<BM, BN, EPI_GELU_MUL, false>), g, dim3(256), 0, s, a, tm, tn);
-  else if (a.c_dtype == G4_F32) hipLaunchKernelGGL((k_gemm_mfma<BM, BN, EPI_STORE, true>), g, dim3(256), 0, s, a, tm, tn);
-  else hipLaunchKernelGGL((k_gemm_mfma<BM, BN, EPI_STORE, false>), g, dim3(256), 0, s, a, tm, tn);
+  dim3 g((unsigned)(tm * tn), 1, (unsigned)a.splits), b(NW * 64);
+  if (a.epi == EPI_GEGLU) hipLaunchKernelGGL((k_gemm_mfma<BM, BN, NW, BK, NS, EPI_GEGLU, false>), g, b, 0, s, a, tm, tn);
+  else if (a.epi == EPI_GELU_MUL) hipLaunchKernelGGL((k_gemm_mfma<BM, BN, NW, BK, NS, EPI_GELU_MUL, false>), g, b, 0, s, a, tm, tn);
+  else if (a.c_dtype == G4_F32) hipLaunchKernelGGL((k_gemm_mfma<BM, BN, NW, BK, NS, EPI_STORE, true>), g, b, 0, s, a, tm, tn);
+  else hipLaunchKernelGGL((k_gemm_mfma<BM, BN, NW, BK, NS, EPI_STORE, false>), g, b, 0, s, a, tm, tn);
   return check_launch("gemm_mfma");
 }
 
@@ -286,11 +323,11 @@ static g4_status launch_mfma(const GemmArgs& a, hipStream_t s) {
 bool gemm_mfma(const GemmArgs& a, hipStream_t s, g4_status* st) {
   const int64_t tiles256 = ((a.M + 255) / 256) * (a.N / (a.epi == EPI_GEGLU ? 128 : 256)) * a.splits;
   if (mfma_ok(a, 256) && tiles256 >= 192) {
-    *st = launch_mfma<256, 256>(a, s);
+    *st = launch_mfma<256, 256, G4_GEMM_NW, G4_GEMM_BK, G4_GEMM_NS>(a, s);
     return true;
   }
   if (mfma_ok(a, 128)) {
-    *st = launch_mfma<128, 128>(a, s);
+    *st = launch_mfma<128, 128, 4, 32, 4>(a, s);
     return true;
   }
   return false;

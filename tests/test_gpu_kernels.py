@@ -271,10 +271,10 @@ def test_linear_vs_oracle(dt, M, N, K):
     assert_close(Cd, ref, dt, "C in dtype")
 
 
-@pytest.mark.parametrize("M,N,K", [(1000, 12288, 544), (520, 24576, 96), (600, 24576, 32), (300, 24576, 2560)])
+@pytest.mark.parametrize("M,N,K", [(1000, 12288, 576), (520, 24576, 128), (600, 24576, 64), (300, 24576, 2560)])
 def test_linear_large_tiles_pipeline_depths(M, N, K):
     """The 256x256-tile MFMA path (at least 192 tiles): ragged M, and K steps fewer than, equal to and
-    more than the LDS stages (K = 32, 96, 544, 2560 in steps of 32)."""
+    more than the LDS stages (K = 64, 128, 576, 2560 in steps of 64)."""
     log(f"linear large tiles {M}x{N}x{K}")
     A = randn((M, K), 74, torch.bfloat16)
     W = randn((N, K), 75, torch.bfloat16, 0.02)
