@@ -92,8 +92,18 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
 // 16 bytes per lane from buffer offset voff + soff straight into LDS at m0 + 16 * lane. Issued through
 // inline assembly so the compiler's wait insertion does not treat every later LDS read as dependent
 // on it; completion is awaited explicitly with vmcnt before the barrier that precedes the reads.
+// The descriptor, scalar offset and LDS base are wave-uniform by construction; readfirstlane states it
+// to the compiler (free for values already in scalar registers).
 __device__ __forceinline__ void lds_dma16(const rsrc_t& r, uint32_t voff, uint32_t soff, uint32_t m0) {
-  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" : : "v"(voff), "s"(r), "s"(soff), "{m0}"(m0) : "memory");
+  rsrc_t u;
+  u.x = __builtin_amdgcn_readfirstlane(r.x);
+  u.y = __builtin_amdgcn_readfirstlane(r.y);
+  u.z = __builtin_amdgcn_readfirstlane(r.z);
+  u.w = __builtin_amdgcn_readfirstlane(r.w);
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(u), "s"(__builtin_amdgcn_readfirstlane(soff)), "{m0}"(__builtin_amdgcn_readfirstlane(m0))
+               : "memory");
 }
 
 // vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt[3:0] and [15:14]).
@@ -118,32 +128,46 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a, int tiles_
   static_assert(NS * STAGE * 2 <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(1024))) bf16 lds[NS * STAGE];
 
-  int im, in_;
-  tile_of(blockIdx.x, tiles_m, tiles_n, im, in_);
-  im = __builtin_amdgcn_readfirstlane(im);  // block-uniform: keeps the buffer descriptors in SGPRs
-  in_ = __builtin_amdgcn_readfirstlane(in_);
-  const int64_t m0 = (int64_t)im * BM;
-  // output columns of this tile (GEGLU: BN B rows make BN/2 output columns)
-  const int64_t n0 = (int64_t)in_ * (EPI == EPI_GEGLU ? BN / 2 : BN);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (feeds the LDS base in M0)
   const int wm = wave >> 1, wn = wave & 1;
+  const int per_split = tiles_m * tiles_n, total = per_split * a.splits;
+  const int64_t kper = ((a.K + a.splits - 1) / a.splits + BK - 1) / BK * BK;  // split-K range length
 
-  // split-K range
-  const int64_t kper = ((a.K + a.splits - 1) / a.splits + BK - 1) / BK * BK;
-  const int64_t kb = (int64_t)blockIdx.z * kper;
-  int64_t ke = kb + kper;
-  if (ke > a.K) ke = a.K;
-  const int nk = ke > kb ? (int)((ke - kb) / BK) : 0;
+  // A tile's place and operands. Tile t: split z = t / (tiles_m tiles_n), then tile_of within the split.
+  struct Tile {
+    int64_t m0, n0;
+    int z, nk;
+    rsrc_t ra, rg, ru;
+  };
+  auto tile_at = [&](int t) {
+    Tile c;
+    c.nk = 0;
+    c.m0 = c.n0 = 0;
+    c.z = 0;
+    if (t < total) {
+      c.z = t / per_split;
+      int im, in_;
+      tile_of(t - c.z * per_split, tiles_m, tiles_n, im, in_);
+      c.m0 = (int64_t)im * BM;
+      c.n0 = (int64_t)in_ * (EPI == EPI_GEGLU ? BN / 2 : BN);  // GEGLU: BN B rows make BN/2 outputs
+      const int64_t kb = (int64_t)c.z * kper;
+      int64_t ke = kb + kper;
+      if (ke > a.K) ke = a.K;
+      c.nk = ke > kb ? (int)((ke - kb) / BK) : 0;
+    }
+    const int64_t kb = (int64_t)c.z * kper;
+    c.ra = make_rsrc((const bf16*)a.A + c.m0 * a.lda + kb, (a.M - c.m0) * a.lda * 2 - kb * 2);
+    c.rg = make_rsrc((const bf16*)a.B + c.n0 * a.ldb + kb, (a.N - c.n0) * a.ldb * 2 - kb * 2);
+    c.ru = EPI == EPI_GEGLU ? make_rsrc((const bf16*)a.B2 + c.n0 * a.ldb + kb, (a.N - c.n0) * a.ldb * 2 - kb * 2) : c.rg;
+    return c;
+  };
 
   // Loader geometry. Load instruction q covers the RPI LDS rows of group g = wave + NW q (A rows for
   // q < AJ, B rows after): lane i fills LDS row RPI g + i / CPR, chunk i % CPR, from global chunk
   // (i % CPR) ^ swz(row). GEGLU: B tile row block b = RPI g / 32 (32 rows) holds gate rows (b even) or
   // up rows (b odd) 32 (b / 2) + (RPI g) % 32 + ...; every row of one instruction sits in one block.
   const int lr = lane / CPR, lcp = lane % CPR;
-  const rsrc_t ra = make_rsrc((const bf16*)a.A + m0 * a.lda + kb, (a.M - m0) * a.lda * 2 - kb * 2);
-  const rsrc_t rg = make_rsrc((const bf16*)a.B + n0 * a.ldb + kb, (a.N - n0) * a.ldb * 2 - kb * 2);
-  const rsrc_t ru = EPI == EPI_GEGLU ? make_rsrc((const bf16*)a.B2 + n0 * a.ldb + kb, (a.N - n0) * a.ldb * 2 - kb * 2) : rg;
   uint32_t voff[LG];
   bool use_up[LG];
 #pragma unroll
@@ -162,22 +186,27 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a, int tiles_
     voff[q] = (uint32_t)(((int64_t)src * (isa ? a.lda : a.ldb) + 8 * chunk) * 2);
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)lds;
-  // Load instruction q of step kt. A step past the range gets an offset beyond the buffer (zeros, no
-  // traffic), so every step keeps the same number of loads in flight.
-  auto dma = [&](int kt, int q) {
-    const uint32_t koff = kt < nk ? (uint32_t)kt * BK * 2 : 0x80000000u;
-    const uint32_t lbase = lds0 + (uint32_t)(kt % NS) * STAGE * 2;
-    if (q < AJ) lds_dma16(ra, voff[q], koff, lbase + (wave + NW * q) * 1024);
-    else lds_dma16(use_up[q] ? ru : rg, voff[q], koff, lbase + ASZ * 2 + (wave + NW * (q - AJ)) * 1024);
-  };
 
-  f32x16_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  // The ring of NS stages runs across this block's tiles: global step G + s is step s of the current
+  // tile (s < cur.nk) or step s - cur.nk of the next one, and lives in stage (G + s) % NS. A step that
+  // belongs to no tile gets an offset beyond the buffer (zeros, no traffic), so every step keeps the
+  // same number of loads in flight. The host runs one tile per block when a tile has fewer than NS
+  // steps, so a step never belongs to the tile after next.
+  Tile cur = tile_at(blockIdx.x), nxt = tile_at(blockIdx.x + gridDim.x);
+  int G = 0;
+  auto dma = [&](int s, int q) {
+    const bool in_cur = s < cur.nk, in_nxt = !in_cur && s - cur.nk < nxt.nk;
+    const int ss = in_cur ? s : s - cur.nk;
+    const uint32_t koff = (in_cur || in_nxt) ? (uint32_t)ss * BK * 2 : 0x80000000u;
+    const uint32_t lbase = lds0 + (uint32_t)((G + s) % NS) * STAGE * 2;
+    // value selects (a reference to one of the two tiles would put them in scratch memory)
+    if (q < AJ) {
+      lds_dma16(in_nxt ? nxt.ra : cur.ra, voff[q], koff, lbase + (wave + NW * q) * 1024);
+    } else {
+      const rsrc_t rc = use_up[q] ? (in_nxt ? nxt.ru : cur.ru) : (in_nxt ? nxt.rg : cur.rg);
+      lds_dma16(rc, voff[q], koff, lbase + ASZ * 2 + (wave + NW * (q - AJ)) * 1024);
+    }
+  };
 
   // fragment addresses (elements within a stage): row r, k chunk 2ks + h at chunk (2ks + h) ^ swz(r)
   const int frow = lane & 31, fh = lane >> 5;
@@ -197,6 +226,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a, int tiles_
 
   // Two fragment sets. Read q of a k-slice comes in the order the MFMAs consume them: A0, B0..B(FN-1),
   // A1..A(FM-1); MFMA q multiplies A fragment q / FN with B fragment q % FN.
+  f32x16_t acc[FM][FN];
   bf16x8_t fa[2][FM], fb[2][FN];
   auto rd = [&](int set, int ks, const bf16* st, int q) {
     if (q == 0) fa[set][0] = *(const bf16x8_t*)(st + aoff[ks][0]);
@@ -208,18 +238,72 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a, int tiles_
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][j], fa[set][i], acc[i][j], 0, 0, 0);
   };
 
-  if (nk > 0) {
+  // Epilogue: lane l holds, for 32x32 block (i, j) and register group g, C[m][n .. n+3] with
+  // m = 32 i + l % 32 and n = 32 j + 8 g + 4 (l / 32) (wave-relative).
+  auto store_tile = [&](int64_t m0, int64_t n0, int z) {
+    const int em = lane & 31, en = (lane >> 5) * 4;
 #pragma unroll
-    for (int kt = 0; kt < NS; ++kt)
+    for (int i = 0; i < FM; ++i) {
+      const int64_t m = m0 + wm * WM + i * 32 + em;
+      if (m >= a.M) continue;
+      if (EPI == EPI_GEGLU) {
 #pragma unroll
-      for (int q = 0; q < LG; ++q) dma(kt, q);
-    G4_WAIT_VMCNT((NS - 1) * LG);  // step 0 landed
-    __syncthreads();
+        for (int p = 0; p < FN / 2; ++p) {
 #pragma unroll
-    for (int q = 0; q < NRD; ++q) rd(0, 0, lds, q);
-    for (int kt = 0; kt < nk; ++kt) {
-      const bf16* st = lds + (kt % NS) * STAGE;
-      const bf16* st1 = lds + ((kt + 1) % NS) * STAGE;
+          for (int g = 0; g < 4; ++g) {
+            const int64_t n = n0 + (wn * (FN / 2) + p) * 32 + 8 * g + en;
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = gelu_tanh(acc[i][2 * p][4 * g + e]) * acc[i][2 * p + 1][4 * g + e];
+            *(uint2*)((bf16*)a.C + m * a.ldc + n) = pack_bf16x4(v);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int64_t n = n0 + wn * WN + j * 32 + 8 * g + en;
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
+            if (EPI == EPI_GELU_MUL) {
+              const float4 x = *(const float4*)(a.aux + m * a.aux_ld + n);
+              v[0] = gelu_tanh(v[0]) * x.x; v[1] = gelu_tanh(v[1]) * x.y;
+              v[2] = gelu_tanh(v[2]) * x.z; v[3] = gelu_tanh(v[3]) * x.w;
+              *(uint2*)((bf16*)a.C + m * a.ldc + n) = pack_bf16x4(v);
+            } else if (CF32) {
+              *(float4*)((float*)a.C + (int64_t)z * a.split_stride + m * a.ldc + n) = make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+              *(uint2*)((bf16*)a.C + m * a.ldc + n) = pack_bf16x4(v);
+            }
+          }
+        }
+      }
+    }
+  };
+
+  if (blockIdx.x >= total) return;
+  // first tile: fill the ring, then the first fragments
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int q = 0; q < LG; ++q) dma(s, q);
+  G4_WAIT_VMCNT((NS - 1) * LG);  // step 0 landed
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < NRD; ++q) rd(0, 0, lds, q);
+
+  for (int t = blockIdx.x; t < total; t += gridDim.x) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    for (int kt = 0; kt < cur.nk; ++kt) {
+      const bf16* st = lds + ((G + kt) % NS) * STAGE;
+      const bf16* st1 = lds + ((G + kt + 1) % NS) * STAGE;
       // k-slices 0 .. KS-2: MFMAs on one set while the next slice's fragments load into the other
 #pragma unroll
       for (int ks = 0; ks < KS - 1; ++ks) {
@@ -233,8 +317,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a, int tiles_
       // step kt + 1 landed in every wave, and every wave has read all of step kt's stage
       G4_WAIT_VMCNT((NS - 2) * LG);
       __syncthreads();
-      // last k-slice; behind its MFMAs the next step's first fragments, then the loads that refill the
-      // stage just released with step kt + NS
+      // last k-slice; behind its MFMAs the next step's first fragments (the next tile's, after the last
+      // step), then the loads that refill the stage just released with step kt + NS
 #pragma unroll
       for (int q = 0; q < NMF; ++q) {
         mf(1, q);
@@ -243,52 +327,13 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a, int tiles_
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    G4_WAIT_VMCNT(0);  // the zero-filling loads past the range land before the block's LDS is released
+    // epilogue, while the next tile's first steps are in flight
+    store_tile(cur.m0, cur.n0, cur.z);
+    G += cur.nk;
+    cur = nxt;
+    nxt = tile_at(t + 2 * gridDim.x);
   }
-
-  // epilogue: lane l holds, for 32x32 block (i, j) and register group g, C[m][n .. n+3] with
-  // m = 32 i + l % 32 and n = 32 j + 8 g + 4 (l / 32) (wave-relative)
-  const int em = lane & 31, en = (lane >> 5) * 4;
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int64_t m = m0 + wm * WM + i * 32 + em;
-    if (m >= a.M) continue;
-    if (EPI == EPI_GEGLU) {
-#pragma unroll
-      for (int p = 0; p < FN / 2; ++p) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int64_t n = n0 + (wn * (FN / 2) + p) * 32 + 8 * g + en;
-          float v[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = gelu_tanh(acc[i][2 * p][4 * g + e]) * acc[i][2 * p + 1][4 * g + e];
-          *(uint2*)((bf16*)a.C + m * a.ldc + n) = pack_bf16x4(v);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int64_t n = n0 + wn * WN + j * 32 + 8 * g + en;
-          float v[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
-          if (EPI == EPI_GELU_MUL) {
-            const float4 x = *(const float4*)(a.aux + m * a.aux_ld + n);
-            v[0] = gelu_tanh(v[0]) * x.x; v[1] = gelu_tanh(v[1]) * x.y;
-            v[2] = gelu_tanh(v[2]) * x.z; v[3] = gelu_tanh(v[3]) * x.w;
-            *(uint2*)((bf16*)a.C + m * a.ldc + n) = pack_bf16x4(v);
-          } else if (CF32) {
-            *(float4*)((float*)a.C + (int64_t)blockIdx.z * a.split_stride + m * a.ldc + n) =
-                make_float4(v[0], v[1], v[2], v[3]);
-          } else {
-            *(uint2*)((bf16*)a.C + m * a.ldc + n) = pack_bf16x4(v);
-          }
-        }
-      }
-    }
-  }
+  G4_WAIT_VMCNT(0);  // loads issued past the last tile land before the block's LDS is released
 }
 
 // Shapes the MFMA kernel takes: bf16, K a multiple of 64, output columns a multiple of the tile,
@@ -307,15 +352,41 @@ static bool mfma_ok(const GemmArgs& a, int BN) {
   return true;
 }
 
+// Blocks of kernel `k` that fit on the device at once (resident blocks per CU times CUs).
+static int resident_blocks(const void* k, int threads) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, threads, 0) != hipSuccess) return 0;
+  return cus * per_cu;
+}
+
+template <int BM, int BN, int NW, int BK, int NS, int EPI, bool CF32>
+static void launch_one(const GemmArgs& a, int tm, int tn, int total, bool persist, hipStream_t s) {
+  const void* k = (const void*)k_gemm_mfma<BM, BN, NW, BK, NS, EPI, CF32>;
+  int grid = total;
+  if (persist) {
+    const int res = resident_blocks(k, NW * 64);
+    if (res > 0 && res < total) grid = res;
+  }
+  hipLaunchKernelGGL((k_gemm_mfma<BM, BN, NW, BK, NS, EPI, CF32>), dim3((unsigned)grid), dim3(NW * 64), 0, s, a, tm, tn);
+}
+
+// One launch walks every (split, tile) pair. When every split spans at least NS K-steps, the grid is
+// what fits on the device at once and each block walks several tiles, prefetching the next tile's
+// first steps under the current tile's last ones; otherwise each block takes one tile.
 template <int BM, int BN, int NW, int BK, int NS>
 static g4_status launch_mfma(const GemmArgs& a, hipStream_t s) {
   const int ncols = a.epi == EPI_GEGLU ? BN / 2 : BN;
   const int tm = (int)((a.M + BM - 1) / BM), tn = (int)(a.N / ncols);
-  dim3 g((unsigned)(tm * tn), 1, (unsigned)a.splits), b(NW * 64);
-  if (a.epi == EPI_GEGLU) hipLaunchKernelGGL((k_gemm_mfma<BM, BN, NW, BK, NS, EPI_GEGLU, false>), g, b, 0, s, a, tm, tn);
-  else if (a.epi == EPI_GELU_MUL) hipLaunchKernelGGL((k_gemm_mfma<BM, BN, NW, BK, NS, EPI_GELU_MUL, false>), g, b, 0, s, a, tm, tn);
-  else if (a.c_dtype == G4_F32) hipLaunchKernelGGL((k_gemm_mfma<BM, BN, NW, BK, NS, EPI_STORE, true>), g, b, 0, s, a, tm, tn);
-  else hipLaunchKernelGGL((k_gemm_mfma<BM, BN, NW, BK, NS, EPI_STORE, false>), g, b, 0, s, a, tm, tn);
+  const int total = tm * tn * a.splits;
+  const int64_t kper = ((a.K + a.splits - 1) / a.splits + BK - 1) / BK * BK;
+  const int64_t last = a.K - (int64_t)(a.splits - 1) * kper;
+  const bool persist = (last < kper ? last : kper) >= (int64_t)NS * BK;
+  if (a.epi == EPI_GEGLU) launch_one<BM, BN, NW, BK, NS, EPI_GEGLU, false>(a, tm, tn, total, persist, s);
+  else if (a.epi == EPI_GELU_MUL) launch_one<BM, BN, NW, BK, NS, EPI_GELU_MUL, false>(a, tm, tn, total, persist, s);
+  else if (a.c_dtype == G4_F32) launch_one<BM, BN, NW, BK, NS, EPI_STORE, true>(a, tm, tn, total, persist, s);
+  else launch_one<BM, BN, NW, BK, NS, EPI_STORE, false>(a, tm, tn, total, persist, s);
   return check_launch("gemm_mfma");
 }
 
