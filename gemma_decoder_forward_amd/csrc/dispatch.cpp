@@ -33,7 +33,13 @@ g4_status gemm(const GemmArgs& a, int32_t dtype, hipStream_t s) {
     if (a.nseg == 1) b.B = a.segB[0];
     return gemm_one(b, dtype, s);
   }
-  // several B matrices: one launch per segment, each writing its own column range of C
+  // several B matrices: one MFMA launch over all of them when each is a whole number of tiles ...
+  if (dtype == G4_BF16) {
+    GemmArgs b = a;
+    b.B = a.segB[0];
+    if (gemm_mfma(b, s, &st)) return st;
+  }
+  // ... else one launch per segment, each writing its own column range of C
   int64_t col = 0;
   for (int i = 0; i < nseg; ++i) {
     GemmArgs b = a;

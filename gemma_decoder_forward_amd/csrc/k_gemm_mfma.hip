@@ -158,7 +158,17 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a, int tiles_
     }
     const int64_t kb = (int64_t)c.z * kper;
     c.ra = make_rsrc((const bf16*)a.A + c.m0 * a.lda + kb, (a.M - c.m0) * a.lda * 2 - kb * 2);
-    c.rg = make_rsrc((const bf16*)a.B + c.n0 * a.ldb + kb, (a.N - c.n0) * a.ldb * 2 - kb * 2);
+    // B rows: one matrix, or (EPI_STORE) up to three stacked matrices; a tile never straddles two
+    const bf16* bbase = (const bf16*)a.B;
+    int64_t nloc = c.n0, nrows = a.N;
+    if (EPI == EPI_STORE && a.nseg > 1) {
+      const int64_t r0 = a.seg_rows[0], r1 = a.seg_rows[1];
+      const int sg = c.n0 < r0 ? 0 : (c.n0 < r0 + r1 ? 1 : 2);
+      bbase = (const bf16*)(sg == 0 ? a.segB[0] : (sg == 1 ? a.segB[1] : a.segB[2]));
+      nloc = c.n0 - (sg == 0 ? 0 : (sg == 1 ? r0 : r0 + r1));
+      nrows = sg == 0 ? r0 : (sg == 1 ? r1 : a.seg_rows[2]);
+    }
+    c.rg = make_rsrc(bbase + nloc * a.ldb + kb, (nrows - nloc) * a.ldb * 2 - kb * 2);
     c.ru = EPI == EPI_GEGLU ? make_rsrc((const bf16*)a.B2 + c.n0 * a.ldb + kb, (a.N - c.n0) * a.ldb * 2 - kb * 2) : c.rg;
     return c;
   };
@@ -349,6 +359,15 @@ static bool mfma_ok(const GemmArgs& a, int BN) {
   if ((a.ldc & 3) || ((uintptr_t)a.C & (f32 ? 15 : 7))) return false;
   if (f32 && a.splits > 1 && (a.split_stride & 3)) return false;
   if (a.epi == EPI_GELU_MUL && ((a.aux_ld & 3) || ((uintptr_t)a.aux & 15))) return false;
+  if (a.nseg > 1) {  // stacked B matrices: each a whole number of tiles, aligned, 32-bit offsets
+    if (a.epi != EPI_STORE || a.nseg > 3) return false;
+    int64_t rows = 0;
+    for (int i = 0; i < a.nseg; ++i) {
+      if (a.seg_rows[i] % ncols || ((uintptr_t)a.segB[i] & 15) || a.seg_rows[i] * a.ldb * 2 > 0x7fffffffLL) return false;
+      rows += a.seg_rows[i];
+    }
+    if (rows != a.N) return false;
+  }
   return true;
 }
 
