@@ -201,6 +201,27 @@ static int32_t pick_splits(int64_t M, int64_t N, int64_t K) {
   return best;
 }
 
+// gelu_tanh(A W^T) * aux into C (dtype). The PLE gate has few output columns (the PLE width), so at
+// prefill sizes it has too few output tiles to fill the device: K is then split over float32 slices in
+// `part` ([splits][M][N]) and a finisher sums them in a fixed order and applies the epilogue.
+static g4_status run_gelu_mul(const void* A, int64_t lda, const void* W, int64_t ldb, void* C, int64_t ldc,
+                              const float* aux, int64_t aux_ld, int64_t M, int64_t N, int64_t K, int32_t dt,
+                              float* part, size_t part_bytes, hipStream_t s) {
+  int32_t splits = 1;
+  if (dt == G4_BF16 && M > 64 && part) {
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    while (splits < 8 && tiles * splits * 2 <= 256 && K / (splits * 2) >= 256 &&
+           (size_t)(splits * 2) * M * N * 4 <= part_bytes)
+      splits *= 2;
+  }
+  if (splits == 1) return run_gemm(A, lda, W, nullptr, ldb, C, ldc, dt, M, N, K, EPI_GELU_MUL, aux, aux_ld, 1, 0, dt, s);
+  g4_status st = run_gemm(A, lda, W, nullptr, ldb, part, N, G4_F32, M, N, K, EPI_STORE, nullptr, 0, splits, M * N, dt, s);
+  if (st != G4_OK) return st;
+  GemmArgs ga{};
+  ga.M = M; ga.N = N; ga.C = C; ga.ldc = ldc; ga.c_dtype = dt; ga.epi = EPI_GELU_MUL; ga.aux = aux; ga.aux_ld = aux_ld;
+  return gemm_skinny_finish(ga, part, splits, N, s);
+}
+
 struct LayerCtx {
   const g4_model_desc* m;
   const g4_layer_desc* l;
@@ -514,8 +535,8 @@ static g4_status layer_impl(const LayerCtx& c) {
   const int64_t Ld = m->n_layers * d;
   {
   TimedScope ts(G4_KC_PLE_GEMM, c.s);
-  G4_TRY(run_gemm(hb, H, l->ple_gate, nullptr, H, gm, d, dt, M, d, H, EPI_GELU_MUL, c.ple_in + (int64_t)c.layer * d,
-                  Ld, 1, 0, dt, c.s));
+  G4_TRY(run_gelu_mul(hb, H, l->ple_gate, H, gm, d, c.ple_in + (int64_t)c.layer * d, Ld, M, d, H, dt, fb,
+                      (size_t)c.p->splits * M * H * 4, c.s));
   // 11-12. PLE projection, h = (h + rms(p) * w_post_ple) * layer_scalar (+ next layer's xn)
   G4_TRY(run_gemm(gm, d, l->ple_proj, nullptr, d, fb, H, G4_F32, M, H, d, EPI_STORE, nullptr, 0, 1, M * H, dt, c.s));
   }
@@ -749,8 +770,7 @@ g4_status g4_ple_inject(float* h, const void* w_gate, const float* ple, int64_t 
   float* pb = (float*)(gmb + al((size_t)M * d * dsize(dtype)));
   g4_status st;
   if ((st = cast_rows(h, hb, M * H, dtype, s)) != G4_OK) return st;
-  if ((st = run_gemm(hb, H, w_gate, nullptr, H, gmb, d, dtype, M, d, H, EPI_GELU_MUL, ple, ple_ld, 1, 0, dtype, s)) !=
-      G4_OK)
+  if ((st = run_gelu_mul(hb, H, w_gate, H, gmb, d, ple, ple_ld, M, d, H, dtype, pb, (size_t)M * H * 4, s)) != G4_OK)
     return st;
   if ((st = run_gemm(gmb, d, w_proj, nullptr, d, pb, H, G4_F32, M, H, d, EPI_STORE, nullptr, 0, 1, 0, dtype, s)) != G4_OK)
     return st;
