@@ -55,6 +55,18 @@ g4_status gemm(const GemmArgs& a, int32_t dtype, hipStream_t s) {
 
 size_t gemm_ws(int64_t, int64_t, int64_t, int32_t) { return 0; }
 
+int device_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      return 256;  // no device visible (host-only sizing): the MI355X count
+    cus = n;
+  }
+  return cus;
+}
+
 g4_status attn_prefill(const AttnArgs& a, int32_t dtype, hipStream_t s) {
   if (a.B * a.T == 0) return G4_OK;
   g4_status st = G4_OK;

@@ -112,7 +112,8 @@ static g4_status check_kv(const g4_kv_entry* kv, int32_t n_kv, int32_t layer, in
 
 // ---- workspace plan of the layer forward -----------------------------------------------------
 struct Plan {
-  size_t xn, qkv, ao, f32buf, act, hb, gm, dec, gws, gws_bytes, fx, fx_bytes, fy, fy_bytes, emb_e, emb_p, total;
+  size_t xn, qkv, ao, f32buf, act, hb, gm, dec, aws, aws_bytes, gws, gws_bytes, fx, fx_bytes, fy, fy_bytes, emb_e, emb_p,
+      total;
   int64_t qkv_ld, splits;
 };
 
@@ -135,6 +136,14 @@ static Plan plan(const g4_model_desc* m, int64_t B, int64_t T, int64_t cap, int3
   p.gm = o; o += al(M * m->ple_dim * E);
   p.dec = o;
   if (mode == G4_DECODE) o += al(attn_decode_ws(B, m->n_heads, hdm, cap > 0 ? cap : 1));
+  p.aws = o;  // key-split partials of a short prefill's attention
+  p.aws_bytes = 0;
+  if (mode == G4_PREFILL) {
+    const size_t s0 = attn_prefill_ws(B, T, m->n_heads, m->n_kv_heads, m->head_dim_swa);
+    const size_t s1 = attn_prefill_ws(B, T, m->n_heads, m->n_kv_heads, m->head_dim_full);
+    p.aws_bytes = s0 > s1 ? s0 : s1;
+    o += al(p.aws_bytes);
+  }
   p.gws = o;
   p.gws_bytes = 0;
   if (M <= 64 && m->dtype == G4_BF16) {  // partial sums of the few-row GEMM
@@ -499,6 +508,7 @@ static g4_status layer_impl(const LayerCtx& c) {
   aa.q = qkv; aa.q_ld = qld; aa.k = src.k; aa.v = src.v; aa.cap = src.cap; aa.pos0 = c.pos;
   aa.B = c.B; aa.T = c.T; aa.nh = nh; aa.nkv = nkv; aa.hd = hd; aa.sliding = sliding; aa.window = m->window;
   aa.scale = 1.f; aa.out = ao; aa.out_ld = nh * hd; aa.ring = src.ring;
+  aa.ws = (float*)(c.ws + c.p->aws); aa.ws_bytes = c.p->aws_bytes;
   {
     TimedScope ts(G4_KC_ATTENTION, c.s);
     if (c.mode == G4_DECODE) G4_TRY(attn_decode(aa, c.ws + c.p->dec, c.p->total - c.p->dec, dt, c.s));

@@ -146,6 +146,9 @@ struct AttnArgs {
   float scale;
   void* out; int64_t out_ld;
   int32_t ring;  // the cache is a ring of cap rows: key j lives in row j mod cap
+  // Prefill only, optional: float32 scratch of attn_prefill_ws() bytes for key-split partial results
+  // (used when a short prefill gives too few query blocks to fill the device); null = no key split.
+  float* ws; size_t ws_bytes;
 };
 
 // Cache row of key position j, and the last key a query at position i can see in the cache.
@@ -158,6 +161,10 @@ __device__ __forceinline__ int64_t kv_last(int64_t i, int64_t cap, int32_t ring)
 g4_status attn_prefill(const AttnArgs& a, int32_t dtype, hipStream_t s);
 g4_status attn_decode(const AttnArgs& a, void* ws, size_t ws_bytes, int32_t dtype, hipStream_t s);
 size_t attn_decode_ws(int64_t B, int64_t nh, int64_t hd, int64_t cap);
+// Compute units of the current device (256 when no device is visible).
+int device_cus();
+// Scratch bytes the prefill attention may use to split key ranges (0 when it would not split).
+size_t attn_prefill_ws(int64_t B, int64_t T, int64_t nh, int64_t nkv, int64_t hd);
 bool attn_decode_mfma(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t s, g4_status* st);
 size_t attn_decode_mfma_ws(int64_t B, int64_t nh, int64_t hd, int64_t cap);
 

@@ -63,7 +63,7 @@ __device__ __forceinline__ void at_dma16(const at_rsrc& r, uint32_t voff, uint32
 }
 
 template <int HD, int HS>
-__global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float sl2) {
+__global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float sl2, int split_from) {
   using L = AttnLds<HD>;
   constexpr int HW = HD / HS;      // head elements owned by one wave
   constexpr int NB = HW / 32;      // O blocks per wave
@@ -79,7 +79,12 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
   const int nruns = (int)((a.T + 31) / 32);
   const int ngroups = nruns * G;
   const int nblk = (ngroups + QG - 1) / QG;
-  const int blk = nblk - 1 - (int)blockIdx.x;  // heaviest (latest) groups first
+  // Work items, heaviest first: blocks split_from .. nblk-1 (the latest queries, whose key ranges are
+  // longest) come as two items each, one per half of the block's key tiles; the others whole.
+  const int nsplit = nblk - split_from;
+  const int v = (int)blockIdx.x;
+  const int blk = v < 2 * nsplit ? nblk - 1 - v / 2 : nblk - 1 - nsplit - (v - 2 * nsplit);
+  const int part = v < 2 * nsplit ? (v & 1) : 0, nparts = v < 2 * nsplit ? 2 : 1;
   const int gi = blk * QG + wave / HS;
   const int64_t g = blockIdx.y, b = blockIdx.z;
   const int run = gi / G;
@@ -99,6 +104,9 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
   int64_t hib = kv_last(imax, a.cap, a.ring);
   const int64_t kstart = lob & ~(int64_t)(AT_KB - 1);
   const int ntiles = hib >= lob ? (int)((hib - kstart) / AT_KB + 1) : 0;
+  const int half_tiles = (ntiles + 1) / 2;
+  const int it0 = nparts == 2 && part == 1 ? half_tiles : 0;
+  const int it1 = nparts == 2 && part == 0 ? half_tiles : ntiles;
   int64_t qlo = a.sliding ? qi - a.window + 1 : 0;
   if (qlo < 0) qlo = 0;
   const int64_t qhi = qi < hib ? qi : hib;  // this query's last visible key
@@ -168,18 +176,18 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
     for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  if (ntiles > 0) {
-    dma(0, 0);
+  if (it1 > it0) {
+    dma(it0, it0 & 1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (edge_tile(0)) {
-      vclean(0, 0);
+    if (edge_tile(it0)) {
+      vclean(it0, it0 & 1);
       __syncthreads();
     }
   }
-  for (int it = 0; it < ntiles; ++it) {
+  for (int it = it0; it < it1; ++it) {
     const int cur = it & 1;
-    if (it + 1 < ntiles) dma(it + 1, cur ^ 1);
+    if (it + 1 < it1) dma(it + 1, cur ^ 1);
     const bf16* ks = lds + cur * L::STAGE;
     const bf16* vs = ks + L::KSZ;
     const int64_t k0 = kstart + (int64_t)it * AT_KB;
@@ -269,7 +277,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
       }
       __builtin_amdgcn_s_waitcnt(0);  // the next tile's direct-to-LDS loads
       __syncthreads();
-      if (it + 1 < ntiles && edge_tile(it + 1)) {
+      if (it + 1 < it1 && edge_tile(it + 1)) {
         vclean(it + 1, cur ^ 1);
         __syncthreads();
       }
@@ -278,6 +286,22 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (!qvalid) return;
+  if (nparts == 2) {  // unnormalised partial O with its reference and normaliser, merged afterwards
+    const int64_t row = ((part * a.B + b) * a.T + tq) * a.nh + head;
+    float* po = a.ws + row * HD + half * HW;
+#pragma unroll
+    for (int d = 0; d < NB; ++d)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *(float4*)(po + 32 * d + 8 * r4 + 4 * h) =
+            make_float4(o[d][4 * r4], o[d][4 * r4 + 1], o[d][4 * r4 + 2], o[d][4 * r4 + 3]);
+    if (h == 0 && half == 0) {
+      float* ml = a.ws + 2 * a.B * a.T * a.nh * HD + 2 * row;
+      ml[0] = m_run;
+      ml[1] = l_tot;
+    }
+    return;
+  }
   const float il = l_tot > 0.f ? 1.f / l_tot : 0.f;
   bf16* orow = (bf16*)a.out + (b * a.T + tq) * a.out_ld + head * HD + half * HW;
 #pragma unroll
@@ -292,21 +316,83 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
     }
 }
 
+// Merges the two key-half partials of each split query row: O = (O0 2^(m0-m) + O1 2^(m1-m)) /
+// (l0 2^(m0-m) + l1 2^(m1-m)) with m = max(m0, m1) (exp2 domain); a row that saw no key stays zero.
+// One wave per (sequence, query token >= tq_lo, head).
+template <int HD>
+__global__ __launch_bounds__(64) void k_attn_merge_split(AttnArgs a, int64_t tq_lo) {
+  constexpr int EPL = HD / 64;
+  const int64_t tq = tq_lo + blockIdx.x, head = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int64_t row0 = ((0 * a.B + b) * a.T + tq) * a.nh + head, row1 = ((1 * a.B + b) * a.T + tq) * a.nh + head;
+  const float* ml = a.ws + 2 * a.B * a.T * a.nh * HD;
+  const float m0 = ml[2 * row0], l0 = ml[2 * row0 + 1], m1 = ml[2 * row1], l1 = ml[2 * row1 + 1];
+  const float m = fmaxf(m0, m1);
+  const float a0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - m);
+  const float a1 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+  const float den = l0 * a0 + l1 * a1;
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  const float* p0 = a.ws + row0 * HD + lane * EPL;
+  const float* p1 = a.ws + row1 * HD + lane * EPL;
+  bf16* out = (bf16*)a.out + (b * a.T + tq) * a.out_ld + head * HD + lane * EPL;
+#pragma unroll
+  for (int e = 0; e < EPL; e += 2) {
+    const float x = (p0[e] * a0 + p1[e] * a1) * inv, y = (p0[e + 1] * a0 + p1[e + 1] * a1) * inv;
+    *(uint32_t*)(out + e) = (uint32_t)f2bf(x) | ((uint32_t)f2bf(y) << 16);
+  }
+}
+
+// Query blocks of one launch and the first block to split: a launch with fewer blocks than CUs splits
+// its heaviest half (causal: the latest queries) or, with a sliding window (every block's key range
+// about the same), all of its blocks. split_from is a multiple of the blocks per 32-token
+// run so that the split rows start at a run boundary. Returns false if the shape is not the MFMA path's.
+static bool attn_plan(int64_t B, int64_t T, int64_t nh, int64_t nkv, int64_t hd, int32_t sliding, int* nblk,
+                      int* split_from, int64_t* tq_lo) {
+  if (nkv <= 0 || nh % nkv) return false;
+  const int64_t G = nh / nkv;
+  if (!(G == 1 || G == 2 || G == 4) || !(hd == 128 || hd == 256 || hd == 512)) return false;
+  const int QG = hd == 512 ? 2 : 4;
+  const int64_t ngroups = ((T + 31) / 32) * G;
+  *nblk = (int)((ngroups + QG - 1) / QG);
+  *split_from = *nblk;
+  if ((int64_t)*nblk * nkv * B < device_cus()) {
+    const int step = G > QG ? (int)(G / QG) : 1;
+    *split_from = sliding ? 0 : (*nblk / 2) / step * step;
+  }
+  *tq_lo = ((int64_t)*split_from * QG / G) * 32;
+  return true;
+}
+
+size_t attn_prefill_ws(int64_t B, int64_t T, int64_t nh, int64_t nkv, int64_t hd) {
+  int nblk = 0, sf = 0;
+  int64_t tq_lo = 0;
+  size_t need = 0;
+  for (int sl = 0; sl < 2; ++sl)
+    if (attn_plan(B, T, nh, nkv, hd, sl, &nblk, &sf, &tq_lo) && sf < nblk) need = (size_t)2 * B * T * nh * (hd + 2) * 4;
+  return need;
+}
+
 // bf16, head_dim 128/256/512, groups of 1, 2 or 4 query heads per kv head, 16-byte aligned rows.
 bool attn_mfma(const AttnArgs& a, hipStream_t s, g4_status* st) {
-  const int64_t G = a.nh / a.nkv;
-  if (!(G == 1 || G == 2 || G == 4)) return false;
-  if (!(a.hd == 128 || a.hd == 256 || a.hd == 512)) return false;
   if ((a.q_ld | a.out_ld) & 7) return false;
   if (((uintptr_t)a.q | (uintptr_t)a.k | (uintptr_t)a.v | (uintptr_t)a.out) & 15) return false;
-  const int HS = a.hd == 512 ? 2 : 1, QG = 4 / HS;
-  const int64_t ngroups = ((a.T + 31) / 32) * G;
-  dim3 grid((unsigned)((ngroups + QG - 1) / QG), (unsigned)a.nkv, (unsigned)a.B);
+  int nblk = 0, split_from = 0;
+  int64_t tq_lo = 0;
+  if (!attn_plan(a.B, a.T, a.nh, a.nkv, a.hd, a.sliding, &nblk, &split_from, &tq_lo)) return false;
+  const size_t need = (size_t)2 * a.B * a.T * a.nh * (a.hd + 2) * 4;
+  if (!a.ws || a.ws_bytes < need || ((uintptr_t)a.ws & 15)) split_from = nblk;  // no scratch: no split
+  const int64_t G = a.nh / a.nkv;
+  dim3 grid((unsigned)(2 * (nblk - split_from) + split_from), (unsigned)a.nkv, (unsigned)a.B);
   const float sl2 = a.scale * 1.4426950408889634f;
-  if (a.hd == 128) hipLaunchKernelGGL((k_attn_mfma<128, 1>), grid, dim3(256), 0, s, a, (int)G, sl2);
-  else if (a.hd == 256) hipLaunchKernelGGL((k_attn_mfma<256, 1>), grid, dim3(256), 0, s, a, (int)G, sl2);
-  else hipLaunchKernelGGL((k_attn_mfma<512, 2>), grid, dim3(256), 0, s, a, (int)G, sl2);
-  *st = check_launch("attn_mfma");
+  if (a.hd == 128) hipLaunchKernelGGL((k_attn_mfma<128, 1>), grid, dim3(256), 0, s, a, (int)G, sl2, split_from);
+  else if (a.hd == 256) hipLaunchKernelGGL((k_attn_mfma<256, 1>), grid, dim3(256), 0, s, a, (int)G, sl2, split_from);
+  else hipLaunchKernelGGL((k_attn_mfma<512, 2>), grid, dim3(256), 0, s, a, (int)G, sl2, split_from);
+  if ((*st = check_launch("attn_mfma")) != G4_OK || split_from == nblk || tq_lo >= a.T) return true;
+  dim3 gm((unsigned)(a.T - tq_lo), (unsigned)a.nh, (unsigned)a.B);
+  if (a.hd == 128) hipLaunchKernelGGL((k_attn_merge_split<128>), gm, dim3(64), 0, s, a, tq_lo);
+  else if (a.hd == 256) hipLaunchKernelGGL((k_attn_merge_split<256>), gm, dim3(64), 0, s, a, tq_lo);
+  else hipLaunchKernelGGL((k_attn_merge_split<512>), gm, dim3(64), 0, s, a, tq_lo);
+  *st = check_launch("attn_merge_split");
   return true;
 }
 
