@@ -1,13 +1,11 @@
 // Flash-style prefill attention on the CDNA4 matrix cores (bf16 operands, float32 softmax and
 // accumulation), causal with an optional sliding window, GQA groups sharing every K/V tile.
 //
-// Block = 4 waves. A "query group" is one head x 32 consecutive tokens; heads of a kv group share its K/V.
-// With HS = 1 each wave owns one query group (4 groups per block); with HS = 2 (head_dim 512, whose Q and
-// O do not fit one wave's registers) a pair of waves owns one group, each wave holding half of the head
-// dimension of Q and O: the pair adds its two partial score tiles through LDS, both run the identical
-// softmax, and each accumulates P V for its half. Keys advance in tiles of 32 staged in LDS, double
-// buffered: the next tile's rows are loaded straight into LDS (buffer_load ... lds, one instruction per
-// row) while the current tile is multiplied.
+// Block = 4 waves. A "query group" is one head x 32 consecutive tokens; each wave owns one, and the
+// block's four groups (the heads of one kv group for G = 4) share every K/V tile. For head dim 512 a
+// wave holds Q (32 x 512, 128 registers) and O (256 accumulation registers). Keys advance in tiles of
+// 32 staged in LDS, double buffered: the next tile's rows are loaded straight into LDS (buffer_load ...
+// lds, one instruction per row) while the current tile is multiplied.
 //   * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: A = K rows from LDS,
 //     B = the wave's Q held in registers for the whole key loop;
 //   * lane l then holds query (l % 32) and 16 of the tile's keys: 8*(j/4) + 4*(l/32) + j%4 for
@@ -62,19 +60,16 @@ __device__ __forceinline__ void at_dma16(const at_rsrc& r, uint32_t voff, uint32
   asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" : : "v"(voff), "s"(r), "s"(soff), "{m0}"(m0) : "memory");
 }
 
-template <int HD, int HS>
+template <int HD>
 __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float sl2, int split_from) {
   using L = AttnLds<HD>;
-  constexpr int HW = HD / HS;      // head elements owned by one wave
-  constexpr int NB = HW / 32;      // O blocks per wave
-  constexpr int KS = HW / 16;      // MFMA k-steps for S
-  constexpr int QG = 4 / HS;       // query groups per block
+  constexpr int NB = HD / 32;      // O blocks per wave
+  constexpr int KS = HD / 16;      // MFMA k-steps for S
+  constexpr int QG = 4;            // query groups per block
   __shared__ __attribute__((aligned(16))) bf16 lds[2 * L::STAGE];
-  __shared__ float xch[HS == 2 ? 4 * 16 * 64 : 1];  // partial score tiles of the wave pairs
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
-  const int half = wave % HS;
   // query groups are numbered run * G + head_in_group; a block takes QG consecutive ones
   const int nruns = (int)((a.T + 31) / 32);
   const int ngroups = nruns * G;
@@ -85,7 +80,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
   const int v = (int)blockIdx.x;
   const int blk = v < 2 * nsplit ? nblk - 1 - v / 2 : nblk - 1 - nsplit - (v - 2 * nsplit);
   const int part = v < 2 * nsplit ? (v & 1) : 0, nparts = v < 2 * nsplit ? 2 : 1;
-  const int gi = blk * QG + wave / HS;
+  const int gi = blk * QG + wave;
   const int64_t g = blockIdx.y, b = blockIdx.z;
   const int run = gi / G;
   const int64_t head = g * G + gi % G;
@@ -124,7 +119,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
   bf16x8_t qf[KS];
   {
     const bf16* qrow = (const bf16*)a.q + (b * a.T + (qvalid ? tq : 0)) * a.q_ld + (qvalid ? head : 0) * HD +
-                       half * HW + 8 * h;
+                       8 * h;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       uint4 v = qvalid ? *(const uint4*)(qrow + 16 * s) : make_uint4(0, 0, 0, 0);
@@ -195,17 +190,10 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
     f32x16_t s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
-    const bf16* kf = ks + col * L::KLD + half * HW + 8 * h;
+    const bf16* kf = ks + col * L::KLD + 8 * h;
 #pragma unroll
     for (int st = 0; st < KS; ++st)
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t*)(kf + 16 * st), qf[st], s, 0, 0, 0);
-    if (HS == 2) {  // add the partner wave's partial scores (the other half of the head dimension)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) xch[(wave * 16 + r) * 64 + lane] = s[r];
-      __syncthreads();
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] += xch[((wave ^ 1) * 16 + r) * 64 + lane];
-    }
     // mask (only on tiles that cut the causal edge, the window start or the block's key range), scale
     // to the exp2 domain, online softmax
     float mt = -INFINITY;
@@ -227,11 +215,13 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
       }
     }
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    // The reference maximum is raised only when the tile's maximum exceeds it by more than 8 (log2
-    // domain): probabilities then stay below 2^8, which float32 sums and bf16 P hold exactly as well,
-    // and the accumulator rescale -- a multiply of every O register -- is skipped on almost all tiles.
-    // The result is the same softmax (every term and the normaliser use one reference).
-    const bool raise = mt > m_run + 8.f;
+    // The reference maximum is raised only when the tile's maximum exceeds it by more than 32 (log2
+    // domain). Probabilities then stay below 2^32: bf16 P keeps its 8-bit relative precision at any
+    // magnitude, and the float32 sums stay far from overflow (below 2^32 x keys x max|v|). The
+    // accumulator rescale -- a multiply of every O register -- then runs only when the maximum has
+    // grown by 2^32, a few times per query row at most. The result is the same softmax: every term and
+    // the normaliser use one reference.
+    const bool raise = mt > m_run + 32.f;
     const float m_new = raise ? mt : m_run;
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     float psum = 0.f;
@@ -245,10 +235,19 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
     if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // some query of the wave moved its reference
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
       l_run *= alpha;
+      // The rescale touches the accumulators through their accumulation registers (read, multiply,
+      // write back one register at a time). Written as plain float code, the compiler keeps every
+      // accumulator in an ordinary register across the key loop instead, which for head dim 512 needs
+      // more registers than a wave has.
 #pragma unroll
       for (int d = 0; d < NB; ++d)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+        for (int r = 0; r < 16; ++r) {
+          float tmp;
+          asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                       : "+a"(o[d][r]), "=&v"(tmp)
+                       : "v"(alpha));
+        }
     }
     l_run += psum;
     m_run = m_new;
@@ -260,7 +259,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
       // kb + a/4 at head elements 32d + 16(q % 2) + 4(a % 4), so lane i gets keys kb .. kb+3 of head
       // element 32d + 16(q % 2) + i: the A operand row of lane 16(q % 2) + i.
       const int a16 = lane & 15, grp = lane >> 4;
-      const bf16* vb = vs + (4 * (grp >> 1) + (a16 >> 2)) * L::VROW + half * HW + 16 * (grp & 1) + 4 * (a16 & 3);
+      const bf16* vb = vs + (4 * (grp >> 1) + (a16 >> 2)) * L::VROW + 16 * (grp & 1) + 4 * (a16 & 3);
 #pragma unroll
       for (int d = 0; d < NB; ++d) {
 #pragma unroll
@@ -288,14 +287,14 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
   if (!qvalid) return;
   if (nparts == 2) {  // unnormalised partial O with its reference and normaliser, merged afterwards
     const int64_t row = ((part * a.B + b) * a.T + tq) * a.nh + head;
-    float* po = a.ws + row * HD + half * HW;
+    float* po = a.ws + row * HD;
 #pragma unroll
     for (int d = 0; d < NB; ++d)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4)
         *(float4*)(po + 32 * d + 8 * r4 + 4 * h) =
             make_float4(o[d][4 * r4], o[d][4 * r4 + 1], o[d][4 * r4 + 2], o[d][4 * r4 + 3]);
-    if (h == 0 && half == 0) {
+    if (h == 0) {
       float* ml = a.ws + 2 * a.B * a.T * a.nh * HD + 2 * row;
       ml[0] = m_run;
       ml[1] = l_tot;
@@ -303,7 +302,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
     return;
   }
   const float il = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  bf16* orow = (bf16*)a.out + (b * a.T + tq) * a.out_ld + head * HD + half * HW;
+  bf16* orow = (bf16*)a.out + (b * a.T + tq) * a.out_ld + head * HD;
 #pragma unroll
   for (int d = 0; d < NB; ++d)
 #pragma unroll
@@ -342,20 +341,23 @@ __global__ __launch_bounds__(64) void k_attn_merge_split(AttnArgs a, int64_t tq_
   }
 }
 
-// Query blocks of one launch and the first block to split: a launch with fewer blocks than CUs splits
-// its heaviest half (causal: the latest queries) or, with a sliding window (every block's key range
-// about the same), all of its blocks. split_from is a multiple of the blocks per 32-token
+// Query blocks of one launch and the first block to split. A causal launch with fewer blocks than
+// twice the CUs splits its heaviest half (the latest queries, whose key ranges are longest); a
+// sliding-window launch (every block's key range about the same) with fewer blocks than CUs splits
+// all of its blocks. split_from is a multiple of the blocks per 32-token
 // run so that the split rows start at a run boundary. Returns false if the shape is not the MFMA path's.
 static bool attn_plan(int64_t B, int64_t T, int64_t nh, int64_t nkv, int64_t hd, int32_t sliding, int* nblk,
                       int* split_from, int64_t* tq_lo) {
   if (nkv <= 0 || nh % nkv) return false;
   const int64_t G = nh / nkv;
   if (!(G == 1 || G == 2 || G == 4) || !(hd == 128 || hd == 256 || hd == 512)) return false;
-  const int QG = hd == 512 ? 2 : 4;
-  const int64_t ngroups = ((T + 31) / 32) * G;
+  const int64_t runs = (T + 31) / 32, cus = device_cus();
+  const int QG = 4;  // query groups (head x 32 tokens) per block
+  const int64_t ngroups = runs * G;
   *nblk = (int)((ngroups + QG - 1) / QG);
   *split_from = *nblk;
-  if ((int64_t)*nblk * nkv * B < device_cus()) {
+  const int64_t blocks = (int64_t)*nblk * nkv * B;
+  if (sliding ? blocks < cus : blocks < 2 * cus) {
     const int step = G > QG ? (int)(G / QG) : 1;
     *split_from = sliding ? 0 : (*nblk / 2) / step * step;
   }
@@ -384,9 +386,9 @@ bool attn_mfma(const AttnArgs& a, hipStream_t s, g4_status* st) {
   const int64_t G = a.nh / a.nkv;
   dim3 grid((unsigned)(2 * (nblk - split_from) + split_from), (unsigned)a.nkv, (unsigned)a.B);
   const float sl2 = a.scale * 1.4426950408889634f;
-  if (a.hd == 128) hipLaunchKernelGGL((k_attn_mfma<128, 1>), grid, dim3(256), 0, s, a, (int)G, sl2, split_from);
-  else if (a.hd == 256) hipLaunchKernelGGL((k_attn_mfma<256, 1>), grid, dim3(256), 0, s, a, (int)G, sl2, split_from);
-  else hipLaunchKernelGGL((k_attn_mfma<512, 2>), grid, dim3(256), 0, s, a, (int)G, sl2, split_from);
+  if (a.hd == 128) hipLaunchKernelGGL((k_attn_mfma<128>), grid, dim3(256), 0, s, a, (int)G, sl2, split_from);
+  else if (a.hd == 256) hipLaunchKernelGGL((k_attn_mfma<256>), grid, dim3(256), 0, s, a, (int)G, sl2, split_from);
+  else hipLaunchKernelGGL((k_attn_mfma<512>), grid, dim3(256), 0, s, a, (int)G, sl2, split_from);
   if ((*st = check_launch("attn_mfma")) != G4_OK || split_from == nblk || tq_lo >= a.T) return true;
   dim3 gm((unsigned)(a.T - tq_lo), (unsigned)a.nh, (unsigned)a.B);
   if (a.hd == 128) hipLaunchKernelGGL((k_attn_merge_split<128>), gm, dim3(64), 0, s, a, tq_lo);
