@@ -164,6 +164,65 @@ __global__ __launch_bounds__(256) void k_rownorm4(const TX* __restrict__ x, int 
   }
 }
 
+// The same tail with one wave per row (four rows per block) for launches with many rows: the two
+// reductions are wave shuffles with no block barrier, and each lane keeps V 4-wide vectors of the row
+// in flight. Slices are added in slice order.
+template <typename TX, typename T, int V>
+__global__ __launch_bounds__(256) void k_rownorm_w(const TX* __restrict__ x, int parts, int64_t part_stride,
+                                                   const T* __restrict__ w, T* __restrict__ y, float* __restrict__ res,
+                                                   float res_scale, const T* __restrict__ w_next, T* __restrict__ y_next,
+                                                   int64_t rows, int64_t dim, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const TX* xr = x + row * dim;
+  const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f), one = make_float4(1.f, 1.f, 1.f, 1.f);
+  float4 v[V], rv[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int64_t c = 4 * (lane + 64 * i);
+    v[i] = rv[i] = zero;
+    if (c < dim) {
+      if (res) rv[i] = ld4(res + row * dim + c);
+      v[i] = ld4(xr + c);
+    }
+  }
+  for (int p = 1; p < parts; ++p) {
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const int64_t c = 4 * (lane + 64 * i);
+      if (c < dim) v[i] = v[i] + ld4(xr + p * part_stride + c);
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < V; ++i) ss += dot4(v[i]);
+  const float inv = 1.f / sqrtf(wave_sum(ss) / (float)dim + eps);
+  float ss2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int64_t c = 4 * (lane + 64 * i);
+    if (c < dim) {
+      const float4 n = v[i] * inv * (w ? ld4(w + c) : one);
+      if (y) st4(y + row * dim + c, n);
+      if (res) {
+        const float4 r = (rv[i] + n) * res_scale;
+        st4(res + row * dim + c, r);
+        v[i] = r;
+        ss2 += dot4(r);
+      }
+    }
+  }
+  if (y_next) {
+    const float inv2 = w_next ? 1.f / sqrtf(wave_sum(ss2) / (float)dim + eps) : 1.f;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const int64_t c = 4 * (lane + 64 * i);
+      if (c < dim) st4(y_next + row * dim + c, w_next ? v[i] * inv2 * ld4(w_next + c) : v[i]);
+    }
+  }
+}
+
 template <typename TX, typename T>
 static void launch_rownorm(int vpt, dim3 g, hipStream_t s, const TX* x, int parts, int64_t ps,
                            const T* w, T* y, float* res, float rs, const T* wn, T* yn, int64_t dim,
@@ -171,6 +230,21 @@ static void launch_rownorm(int vpt, dim3 g, hipStream_t s, const TX* x, int part
   const bool vec = (dim % 4) == 0 && (ps % 4) == 0 && dim <= 4096 &&
                    (((uintptr_t)x | (uintptr_t)w | (uintptr_t)y | (uintptr_t)res | (uintptr_t)wn | (uintptr_t)yn) &
                     15) == 0;
+  if (vec && g.x >= 1024 && parts >= 1) {  // many rows: one wave per row
+    const int64_t rows = g.x;
+    const int vw = (int)((dim / 4 + 63) / 64);
+    const dim3 gw((unsigned)((rows + 3) / 4));
+#define G4_RNW(V)                                                                                             \
+  hipLaunchKernelGGL((k_rownorm_w<TX, T, V>), gw, dim3(256), 0, s, x, parts, ps, w, y, res, rs, wn, yn, rows, dim, \
+                     eps)
+    if (vw <= 2) G4_RNW(2);
+    else if (vw <= 4) G4_RNW(4);
+    else if (vw <= 8) G4_RNW(8);
+    else if (vw <= 10) G4_RNW(10);
+    else G4_RNW(16);
+#undef G4_RNW
+    return;
+  }
   if (vec) {
     const int v4 = (int)((dim / 4 + 255) / 256);
 #define G4_RN4(V) \

@@ -13,7 +13,8 @@ pytestmark = pytest.mark.gpu
 
 # ------------------------------------------------------------------------------- rmsnorm
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-@pytest.mark.parametrize("rows,dim,parts", [(37, 2560, 3), (5, 300, 1), (1, 64, 2), (0, 64, 1)])
+@pytest.mark.parametrize("rows,dim,parts", [(37, 2560, 3), (5, 300, 1), (1, 64, 2), (0, 64, 1),
+                                            (1030, 2560, 3), (1025, 4096, 1), (1500, 300, 2)])
 def test_rmsnorm_fused_tail(dt, rows, dim, parts):
     log(f"rmsnorm {dt} rows={rows} dim={dim} parts={parts}")
     gdt, tdt = DT[dt]
