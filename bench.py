@@ -60,6 +60,60 @@ def attn_flops(cfg, T):
     return tot
 
 
+def class_rates(cfg, M, decode, per_ms):
+    """Achieved rate of each timed kernel class from its per-step time, against its own bound.
+
+    Prefill GEMMs and attention: algorithmic TFLOP/s against bf16 dense MFMA. Decode GEMMs: weight bytes
+    streamed, attention: K and V bytes read (shared layers re-read their source), both against HBM.
+    Row tails and head norms (elementwise, HBM): bytes each step needs at the layer's dtypes, with the
+    float32 projection outputs counted once (split-K slices are an implementation choice, not counted).
+    """
+    H, nh, nkv, F, d = cfg["hidden"], cfg["n_heads"], cfg["n_kv_heads"], cfg["ffn"], cfg["ple_dim"]
+    E = 2 if cfg["dtype"] == "bf16" else 4
+    from gemma_decoder_forward_amd import binding as bd
+    srcs = bd.g4_kv_sources([1 if t == "S" else 0 for t in cfg["layer_types"]], cfg["n_shared"])
+    L = cfg["n_layers"]
+    out = {}
+    gf = gemm_flops(cfg, M)
+    keyname = dict(qkv="qkv_gemm", o="o_gemm", gate_up="gate_up_gemm", down="down_gemm", ple="ple_gemm")
+    for k, f in gf.items():
+        ms = per_ms.get(keyname[k], 0)
+        if ms <= 0:
+            continue
+        if decode:
+            gb = f / (2 * M) * E / (ms / 1e3) / 1e9  # weight bytes = flops / (2M) elements
+            out[keyname[k]] = dict(GB_s=round(gb, 1), frac_hbm=round(gb / PEAK_HBM_GBS, 3))
+        else:
+            tf = f / (ms / 1e3) / 1e12
+            out[keyname[k]] = dict(TFLOP_s=round(tf, 1), frac_mfma=round(tf / PEAK_BF16_TFLOPS, 3))
+    ms = per_ms.get("attention", 0)
+    if ms > 0:
+        if decode:
+            kv = 0
+            for t in cfg["layer_types"]:
+                hd = cfg["head_dim_swa"] if t == "S" else cfg["head_dim_full"]
+                keys = min(cfg["ctx"], cfg["window"]) if t == "S" else cfg["ctx"]
+                kv += 2 * nkv * keys * hd * E * M
+            gb = kv / (ms / 1e3) / 1e9
+            out["attention"] = dict(GB_s=round(gb, 1), frac_hbm=round(gb / PEAK_HBM_GBS, 3))
+        else:
+            tf = attn_flops(cfg, cfg["T"]) / (ms / 1e3) / 1e12
+            out["attention"] = dict(TFLOP_s=round(tf, 1), frac_mfma=round(tf / PEAK_BF16_TFLOPS, 3))
+    # per token per layer: three residual tails (read f32 projection + h, write h + one dtype row) and the
+    # pre-attention norm of the first layer; head norms read and write q (and k, v when the layer owns them)
+    tail = L * 3 * (4 * H + 4 * H + 4 * H + E * H) + (4 * H + E * H)
+    qk = 0
+    for l, t in enumerate(cfg["layer_types"]):
+        hd = cfg["head_dim_swa"] if t == "S" else cfg["head_dim_full"]
+        qk += 2 * (nh + (2 * nkv if srcs[l] == l else 0)) * hd * E
+    for name, per_tok in (("row_tail", tail), ("qk_norm_rope", qk)):
+        ms = per_ms.get(name, 0)
+        if ms > 0:
+            gb = per_tok * M / (ms / 1e3) / 1e9
+            out[name] = dict(GB_s=round(gb, 1), frac_hbm=round(gb / PEAK_HBM_GBS, 3))
+    return out
+
+
 def gate_up_weight_bytes(cfg):
     return 2 * cfg["ffn"] * cfg["hidden"] * 2
 
@@ -302,6 +356,7 @@ def main():
         extra["model_tflops"] = round((sum(gf.values()) + af) / (ms / 1e3) / 1e12, 2)
     if "breakdown_ms_per_step" in r:
         extra["breakdown_ms_per_step"] = r["breakdown_ms_per_step"]
+        extra["class_rates"] = class_rates(cfg, tokens, decode, r["breakdown_ms_per_step"])
     line = dict(
         metric="prefill tokens/s" if not decode else "decode tokens/s",
         value=round(tokens / (ms / 1e3), 2), unit="tokens/s", n_gpus=1, steps=args.steps, warmup=args.warmup,

@@ -293,7 +293,7 @@ g4_status rownorm(const void* x, int32_t x_dtype, int32_t x_parts, int64_t part_
 // --------------------------------------------------------------------------------------------
 // Per-head RMSNorm + NeoX RoPE (cortiq-engine q/k/v head loops; turbospark per-head norms and
 // `encode_rope_proportional_neox`; taconite `rope_half`). One block per (token row, four heads), one
-// wave per head; each block puts the cos/sin of the row's position in LDS for its heads.
+// wave per head.
 // Pair j of a head pairs elements j and j + hd/2; pairs j >= n_rot are left untouched (zero frequency).
 // --------------------------------------------------------------------------------------------
 struct SegDev {
@@ -304,81 +304,153 @@ struct SegDev {
 };
 struct SegPack { SegDev s[3]; int n; int total_heads; int parts; int64_t part_stride; };
 
-// TI: input element type (float for summed split-K slices); T: output type. PPL: pairs per lane
-// (hd/2 <= 64*PPL).
-template <typename TI, typename T, int PPL>
-__global__ __launch_bounds__(256) void k_qknr(SegPack pk, const int32_t* __restrict__ pos, int64_t T_,
-                                              int hd, double rstep, int n_rot, float eps) {
-  __shared__ float cs[256], sn[256];
+// Rotation frequencies of the launch in revolutions per position, inv_j / (2 pi), from the host in f64.
+struct RopeTab { double rev[256]; };
+
+// EPL consecutive values of one row (EPL in {1, 2, 4}) as floats, and back: one vector access when VEC,
+// else element by element, the first n of them.
+template <int EPL, bool VEC> __device__ __forceinline__ void ldv(const float* p, float* v, int n) {
+  if (!VEC) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) v[e] = e < n ? p[e] : 0.f;
+  } else if (EPL == 4) {
+    const float4 t = *(const float4*)p; v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+  } else if (EPL == 2) {
+    const float2 t = *(const float2*)p; v[0] = t.x; v[1] = t.y;
+  } else {
+    v[0] = *p;
+  }
+}
+template <int EPL, bool VEC> __device__ __forceinline__ void ldv(const bf16* p, float* v, int n) {
+  if (!VEC) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) v[e] = e < n ? bf2f(p[e]) : 0.f;
+  } else if (EPL == 4) {
+    const uint2 u = *(const uint2*)p;
+    v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
+    v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
+  } else if (EPL == 2) {
+    const uint32_t u = *(const uint32_t*)p;
+    v[0] = __uint_as_float(u << 16); v[1] = __uint_as_float(u & 0xffff0000u);
+  } else {
+    v[0] = bf2f(*p);
+  }
+}
+template <int EPL, bool VEC> __device__ __forceinline__ void stv(float* p, const float* v, int n) {
+  if (!VEC) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) if (e < n) p[e] = v[e];
+  } else if (EPL == 4) {
+    *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
+  } else if (EPL == 2) {
+    *(float2*)p = make_float2(v[0], v[1]);
+  } else {
+    *p = v[0];
+  }
+}
+template <int EPL, bool VEC> __device__ __forceinline__ void stv(bf16* p, const float* v, int n) {
+  if (!VEC) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) if (e < n) p[e] = f2bf(v[e]);
+  } else if (EPL == 4) {
+    *(uint2*)p = pack_bf16x4(v);
+  } else if (EPL == 2) {
+    *(uint32_t*)p = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+  } else {
+    *p = f2bf(v[0]);
+  }
+}
+
+// TI: input element type (float for summed split-K slices); T: output type. One wave per head; lane l
+// owns pairs EPL l .. EPL l + EPL - 1 of the head (hd / 2 <= 64 EPL), i.e. elements j and j + hd/2 of
+// each. VEC: rows aligned for EPL-wide accesses and hd / 2 a multiple of EPL. The lane's angles come
+// while its loads are in flight: angle of pair j in revolutions, p * rev_j, reduced to [-1/2, 1/2] in
+// float64, then the hardware sine and cosine of one revolution-scaled float32 (v_sin_f32 / v_cos_f32).
+template <typename TI, typename T, int EPL, bool VEC>
+__global__ __launch_bounds__(256) void k_qknr(SegPack pk, RopeTab tab, const int32_t* __restrict__ pos, int64_t T_,
+                                              int hd, int n_rot, float eps) {
+  const int gh = __builtin_amdgcn_readfirstlane(blockIdx.y * 4 + (threadIdx.x >> 6));  // wave-uniform
+  if (gh >= pk.total_heads) return;
+  const int lane = threadIdx.x & 63;
   const int64_t m = blockIdx.x;
-  const int64_t b = m / T_, t = m % T_;
+  const uint32_t b = (uint32_t)blockIdx.x / (uint32_t)T_, t = (uint32_t)blockIdx.x % (uint32_t)T_;  // B T < 2^32
   const int64_t p = pos ? (int64_t)pos[b] + t : 0;
   const int half = hd >> 1;
-  // angle of pair j: p * theta^(-2j/hd) = p * rstep^j, in float64 (rstep^j by binary powering), reduced
-  // to [-pi, pi] in float64 with 2*pi split into two doubles, then cos/sin in float32
-  for (int j = threadIdx.x; j < n_rot; j += 256) {
-    double inv = 1.0, base = rstep;
-    for (int e = j; e; e >>= 1) {
-      if (e & 1) inv *= base;
-      base *= base;
-    }
-    const double ang = (double)p * inv;
-    const double k = rint(ang * 0.15915494309189535);
-    double r = fma(-k, 6.283185307179586, ang);
-    r = fma(-k, 2.4492935982947064e-16, r);
-    float sv, cv;
-    sincosf((float)r, &sv, &cv);
-    cs[j] = cv;
-    sn[j] = sv;
-  }
-  __syncthreads();
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int gh = blockIdx.y * 4 + wave; gh < pk.total_heads; gh += 4 * gridDim.y) {
-    int si = 0, h = gh;
-    while (si < pk.n - 1 && h >= pk.s[si].heads) { h -= pk.s[si].heads; ++si; }
-    const SegDev& sg = pk.s[si];
-    const TI* xh = (const TI*)sg.x + m * sg.x_ld + (int64_t)h * hd;
-    float a[PPL], c[PPL];
-    float ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < PPL; ++i) {
-      const int j = lane + 64 * i;
-      a[i] = c[i] = 0.f;
-      if (j < half)
-#pragma unroll 4
-        for (int pp = 0; pp < pk.parts; ++pp) {
-          a[i] += ldf(xh + pp * pk.part_stride + j);
-          c[i] += ldf(xh + pp * pk.part_stride + j + half);
-        }
-      ss += a[i] * a[i] + c[i] * c[i];
-    }
-    ss = wave_sum(ss);
-    const float inv = 1.f / sqrtf(ss / (float)hd + eps);
-    T* yh;
-    if (sg.y_cap > 0) {
-      if (p < 0 || (!sg.ring && p >= sg.y_cap)) continue;  // out-of-range position: no write
-      const int64_t row = sg.ring ? p % sg.y_cap : p;
-      yh = (T*)sg.y + (((b * sg.heads + h) * sg.y_cap) + row) * hd;
-    } else {
-      yh = (T*)sg.y + m * sg.y_ld + (int64_t)h * hd;
-    }
-    const T* wv = (const T*)sg.w;
-#pragma unroll
-    for (int i = 0; i < PPL; ++i) {
-      const int j = lane + 64 * i;
-      if (j >= half) continue;
-      float u = a[i] * inv, v = c[i] * inv;
-      if (wv) { u *= ldf(wv + j); v *= ldf(wv + j + half); }
-      if (sg.rope && j < n_rot) {
-        const float co = cs[j], si2 = sn[j];
-        const float u2 = u * co - v * si2;
-        const float v2 = v * co + u * si2;
-        u = u2; v = v2;
-      }
-      stf(yh + j, u);
-      stf(yh + j + half, v);
+  const int j0 = EPL * lane;
+  const bool on = j0 < half;
+  const int nv = half - j0;  // pairs of this lane inside the head (at least EPL when VEC)
+  // the head's segment, picked with constant indexes so its fields come in scalar loads
+  int h = gh;
+  SegDev sg = pk.s[0];
+  if (pk.n > 1 && h >= pk.s[0].heads) {
+    h -= pk.s[0].heads;
+    sg = pk.s[1];
+    if (pk.n > 2 && h >= pk.s[1].heads) {
+      h -= pk.s[1].heads;
+      sg = pk.s[2];
     }
   }
+  const bool rope = sg.rope != 0;
+  double rv[EPL];  // j0 + e <= 255: inside the table, zero past the rotated pairs
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) rv[e] = tab.rev[j0 + e];
+  const TI* xh = (const TI*)sg.x + m * sg.x_ld + (int64_t)h * hd;
+  float a[EPL], c[EPL], wa[EPL], wc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) a[e] = c[e] = 0.f, wa[e] = wc[e] = 1.f;
+  // without a weight the loads read the head's own input (in range for either type) and the weight is 1
+  const T* wp = sg.w ? (const T*)sg.w : (const T*)(const void*)xh;
+  if (on) {
+    ldv<EPL, VEC>(xh + j0, a, nv);
+    ldv<EPL, VEC>(xh + j0 + half, c, nv);
+    ldv<EPL, VEC>(wp + j0, wa, nv);
+    ldv<EPL, VEC>(wp + j0 + half, wc, nv);
+  }
+  if (!sg.w)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) wa[e] = wc[e] = 1.f;
+  float co[EPL], sn[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    double r = (double)p * rv[e];
+    r -= rint(r);
+    co[e] = __builtin_amdgcn_cosf((float)r);
+    sn[e] = __builtin_amdgcn_sinf((float)r);
+  }
+  if (on)  // further split-K slices, summed in order after the first
+    for (int pp = 1; pp < pk.parts; ++pp) {
+      float ta[EPL], tc[EPL];
+      ldv<EPL, VEC>(xh + pp * pk.part_stride + j0, ta, nv);
+      ldv<EPL, VEC>(xh + pp * pk.part_stride + j0 + half, tc, nv);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) { a[e] += ta[e]; c[e] += tc[e]; }
+    }
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) ss += a[e] * a[e] + c[e] * c[e];
+  ss = wave_sum(ss);
+  const float inv = 1.f / sqrtf(ss / (float)hd + eps);
+  T* yh;
+  if (sg.y_cap > 0) {
+    if (p < 0 || (!sg.ring && p >= sg.y_cap)) return;  // out-of-range position: no write
+    const int64_t row = sg.ring ? p % sg.y_cap : p;
+    yh = (T*)sg.y + ((((int64_t)b * sg.heads + h) * sg.y_cap) + row) * hd;
+  } else {
+    yh = (T*)sg.y + m * sg.y_ld + (int64_t)h * hd;
+  }
+  if (!on) return;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    float u = a[e] * inv * wa[e], v = c[e] * inv * wc[e];
+    if (rope && j0 + e < n_rot) {
+      const float u2 = u * co[e] - v * sn[e];
+      const float v2 = v * co[e] + u * sn[e];
+      u = u2; v = v2;
+    }
+    a[e] = u; c[e] = v;
+  }
+  stv<EPL, VEC>(yh + j0, a, nv);
+  stv<EPL, VEC>(yh + j0 + half, c, nv);
 }
 
 static g4_status qknr_launch(const HeadSeg* segs, int nseg, int parts, int64_t part_stride, bool f32_in,
@@ -399,19 +471,37 @@ static g4_status qknr_launch(const HeadSeg* segs, int nseg, int parts, int64_t p
     any_rope |= segs[i].rope;
   }
   const int nr = any_rope ? (int)n_rot : 0;
-  const double rstep = pow((double)theta, -2.0 / (double)hd);
+  RopeTab tab;
+  for (int j = 0; j < 256; ++j)
+    tab.rev[j] = j < nr ? pow((double)theta, -2.0 * j / (double)hd) / 6.283185307179586 : 0.0;
+  // pairs per lane: vector accesses when every row start is aligned to them, else per element
+  const int64_t half = hd / 2;
+  const size_t isz = f32_in ? 4 : (dtype == G4_BF16 ? 2 : 4), osz = dtype == G4_BF16 ? 2 : 4;
+  auto aligned = [&](int e) {
+    if ((half % e) || (part_stride % e)) return false;
+    for (int i = 0; i < nseg; ++i) {
+      if ((segs[i].x_ld % e) || ((uintptr_t)segs[i].x % (isz * e)) || ((uintptr_t)segs[i].y % (osz * e))) return false;
+      if (segs[i].y_cap == 0 && (segs[i].y_ld % e)) return false;
+      if (segs[i].w && ((uintptr_t)segs[i].w % (osz * e))) return false;
+    }
+    return true;
+  };
+  const int need = half <= 64 ? 1 : (half <= 128 ? 2 : 4);  // fewest pairs per lane that cover the head
+  const bool vec = need == 1 || aligned(need);
   // one wave per head: blocks of four heads, so a token's heads run in parallel
   dim3 g((unsigned)(B * T), (unsigned)((pk.total_heads + 3) / 4));
-  const int ppl = (int)((hd / 2 + 63) / 64);
-#define G4_QK(TI, TT, P) \
-  hipLaunchKernelGGL((k_qknr<TI, TT, P>), g, dim3(256), 0, s, pk, pos, T, (int)hd, rstep, nr, eps)
-  if (dtype == G4_BF16 && f32_in) {
-    if (ppl <= 1) G4_QK(float, bf16, 1); else if (ppl <= 2) G4_QK(float, bf16, 2); else G4_QK(float, bf16, 4);
-  } else if (dtype == G4_BF16) {
-    if (ppl <= 1) G4_QK(bf16, bf16, 1); else if (ppl <= 2) G4_QK(bf16, bf16, 2); else G4_QK(bf16, bf16, 4);
-  } else {
-    if (ppl <= 1) G4_QK(float, float, 1); else if (ppl <= 2) G4_QK(float, float, 2); else G4_QK(float, float, 4);
-  }
+#define G4_QK(TI, TT, P, V) \
+  hipLaunchKernelGGL((k_qknr<TI, TT, P, V>), g, dim3(256), 0, s, pk, tab, pos, T, (int)hd, nr, eps)
+#define G4_QKE(TI, TT)                                                      \
+  do {                                                                      \
+    if (need == 1) G4_QK(TI, TT, 1, true);                                  \
+    else if (need == 2) { if (vec) G4_QK(TI, TT, 2, true); else G4_QK(TI, TT, 2, false); } \
+    else { if (vec) G4_QK(TI, TT, 4, true); else G4_QK(TI, TT, 4, false); } \
+  } while (0)
+  if (dtype == G4_BF16 && f32_in) G4_QKE(float, bf16);
+  else if (dtype == G4_BF16) G4_QKE(bf16, bf16);
+  else G4_QKE(float, float);
+#undef G4_QKE
 #undef G4_QK
   return check_launch("qk_norm_rope");
 }
