@@ -85,10 +85,31 @@ __device__ __forceinline__ float4 operator*(float4 a, float4 b) { return make_fl
 __device__ __forceinline__ float4 operator*(float4 a, float s) { return make_float4(a.x * s, a.y * s, a.z * s, a.w * s); }
 __device__ __forceinline__ float dot4(float4 a) { return a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w; }
 
-// The same tail for dim % 4 == 0 with 4-wide loads; the split-K slices are read 8 at a time so that a
-// row with many slices still costs few memory round trips. Slices are added in slice order.
+// A row of `bytes` bytes as a buffer: a load past its end, or from a NULL row, reads zero and moves no
+// data. Loads through it need no branch around them, so the compiler keeps them all in flight together
+// (a branch per optional operand would put a wait for memory at every join).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, p ? (int)bytes : 0, 0x00020000);
+}
+// values c .. c+3 of a buffer row of floats / bf16s
+__device__ __forceinline__ float4 bld4(__amdgpu_buffer_rsrc_t r, const float*, int64_t c) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(c * 4), 0, 0);
+  const uint4 u = *(const uint4*)&v;
+  return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+}
+__device__ __forceinline__ float4 bld4(__amdgpu_buffer_rsrc_t r, const bf16*, int64_t c) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)(c * 2), 0, 0);
+  const uint2 u = *(const uint2*)&v;
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xffff0000u));
+}
+
+// The same tail for dim % 4 == 0 with 4-wide loads, for launches with few rows (decode), where the row's
+// latency is the cost: every load goes through a row buffer (above), the residual and both weights in
+// one batch and the split-K slices eight at a time, so a row costs one memory round trip per eight
+// slices. Slices are added in slice order.
 template <typename TX, typename T, int V4>
-__global__ __launch_bounds__(256) void k_rownorm4(const TX* __restrict__ x, int parts, int64_t part_stride,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) void k_rownorm4(const TX* __restrict__ x, int parts, int64_t part_stride,
                                                   const T* __restrict__ w, T* __restrict__ y,
                                                   float* __restrict__ res, float res_scale,
                                                   const T* __restrict__ w_next, T* __restrict__ y_next,
@@ -96,39 +117,41 @@ __global__ __launch_bounds__(256) void k_rownorm4(const TX* __restrict__ x, int 
   __shared__ float sh[32];
   const int64_t row = blockIdx.x;
   const TX* xr = x + row * dim;
-  const float4 one = make_float4(1.f, 1.f, 1.f, 1.f), zero = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+  const auto rr = row_rsrc(res ? res + row * dim : nullptr, dim * 4);
+  const auto rw = row_rsrc(w, dim * (int64_t)sizeof(T)), rn = row_rsrc(w_next, dim * (int64_t)sizeof(T));
   float4 v[V4], rv[V4], wv[V4], wn[V4];
 #pragma unroll
-  for (int i = 0; i < V4; ++i) {
-    const int64_t c = 4 * (threadIdx.x + (int64_t)i * 256);
-    v[i] = rv[i] = zero;
-    wv[i] = wn[i] = one;
-    if (c < dim) {
-      if (res) rv[i] = ld4(res + row * dim + c);
-      if (w) wv[i] = ld4(w + c);
-      if (w_next) wn[i] = ld4(w_next + c);
-    }
-  }
-  int p = 0;
-  for (; p + 8 <= parts; p += 8) {
+  for (int i = 0; i < V4; ++i) v[i] = zero;
+  for (int p = 0; p < parts; p += 8) {
+    __amdgpu_buffer_rsrc_t rx[8];  // slices past the last read zero
 #pragma unroll
-    for (int i = 0; i < V4; ++i) {
-      const int64_t c = 4 * (threadIdx.x + (int64_t)i * 256);
-      if (c < dim) {
-        float4 t[8];
+    for (int j = 0; j < 8; ++j)
+      rx[j] = row_rsrc(p + j < parts ? xr + (int64_t)(p + j) * part_stride : nullptr, dim * (int64_t)sizeof(TX));
+    float4 t[V4][8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) t[j] = ld4(xr + (p + j) * part_stride + c);
+    for (int i = 0; i < V4; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[i] = v[i] + t[j];
+      for (int j = 0; j < 8; ++j) t[i][j] = bld4(rx[j], x, 4 * (threadIdx.x + (int64_t)i * 256));
+    if (p == 0)  // the other operands ride behind the first slices
+#pragma unroll
+      for (int i = 0; i < V4; ++i) {
+        const int64_t c = 4 * (threadIdx.x + (int64_t)i * 256);
+        rv[i] = bld4(rr, (const float*)nullptr, c);
+        wv[i] = bld4(rw, w, c);
+        wn[i] = bld4(rn, w_next, c);
       }
-    }
-  }
-  for (; p < parts; ++p) {
 #pragma unroll
-    for (int i = 0; i < V4; ++i) {
-      const int64_t c = 4 * (threadIdx.x + (int64_t)i * 256);
-      if (c < dim) v[i] = v[i] + ld4(xr + p * part_stride + c);
-    }
+    for (int i = 0; i < V4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[i] = v[i] + t[i][j];
+  }
+  // a missing weight read as zero and stands for ones
+  const float w1 = w ? 0.f : 1.f, n1 = w_next ? 0.f : 1.f;
+#pragma unroll
+  for (int i = 0; i < V4; ++i) {
+    wv[i] = wv[i] + make_float4(w1, w1, w1, w1);
+    wn[i] = wn[i] + make_float4(n1, n1, n1, n1);
   }
   float ss = 0.f;
 #pragma unroll
@@ -164,61 +187,101 @@ __global__ __launch_bounds__(256) void k_rownorm4(const TX* __restrict__ x, int 
   }
 }
 
+// Four consecutive values of a buffer row as loaded (8 bytes of bf16, 16 of float), converted at use.
+template <typename T> struct Raw4;
+template <> struct Raw4<float> { uint4 u; };
+template <> struct Raw4<bf16> { uint2 u; };
+__device__ __forceinline__ Raw4<float> braw4(__amdgpu_buffer_rsrc_t r, const float*, int64_t c) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(c * 4), 0, 0);
+  return Raw4<float>{*(const uint4*)&v};
+}
+__device__ __forceinline__ Raw4<bf16> braw4(__amdgpu_buffer_rsrc_t r, const bf16*, int64_t c) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)(c * 2), 0, 0);
+  return Raw4<bf16>{*(const uint2*)&v};
+}
+__device__ __forceinline__ float4 cvt4(Raw4<float> r) {
+  return make_float4(__uint_as_float(r.u.x), __uint_as_float(r.u.y), __uint_as_float(r.u.z), __uint_as_float(r.u.w));
+}
+__device__ __forceinline__ float4 cvt4(Raw4<bf16> r) {
+  return make_float4(__uint_as_float(r.u.x << 16), __uint_as_float(r.u.x & 0xffff0000u), __uint_as_float(r.u.y << 16),
+                     __uint_as_float(r.u.y & 0xffff0000u));
+}
+
 // The same tail with one wave per row (four rows per block) for launches with many rows: the two
-// reductions are wave shuffles with no block barrier, and each lane keeps V 4-wide vectors of the row
-// in flight. Slices are added in slice order.
+// reductions are wave reductions with no block barrier, and the row's loads (the first split-K slice
+// and the residual) are all issued before the first wait, through row buffers. Further slices come four
+// per round trip and are added in slice order.
 template <typename TX, typename T, int V>
 __global__ __launch_bounds__(256) void k_rownorm_w(const TX* __restrict__ x, int parts, int64_t part_stride,
                                                    const T* __restrict__ w, T* __restrict__ y, float* __restrict__ res,
                                                    float res_scale, const T* __restrict__ w_next, T* __restrict__ y_next,
                                                    int64_t rows, int64_t dim, float eps) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  // wave-uniform row (rows < 2^31): the row buffers' descriptors stay in scalar registers
+  const int64_t row = __builtin_amdgcn_readfirstlane((int)blockIdx.x * 4 + (int)(threadIdx.x >> 6));
   if (row >= rows) return;
   const TX* xr = x + row * dim;
-  const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f), one = make_float4(1.f, 1.f, 1.f, 1.f);
-  float4 v[V], rv[V];
+  const int64_t xbytes = dim * (int64_t)sizeof(TX), wbytes = dim * (int64_t)sizeof(T);
+  const auto rx = row_rsrc(xr, xbytes), rr = row_rsrc(res ? res + row * dim : nullptr, dim * 4);
+  Raw4<TX> xa[V];
+  Raw4<float> ra[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) {
     const int64_t c = 4 * (lane + 64 * i);
-    v[i] = rv[i] = zero;
-    if (c < dim) {
-      if (res) rv[i] = ld4(res + row * dim + c);
-      v[i] = ld4(xr + c);
-    }
+    xa[i] = braw4(rx, x, c);
+    ra[i] = braw4(rr, (const float*)nullptr, c);
   }
-  for (int p = 1; p < parts; ++p) {
+  float4 v[V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-      const int64_t c = 4 * (lane + 64 * i);
-      if (c < dim) v[i] = v[i] + ld4(xr + p * part_stride + c);
-    }
+  for (int i = 0; i < V; ++i) v[i] = cvt4(xa[i]);
+  for (int p = 1; p < parts; p += 4) {
+    __amdgpu_buffer_rsrc_t rp[4];  // slices past the last read zero
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rp[j] = row_rsrc(p + j < parts ? xr + (int64_t)(p + j) * part_stride : nullptr, xbytes);
+    Raw4<TX> t[4][V];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < V; ++i) t[j][i] = braw4(rp[j], x, 4 * (lane + 64 * i));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < V; ++i) v[i] = v[i] + cvt4(t[j][i]);
   }
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < V; ++i) ss += dot4(v[i]);
+  // the weights (shared by every row, so mostly cache hits) after the first reduction
+  const auto rw = row_rsrc(w, wbytes), rn = row_rsrc(w_next, wbytes);
+  Raw4<T> wa[V], na[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    wa[i] = braw4(rw, w, 4 * (lane + 64 * i));
+    na[i] = braw4(rn, w_next, 4 * (lane + 64 * i));
+  }
   const float inv = 1.f / sqrtf(wave_sum(ss) / (float)dim + eps);
+  // a missing weight read as zero and stands for ones
+  const float w1 = w ? 0.f : 1.f, n1 = w_next ? 0.f : 1.f;
+  const float4 w1v = make_float4(w1, w1, w1, w1), n1v = make_float4(n1, n1, n1, n1);
   float ss2 = 0.f;
 #pragma unroll
   for (int i = 0; i < V; ++i) {
     const int64_t c = 4 * (lane + 64 * i);
-    if (c < dim) {
-      const float4 n = v[i] * inv * (w ? ld4(w + c) : one);
-      if (y) st4(y + row * dim + c, n);
-      if (res) {
-        const float4 r = (rv[i] + n) * res_scale;
-        st4(res + row * dim + c, r);
-        v[i] = r;
-        ss2 += dot4(r);
-      }
+    const float4 n = v[i] * inv * (cvt4(wa[i]) + w1v);
+    if (res) {
+      const float4 r = (cvt4(ra[i]) + n) * res_scale;
+      v[i] = r;
+      ss2 += dot4(r);  // zero past the row's end
+      if (c < dim) st4(res + row * dim + c, r);
     }
+    if (y && c < dim) st4(y + row * dim + c, n);
   }
   if (y_next) {
     const float inv2 = w_next ? 1.f / sqrtf(wave_sum(ss2) / (float)dim + eps) : 1.f;
 #pragma unroll
     for (int i = 0; i < V; ++i) {
       const int64_t c = 4 * (lane + 64 * i);
-      if (c < dim) st4(y_next + row * dim + c, w_next ? v[i] * inv2 * ld4(w_next + c) : v[i]);
+      if (c < dim) st4(y_next + row * dim + c, w_next ? v[i] * inv2 * (cvt4(na[i]) + n1v) : v[i]);
     }
   }
 }
@@ -417,13 +480,20 @@ __global__ __launch_bounds__(256) void k_qknr(SegPack pk, RopeTab tab, const int
     co[e] = __builtin_amdgcn_cosf((float)r);
     sn[e] = __builtin_amdgcn_sinf((float)r);
   }
-  if (on)  // further split-K slices, summed in order after the first
-    for (int pp = 1; pp < pk.parts; ++pp) {
-      float ta[EPL], tc[EPL];
-      ldv<EPL, VEC>(xh + pp * pk.part_stride + j0, ta, nv);
-      ldv<EPL, VEC>(xh + pp * pk.part_stride + j0 + half, tc, nv);
+  if (on)  // further split-K slices, summed in order after the first, four per round trip
+    for (int p0 = 1; p0 < pk.parts; p0 += 4) {
+      float ta[4][EPL], tc[4][EPL];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) { a[e] += ta[e]; c[e] += tc[e]; }
+      for (int q = 0; q < 4; ++q) {
+        const int64_t off = (int64_t)min(p0 + q, pk.parts - 1) * pk.part_stride;  // past the last: re-read it
+        ldv<EPL, VEC>(xh + off + j0, ta[q], nv);
+        ldv<EPL, VEC>(xh + off + j0 + half, tc[q], nv);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (p0 + q < pk.parts)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) { a[e] += ta[q][e]; c[e] += tc[q][e]; }
     }
   float ss = 0.f;
 #pragma unroll
