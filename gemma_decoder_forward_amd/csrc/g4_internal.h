@@ -162,7 +162,10 @@ struct AttnArgs {
 
 // Cache row of key position j, and the last key a query at position i can see in the cache.
 __device__ __forceinline__ int64_t kv_row(int64_t j, int64_t cap, int32_t ring) {
-  return ring ? (int64_t)((uint64_t)j % (uint64_t)cap) : j;
+  if (!ring) return j;
+  // positions and capacities below 2^32 (every real cache) take the much shorter 32-bit remainder
+  if (((uint64_t)j | (uint64_t)cap) >> 32) return (int64_t)((uint64_t)j % (uint64_t)cap);
+  return (int64_t)((uint32_t)j % (uint32_t)cap);
 }
 __device__ __forceinline__ int64_t kv_last(int64_t i, int64_t cap, int32_t ring) {
   return ring || i < cap - 1 ? i : cap - 1;

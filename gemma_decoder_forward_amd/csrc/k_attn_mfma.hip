@@ -4,8 +4,8 @@
 // Block = 4 waves. A "query group" is one head x 32 consecutive tokens; each wave owns one, and the
 // block's four groups (the heads of one kv group for G = 4) share every K/V tile. For head dim 512 a
 // wave holds Q (32 x 512, 128 registers) and O (256 accumulation registers). Keys advance in tiles of
-// 32 staged in LDS, double buffered: the next tile's rows are loaded straight into LDS (buffer_load ...
-// lds, one instruction per row) while the current tile is multiplied.
+// 32 staged in an LDS ring of two or four stages: later tiles' rows are loaded straight into LDS
+// (buffer_load ... lds, one instruction per row) while the current tile is multiplied.
 //   * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: A = K rows from LDS,
 //     B = the wave's Q held in registers for the whole key loop;
 //   * lane l then holds query (l % 32) and 16 of the tile's keys: 8*(j/4) + 4*(l/32) + j%4 for
@@ -60,13 +60,23 @@ __device__ __forceinline__ void at_dma16(const at_rsrc& r, uint32_t voff, uint32
   asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" : : "v"(voff), "s"(r), "s"(soff), "{m0}"(m0) : "memory");
 }
 
+// K/V stages in the LDS ring: the loads of a tile are issued NS - 1 tiles ahead of its use. A tile of
+// 32 keys at head dim 256 or less is a short stretch of matrix work, shorter than a trip to memory, so
+// those dims keep four stages in flight (137 KB of LDS at 256); head dim 512 fits two (134 KB).
+template <int HD> struct AttnStages { static constexpr int NS = HD == 512 ? 2 : 4; };
+
+#define G4_ATT_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+
 template <int HD>
 __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float sl2, int split_from) {
   using L = AttnLds<HD>;
   constexpr int NB = HD / 32;      // O blocks per wave
   constexpr int KS = HD / 16;      // MFMA k-steps for S
   constexpr int QG = 4;            // query groups per block
-  __shared__ __attribute__((aligned(16))) bf16 lds[2 * L::STAGE];
+  constexpr int NS = AttnStages<HD>::NS;
+  constexpr int LPT = 2 * (AT_KB / 4);  // direct-to-LDS load instructions per wave per tile (K and V rows)
+  static_assert((NS - 2) * LPT <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) bf16 lds[NS * L::STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
@@ -126,6 +136,11 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
       qf[s] = *(bf16x8_t*)&v;
     }
   }
+  // Q has landed before the first tile load is issued. The compiler does not see the direct-to-LDS
+  // loads (inline assembly); left to itself it would wait for Q at its first use inside the key loop
+  // with a full memory wait, which also waits out the tiles in flight, on every step.
+#pragma unroll
+  for (int s = 0; s < KS; ++s) asm volatile("" : : "v"(qf[s]));
 
   const bf16* Kb = (const bf16*)a.k + (b * a.nkv + g) * a.cap * HD;
   const bf16* Vb = (const bf16*)a.v + (b * a.nkv + g) * a.cap * HD;
@@ -133,17 +148,26 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
   // clamp to its last row (they are masked); V rows whose keys lie outside [lob, hib] are zeroed after
   // they land (a masked probability times a stale value must stay zero, not NaN).
   const at_rsrc rks = at_make_rsrc(Kb, a.cap * HD * 2), rvs = at_make_rsrc(Vb, a.cap * HD * 2);
-  auto dma = [&](int it, int buf) {
+  // Tile it into ring slot it % NS. A tile past the block's range (the ring keeps issuing one tile per
+  // step) gets a scalar offset beyond the buffer, which the range check turns into zeros without moving
+  // data, so every step keeps the same number of loads in flight and the waits below stay exact.
+  auto dma = [&](int it) {
     const int64_t k0 = kstart + (int64_t)it * AT_KB;
-    const uint32_t kb0 = (uint32_t)(uintptr_t)(at_lds_void*)(lds + buf * L::STAGE);
+    const bool live = it < it1;
+    const uint32_t kb0 = (uint32_t)(uintptr_t)(at_lds_void*)(lds + (it % NS) * L::STAGE);
     const uint32_t vb0 = kb0 + L::KSZ * 2;
     const int wv = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform: offsets and M0 live in SGPRs
+    // cache row of this wave's first key (one remainder per tile); the next rows follow it, wrapping once
+    const int64_t kb = k0 + (AT_KB / 4) * wv;
+    const int64_t rb = kv_row(kb, a.cap, a.ring);
 #pragma unroll
     for (int r = 0; r < AT_KB / 4; ++r) {
       const int row = (AT_KB / 4) * wv + r;
-      int64_t key = k0 + row;
-      if (!a.ring && key > a.cap - 1) key = a.cap - 1;
-      const uint32_t src = __builtin_amdgcn_readfirstlane((uint32_t)(kv_row(key, a.cap, a.ring) * HD * 2));
+      int64_t cr;
+      if (!a.ring) cr = kb + r > a.cap - 1 ? a.cap - 1 : kb + r;  // keys past the cache clamp to its last row
+      else if (a.cap >= AT_KB / 4) cr = rb + r >= a.cap ? rb + r - a.cap : rb + r;
+      else cr = kv_row(kb + r, a.cap, a.ring);
+      const uint32_t src = live ? __builtin_amdgcn_readfirstlane((uint32_t)(cr * HD * 2)) : 0x80000000u;
       if (lane < HD / 8) {  // a row is HD / 8 lanes of 16 bytes
         at_dma16(rks, (uint32_t)lane * 16, src, kb0 + (uint32_t)(row * L::KLD * 2));
         at_dma16(rvs, (uint32_t)lane * 16, src, vb0 + (uint32_t)(row * L::VROW * 2));
@@ -172,17 +196,18 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
   float m_run = -INFINITY, l_run = 0.f;
 
   if (it1 > it0) {
-    dma(it0, it0 & 1);
-    __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j) dma(it0 + j);
+    G4_ATT_WAIT_VMCNT((NS - 2) * LPT);  // tile it0 landed
     __syncthreads();
     if (edge_tile(it0)) {
-      vclean(it0, it0 & 1);
+      vclean(it0, it0 % NS);
       __syncthreads();
     }
   }
   for (int it = it0; it < it1; ++it) {
-    const int cur = it & 1;
-    if (it + 1 < it1) dma(it + 1, cur ^ 1);
+    const int cur = it % NS;
+    dma(it + NS - 1);  // into the slot read in the previous step, which every wave has left
     const bf16* ks = lds + cur * L::STAGE;
     const bf16* vs = ks + L::KSZ;
     const int64_t k0 = kstart + (int64_t)it * AT_KB;
@@ -274,10 +299,10 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
           o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[st], o[d], 0, 0, 0);
         }
       }
-      __builtin_amdgcn_s_waitcnt(0);  // the next tile's direct-to-LDS loads
+      G4_ATT_WAIT_VMCNT((NS - 2) * LPT);  // tile it + 1 landed; later tiles may still be in flight
       __syncthreads();
       if (it + 1 < it1 && edge_tile(it + 1)) {
-        vclean(it + 1, cur ^ 1);
+        vclean(it + 1, (it + 1) % NS);
         __syncthreads();
       }
     }
@@ -313,6 +338,280 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
       pk.y = (uint32_t)f2bf(o[d][4 * r4 + 2] * il) | ((uint32_t)f2bf(o[d][4 * r4 + 3] * il) << 16);
       *(uint2*)(orow + hd0) = pk;
     }
+}
+
+// --------------------------------------------------------------------------------------------
+// The same attention with 16-query waves on v_mfma_f32_16x16x32_bf16, eight waves per block.
+//
+// A query group (head x 32 tokens) is split between two waves of 16 queries each, so a wave holds Q
+// (16 x HD: HD / 8 registers) and O (HD / 4 accumulation registers) -- for head dim 512, 64 and 128
+// instead of 128 and 256 -- and two waves fit on each SIMD: one wave's LDS reads, softmax and tile
+// bookkeeping run while the other's matrix instructions execute. The block covers the same four
+// query groups, key tiles and work items as k_attn_mfma (same grid and scratch layout), so every K/V
+// tile staged in LDS still feeds 128 query rows.
+//   * S^T = K Q^T in 16x16 blocks: A = 16 keys x 32 head elements of K from LDS, B = the wave's Q in
+//     registers. Lane l holds query l % 16 and, per key block kb, keys 16 kb + 4 (l / 16) + 0..3.
+//   * O^T += V^T P^T: the B operand's 32 k-slots of lane group q = l / 16 are keys {4q + 0..3,
+//     16 + 4q + 0..3}, exactly the lane's eight probabilities; the A operand reads V^T at those keys
+//     with two LDS transpose reads (four consecutive key rows of 16 head elements each).
+//   * A query's 32 scores of a tile sit in the four lanes l % 16 + 16j: its maximum takes two
+//     cross-lane steps; the normaliser is summed per lane and across the four lanes at the end.
+// --------------------------------------------------------------------------------------------
+template <int HD>
+__global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl2, int split_from) {
+  using L = AttnLds<HD>;
+  typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+  constexpr int NO = HD / 16;      // O blocks (16 head elements each) per wave
+  constexpr int KS = HD / 32;      // k-steps of S (32 head elements each)
+  constexpr int QG = 4;            // query groups per block, two waves each
+  constexpr int NS = AttnStages<HD>::NS;
+  constexpr int RPW = AT_KB / 8;   // tile rows staged by each wave
+  constexpr int LPT = 2 * RPW;     // direct-to-LDS load instructions per wave per tile (K and V rows)
+  static_assert((NS - 2) * LPT <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) bf16 lds[NS * L::STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ql = lane & 15, qq = lane >> 4;  // query of the lane within the wave; lane group
+  const int nruns = (int)((a.T + 31) / 32);
+  const int ngroups = nruns * G;
+  const int nblk = (ngroups + QG - 1) / QG;
+  const int nsplit = nblk - split_from;
+  const int v = (int)blockIdx.x;
+  const int blk = v < 2 * nsplit ? nblk - 1 - v / 2 : nblk - 1 - nsplit - (v - 2 * nsplit);
+  const int part = v < 2 * nsplit ? (v & 1) : 0, nparts = v < 2 * nsplit ? 2 : 1;
+  const int gi = blk * QG + (wave >> 1);
+  const int64_t g = blockIdx.y, b = blockIdx.z;
+  const int run = gi / G;
+  const int64_t head = g * G + gi % G;
+  const int64_t tq0 = (int64_t)run * 32 + 16 * (wave & 1);  // the wave's first query token
+  const int64_t tq = tq0 + ql;                                // this lane's query token
+  const int64_t p0 = a.pos0[b];
+  const bool qvalid = gi < ngroups && tq < a.T;
+  const int64_t qi = p0 + tq;
+
+  // block key range (union over its groups), as in k_attn_mfma
+  const int g_first = blk * QG, g_last = (blk * QG + QG - 1) < ngroups - 1 ? blk * QG + QG - 1 : ngroups - 1;
+  int64_t tlast = (int64_t)(g_last / G) * 32 + 31;
+  if (tlast > a.T - 1) tlast = a.T - 1;
+  const int64_t imin = p0 + (int64_t)(g_first / G) * 32, imax = p0 + tlast;
+  int64_t lob = a.sliding ? imin - a.window + 1 : 0;
+  if (lob < 0) lob = 0;
+  const int64_t hib = kv_last(imax, a.cap, a.ring);
+  const int64_t kstart = lob & ~(int64_t)(AT_KB - 1);
+  const int ntiles = hib >= lob ? (int)((hib - kstart) / AT_KB + 1) : 0;
+  const int half_tiles = (ntiles + 1) / 2;
+  const int it0 = nparts == 2 && part == 1 ? half_tiles : 0;
+  const int it1 = nparts == 2 && part == 0 ? half_tiles : ntiles;
+  int64_t qlo = a.sliding ? qi - a.window + 1 : 0;
+  if (qlo < 0) qlo = 0;
+  const int64_t qhi = qi < hib ? qi : hib;
+  // the lane's visible keys relative to the first tile, in 32 bits (none for an invalid query)
+  const int vlo = qvalid ? (int)(qlo - kstart) : 0x7fffffff, vhi = qvalid ? (int)(qhi - kstart) : -1;
+  // keys visible to every query of the wave (empty when some query of the wave is invalid)
+  int64_t wlo_all, whi_all;
+  {
+    const int64_t first = p0 + tq0, last = p0 + tq0 + 15;
+    wlo_all = a.sliding ? last - a.window + 1 : 0;
+    if (wlo_all < lob) wlo_all = lob;
+    whi_all = first < hib ? first : hib;
+    if (!(gi < ngroups && tq0 + 15 < a.T)) { wlo_all = 1; whi_all = 0; }
+  }
+
+  // Q fragments (B operand of S^T): query ql, head elements 32 s + 8 qq .. +7
+  bf16x8_t qf[KS];
+  {
+    const bf16* qrow = (const bf16*)a.q + (b * a.T + (qvalid ? tq : 0)) * a.q_ld + (qvalid ? head : 0) * HD + 8 * qq;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      uint4 u = qvalid ? *(const uint4*)(qrow + 32 * s) : make_uint4(0, 0, 0, 0);
+      qf[s] = *(bf16x8_t*)&u;
+    }
+  }
+  // Q lands before the first tile load (see k_attn_mfma)
+#pragma unroll
+  for (int s = 0; s < KS; ++s) asm volatile("" : : "v"(qf[s]));
+
+  const bf16* Kb = (const bf16*)a.k + (b * a.nkv + g) * a.cap * HD;
+  const bf16* Vb = (const bf16*)a.v + (b * a.nkv + g) * a.cap * HD;
+  const at_rsrc rks = at_make_rsrc(Kb, a.cap * HD * 2), rvs = at_make_rsrc(Vb, a.cap * HD * 2);
+  // Tile it into ring slot it % NS; rows RPW w .. RPW w + RPW - 1 from wave w (see k_attn_mfma for the
+  // out-of-range tiles and the clamped rows).
+  auto dma = [&](int it) {
+    const int64_t k0 = kstart + (int64_t)it * AT_KB;
+    const bool live = it < it1;
+    const uint32_t kb0 = (uint32_t)(uintptr_t)(at_lds_void*)(lds + (it % NS) * L::STAGE);
+    const uint32_t vb0 = kb0 + L::KSZ * 2;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int64_t kb = k0 + RPW * wv;
+    const int64_t rb = kv_row(kb, a.cap, a.ring);
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int row = RPW * wv + r;
+      int64_t cr;
+      if (!a.ring) cr = kb + r > a.cap - 1 ? a.cap - 1 : kb + r;
+      else if (a.cap >= RPW) cr = rb + r >= a.cap ? rb + r - a.cap : rb + r;
+      else cr = kv_row(kb + r, a.cap, a.ring);
+      const uint32_t src = live ? __builtin_amdgcn_readfirstlane((uint32_t)(cr * HD * 2)) : 0x80000000u;
+      if (lane < HD / 8) {
+        at_dma16(rks, (uint32_t)lane * 16, src, kb0 + (uint32_t)(row * L::KLD * 2));
+        at_dma16(rvs, (uint32_t)lane * 16, src, vb0 + (uint32_t)(row * L::VROW * 2));
+      }
+    }
+  };
+  auto edge_tile = [&](int it) {
+    const int64_t k0 = kstart + (int64_t)it * AT_KB;
+    return !(k0 >= lob && k0 + AT_KB - 1 <= hib);
+  };
+  auto vclean = [&](int it, int buf) {
+    const int64_t k0 = kstart + (int64_t)it * AT_KB;
+    bf16* vs = lds + buf * L::STAGE + L::KSZ;
+    for (int u = tid; u < AT_KB * (HD / 8); u += 512) {
+      const int row = u / (HD / 8);
+      const int64_t key = k0 + row;
+      if (key < lob || key > hib) *(uint4*)(vs + row * L::VROW + 8 * (u % (HD / 8))) = make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  f32x4_t o[NO];
+#pragma unroll
+  for (int d = 0; d < NO; ++d) o[d] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  if (it1 > it0) {
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j) dma(it0 + j);
+    G4_ATT_WAIT_VMCNT((NS - 2) * LPT);
+    __syncthreads();
+    if (edge_tile(it0)) {
+      vclean(it0, it0 % NS);
+      __syncthreads();
+    }
+  }
+  // operand addresses within a stage (bf16 elements)
+  const int kfo = ql * L::KLD + 8 * qq;                                   // K: key row ql, chunk qq
+  const int vfo = (4 * qq + (ql >> 2)) * L::VROW + 4 * (ql & 3);          // V^T: rows 4qq + ql/4
+  for (int it = it0; it < it1; ++it) {
+    const int cur = it % NS;
+    dma(it + NS - 1);
+    const bf16* ks = lds + cur * L::STAGE;
+    const bf16* vs = ks + L::KSZ;
+    const int64_t k0 = kstart + (int64_t)it * AT_KB;
+    // S^T for key blocks 0 and 1 (two independent accumulation chains). K fragments are read PK steps
+    // ahead in a rolling window (pinned by scheduling barriers: hoisted further, the reads would need
+    // more registers than two waves per SIMD leave); the SIMD's other wave covers the rest of the
+    // read latency.
+    constexpr int PK = 2;
+    f32x4_t s0 = (f32x4_t){0.f, 0.f, 0.f, 0.f}, s1 = s0;
+    bf16x8_t kw0[PK], kw1[PK];
+#pragma unroll
+    for (int j = 0; j < PK; ++j) {
+      kw0[j] = *(const bf16x8_t*)(ks + kfo + 32 * j);
+      kw1[j] = *(const bf16x8_t*)(ks + kfo + 16 * L::KLD + 32 * j);
+    }
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kw0[st % PK], qf[st], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kw1[st % PK], qf[st], s1, 0, 0, 0);
+      if (st + PK < KS) {
+        kw0[st % PK] = *(const bf16x8_t*)(ks + kfo + 32 * (st + PK));
+        kw1[st % PK] = *(const bf16x8_t*)(ks + kfo + 16 * L::KLD + 32 * (st + PK));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    float sc[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { sc[i] = s0[i]; sc[4 + i] = s1[i]; }
+    float mt = -INFINITY;
+    if (k0 >= wlo_all && k0 + AT_KB - 1 <= whi_all) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        sc[r] *= sl2;
+        mt = fmaxf(mt, sc[r]);
+      }
+    } else {
+      const int kt = it * AT_KB;  // the tile's first key relative to kstart
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int kk = kt + 16 * (r >> 2) + 4 * qq + (r & 3);
+        const bool vis = kk >= vlo && kk <= vhi;
+        const float x = vis ? sc[r] * sl2 : -INFINITY;
+        sc[r] = x;
+        mt = fmaxf(mt, x);
+      }
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    // lazy reference, as in k_attn_mfma: raised only when the tile exceeds it by more than 32 (log2)
+    const bool raise = mt > m_run + 32.f;
+    const float m_new = raise ? mt : m_run;
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    float psum = 0.f;
+    bf16x8_t pb;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const float pr = __builtin_amdgcn_exp2f(sc[r] - m_use);
+      psum += pr;
+      pb[r] = (__bf16)pr;
+    }
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < NO; ++d) o[d] *= alpha;
+    }
+    l_run += psum;
+    m_run = m_new;
+    // O^T += V^T P^T, 16 head elements per MFMA; V^T fragments read PV blocks ahead
+    constexpr int PV = 4;
+    auto vread = [&](int d) {
+      const bf16* va = vs + vfo + 16 * d;
+      const bf16x4_t lo = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((at_lds_v4s*)(at_lds_void*)va));
+      const bf16x4_t hi = __builtin_bit_cast(
+          bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((at_lds_v4s*)(at_lds_void*)(va + 16 * L::VROW)));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    bf16x8_t vw[PV];
+#pragma unroll
+    for (int j = 0; j < PV; ++j) vw[j] = vread(j);
+#pragma unroll
+    for (int d = 0; d < NO; ++d) {
+      o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vw[d % PV], pb, o[d], 0, 0, 0);
+      if (d + PV < NO) vw[d % PV] = vread(d + PV);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    G4_ATT_WAIT_VMCNT((NS - 2) * LPT);  // tile it + 1 landed
+    __syncthreads();
+    if (it + 1 < it1 && edge_tile(it + 1)) {
+      vclean(it + 1, (it + 1) % NS);
+      __syncthreads();
+    }
+  }
+
+  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  if (!qvalid) return;
+  // lane holds head elements 16 d + 4 qq + 0..3 of query tq
+  if (nparts == 2) {
+    const int64_t row = ((part * a.B + b) * a.T + tq) * a.nh + head;
+    float* po = a.ws + row * HD;
+#pragma unroll
+    for (int d = 0; d < NO; ++d) *(float4*)(po + 16 * d + 4 * qq) = make_float4(o[d][0], o[d][1], o[d][2], o[d][3]);
+    if (qq == 0) {
+      float* ml = a.ws + 2 * a.B * a.T * a.nh * HD + 2 * row;
+      ml[0] = m_run;
+      ml[1] = l_tot;
+    }
+    return;
+  }
+  const float il = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  bf16* orow = (bf16*)a.out + (b * a.T + tq) * a.out_ld + head * HD;
+#pragma unroll
+  for (int d = 0; d < NO; ++d) {
+    uint2 pk;
+    pk.x = (uint32_t)f2bf(o[d][0] * il) | ((uint32_t)f2bf(o[d][1] * il) << 16);
+    pk.y = (uint32_t)f2bf(o[d][2] * il) | ((uint32_t)f2bf(o[d][3] * il) << 16);
+    *(uint2*)(orow + 16 * d + 4 * qq) = pk;
+  }
 }
 
 // Merges the two key-half partials of each split query row: O = (O0 2^(m0-m) + O1 2^(m1-m)) /
@@ -388,7 +687,7 @@ bool attn_mfma(const AttnArgs& a, hipStream_t s, g4_status* st) {
   const float sl2 = a.scale * 1.4426950408889634f;
   if (a.hd == 128) hipLaunchKernelGGL((k_attn_mfma<128>), grid, dim3(256), 0, s, a, (int)G, sl2, split_from);
   else if (a.hd == 256) hipLaunchKernelGGL((k_attn_mfma<256>), grid, dim3(256), 0, s, a, (int)G, sl2, split_from);
-  else hipLaunchKernelGGL((k_attn_mfma<512>), grid, dim3(256), 0, s, a, (int)G, sl2, split_from);
+  else hipLaunchKernelGGL((k_attn_w16<512>), grid, dim3(512), 0, s, a, (int)G, sl2, split_from);
   if ((*st = check_launch("attn_mfma")) != G4_OK || split_from == nblk || tq_lo >= a.T) return true;
   dim3 gm((unsigned)(a.T - tq_lo), (unsigned)a.nh, (unsigned)a.B);
   if (a.hd == 128) hipLaunchKernelGGL((k_attn_merge_split<128>), gm, dim3(64), 0, s, a, tq_lo);

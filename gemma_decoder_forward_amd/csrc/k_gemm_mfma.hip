@@ -269,8 +269,20 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a, int tiles_
           }
         }
       } else {
+        // GELU_MUL factors, JC column blocks at a time, loaded before the first store of those blocks
+        // (which could alias them as far as the compiler knows, and would otherwise hold each load back
+        // behind the store before it)
+        constexpr int JC = FN <= 2 ? FN : 2;
+        float4 xs[EPI == EPI_GELU_MUL ? JC : 1][4];
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
+          if (EPI == EPI_GELU_MUL && j % JC == 0)
+#pragma unroll
+            for (int jj = 0; jj < JC; ++jj)
+#pragma unroll
+              for (int g = 0; g < 4; ++g)
+                xs[EPI == EPI_GELU_MUL ? jj : 0][g] =
+                    *(const float4*)(a.aux + m * a.aux_ld + n0 + wn * WN + (j + jj) * 32 + 8 * g + en);
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int64_t n = n0 + wn * WN + j * 32 + 8 * g + en;
@@ -278,7 +290,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a, int tiles_
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
             if (EPI == EPI_GELU_MUL) {
-              const float4 x = *(const float4*)(a.aux + m * a.aux_ld + n);
+              const float4 x = xs[EPI == EPI_GELU_MUL ? j % JC : 0][g];
               v[0] = gelu_tanh(v[0]) * x.x; v[1] = gelu_tanh(v[1]) * x.y;
               v[2] = gelu_tanh(v[2]) * x.z; v[3] = gelu_tanh(v[3]) * x.w;
               *(uint2*)((bf16*)a.C + m * a.ldc + n) = pack_bf16x4(v);
