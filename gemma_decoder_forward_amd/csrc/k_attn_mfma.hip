@@ -686,7 +686,7 @@ bool attn_mfma(const AttnArgs& a, hipStream_t s, g4_status* st) {
   dim3 grid((unsigned)(2 * (nblk - split_from) + split_from), (unsigned)a.nkv, (unsigned)a.B);
   const float sl2 = a.scale * 1.4426950408889634f;
   if (a.hd == 128) hipLaunchKernelGGL((k_attn_mfma<128>), grid, dim3(256), 0, s, a, (int)G, sl2, split_from);
-  else if (a.hd == 256) hipLaunchKernelGGL((k_attn_mfma<256>), grid, dim3(256), 0, s, a, (int)G, sl2, split_from);
+  else if (a.hd == 256) hipLaunchKernelGGL((k_attn_w16<256>), grid, dim3(512), 0, s, a, (int)G, sl2, split_from);
   else hipLaunchKernelGGL((k_attn_w16<512>), grid, dim3(512), 0, s, a, (int)G, sl2, split_from);
   if ((*st = check_launch("attn_mfma")) != G4_OK || split_from == nblk || tq_lo >= a.T) return true;
   dim3 gm((unsigned)(a.T - tq_lo), (unsigned)a.nh, (unsigned)a.B);
