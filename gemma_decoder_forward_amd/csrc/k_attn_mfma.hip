@@ -167,10 +167,13 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
       if (!a.ring) cr = kb + r > a.cap - 1 ? a.cap - 1 : kb + r;  // keys past the cache clamp to its last row
       else if (a.cap >= AT_KB / 4) cr = rb + r >= a.cap ? rb + r - a.cap : rb + r;
       else cr = kv_row(kb + r, a.cap, a.ring);
-      const uint32_t src = live ? __builtin_amdgcn_readfirstlane((uint32_t)(cr * HD * 2)) : 0x80000000u;
+      // the row's byte offset in the per-lane offset: no scalar register written by a vector
+      // instruction feeds the load (the compiler's hazard checks do not see into the assembly)
+      const uint32_t voff = (uint32_t)(cr * HD * 2) + (uint32_t)lane * 16;
+      const uint32_t oob = live ? 0u : 0x80000000u;
       if (lane < HD / 8) {  // a row is HD / 8 lanes of 16 bytes
-        at_dma16(rks, (uint32_t)lane * 16, src, kb0 + (uint32_t)(row * L::KLD * 2));
-        at_dma16(rvs, (uint32_t)lane * 16, src, vb0 + (uint32_t)(row * L::VROW * 2));
+        at_dma16(rks, voff, oob, kb0 + (uint32_t)(row * L::KLD * 2));
+        at_dma16(rvs, voff, oob, vb0 + (uint32_t)(row * L::VROW * 2));
       }
     }
   };
@@ -416,6 +419,9 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl
     whi_all = first < hib ? first : hib;
     if (!(gi < ngroups && tq0 + 15 < a.T)) { wlo_all = 1; whi_all = 0; }
   }
+  // per-tile range tests in 32 bits, relative to the first tile's first key
+  const int lob_r = (int)(lob - kstart), hib_r = (int)(hib - kstart);
+  const int wlo_r = (int)(wlo_all - kstart), whi_r = wlo_all > whi_all ? -1 : (int)(whi_all - kstart);
 
   // Q fragments (B operand of S^T): query ql, head elements 32 s + 8 qq .. +7
   bf16x8_t qf[KS];
@@ -436,39 +442,45 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl
   const at_rsrc rks = at_make_rsrc(Kb, a.cap * HD * 2), rvs = at_make_rsrc(Vb, a.cap * HD * 2);
   // Tile it into ring slot it % NS; rows RPW w .. RPW w + RPW - 1 from wave w (see k_attn_mfma for the
   // out-of-range tiles and the clamped rows).
+  // Cache rows in 32 bits: the byte offsets of a cache fit the 31-bit buffer range (the descriptor's
+  // size saturates there), so every row index that reaches a load does too.
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int cap32 = (int)a.cap;
+  const uint32_t lds_k = (uint32_t)(uintptr_t)(at_lds_void*)lds + (uint32_t)(RPW * wv * L::KLD * 2);
+  const uint32_t lds_v = (uint32_t)(uintptr_t)(at_lds_void*)lds + L::KSZ * 2 + (uint32_t)(RPW * wv * L::VROW * 2);
   auto dma = [&](int it) {
-    const int64_t k0 = kstart + (int64_t)it * AT_KB;
     const bool live = it < it1;
-    const uint32_t kb0 = (uint32_t)(uintptr_t)(at_lds_void*)(lds + (it % NS) * L::STAGE);
-    const uint32_t vb0 = kb0 + L::KSZ * 2;
-    const int wv = __builtin_amdgcn_readfirstlane(wave);
-    const int64_t kb = k0 + RPW * wv;
-    const int64_t rb = kv_row(kb, a.cap, a.ring);
+    const uint32_t so = (uint32_t)(it % NS) * L::STAGE * 2;
+    const int64_t kb = kstart + (int64_t)it * AT_KB + RPW * wv;  // the wave's first key of the tile
+    const int rb = a.ring ? (int)kv_row(kb, a.cap, a.ring) : (int)(kb < a.cap ? kb : a.cap - 1);
+    // The row's byte offset rides in the per-lane offset, so no scalar register written by a vector
+    // instruction feeds the load (the compiler's hazard checks do not see into the assembly); the
+    // scalar offset only marks a tile past the range.
+    const uint32_t oob = live ? 0u : 0x80000000u;
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
-      const int row = RPW * wv + r;
-      int64_t cr;
-      if (!a.ring) cr = kb + r > a.cap - 1 ? a.cap - 1 : kb + r;
-      else if (a.cap >= RPW) cr = rb + r >= a.cap ? rb + r - a.cap : rb + r;
-      else cr = kv_row(kb + r, a.cap, a.ring);
-      const uint32_t src = live ? __builtin_amdgcn_readfirstlane((uint32_t)(cr * HD * 2)) : 0x80000000u;
+      int cr;
+      if (!a.ring) cr = rb + r < cap32 - 1 ? rb + r : cap32 - 1;  // keys past the cache clamp to its last row
+      else if (cap32 >= RPW) cr = rb + r >= cap32 ? rb + r - cap32 : rb + r;
+      else cr = (int)kv_row(kb + r, a.cap, a.ring);
+      const uint32_t voff = (uint32_t)cr * (HD * 2) + (uint32_t)lane * 16;
       if (lane < HD / 8) {
-        at_dma16(rks, (uint32_t)lane * 16, src, kb0 + (uint32_t)(row * L::KLD * 2));
-        at_dma16(rvs, (uint32_t)lane * 16, src, vb0 + (uint32_t)(row * L::VROW * 2));
+        at_dma16(rks, voff, oob, lds_k + so + (uint32_t)(r * L::KLD * 2));
+        at_dma16(rvs, voff, oob, lds_v + so + (uint32_t)(r * L::VROW * 2));
       }
     }
   };
   auto edge_tile = [&](int it) {
-    const int64_t k0 = kstart + (int64_t)it * AT_KB;
-    return !(k0 >= lob && k0 + AT_KB - 1 <= hib);
+    const int kt = it * AT_KB;
+    return !(kt >= lob_r && kt + AT_KB - 1 <= hib_r);
   };
   auto vclean = [&](int it, int buf) {
-    const int64_t k0 = kstart + (int64_t)it * AT_KB;
+    const int kt = it * AT_KB;
     bf16* vs = lds + buf * L::STAGE + L::KSZ;
     for (int u = tid; u < AT_KB * (HD / 8); u += 512) {
       const int row = u / (HD / 8);
-      const int64_t key = k0 + row;
-      if (key < lob || key > hib) *(uint4*)(vs + row * L::VROW + 8 * (u % (HD / 8))) = make_uint4(0, 0, 0, 0);
+      const int key = kt + row;
+      if (key < lob_r || key > hib_r) *(uint4*)(vs + row * L::VROW + 8 * (u % (HD / 8))) = make_uint4(0, 0, 0, 0);
     }
   };
 
@@ -495,7 +507,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl
     dma(it + NS - 1);
     const bf16* ks = lds + cur * L::STAGE;
     const bf16* vs = ks + L::KSZ;
-    const int64_t k0 = kstart + (int64_t)it * AT_KB;
+    const int kt = it * AT_KB;  // the tile's first key relative to kstart
     // S^T for key blocks 0 and 1 (two independent accumulation chains). K fragments are read PK steps
     // ahead in a rolling window (pinned by scheduling barriers: hoisted further, the reads would need
     // more registers than two waves per SIMD leave); the SIMD's other wave covers the rest of the
@@ -522,14 +534,13 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl
 #pragma unroll
     for (int i = 0; i < 4; ++i) { sc[i] = s0[i]; sc[4 + i] = s1[i]; }
     float mt = -INFINITY;
-    if (k0 >= wlo_all && k0 + AT_KB - 1 <= whi_all) {
+    if (kt >= wlo_r && kt + AT_KB - 1 <= whi_r) {
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         sc[r] *= sl2;
         mt = fmaxf(mt, sc[r]);
       }
     } else {
-      const int kt = it * AT_KB;  // the tile's first key relative to kstart
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         const int kk = kt + 16 * (r >> 2) + 4 * qq + (r & 3);
