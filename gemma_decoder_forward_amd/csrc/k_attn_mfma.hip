@@ -63,6 +63,16 @@ __device__ __forceinline__ void at_dma16(const at_rsrc& r, uint32_t voff, uint32
 // K/V stages in the LDS ring: the loads of a tile are issued NS - 1 tiles ahead of its use. A tile of
 // 32 keys at head dim 256 or less is a short stretch of matrix work, shorter than a trip to memory, so
 // those dims keep four stages in flight (137 KB of LDS at 256); head dim 512 fits two (134 KB).
+// The 16-query kernel's staging: K rows padded by 32 bytes (see k_attn_w16), V rows as above.
+template <int HD>
+struct AttnLdsW {
+  static constexpr int KLD = HD + 16;
+  static constexpr int VROW = HD + 16;
+  static constexpr int KSZ = AT_KB * KLD;
+  static constexpr int VSZ = AT_KB * VROW;
+  static constexpr int STAGE = KSZ + VSZ;
+};
+
 template <int HD> struct AttnStages { static constexpr int NS = HD == 512 ? 2 : 4; };
 
 #define G4_ATT_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
@@ -353,7 +363,8 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
 // query groups, key tiles and work items as k_attn_mfma (same grid and scratch layout), so every K/V
 // tile staged in LDS still feeds 128 query rows.
 //   * S^T = K Q^T in 16x16 blocks: A = 16 keys x 32 head elements of K from LDS, B = the wave's Q in
-//     registers. Lane l holds query l % 16 and, per key block kb, keys 16 kb + 4 (l / 16) + 0..3.
+//     registers. K rows are padded by 32 bytes: the operand read (16 rows x four 16-byte chunks) is
+//     then free of bank conflicts (measured; a 16-byte pad made every such read a two-way conflict). Lane l holds query l % 16 and, per key block kb, keys 16 kb + 4 (l / 16) + 0..3.
 //   * O^T += V^T P^T: the B operand's 32 k-slots of lane group q = l / 16 are keys {4q + 0..3,
 //     16 + 4q + 0..3}, exactly the lane's eight probabilities; the A operand reads V^T at those keys
 //     with two LDS transpose reads (four consecutive key rows of 16 head elements each).
@@ -362,7 +373,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
 // --------------------------------------------------------------------------------------------
 template <int HD>
 __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl2, int split_from) {
-  using L = AttnLds<HD>;
+  using L = AttnLdsW<HD>;
   typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
   constexpr int NO = HD / 16;      // O blocks (16 head elements each) per wave
   constexpr int KS = HD / 32;      // k-steps of S (32 head elements each)
