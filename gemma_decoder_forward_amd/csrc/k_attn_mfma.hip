@@ -1,5 +1,7 @@
 // Flash-style prefill attention on the CDNA4 matrix cores (bf16 operands, float32 softmax and
 // accumulation), causal with an optional sliding window, GQA groups sharing every K/V tile.
+// Two kernels: k_attn_w16 (16-query waves, head dims 256 and 512, described before it) and
+// k_attn_mfma (32-query waves, head dim 128), described here.
 //
 // Block = 4 waves. A "query group" is one head x 32 consecutive tokens; each wave owns one, and the
 // block's four groups (the heads of one kv group for G = 4) share every K/V tile. For head dim 512 a
