@@ -306,6 +306,46 @@ def test_linear_few_rows_weight_streaming(M, N, K):
     assert_close(Cb, ref, "bf16", "bf16 out")
 
 
+def _sample_rows(M):
+    return sorted(set(list(range(24)) + list(range(M // 2 - 8, M // 2 + 8)) + list(range(M - 24, M))))
+
+
+def test_linear_bf16_e4b_gate_up_shape():
+    """M = 2048, N = 20480 (the E4B gate and up rows at T = 2048) with bf16 output: 640 big tiles, a
+    persistent grid walking several tiles per block; sampled rows over every column block."""
+    M, N, K = 2048, 20480, 256
+    log(f"linear bf16 {M}x{N}x{K}")
+    A = randn((M, K), 76, torch.bfloat16)
+    W = randn((N, K), 77, torch.bfloat16, 0.05)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    bd.g4_linear(A.data_ptr(), W.data_ptr(), C.data_ptr(), M, N, K, bd.G4_BF16, bd.G4_BF16, None, 0, stream())
+    torch.cuda.synchronize()
+    rows = _sample_rows(M)
+    ref = O.f64(A[rows]) @ O.f64(W).T
+    # every column block within the bf16 bound
+    for c0 in range(0, N, 2048):
+        assert_close(C[rows, c0:c0 + 2048], ref[:, c0:c0 + 2048], "bf16", f"columns {c0}..")
+
+
+def test_ffn_geglu_e4b_rows():
+    """E4B FFN (H 2560, F 10240) at T = 2048: the gate/up GEMM with its GEGLU epilogue, then down; sampled rows."""
+    M, H, F = 2048, 2560, 10240
+    log("ffn geglu E4B T=2048")
+    x = randn((M, H), 84, torch.bfloat16)
+    wg, wu = randn((F, H), 85, torch.bfloat16, 0.02), randn((F, H), 86, torch.bfloat16, 0.02)
+    wd = randn((H, F), 87, torch.bfloat16, 0.02)
+    out = torch.empty((M, H), dtype=torch.float32, device="cuda")
+    wsb = bd.g4_ffn_geglu_ws(M, H, F, bd.G4_BF16)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    bd.g4_ffn_geglu(x.data_ptr(), wg.data_ptr(), wu.data_ptr(), wd.data_ptr(), out.data_ptr(), M, H, F, ws.data_ptr(),
+                    wsb, bd.G4_BF16, stream())
+    torch.cuda.synchronize()
+    rows = _sample_rows(M)
+    xv = O.f64(x[rows])
+    ref = (O.gelu_tanh(xv @ O.f64(wg).T) * (xv @ O.f64(wu).T)) @ O.f64(wd).T
+    assert_close(out[rows], ref, "bf16", "ffn rows")
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_ffn_geglu_vs_oracle(dt):
     gdt, tdt = DT[dt]
