@@ -71,18 +71,28 @@ __global__ __launch_bounds__(256) void k_attn_dec_mfma(AttnArgs a, int chunk, in
   for (int64_t kt = k0; kt < k1; kt += 16) {
     const int64_t key = kt + col;
     const bool kv = key < k1;
+    // Every load of the step is issued before its first use: the K rows of the scores and the 16 V
+    // rows of P V (a key past the range reads the range's last row; its probability is exactly 0).
+    const bf16* kr = Kb + kv_row(kv ? key : kt, a.cap, a.ring) * HD + 8 * q4;
+    uint4 kw[NC][4];
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) kw[cc][t] = *(const uint4*)(kr + 128 * cc + 32 * t);
+    typedef __attribute__((ext_vector_type(EPL / 2))) uint32_t vraw_t;
+    vraw_t vw[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int64_t kj = kt + j < k1 ? kt + j : k1 - 1;
+      vw[j] = *(const vraw_t*)(Vb + kv_row(kj, a.cap, a.ring) * HD + lane * EPL);
+    }
     // scores S[head][key] for 16 keys
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-    const bf16* kr = Kb + kv_row(kv ? key : kt, a.cap, a.ring) * HD + 8 * q4;
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc) {
-      uint4 kw[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) kw[t] = *(const uint4*)(kr + 128 * cc + 32 * t);
+    for (int cc = 0; cc < NC; ++cc)
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[cc][t], *(bf16x8_t*)&kw[t], s, 0, 0, 0);
-    }
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[cc][t], *(bf16x8_t*)&kw[cc][t], s, 0, 0, 0);
     // lanes 0..15: s[h] = score of head h for key kt + col
     float p[DM_G];
 #pragma unroll
@@ -102,22 +112,13 @@ __global__ __launch_bounds__(256) void k_attn_dec_mfma(AttnArgs a, int chunk, in
       for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
     }
     // P V over the 16 keys
-    const int nkeys = (int)((k1 - kt) < 16 ? (k1 - kt) : 16);
-    for (int j = 0; j < nkeys; ++j) {
-      const bf16* vr = Vb + kv_row(kt + j, a.cap, a.ring) * HD + lane * EPL;
-      float vv[EPL];
-      if (EPL == 8) {
-        const uint4 w = *(const uint4*)vr;
-        const uint32_t* pw = (const uint32_t*)&w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { vv[2 * e] = __uint_as_float(pw[e] << 16); vv[2 * e + 1] = __uint_as_float(pw[e] & 0xffff0000u); }
-      } else if (EPL == 4) {
-        const uint2 w = *(const uint2*)vr;
-        vv[0] = __uint_as_float(w.x << 16); vv[1] = __uint_as_float(w.x & 0xffff0000u);
-        vv[2] = __uint_as_float(w.y << 16); vv[3] = __uint_as_float(w.y & 0xffff0000u);
-      } else {
-        const uint32_t w = *(const uint32_t*)vr;
-        vv[0] = __uint_as_float(w << 16); vv[1] = __uint_as_float(w & 0xffff0000u);
+    for (int j = 0; j < 16; ++j) {
+      float vv[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL / 2; ++e) {
+        vv[2 * e] = __uint_as_float(vw[j][e] << 16);
+        vv[2 * e + 1] = __uint_as_float(vw[j][e] & 0xffff0000u);
       }
 #pragma unroll
       for (int h = 0; h < DM_G; ++h) {
