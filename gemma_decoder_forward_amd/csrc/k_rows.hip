@@ -209,10 +209,11 @@ __device__ __forceinline__ float4 cvt4(Raw4<bf16> r) {
 
 // The same tail with one wave per row (four rows per block) for launches with many rows: the two
 // reductions are wave reductions with no block barrier, and the row's loads (the first split-K slice
-// and the residual) are all issued before the first wait, through row buffers. Further slices come four
-// per round trip and are added in slice order.
+// and the residual) are all issued before the first wait, through row buffers. Further slices come
+// one per round trip, added in slice order: a batch of slices held registers enough to cost a wave
+// per SIMD, and three waves per SIMD keep more rows in flight than the saved round trips.
 template <typename TX, typename T, int V>
-__global__ __launch_bounds__(256) void k_rownorm_w(const TX* __restrict__ x, int parts, int64_t part_stride,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(V <= 10 ? 3 : 1))) void k_rownorm_w(const TX* __restrict__ x, int parts, int64_t part_stride,
                                                    const T* __restrict__ w, T* __restrict__ y, float* __restrict__ res,
                                                    float res_scale, const T* __restrict__ w_next, T* __restrict__ y_next,
                                                    int64_t rows, int64_t dim, float eps) {
@@ -234,19 +235,13 @@ __global__ __launch_bounds__(256) void k_rownorm_w(const TX* __restrict__ x, int
   float4 v[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) v[i] = cvt4(xa[i]);
-  for (int p = 1; p < parts; p += 4) {
-    __amdgpu_buffer_rsrc_t rp[4];  // slices past the last read zero
+  for (int p = 1; p < parts; ++p) {
+    const auto rp = row_rsrc(xr + (int64_t)p * part_stride, xbytes);
+    Raw4<TX> t[V];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) rp[j] = row_rsrc(p + j < parts ? xr + (int64_t)(p + j) * part_stride : nullptr, xbytes);
-    Raw4<TX> t[4][V];
+    for (int i = 0; i < V; ++i) t[i] = braw4(rp, x, 4 * (lane + 64 * i));
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < V; ++i) t[j][i] = braw4(rp[j], x, 4 * (lane + 64 * i));
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < V; ++i) v[i] = v[i] + cvt4(t[j][i]);
+    for (int i = 0; i < V; ++i) v[i] = v[i] + cvt4(t[i]);
   }
   float ss = 0.f;
 #pragma unroll
