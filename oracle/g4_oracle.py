@@ -24,6 +24,10 @@ Readings where the pages are silent or disagree (each also listed in the design 
     shared layer with no such layer keeps its own K/V.
   * Window: query at position i sees keys i-W < j <= i.
   * Out-of-range token ids give a zero embedding row and a zero PLE table term.
+  * Variants: full layers may have their own KV head count; per-layer FFN widths follow the weight
+    shapes (page 2 `ffn_dim`); with K=V a full layer's V is the K projection output before the K norm
+    and RoPE, normed without scale (page 5 `forward_layer`). Page 2 instead clones the normed, rotated
+    K when a layer has no V projection; the page-5 reading is the one taken here.
 
 All arithmetic is numpy float64 on the given inputs (bf16 inputs are converted exactly).
 """
@@ -152,6 +156,23 @@ def layer_geometry(cfg, layer):
     return sliding, hd, theta, rotated_pairs(cfg, sliding)
 
 
+def kv_heads(cfg, layer):
+    """KV head count of a layer (page 5 `forward_layer`: full layers take `num_full_kv_heads`, sliding
+    layers `num_kv_heads`). A config without a separate full-layer count uses one count for both."""
+    if cfg["layer_types"][layer] == "S":
+        return cfg["n_kv_heads"]
+    return cfg.get("n_kv_heads_full") or cfg["n_kv_heads"]
+
+
+def value_weight(cfg, lw, layer):
+    """Weight whose projection gives V (page 5 `forward_layer`: a full layer of a model flagged
+    `attention_k_eq_v` projects V with the K projection's weight; V is then normed without scale and
+    never rotated, like any other V)."""
+    if cfg.get("k_eq_v") and cfg["layer_types"][layer] != "S":
+        return lw["wk"]
+    return lw["wv"]
+
+
 # --------------------------------------------------------------------------------------------
 # Attention (page 1 `attend_all_heads(..., 1.0, window, ...)`; page 4 `text_attention`)
 # --------------------------------------------------------------------------------------------
@@ -239,7 +260,7 @@ def layer_forward(cfg, lw, layer, src, h, ple_l, pos, caches, trace=None):
     intermediates.
     """
     eps = cfg["eps"]
-    nh, nkv = cfg["n_heads"], cfg["n_kv_heads"]
+    nh, nkv = cfg["n_heads"], kv_heads(cfg, layer)
     sliding, hd, theta, n_rot = layer_geometry(cfg, layer)
     inv = inv_freq(hd, theta, n_rot)
     h = f64(h).copy()
@@ -253,7 +274,7 @@ def layer_forward(cfg, lw, layer, src, h, ple_l, pos, caches, trace=None):
     if src == layer:
         k = (xn @ f64(lw["wk"]).T).reshape(B, T, nkv, hd)
         k = rope(rms_norm(k, lw["k_norm"], eps), pos[:, :, None], inv)
-        v = rms_norm((xn @ f64(lw["wv"]).T).reshape(B, T, nkv, hd), None, eps)
+        v = rms_norm((xn @ f64(value_weight(cfg, lw, layer)).T).reshape(B, T, nkv, hd), None, eps)
         K, V = caches[layer]
         for b in range(B):
             for t in range(T):
@@ -292,7 +313,7 @@ def layer_forward_rows(cfg, lw, layer, h, ple_l, pos0, rows):
     checked at a few rows. Same formulas as `layer_forward`, restricted to rows.
     """
     eps = cfg["eps"]
-    nh, nkv = cfg["n_heads"], cfg["n_kv_heads"]
+    nh, nkv = cfg["n_heads"], kv_heads(cfg, layer)
     sliding, hd, theta, n_rot = layer_geometry(cfg, layer)
     inv = inv_freq(hd, theta, n_rot)
     h = f64(h)
@@ -306,7 +327,7 @@ def layer_forward_rows(cfg, lw, layer, h, ple_l, pos0, rows):
     xk = rms_norm(h[need], lw["input_norm"], eps)
     pk = (pos0 + need)[:, None]
     k = rope(rms_norm((xk @ f64(lw["wk"]).T).reshape(len(need), nkv, hd), lw["k_norm"], eps), pk, inv)
-    v = rms_norm((xk @ f64(lw["wv"]).T).reshape(len(need), nkv, hd), None, eps)
+    v = rms_norm((xk @ f64(value_weight(cfg, lw, layer)).T).reshape(len(need), nkv, hd), None, eps)
     cap = pos0 + int(rows.max()) + 1
     K, V = np.zeros((nkv, cap, hd)), np.zeros((nkv, cap, hd))
     K[:, pos0 + need, :] = k.transpose(1, 0, 2)
@@ -335,7 +356,8 @@ def new_caches(cfg, B, cap, srcs=None):
     for l, s in enumerate(srcs):
         if s == l:
             _, hd, _, _ = layer_geometry(cfg, l)
-            out[l] = (np.zeros((B, cfg["n_kv_heads"], cap, hd)), np.zeros((B, cfg["n_kv_heads"], cap, hd)))
+            nkv = kv_heads(cfg, l)
+            out[l] = (np.zeros((B, nkv, cap, hd)), np.zeros((B, nkv, cap, hd)))
     return out
 
 

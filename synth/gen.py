@@ -12,7 +12,7 @@ Distributions (one recipe for every config):
   * token ids ~ U[0, vocab)
   * decode KV caches: rows [0, ctx-1) ~ N(0, 1), the row of the new token is zero
 This module holds no step of the method: K/V weights are drawn for every layer, whether or not the
-routing later gives that layer its own cache.
+routing later gives that layer its own cache (a full layer of a K=V model has no V weight to draw).
 """
 import zlib
 
@@ -55,6 +55,24 @@ def head_dim(cfg, layer):
     return cfg["head_dim_swa"] if cfg["layer_types"][layer] == "S" else cfg["head_dim_full"]
 
 
+def kv_heads(cfg, layer):
+    """Shape data: KV head count of a layer (full layers may carry their own, `n_kv_heads_full`)."""
+    if cfg["layer_types"][layer] == "S":
+        return cfg["n_kv_heads"]
+    return cfg.get("n_kv_heads_full") or cfg["n_kv_heads"]
+
+
+def ffn_dim(cfg, layer):
+    """Shape data: FFN width of a layer (`ffn_dims` lists one per layer, else every layer has `ffn`)."""
+    dims = cfg.get("ffn_dims")
+    return int(dims[layer]) if dims else cfg["ffn"]
+
+
+def has_v_proj(cfg, layer):
+    """Weight inventory: a full layer of a K=V model carries no V projection weight."""
+    return not (cfg.get("k_eq_v") and cfg["layer_types"][layer] != "S")
+
+
 def model_globals(cfg, device="cpu"):
     """Embedding table, PLE table, PLE model projection and PLE norm (configs built from token ids)."""
     s, dt = seed_of_model(cfg), TORCH_DTYPES[cfg["dtype"]]
@@ -74,16 +92,15 @@ def seed_of_model(cfg):
 
 def layer_weights(cfg, layer, device="cpu"):
     s, dt = seed_of_model(cfg), TORCH_DTYPES[cfg["dtype"]]
-    H, nh, nkv, F, d = cfg["hidden"], cfg["n_heads"], cfg["n_kv_heads"], cfg["ffn"], cfg["ple_dim"]
-    hd = head_dim(cfg, layer)
+    H, nh, d = cfg["hidden"], cfg["n_heads"], cfg["ple_dim"]
+    nkv, F, hd = kv_heads(cfg, layer), ffn_dim(cfg, layer), head_dim(cfg, layer)
     p = f"L{layer}."
     w = lambda shape, name: normal(shape, 0.02, 0.0, s, p + name, device, dt)  # noqa: E731
     n = lambda size, name: normal((size,), 0.1, 1.0, s, p + name, device, dt)  # noqa: E731
-    return dict(
+    out = dict(
         input_norm=n(H, "input_norm"),
         wq=w((nh * hd, H), "wq"),
         wk=w((nkv * hd, H), "wk"),
-        wv=w((nkv * hd, H), "wv"),
         wo=w((H, nh * hd), "wo"),
         q_norm=n(hd, "q_norm"),
         k_norm=n(hd, "k_norm"),
@@ -98,6 +115,9 @@ def layer_weights(cfg, layer, device="cpu"):
         post_ple_norm=n(H, "post_ple_norm"),
         layer_scalar=1.0,
     )
+    if has_v_proj(cfg, layer):
+        out["wv"] = w((nkv * hd, H), "wv")
+    return out
 
 
 def activations(cfg, device="cpu"):
@@ -121,7 +141,7 @@ def activations(cfg, device="cpu"):
 def decode_cache(cfg, layer, device="cpu"):
     """K and V of one layer, [B, nkv, ctx, hd]: rows before the new token ~ N(0,1), its row zero."""
     s, dt = seed_of(cfg), TORCH_DTYPES[cfg["dtype"]]
-    B, nkv, ctx = cfg["B"], cfg["n_kv_heads"], cfg["ctx"]
+    B, nkv, ctx = cfg["B"], kv_heads(cfg, layer), cfg["ctx"]
     hd = head_dim(cfg, layer)
     kv = []
     for nm in ("k", "v"):

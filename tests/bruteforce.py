@@ -52,8 +52,11 @@ def attend(qh, keys, vals):
 def layer(cfg, lw, layer_idx, own_kv, h_rows, ple_rows, positions, cache):
     """One layer for one sequence. h_rows: list of T lists (H); cache: dict with 'k','v' lists
     indexed [g][pos] -> list(hd) (mutated when own_kv). Returns the new list of rows."""
-    eps, nh, nkv = cfg["eps"], cfg["n_heads"], cfg["n_kv_heads"]
+    eps, nh = cfg["eps"], cfg["n_heads"]
     sliding = cfg["layer_types"][layer_idx] == "S"
+    # variants: a full layer may have its own KV head count, and with K=V its V comes from the K weight
+    nkv = cfg["n_kv_heads"] if sliding or not cfg.get("n_kv_heads_full") else cfg["n_kv_heads_full"]
+    wv = lw["wk"] if (cfg.get("k_eq_v") and not sliding) else lw["wv"]
     hd = cfg["head_dim_swa"] if sliding else cfg["head_dim_full"]
     theta = cfg["theta_swa"] if sliding else cfg["theta_full"]
     n_rot = hd // 2 if sliding else int(hd * cfg["partial_rotary"] / 2)
@@ -73,7 +76,7 @@ def layer(cfg, lw, layer_idx, own_kv, h_rows, ple_rows, positions, cache):
         qs.append(heads)
         if own_kv:
             k = matvec(lw["wk"], xn)
-            v = matvec(lw["wv"], xn)
+            v = matvec(wv, xn)
             for g in range(nkv):
                 kg = rms(k[g * hd:(g + 1) * hd], lw["k_norm"], eps)
                 cache["k"][g][positions[t]] = rope_complex(kg, positions[t], theta, n_rot)

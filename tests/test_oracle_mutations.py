@@ -21,8 +21,13 @@ MUTATIONS = {
     "window_off_by_one": ("vis &= j[None, :] > p[:, None] - window", "vis &= j[None, :] >= p[:, None] - window"),
     "ple_gate_on_xn2": ('g = gelu_tanh(h @ f64(lw["ple_gate"]).T)', 'g = gelu_tanh(xn2 @ f64(lw["ple_gate"]).T)'),
     "drop_attn_residual": ('h = h + rms_norm(a, lw["post_attn_norm"], eps)', 'h = rms_norm(a, lw["post_attn_norm"], eps)'),
-    "v_norm_weighted": ('v = rms_norm((xn @ f64(lw["wv"]).T).reshape(B, T, nkv, hd), None, eps)',
-                        'v = rms_norm((xn @ f64(lw["wv"]).T).reshape(B, T, nkv, hd), lw["k_norm"], eps)'),
+    "v_norm_weighted": ('v = rms_norm((xn @ f64(value_weight(cfg, lw, layer)).T).reshape(B, T, nkv, hd), None, eps)',
+                        'v = rms_norm((xn @ f64(value_weight(cfg, lw, layer)).T).reshape(B, T, nkv, hd), lw["k_norm"], eps)'),
+    "k_eq_v_on_sliding_layers": ('if cfg.get("k_eq_v") and cfg["layer_types"][layer] != "S":', 'if cfg.get("k_eq_v"):'),
+    "k_eq_v_value_is_rotated_k": ('v = rms_norm((xn @ f64(value_weight(cfg, lw, layer)).T).reshape(B, T, nkv, hd), None, eps)',
+                                  'v = rms_norm(k, None, eps) if cfg.get("k_eq_v") and not sliding else '
+                                  'rms_norm((xn @ f64(value_weight(cfg, lw, layer)).T).reshape(B, T, nkv, hd), None, eps)'),
+    "full_kv_heads_ignored": ('return cfg.get("n_kv_heads_full") or cfg["n_kv_heads"]', 'return cfg["n_kv_heads"]'),
     "eps_outside_mean": ("y = x * (ms + eps) ** -0.5", "y = x * (ms ** -0.5 + eps)"),
     "partial_rotary_denominator": ("inv = float(theta) ** (-2.0 * j / hd)",
                                    "inv = float(theta) ** (-2.0 * j / (2 * max(n_rot, 1)))"),

@@ -248,9 +248,13 @@ def _run_oracle_stack(cfg, layers, h0, ple, pos, srcs, cap):
     return O.forward(cfg, layers, h0, ple, pos, caches, srcs), caches
 
 
-@pytest.mark.parametrize("types,n_shared", [("SSF", 0), ("SFSSF", 2)])
-def test_stack_brute_force(types, n_shared):
-    cfg = configs.tiny(layer_types=types, n_shared=n_shared, T=6)
+VARIANT = dict(n_kv_heads_full=4, k_eq_v=True, ffn_dims=[48, 40, 56, 32, 24])
+
+
+@pytest.mark.parametrize("types,n_shared,extra", [("SSF", 0, {}), ("SFSSF", 2, {}), ("SFSSF", 2, VARIANT),
+                                                  ("SFSFF", 0, dict(VARIANT, n_kv_heads_full=1))])
+def test_stack_brute_force(types, n_shared, extra):
+    cfg = configs.tiny(layer_types=types, n_shared=n_shared, T=6, **extra)
     glob, layers = _tiny_model(cfg)
     for lw in layers:
         lw["layer_scalar"] = 0.9
@@ -264,13 +268,79 @@ def test_stack_brute_force(types, n_shared):
     for l in range(cfg["n_layers"]):
         hd = cfg["head_dim_swa"] if types[l] == "S" else cfg["head_dim_full"]
         if srcs[l] == l:
-            bcache[l] = {"k": [[None] * cfg["T"] for _ in range(cfg["n_kv_heads"])],
-                         "v": [[None] * cfg["T"] for _ in range(cfg["n_kv_heads"])]}
+            nkv = layers[l]["wk"].shape[0] // hd
+            bcache[l] = {"k": [[None] * cfg["T"] for _ in range(nkv)],
+                         "v": [[None] * cfg["T"] for _ in range(nkv)]}
         lw = {k: (f64l(v) if isinstance(v, torch.Tensor) else v) for k, v in layers[l].items()}
         rows = bf.layer(cfg, lw, l, srcs[l] == l, rows, ple[0, :, l, :].tolist(), list(range(cfg["T"])),
                         bcache[srcs[l]])
         assert len(rows[0]) == cfg["hidden"] and hd > 0
     np.testing.assert_allclose(got[0], np.array(rows), rtol=1e-10, atol=1e-11)
+
+
+def test_k_eq_v_full_layer_is_base_layer_with_v_weight_from_k():
+    """K=V (page 5 `forward_layer`): a full layer projects V with the K weight; sliding layers keep theirs."""
+    base = configs.tiny(layer_types="SF")
+    var = dict(base, k_eq_v=True)
+    _, lb = _tiny_model(base)
+    _, lv = _tiny_model(var)
+    assert "wv" not in lv[1] and "wv" in lv[0]
+    h = rng.normal(size=(1, 5, base["hidden"]))
+    ple = rng.normal(size=(1, 5, base["ple_dim"]))
+    pos = O.prefill_positions([0], 5)
+    got = O.layer_forward(var, lv[1], 1, 1, h, ple, pos, O.new_caches(var, 1, 5))
+    want = O.layer_forward(base, dict(lb[1], wv=lb[1]["wk"]), 1, 1, h, ple, pos, O.new_caches(base, 1, 5))
+    assert np.array_equal(got, want)
+    got = O.layer_forward(var, lv[0], 0, 0, h, ple, pos, O.new_caches(var, 1, 5))
+    want = O.layer_forward(base, lb[0], 0, 0, h, ple, pos, O.new_caches(base, 1, 5))
+    assert np.array_equal(got, want)
+    # V is not the normed, rotated K: with the same projection, the cached V rows differ from K rows
+    caches = O.new_caches(var, 1, 5)
+    O.layer_forward(var, lv[1], 1, 1, h, ple, pos, caches)
+    K, V = caches[1]
+    raw = (O.rms_norm(h, lv[1]["input_norm"], var["eps"]) @ O.f64(lv[1]["wk"]).T).reshape(1, 5, 2, 16)
+    np.testing.assert_allclose(V[0].transpose(1, 0, 2), raw[0] / np.sqrt((raw[0] ** 2).mean(-1, keepdims=True) + 1e-6),
+                               rtol=1e-12)
+    assert not np.allclose(K, V)
+
+
+def test_full_layer_kv_heads_repeated_equal_fewer_heads():
+    """A full layer with its own KV head count: 4 KV heads that repeat in pairs equal 2 KV heads (each of the
+    4 query heads then reads its own copy, page 4 `text_attention` head map)."""
+    base = configs.tiny(layer_types="SF")
+    var = dict(base, n_kv_heads_full=4)
+    _, lb = _tiny_model(base)
+    hd = base["head_dim_full"]
+    rep = lambda w: w.reshape(2, hd, -1).repeat_interleave(2, dim=0).reshape(4 * hd, -1)  # noqa: E731
+    lv = dict(lb[1], wk=rep(lb[1]["wk"]), wv=rep(lb[1]["wv"]))
+    h = rng.normal(size=(1, 5, base["hidden"]))
+    ple = rng.normal(size=(1, 5, base["ple_dim"]))
+    pos = O.prefill_positions([0], 5)
+    cv = O.new_caches(var, 1, 5)
+    got = O.layer_forward(var, lv, 1, 1, h, ple, pos, cv)
+    want = O.layer_forward(base, lb[1], 1, 1, h, ple, pos, O.new_caches(base, 1, 5))
+    assert cv[1][0].shape == (1, 4, 5, hd)
+    np.testing.assert_allclose(got, want, rtol=1e-13, atol=1e-13)
+    # sliding layers keep the shared count
+    assert O.new_caches(var, 1, 5)[0][0].shape[1] == base["n_kv_heads"]
+
+
+def test_ffn_width_zero_padding_is_invisible():
+    """Per-layer FFN width (page 2 `ffn_dim`): extra units with zero gate/up rows and zero down columns add
+    gelu(0) * 0 = 0, so a wider layer built that way equals the narrower one."""
+    cfg = configs.tiny(layer_types="SF")
+    _, layers = _tiny_model(cfg)
+    lw = layers[0]
+    F, H = lw["w_gate"].shape
+    z = torch.zeros((16, H), dtype=lw["w_gate"].dtype)
+    wide = dict(lw, w_gate=torch.cat([lw["w_gate"], z]), w_up=torch.cat([lw["w_up"], z]),
+                w_down=torch.cat([lw["w_down"], z.T], dim=1))
+    h = rng.normal(size=(1, 5, cfg["hidden"]))
+    ple = rng.normal(size=(1, 5, cfg["ple_dim"]))
+    pos = O.prefill_positions([0], 5)
+    a = O.layer_forward(cfg, lw, 0, 0, h, ple, pos, O.new_caches(cfg, 1, 5))
+    b = O.layer_forward(cfg, wide, 0, 0, h, ple, pos, O.new_caches(cfg, 1, 5))
+    np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-13)
 
 
 def test_layer_zero_branches_leave_h_scaled_exactly():
