@@ -32,15 +32,21 @@ def workload(cid, batch):
     return configs.get(cid)
 
 
+def layer_shape(cfg, l):
+    """(head dim, kv heads, FFN width, has a V projection) of layer l."""
+    from synth import gen
+    return gen.head_dim(cfg, l), gen.kv_heads(cfg, l), gen.ffn_dim(cfg, l), gen.has_v_proj(cfg, l)
+
+
 def gemm_flops(cfg, M):
     """Algorithmic GEMM flops of one layer-stack pass (2MNK), by kernel class."""
-    H, nh, nkv, F, d = cfg["hidden"], cfg["n_heads"], cfg["n_kv_heads"], cfg["ffn"], cfg["ple_dim"]
+    H, nh, d = cfg["hidden"], cfg["n_heads"], cfg["ple_dim"]
     from gemma_decoder_forward_amd import binding as bd
     srcs = bd.g4_kv_sources([1 if t == "S" else 0 for t in cfg["layer_types"]], cfg["n_shared"])
     out = dict(qkv=0, o=0, gate_up=0, down=0, ple=0)
-    for l, t in enumerate(cfg["layer_types"]):
-        hd = cfg["head_dim_swa"] if t == "S" else cfg["head_dim_full"]
-        nq = nh * hd + (2 * nkv * hd if srcs[l] == l else 0)
+    for l in range(cfg["n_layers"]):
+        hd, nkv, F, has_v = layer_shape(cfg, l)
+        nq = nh * hd + ((2 if has_v else 1) * nkv * hd if srcs[l] == l else 0)
         out["qkv"] += 2 * M * nq * H
         out["o"] += 2 * M * H * nh * hd
         out["gate_up"] += 2 * M * 2 * F * H
@@ -68,7 +74,7 @@ def class_rates(cfg, M, decode, per_ms):
     Row tails and head norms (elementwise, HBM): bytes each step needs at the layer's dtypes, with the
     float32 projection outputs counted once (split-K slices are an implementation choice, not counted).
     """
-    H, nh, nkv, F, d = cfg["hidden"], cfg["n_heads"], cfg["n_kv_heads"], cfg["ffn"], cfg["ple_dim"]
+    H, nh = cfg["hidden"], cfg["n_heads"]
     E = 2 if cfg["dtype"] == "bf16" else 4
     from gemma_decoder_forward_amd import binding as bd
     srcs = bd.g4_kv_sources([1 if t == "S" else 0 for t in cfg["layer_types"]], cfg["n_shared"])
@@ -90,8 +96,8 @@ def class_rates(cfg, M, decode, per_ms):
     if ms > 0:
         if decode:
             kv = 0
-            for t in cfg["layer_types"]:
-                hd = cfg["head_dim_swa"] if t == "S" else cfg["head_dim_full"]
+            for l, t in enumerate(cfg["layer_types"]):
+                hd, nkv, _, _ = layer_shape(cfg, l)
                 keys = min(cfg["ctx"], cfg["window"]) if t == "S" else cfg["ctx"]
                 kv += 2 * nkv * keys * hd * E * M
             gb = kv / (ms / 1e3) / 1e9
@@ -103,8 +109,9 @@ def class_rates(cfg, M, decode, per_ms):
     # pre-attention norm of the first layer; head norms read and write q (and k, v when the layer owns them)
     tail = L * 3 * (4 * H + 4 * H + 4 * H + E * H) + (4 * H + E * H)
     qk = 0
-    for l, t in enumerate(cfg["layer_types"]):
-        hd = cfg["head_dim_swa"] if t == "S" else cfg["head_dim_full"]
+    for l in range(L):
+        hd, nkv, _, _ = layer_shape(cfg, l)
+        # reads q (and k, v: a K=V layer reads its k columns twice) and writes q, k, v rows
         qk += 2 * (nh + (2 * nkv if srcs[l] == l else 0)) * hd * E
     for name, per_tok in (("row_tail", tail), ("qk_norm_rope", qk)):
         ms = per_ms.get(name, 0)
@@ -114,8 +121,13 @@ def class_rates(cfg, M, decode, per_ms):
     return out
 
 
+def mean_ffn(cfg):
+    """FFN width averaged over the layers (the gate/up kernel runs once per layer)."""
+    return sum(layer_shape(cfg, l)[2] for l in range(cfg["n_layers"])) / cfg["n_layers"]
+
+
 def gate_up_weight_bytes(cfg):
-    return 2 * cfg["ffn"] * cfg["hidden"] * 2
+    return 2 * mean_ffn(cfg) * cfg["hidden"] * 2
 
 
 def run_gpu(cfg, steps, warmup, breakdown, use_graph=True):
@@ -308,7 +320,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5, 6])
     ap.add_argument("--batch", type=int, default=64, help="decode batch (workload 4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
@@ -333,17 +345,18 @@ def main():
     decode = cfg["mode"] == "decode"
     dom_avg_s = r["dom_ms"] / max(r["dom_n"], 1) / 1e3
     names = {2: "e4b-layer-pair prefill", 3: "e4b-42-layer prefill from token ids", 4: "e4b-42-layer decode",
-             5: "e4b-12-layer long-context prefill"}
+             5: "e4b-12-layer long-context prefill",
+             6: "e4b-width 6-layer prefill with the variants (full-layer kv heads, K=V, per-layer FFN widths)"}
     wname = f"{names[args.workload]}: B={B} T={T}" + (f" ctx={cfg['ctx']}" if decode else "")
     traffic = counted_traffic(wname, "gate_up_gemm")
     if decode:
-        per_launch = gate_up_weight_bytes(cfg) + 2 * B * cfg["hidden"] + 2 * B * cfg["ffn"]
+        per_launch = gate_up_weight_bytes(cfg) + 2 * B * cfg["hidden"] + 2 * B * mean_ffn(cfg)
         achieved = per_launch / dom_avg_s / 1e9
         roof = dict(bound="hbm", kernel="gate_up_gemm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=round(achieved / PEAK_HBM_GBS, 4), traffic=traffic, bytes_per_launch=per_launch,
                     avg_launch_us=round(dom_avg_s * 1e6, 2))
     else:
-        per_launch = 2 * tokens * 2 * cfg["ffn"] * cfg["hidden"]
+        per_launch = 2 * tokens * 2 * mean_ffn(cfg) * cfg["hidden"]
         achieved = per_launch / dom_avg_s / 1e12
         roof = dict(bound="mfma", kernel="gate_up_gemm", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS,
                     unit="TFLOP/s", frac=round(achieved / PEAK_BF16_TFLOPS, 4), traffic=traffic,
@@ -363,8 +376,11 @@ def main():
         ms_per_step=round(ms, 4), higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16",
         data="synthetic (seeded N(0,0.02) weights, N(0,1) activations / uniform token ids)",
         config=dict(workload=wname,
-                    layers=cfg["n_layers"], layer_types=cfg["layer_types"], hidden=cfg["hidden"], ffn=cfg["ffn"],
-                    heads=f"{cfg['n_heads']}/{cfg['n_kv_heads']}",
+                    layers=cfg["n_layers"], layer_types=cfg["layer_types"], hidden=cfg["hidden"],
+                    ffn=cfg.get("ffn_dims") or cfg["ffn"],
+                    heads=f"{cfg['n_heads']}/{cfg['n_kv_heads']}"
+                    + (f" (full layers /{cfg['n_kv_heads_full']})" if cfg.get("n_kv_heads_full") else ""),
+                    k_eq_v=bool(cfg.get("k_eq_v")),
                     head_dim=f"{cfg['head_dim_swa']}/{cfg['head_dim_full']}", window=cfg["window"],
                     global_batch=B, seq_len=T, parallelism="none (1 GPU)"),
         roofline=roof, extra=extra,

@@ -20,7 +20,7 @@ class ModelDesc(C.Structure):
     _fields_ = [("hidden", i64), ("n_heads", i64), ("n_kv_heads", i64), ("head_dim_swa", i64),
                 ("head_dim_full", i64), ("ffn", i64), ("ple_dim", i64), ("n_layers", i64), ("window", i64),
                 ("vocab", i64), ("ple_vocab", i64), ("eps", f32), ("theta_swa", f32), ("theta_full", f32),
-                ("partial_rotary", f32), ("dtype", i32), ("reserved", i32)]
+                ("partial_rotary", f32), ("dtype", i32), ("k_eq_v", i32), ("n_kv_heads_full", i64)]
 
 
 LAYER_PTRS = ["input_norm", "wq", "wk", "wv", "wo", "q_norm", "k_norm", "post_attn_norm", "pre_ffn_norm",
@@ -28,7 +28,7 @@ LAYER_PTRS = ["input_norm", "wq", "wk", "wv", "wo", "q_norm", "k_norm", "post_at
 
 
 class LayerDesc(C.Structure):
-    _fields_ = [("sliding", i32), ("kv_src", i32), ("layer_scalar", f32), ("reserved", i32)] + \
+    _fields_ = [("sliding", i32), ("kv_src", i32), ("layer_scalar", f32), ("ffn", i32)] + \
                [(n, vp) for n in LAYER_PTRS]
 
 

@@ -4,6 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 
 #include "g4_internal.h"
@@ -65,6 +66,10 @@ static g4_status check_model(const g4_model_desc* m) {
          G4_EINVAL, "model sizes must be positive");
   G4_REQ(m->n_heads % m->n_kv_heads == 0, G4_EGEOM, "n_heads %lld is not a multiple of n_kv_heads %lld",
          (long long)m->n_heads, (long long)m->n_kv_heads);
+  G4_REQ(m->n_kv_heads_full >= 0 && (m->n_kv_heads_full == 0 || m->n_heads % m->n_kv_heads_full == 0), G4_EGEOM,
+         "n_heads %lld is not a multiple of n_kv_heads_full %lld", (long long)m->n_heads,
+         (long long)m->n_kv_heads_full);
+  G4_REQ(m->k_eq_v == 0 || m->k_eq_v == 1, G4_EINVAL, "k_eq_v must be 0 or 1");
   G4_REQ(m->head_dim_swa % 2 == 0 && m->head_dim_full % 2 == 0, G4_EGEOM, "head dims must be even");
   G4_REQ(m->head_dim_swa <= 512 && m->head_dim_full <= 512, G4_ERANGE, "head dims above 512 are not supported");
   G4_REQ(m->window >= 1, G4_ERANGE, "window %lld < 1", (long long)m->window);
@@ -76,6 +81,21 @@ static g4_status check_model(const g4_model_desc* m) {
   G4_REQ(m->ple_dim <= 512, G4_ERANGE, "ple_dim %lld > 512", (long long)m->ple_dim);
   return G4_OK;
 }
+
+// KV heads of a layer type: full layers may carry their own count.
+static int64_t kv_heads(const g4_model_desc* m, int sliding) {
+  return (!sliding && m->n_kv_heads_full > 0) ? m->n_kv_heads_full : m->n_kv_heads;
+}
+
+static int64_t max_kv_heads(const g4_model_desc* m) {
+  return m->n_kv_heads_full > m->n_kv_heads ? m->n_kv_heads_full : m->n_kv_heads;
+}
+
+// FFN width of a layer (0 in the descriptor: the model's).
+static int64_t ffn_of(const g4_model_desc* m, const g4_layer_desc* l) { return l->ffn > 0 ? l->ffn : m->ffn; }
+
+// A full layer of a K=V model takes V from the K projection's output.
+static bool v_from_k(const g4_model_desc* m, const g4_layer_desc* l) { return m->k_eq_v && !l->sliding; }
 
 static int64_t rot_pairs(const g4_model_desc* m, int sliding) {
   if (sliding) return m->head_dim_swa / 2;
@@ -124,7 +144,7 @@ static Plan plan(const g4_model_desc* m, int64_t B, int64_t T, int64_t cap, int3
   const size_t E = dsize(m->dtype);
   const int64_t M = B * T;
   const int64_t hdm = m->head_dim_swa > m->head_dim_full ? m->head_dim_swa : m->head_dim_full;
-  p.qkv_ld = (m->n_heads + 2 * m->n_kv_heads) * hdm;
+  p.qkv_ld = (m->n_heads + 2 * max_kv_heads(m)) * hdm;
   p.splits = 4;
   size_t o = 0;
   p.xn = o; o += al(M * m->hidden * E);
@@ -139,33 +159,39 @@ static Plan plan(const g4_model_desc* m, int64_t B, int64_t T, int64_t cap, int3
   p.aws = o;  // key-split partials of a short prefill's attention
   p.aws_bytes = 0;
   if (mode == G4_PREFILL) {
-    const size_t s0 = attn_prefill_ws(B, T, m->n_heads, m->n_kv_heads, m->head_dim_swa);
-    const size_t s1 = attn_prefill_ws(B, T, m->n_heads, m->n_kv_heads, m->head_dim_full);
+    const size_t s0 = attn_prefill_ws(B, T, m->n_heads, kv_heads(m, 1), m->head_dim_swa);
+    const size_t s1 = attn_prefill_ws(B, T, m->n_heads, kv_heads(m, 0), m->head_dim_full);
     p.aws_bytes = s0 > s1 ? s0 : s1;
     o += al(p.aws_bytes);
   }
   p.gws = o;
   p.gws_bytes = 0;
   if (M <= 64 && m->dtype == G4_BF16) {  // partial sums of the few-row GEMM
-    const int64_t H = m->hidden, nh = m->n_heads, nkv = m->n_kv_heads, hs = m->head_dim_swa, hf = m->head_dim_full;
-    const int64_t shapes[10][2] = {{nh * hs, H}, {(nh + 2 * nkv) * hs, H}, {nh * hf, H}, {(nh + 2 * nkv) * hf, H},
-                                   {2 * m->ffn, H}, {H, m->ffn}, {H, nh * hs}, {H, nh * hf},
-                                   {m->ple_dim, H}, {H, m->ple_dim}};
-    for (auto& sh : shapes) {
-      const size_t b = gemm_skinny_ws(M, (sh[0] + 63) / 64 * 64, (sh[1] + 127) / 128 * 128);
-      if (b > p.gws_bytes) p.gws_bytes = b;
+    const int64_t H = m->hidden, nh = m->n_heads, hs = m->head_dim_swa, hf = m->head_dim_full;
+    const int64_t ns = kv_heads(m, 1), nf = kv_heads(m, 0);
+    auto ws_x = [&](int64_t rows) { return gemm_skinny_ws(M, (rows + 63) / 64 * 64, (H + 127) / 128 * 128); };
+    auto ws_y = [&](int64_t k) { return gemm_skinny_ws(M, (H + 63) / 64 * 64, (k + 127) / 128 * 128); };
+    // the FFN's two GEMMs at every width a layer may have (the split count depends on the width, so the
+    // scratch is not largest at the largest width); the few-row kernels take multiples of 64 only
+    size_t ffn_x = 0, ffn_y = 0;
+    for (int64_t f = 64;; f += 64) {
+      if (f > m->ffn) f = m->ffn;
+      ffn_x = std::max(ffn_x, ws_x(2 * f));
+      ffn_y = std::max(ffn_y, ws_y(f));
+      if (f == m->ffn) break;
     }
+    p.gws_bytes = std::max(ffn_x, ffn_y);
+    for (const int64_t rows : {nh * hs, (nh + 2 * ns) * hs, nh * hf, (nh + nf) * hf, (nh + 2 * nf) * hf, m->ple_dim})
+      p.gws_bytes = std::max(p.gws_bytes, ws_x(rows));
+    for (const int64_t k : {nh * hs, nh * hf, m->ple_dim}) p.gws_bytes = std::max(p.gws_bytes, ws_y(k));
     o += al(p.gws_bytes);
     // the few-row layer path: split-K partials of q/k/v, gate/up and the PLE gate (fx) and of the
     // projections back to H (fy); a GEMM reading one region writes the other
-    for (const int64_t rows : {(nh + 2 * nkv) * hs, (nh + 2 * nkv) * hf, 2 * m->ffn, m->ple_dim}) {
-      const size_t b = gemm_skinny_ws(M, (rows + 63) / 64 * 64, (H + 127) / 128 * 128);
-      if (b > p.fx_bytes) p.fx_bytes = b;
-    }
-    for (const int64_t k : {m->ffn, nh * hs, nh * hf, m->ple_dim}) {
-      const size_t b = gemm_skinny_ws(M, (H + 63) / 64 * 64, (k + 127) / 128 * 128);
-      if (b > p.fy_bytes) p.fy_bytes = b;
-    }
+    p.fx_bytes = ffn_x;  // q only (shared layers), q/k (K=V full layers) or q/k/v
+    for (const int64_t rows : {nh * hs, (nh + 2 * ns) * hs, nh * hf, (nh + nf) * hf, (nh + 2 * nf) * hf, m->ple_dim})
+      p.fx_bytes = std::max(p.fx_bytes, ws_x(rows));
+    p.fy_bytes = ffn_y;
+    for (const int64_t k : {nh * hs, nh * hf, m->ple_dim}) p.fy_bytes = std::max(p.fy_bytes, ws_y(k));
     p.fx = o; o += al(p.fx_bytes);
     p.fy = o; o += al(p.fy_bytes);
   }
@@ -255,10 +281,14 @@ static g4_status check_layer(const g4_model_desc* m, const g4_layer_desc* l, int
   G4_REQ(layer >= 0 && layer < m->n_layers, G4_EINVAL, "layer %d outside [0, %lld)", layer, (long long)m->n_layers);
   G4_REQ(n_kv == m->n_layers, G4_EINVAL, "n_kv %d != n_layers %lld", n_kv, (long long)m->n_layers);
   G4_REQ(l->sliding == 0 || l->sliding == 1, G4_EINVAL, "layer %d: sliding must be 0 or 1", layer);
+  G4_REQ(l->ffn >= 0 && l->ffn <= m->ffn, G4_ERANGE, "layer %d: ffn %d outside [0, model ffn %lld]", layer, l->ffn,
+         (long long)m->ffn);
   G4_REQ(l->input_norm && l->wq && l->wo && l->q_norm && l->post_attn_norm && l->pre_ffn_norm && l->w_gate &&
              l->w_up && l->w_down && l->post_ffn_norm && l->ple_gate && l->ple_proj && l->post_ple_norm,
          G4_EINVAL, "layer %d: a weight pointer is NULL", layer);
-  if (l->kv_src == layer) G4_REQ(l->wk && l->wv && l->k_norm, G4_EINVAL, "layer %d owns its cache but wk/wv/k_norm is NULL", layer);
+  if (l->kv_src == layer)
+    G4_REQ(l->wk && (l->wv || v_from_k(m, l)) && l->k_norm, G4_EINVAL,
+           "layer %d owns its cache but wk/wv/k_norm is NULL", layer);
   else G4_REQ(l->kv_src < layer, G4_EGEOM, "layer %d: kv_src %d is not an earlier layer", layer, l->kv_src);
   const int64_t hd = l->sliding ? m->head_dim_swa : m->head_dim_full;
   return check_kv(kv, n_kv, layer, l->kv_src, l->sliding, hd, T, mode, m->window);
@@ -272,22 +302,23 @@ static g4_status check_layer(const g4_model_desc* m, const g4_layer_desc* l, int
 static bool few_row_ok(const LayerCtx& c) {
   const g4_model_desc* m = c.m;
   const g4_layer_desc* l = c.l;
-  const int64_t M = c.B * c.T, H = m->hidden, nh = m->n_heads, nkv = m->n_kv_heads;
+  const int64_t M = c.B * c.T, H = m->hidden, nh = m->n_heads, nkv = kv_heads(m, l->sliding), F = ffn_of(m, l);
   const int64_t hd = l->sliding ? m->head_dim_swa : m->head_dim_full;
   if (m->dtype != G4_BF16 || M > 64 || c.p->fx_bytes == 0) return false;
   const void* q3[3] = {l->wq, l->wk, l->wv};
   const int64_t r3[3] = {nh * hd, nkv * hd, nkv * hd};
+  const int nseg = l->kv_src != c.layer ? 1 : (v_from_k(m, l) ? 2 : 3);
   const void* gu[2] = {l->w_gate, l->w_up};
-  const int64_t rgu[2] = {m->ffn, m->ffn};
+  const int64_t rgu[2] = {F, F};
   const void* wo[1] = {l->wo};
   const void* wd[1] = {l->w_down};
   const void* pg[1] = {l->ple_gate};
   const void* pp[1] = {l->ple_proj};
   const int64_t rH[1] = {H}, rd[1] = {m->ple_dim};
-  return skinny_ok(M, H, q3, r3, l->kv_src == c.layer ? 3 : 1, H) && skinny_ok(M, nh * hd, wo, rH, 1, nh * hd) &&
-         skinny_ok(M, H, gu, rgu, 2, H) && skinny_ok(M, m->ffn, wd, rH, 1, m->ffn) &&
+  return skinny_ok(M, H, q3, r3, nseg, H) && skinny_ok(M, nh * hd, wo, rH, 1, nh * hd) &&
+         skinny_ok(M, H, gu, rgu, 2, H) && skinny_ok(M, F, wd, rH, 1, F) &&
          skinny_ok(M, H, pg, rd, 1, H) && skinny_ok(M, m->ple_dim, pp, rH, 1, m->ple_dim) &&
-         (m->ffn % 4) == 0 && (m->ple_dim % 4) == 0 && ((uintptr_t)c.ple_in & 15) == 0;
+         (F % 4) == 0 && (m->ple_dim % 4) == 0 && ((uintptr_t)c.ple_in & 15) == 0;
 }
 
 // Whether the consumer GEMM (K x Nc weights) should form its A operand from `parts` float32 slices while
@@ -305,10 +336,12 @@ static g4_status few_row_layer(const LayerCtx& c) {
   const g4_layer_desc* l = c.l;
   const int32_t dt = m->dtype;
   const size_t E = dsize(dt);
-  const int64_t M = c.B * c.T, H = m->hidden, nh = m->n_heads, nkv = m->n_kv_heads, F = m->ffn, d = m->ple_dim;
+  const int64_t M = c.B * c.T, H = m->hidden, nh = m->n_heads, d = m->ple_dim;
   const int sliding = l->sliding;
+  const int64_t nkv = kv_heads(m, sliding), F = ffn_of(m, l);
   const int64_t hd = sliding ? m->head_dim_swa : m->head_dim_full;
   const bool own = l->kv_src == c.layer;
+  const bool vk = v_from_k(m, l);
   char* xn = c.ws + c.p->xn;
   char* qkv = c.ws + c.p->qkv;
   char* ao = c.ws + c.p->ao;
@@ -326,8 +359,10 @@ static g4_status few_row_layer(const LayerCtx& c) {
   } while (0)
   if (!c.xn_ready)
     G4_TRY(rownorm(c.h, G4_F32, 1, 0, l->input_norm, xn, nullptr, 1.f, nullptr, nullptr, M, H, m->eps, dt, c.s));
-  // q, k, v partials, then per-head norms + RoPE from their sums; k and v land in the cache
-  const int64_t Nq = nh * hd + (own ? 2 * nkv * hd : 0);
+  // q, k, v partials, then per-head norms + RoPE from their sums; k and v land in the cache (with K=V
+  // there is no v projection: the v heads are formed from the k partials, without scale and rotation)
+  const int nseg = own ? (vk ? 2 : 3) : 1;
+  const int64_t Nq = nh * hd + (nseg - 1) * nkv * hd;
   int s1 = 0;
   {
     TimedScope ts(G4_KC_QKV_GEMM, c.s);
@@ -335,7 +370,7 @@ static g4_status few_row_layer(const LayerCtx& c) {
     const int64_t rows[3] = {nh * hd, nkv * hd, nkv * hd};
     SkA sa{};
     sa.a = xn; sa.lda = H; sa.kind = SKA_BF16;
-    G4_TRY(gemm_skinny_part(sa, M, H, segs, rows, own ? 3 : 1, H, X, XB, &s1, c.s));
+    G4_TRY(gemm_skinny_part(sa, M, H, segs, rows, nseg, H, X, XB, &s1, c.s));
   }
   {
     TimedScope ts(G4_KC_QK_NORM_ROPE, c.s);
@@ -345,7 +380,7 @@ static g4_status few_row_layer(const LayerCtx& c) {
     if (own) {
       const g4_kv_entry& e = c.kv[c.layer];
       segs[ns++] = HeadSeg{X + nh * hd, Nq, l->k_norm, e.k, 0, e.cap, (int32_t)nkv, 1, e.ring};
-      segs[ns++] = HeadSeg{X + (nh + nkv) * hd, Nq, nullptr, e.v, 0, e.cap, (int32_t)nkv, 0, e.ring};
+      segs[ns++] = HeadSeg{X + (vk ? nh : nh + nkv) * hd, Nq, nullptr, e.v, 0, e.cap, (int32_t)nkv, 0, e.ring};
     }
     G4_TRY(qk_norm_rope_parts(segs, ns, s1, M * Nq, c.pos, c.B, c.T, hd, sliding ? m->theta_swa : m->theta_full,
                               rot_pairs(m, sliding), m->eps, dt, c.s));
@@ -449,9 +484,11 @@ static g4_status layer_impl(const LayerCtx& c) {
   const g4_layer_desc* l = c.l;
   const int32_t dt = m->dtype;
   const size_t E = dsize(dt);
-  const int64_t M = c.B * c.T, H = m->hidden, nh = m->n_heads, nkv = m->n_kv_heads, F = m->ffn, d = m->ple_dim;
+  const int64_t M = c.B * c.T, H = m->hidden, nh = m->n_heads, d = m->ple_dim;
   const int sliding = l->sliding;
+  const int64_t nkv = kv_heads(m, sliding), F = ffn_of(m, l);
   const int64_t hd = sliding ? m->head_dim_swa : m->head_dim_full;
+  const bool vk = v_from_k(m, l);
   const float theta = sliding ? m->theta_swa : m->theta_full;
   const int64_t nrot = rot_pairs(m, sliding);
   const bool own = l->kv_src == c.layer;
@@ -475,17 +512,17 @@ static g4_status layer_impl(const LayerCtx& c) {
   // 1. pre-attention norm
   if (!c.xn_ready)
     G4_TRY(rownorm(c.h, G4_F32, 1, 0, l->input_norm, xn, nullptr, 1.f, nullptr, nullptr, M, H, m->eps, dt, c.s));
-  // 2. projections: q, and k, v when the layer owns its cache
+  // 2. projections: q, and k, v when the layer owns its cache (k only with K=V: v is formed from it)
   {
     TimedScope ts(G4_KC_QKV_GEMM, c.s);
     GemmArgs ga{};
     ga.A = xn; ga.lda = H; ga.ldb = H; ga.C = qkv; ga.ldc = qld; ga.c_dtype = dt; ga.M = M; ga.K = H;
     ga.epi = EPI_STORE; ga.splits = 1; ga.ws = g_gws; ga.ws_bytes = g_gws_bytes;
-    ga.nseg = own ? 3 : 1;
+    ga.nseg = own ? (vk ? 2 : 3) : 1;
     ga.segB[0] = l->wq; ga.seg_rows[0] = nh * hd;
     ga.segB[1] = l->wk; ga.seg_rows[1] = nkv * hd;
     ga.segB[2] = l->wv; ga.seg_rows[2] = nkv * hd;
-    ga.N = nh * hd + (own ? 2 * nkv * hd : 0);
+    ga.N = nh * hd + (ga.nseg - 1) * nkv * hd;
     ga.B = l->wq;
     G4_TRY(gemm(ga, dt, c.s));
   }
@@ -496,7 +533,7 @@ static g4_status layer_impl(const LayerCtx& c) {
   if (own) {
     const g4_kv_entry& e = c.kv[c.layer];
     segs[ns++] = HeadSeg{qkv + nh * hd * E, qld, l->k_norm, e.k, 0, e.cap, (int32_t)nkv, 1, e.ring};
-    segs[ns++] = HeadSeg{qkv + (nh + nkv) * hd * E, qld, nullptr, e.v, 0, e.cap, (int32_t)nkv, 0, e.ring};
+    segs[ns++] = HeadSeg{qkv + (vk ? nh : nh + nkv) * hd * E, qld, nullptr, e.v, 0, e.cap, (int32_t)nkv, 0, e.ring};
   }
   {
     TimedScope ts(G4_KC_QK_NORM_ROPE, c.s);
@@ -579,7 +616,7 @@ const char* g4_status_str(int status) {
 
 const char* g4_last_error(void) { return g_last_error.c_str(); }
 
-int g4_version(void) { return 100; }
+int g4_version(void) { return 200; }
 
 g4_status g4_kv_sources(const int32_t* sliding, int32_t n_layers, int32_t n_shared, int32_t* kv_src) {
   G4_REQ(sliding && kv_src, G4_EINVAL, "sliding or kv_src is NULL");

@@ -22,8 +22,10 @@ def _stream():
 class G4Model:
     """A Gemma-4 E-series text stack resident on one GPU.
 
-    cfg: a workload dict (hidden, n_heads, ..., layer_types "S"/"F" per layer, n_shared, dtype).
-    layers: list of per-layer dicts of device tensors (names as in g4_layer_desc).
+    cfg: a workload dict (hidden, n_heads, ..., layer_types "S"/"F" per layer, n_shared, dtype; optional
+    n_kv_heads_full, k_eq_v and per-layer ffn_dims).
+    layers: list of per-layer dicts of device tensors (names as in g4_layer_desc; each layer's FFN width
+    is read from its w_gate).
     glob: optional dict with embed, ple_embed, ple_model_proj, ple_norm (device tensors).
     """
 
@@ -34,10 +36,12 @@ class G4Model:
         self.L = L
         self.desc = bd.ModelDesc(
             hidden=cfg["hidden"], n_heads=cfg["n_heads"], n_kv_heads=cfg["n_kv_heads"],
-            head_dim_swa=cfg["head_dim_swa"], head_dim_full=cfg["head_dim_full"], ffn=cfg["ffn"],
+            head_dim_swa=cfg["head_dim_swa"], head_dim_full=cfg["head_dim_full"],
+            ffn=max([cfg["ffn"]] + [int(f) for f in cfg.get("ffn_dims") or []]),
             ple_dim=cfg["ple_dim"], n_layers=L, window=cfg["window"], vocab=cfg.get("vocab", 1),
             ple_vocab=cfg.get("ple_vocab", 1), eps=cfg["eps"], theta_swa=cfg["theta_swa"],
-            theta_full=cfg["theta_full"], partial_rotary=cfg["partial_rotary"], dtype=self.g4_dtype)
+            theta_full=cfg["theta_full"], partial_rotary=cfg["partial_rotary"], dtype=self.g4_dtype,
+            k_eq_v=1 if cfg.get("k_eq_v") else 0, n_kv_heads_full=int(cfg.get("n_kv_heads_full") or 0))
         self.sliding = [1 if t == "S" else 0 for t in cfg["layer_types"]]
         self.kv_src = bd.g4_kv_sources(self.sliding, cfg["n_shared"])
         self.layers = layers
@@ -48,6 +52,7 @@ class G4Model:
             d.sliding = self.sliding[l]
             d.kv_src = self.kv_src[l]
             d.layer_scalar = float(lw.get("layer_scalar", 1.0))
+            d.ffn = int(lw["w_gate"].shape[0])
             own = self.kv_src[l] == l
             for name in bd.LAYER_PTRS:
                 t = lw.get(name)
@@ -58,6 +63,11 @@ class G4Model:
 
     def head_dim(self, l):
         return self.cfg["head_dim_swa"] if self.sliding[l] else self.cfg["head_dim_full"]
+
+    def kv_heads(self, l):
+        if self.sliding[l] or not self.cfg.get("n_kv_heads_full"):
+            return self.cfg["n_kv_heads"]
+        return self.cfg["n_kv_heads_full"]
 
     def new_caches(self, B, cap, fill=None, ring=0):
         """Device K/V caches [B, nkv, rows, hd] for every owning layer, plus the C table.
@@ -76,7 +86,7 @@ class G4Model:
             if fill is not None:
                 k, v = fill(l)
             else:
-                k = torch.zeros((B, self.cfg["n_kv_heads"], rows, hd), dtype=self.torch_dtype, device="cuda")
+                k = torch.zeros((B, self.kv_heads(l), rows, hd), dtype=self.torch_dtype, device="cuda")
                 v = torch.zeros_like(k)
             caches[l] = (k, v)
             table[l] = bd.KvEntry(k=k.data_ptr(), v=v.data_ptr(), cap=rows, hd=hd, sliding=self.sliding[l],

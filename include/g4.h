@@ -8,7 +8,8 @@
  *    stream `h` and per-layer inputs are always float32. Accumulation is always float32.
  *  - Weight matrices use the [out, in] layout: y = x W^T, rows of W are contiguous in `in`.
  *  - Token-major activations: row m = b*T + t holds token t of sequence b.
- *  - KV caches are [B, n_kv_heads, cap, head_dim]; token t of sequence b sits at row pos[b] + t.
+ *  - KV caches are [B, nkv, cap, head_dim], nkv the kv head count of the owning layer's type; token t of
+ *    sequence b sits at row pos[b] + t.
  *  - `pos` is a DEVICE int32 array [B] with the position of each sequence's first token in the call.
  *    Positions are not visible to the host: kernels skip cache writes and clip key ranges that fall
  *    outside [0, cap), so a bad position yields wrong values but never an out-of-bounds access.
@@ -47,10 +48,12 @@ typedef enum g4_mode { G4_PREFILL = 0, G4_DECODE = 1 } g4_mode;
 typedef struct g4_model_desc {
   int64_t hidden;        /* H */
   int64_t n_heads;       /* query heads nh */
-  int64_t n_kv_heads;    /* kv heads nkv; nh % nkv == 0, head h reads kv head h / (nh/nkv) */
+  int64_t n_kv_heads;    /* kv heads nkv of sliding layers (and of full layers when n_kv_heads_full == 0);
+                            nh % nkv == 0, head h reads kv head h / (nh/nkv) */
   int64_t head_dim_swa;  /* head width of sliding layers */
   int64_t head_dim_full; /* head width of full layers (global_head_dim) */
-  int64_t ffn;           /* gated FFN width F */
+  int64_t ffn;           /* gated FFN width F of every layer whose descriptor gives none; the workspace is
+                            sized for it, so it must be the largest width of the model */
   int64_t ple_dim;       /* per-layer input width d */
   int64_t n_layers;      /* L */
   int64_t window;        /* sliding window W: a query at i sees keys i-W < j <= i */
@@ -61,7 +64,11 @@ typedef struct g4_model_desc {
   float theta_full;      /* RoPE base of full layers */
   float partial_rotary;  /* full layers rotate floor(head_dim_full * partial_rotary / 2) pairs */
   int32_t dtype;         /* g4_dtype of weights and activations */
-  int32_t reserved;
+  int32_t k_eq_v;        /* 1: full layers have no V projection; V is the K projection's output, normed
+                            without scale and not rotated (turbospark-runtime families/gemma4/attn.rs,
+                            forward_layer, `attention_k_eq_v`); 0: every layer projects V with wv */
+  int64_t n_kv_heads_full; /* kv heads of full layers (turbospark-runtime forward_layer, `num_full_kv_heads`);
+                              0: the same as n_kv_heads */
 } g4_model_desc;
 
 /* One layer's weights (cortiq-engine `G4eLayer`). Norm weights are [H] or [head_dim]; all in dtype. */
@@ -69,17 +76,18 @@ typedef struct g4_layer_desc {
   int32_t sliding;       /* 1: sliding-window layer (head_dim_swa, theta_swa); 0: full layer */
   int32_t kv_src;        /* layer whose cache this layer attends over; == its own index if it owns one */
   float layer_scalar;    /* h *= layer_scalar after the block (1.0 when the model has none) */
-  int32_t reserved;
+  int32_t ffn;           /* this layer's FFN width, 1 .. model ffn (ferrox-models gemma4_engine.rs,
+                            Gemma4Hparams::ffn_dim); 0: the model's ffn */
   const void* input_norm;     /* [H] */
   const void* wq;             /* [nh*hd, H] */
   const void* wk;             /* [nkv*hd, H]; read only when the layer owns its cache */
-  const void* wv;             /* [nkv*hd, H]; idem */
+  const void* wv;             /* [nkv*hd, H]; idem; not read (may be NULL) on a full layer of a k_eq_v model */
   const void* wo;             /* [H, nh*hd] */
   const void* q_norm;         /* [hd] */
   const void* k_norm;         /* [hd]; idem */
   const void* post_attn_norm; /* [H] */
   const void* pre_ffn_norm;   /* [H] */
-  const void* w_gate;         /* [F, H] */
+  const void* w_gate;         /* [F, H], F the layer's FFN width */
   const void* w_up;           /* [F, H] */
   const void* w_down;         /* [H, F] */
   const void* post_ffn_norm;  /* [H] */

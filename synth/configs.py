@@ -1,4 +1,4 @@
-"""Workload descriptions: the five Gemma-4 E-series shapes this repository is tested and timed on.
+"""Workload descriptions: the Gemma-4 E-series shapes this repository is tested and timed on.
 
 Plain data only (sizes, dtypes, the layer-type pattern, how many tail layers share KV). Nothing here
 computes any step of the method; the routing of shared layers, head widths per type, frequencies and so
@@ -35,6 +35,12 @@ CONFIGS = {
     # Long-context, attention-heavy 12-layer slice.
     5: dict(E4B, name="e4b-12L-T32k", dtype="bf16", mode="prefill", B=1, T=32768,
             layer_types="SSSSSF" * 2, n_shared=4, embed=False),
+    # The variants at E4B widths: full layers with their own KV head count and V taken from the K
+    # projection (turbospark-runtime gemma4 `forward_layer`), and one FFN width per layer (ferrox-models
+    # `Gemma4Hparams::ffn_dim`). The two tail layers share KV, so the last full layer reads a K=V cache.
+    6: dict(E4B, name="e4b-variants-6L", dtype="bf16", mode="prefill", B=1, T=2048, layer_types="SSFSSF",
+            n_shared=2, embed=False, n_kv_heads_full=4, k_eq_v=True,
+            ffn_dims=[10240, 6144, 8192, 10240, 4096, 8192]),
 }
 
 

@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported_and_bound():
 
 
 def test_version_and_status_strings():
-    assert bd.lib().g4_version() >= 100
+    assert bd.lib().g4_version() >= 200
     assert bd.lib().g4_status_str(bd.G4_EGEOM) == b"G4_EGEOM"
 
 
@@ -129,6 +129,73 @@ def test_layer_validation_errors():
     assert call(model=m3) == bd.G4_EINVAL
     assert bd.g4_workspace_size(m, 1, 2048, 2048, bd.G4_PREFILL) > 0
     assert bd.g4_workspace_size(m3, 1, 2048, 2048, bd.G4_PREFILL) == 0
+
+
+def test_variant_validation_errors():
+    """Per-type KV heads, per-layer FFN widths and K=V are checked on the host before any launch."""
+    ld = bd.LayerDesc(sliding=0, kv_src=1, layer_scalar=1.0)
+    for n in bd.LAYER_PTRS:
+        setattr(ld, n, FAKE)
+    t = _table([(64, 256, 1), (64, 512, 0)])
+    L = bd.lib()
+
+    def call(model, desc, ws_bytes=1 << 40):
+        return L.g4_layer_forward(C.byref(model), C.byref(desc), 1, FAKE, FAKE, t, len(t), FAKE, 1, 8,
+                                  bd.G4_PREFILL, FAKE, ws_bytes, None)
+
+    m = _model()
+    m.n_kv_heads_full = 3
+    assert call(m, ld) == bd.G4_EGEOM                 # 8 query heads do not split into 3 kv groups
+    assert b"n_kv_heads_full" in L.g4_last_error()
+    m = _model()
+    m.k_eq_v = 2
+    assert call(m, ld) == bd.G4_EINVAL
+    no_v = bd.LayerDesc.from_buffer_copy(ld)
+    no_v.wv = None
+    assert call(_model(), no_v) == bd.G4_EINVAL       # a full layer needs wv unless the model is K=V
+    wide = bd.LayerDesc.from_buffer_copy(ld)
+    wide.ffn = _model().ffn + 64
+    assert call(_model(), wide) == bd.G4_ERANGE       # wider than the model's (workspace) width
+    wide.ffn = -1
+    assert call(_model(), wide) == bd.G4_ERANGE
+    # K=V model: the full layer may omit wv; the descriptor passes every check up to the (too small)
+    # workspace, so nothing is launched
+    m = _model()
+    m.k_eq_v = 1
+    m.n_kv_heads_full = 1
+    assert call(m, no_v, ws_bytes=1) == bd.G4_EINVAL
+    assert b"workspace" in L.g4_last_error()
+    # workspace grows with the larger of the two kv head counts
+    a = bd.g4_workspace_size(_model(), 1, 256, 256, bd.G4_PREFILL)
+    m = _model()
+    m.n_kv_heads_full = 8
+    assert bd.g4_workspace_size(m, 1, 256, 256, bd.G4_PREFILL) > a
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """The ctypes structs agree with the C compiler's layout of include/g4.h (size and every offset)."""
+    structs = {"g4_model_desc": bd.ModelDesc, "g4_layer_desc": bd.LayerDesc, "g4_kv_entry": bd.KvEntry}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "g4.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'  printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    import subprocess
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {}
+    for ln in out:
+        if ln:
+            a, b, c = ln.split()
+            got[(a, b)] = int(c)
+    for cname, py in structs.items():
+        assert got[(cname, "size")] == C.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert got[(cname, f)] == getattr(py, f).offset, (cname, f)
 
 
 def test_row_op_validation_errors():
