@@ -22,7 +22,8 @@ Readings where the pages are silent or disagree (each also listed in the design 
     identity for R <= j < hd_full/2 (the "zero tail" of `G4eGlobals::inv_freq_global`).
   * Shared-KV source: the last non-shared layer of the same attention type (page 1 module doc). A
     shared layer with no such layer keeps its own K/V.
-  * Window: query at position i sees keys i-W < j <= i.
+  * Window: query at position i sees keys i-W < j <= i. The encoder (page 4 `text_attention`) is not
+    causal: it sees the call's keys with |i - j| <= W on sliding layers and all of them on full layers.
   * Out-of-range token ids give a zero embedding row and a zero PLE table term.
   * Variants: full layers may have their own KV head count; per-layer FFN widths follow the weight
     shapes (page 2 `ffn_dim`); with K=V a full layer's V is the K projection output before the K norm
@@ -209,6 +210,38 @@ def attention(q, K, V, qpos, window=None, scale=1.0, chunk=256):
     return out
 
 
+def attention_bidirectional(q, K, V, qpos, k0, k1, window=None, scale=1.0, chunk=256):
+    """Non-causal GQA softmax attention of one sequence over its own keys (page 4 `text_attention`).
+
+    q [T, nh, hd]; K, V [nkv, cap, hd]; qpos [T] absolute positions; the sequence's keys are the cache
+    rows k0 <= j < k1. A query at position i sees all of them on a full layer, and on a sliding layer
+    those with |i - j| <= W (up to W keys on either side of it, itself included). Score scale 1.0.
+    """
+    q, K, V = f64(q), f64(K), f64(V)
+    qpos = _ints(qpos)
+    T, nh, hd = q.shape
+    nkv = K.shape[0]
+    grp = nh // nkv
+    out = np.zeros((T, nh, V.shape[-1]))
+    for t0 in range(0, T, chunk):
+        t1 = min(T, t0 + chunk)
+        p = qpos[t0:t1]
+        lo = k0 if window is None else max(k0, int(p.min()) - window)
+        hi = k1 if window is None else min(k1, int(p.max()) + window + 1)
+        j = np.arange(lo, hi)
+        vis = np.ones((t1 - t0, hi - lo), dtype=bool)
+        if window is not None:
+            vis &= np.abs(j[None, :] - p[:, None]) <= window
+        for h in range(nh):
+            g = h // grp
+            s = scale * (q[t0:t1, h, :] @ K[g, lo:hi, :].T)
+            s = np.where(vis, s, -np.inf)
+            s = s - s.max(axis=1, keepdims=True)
+            e = np.exp(s)
+            out[t0:t1, h, :] = (e / e.sum(axis=1, keepdims=True)) @ V[g, lo:hi, :]
+    return out
+
+
 # --------------------------------------------------------------------------------------------
 # Entry: embedding and per-layer inputs (page 1 `extend_embedding`; page 2 `project_per_layer_inputs`)
 # --------------------------------------------------------------------------------------------
@@ -251,13 +284,14 @@ def ple_inputs(ids, e, W_pm, ple_norm, Tab, cfg):
 # One decoder layer (page 1 `g4e_forward` body; page 2 `forward_token_on_worker`)
 # --------------------------------------------------------------------------------------------
 
-def layer_forward(cfg, lw, layer, src, h, ple_l, pos, caches, trace=None):
+def layer_forward(cfg, lw, layer, src, h, ple_l, pos, caches, trace=None, bidirectional=False):
     """One layer over all tokens of a batch.
 
     h [B, T, H] residual (f64, updated copy returned); ple_l [B, T, d] this layer's per-layer input;
     pos [B, T] absolute positions; caches {layer: (K, V)} with K, V [B, nkv, cap, hd] float64 arrays,
     modified in place when the layer owns its cache (src == layer). `trace`, if a dict, receives the
-    intermediates.
+    intermediates. `bidirectional`: the encoder's attention (page 4 `text_attention`) over the call's
+    own keys, positions pos[b, 0] .. pos[b, 0] + T - 1, instead of the causal one.
     """
     eps = cfg["eps"]
     nh, nkv = cfg["n_heads"], kv_heads(cfg, layer)
@@ -284,7 +318,11 @@ def layer_forward(cfg, lw, layer, src, h, ple_l, pos, caches, trace=None):
     if K.shape[-1] != hd:
         raise ValueError(f"layer {layer}: source cache head_dim {K.shape[-1]} != {hd}")
     window = cfg["window"] if sliding else None
-    o = np.stack([attention(q[b], K[b], V[b], pos[b], window) for b in range(B)])
+    if bidirectional:
+        o = np.stack([attention_bidirectional(q[b], K[b], V[b], pos[b], int(pos[b, 0]), int(pos[b, 0]) + T, window)
+                      for b in range(B)])
+    else:
+        o = np.stack([attention(q[b], K[b], V[b], pos[b], window) for b in range(B)])
     a = o.reshape(B, T, nh * hd) @ f64(lw["wo"]).T
     h = h + rms_norm(a, lw["post_attn_norm"], eps)
 
@@ -305,12 +343,12 @@ def layer_forward(cfg, lw, layer, src, h, ple_l, pos, caches, trace=None):
     return h
 
 
-def layer_forward_rows(cfg, lw, layer, h, ple_l, pos0, rows):
+def layer_forward_rows(cfg, lw, layer, h, ple_l, pos0, rows, bidirectional=False):
     """Selected output rows of one cache-owning layer over a prefill of one sequence.
 
     h [T, H] is the layer's input for tokens at positions pos0 .. pos0+T-1 (nothing cached before pos0),
     ple_l [T, d]. Only the K/V rows the selected queries can see are formed, so a long sequence can be
-    checked at a few rows. Same formulas as `layer_forward`, restricted to rows.
+    checked at a few rows. Same formulas as `layer_forward`, restricted to rows (`bidirectional` as there).
     """
     eps = cfg["eps"]
     nh, nkv = cfg["n_heads"], kv_heads(cfg, layer)
@@ -319,23 +357,29 @@ def layer_forward_rows(cfg, lw, layer, h, ple_l, pos0, rows):
     h = f64(h)
     rows = np.asarray(sorted(set(int(r) for r in rows)))
     W = cfg["window"]
+    T = h.shape[0]
     need = set()
     for r in rows:
-        lo = max(0, r - W + 1) if sliding else 0
-        need.update(range(lo, r + 1))
+        if bidirectional:
+            need.update(range(max(0, r - W), min(T, r + W + 1)) if sliding else range(T))
+        else:
+            need.update(range(max(0, r - W + 1) if sliding else 0, r + 1))
     need = np.asarray(sorted(need))
     xk = rms_norm(h[need], lw["input_norm"], eps)
     pk = (pos0 + need)[:, None]
     k = rope(rms_norm((xk @ f64(lw["wk"]).T).reshape(len(need), nkv, hd), lw["k_norm"], eps), pk, inv)
     v = rms_norm((xk @ f64(value_weight(cfg, lw, layer)).T).reshape(len(need), nkv, hd), None, eps)
-    cap = pos0 + int(rows.max()) + 1
+    cap = pos0 + int(need.max()) + 1
     K, V = np.zeros((nkv, cap, hd)), np.zeros((nkv, cap, hd))
     K[:, pos0 + need, :] = k.transpose(1, 0, 2)
     V[:, pos0 + need, :] = v.transpose(1, 0, 2)
     hr = h[rows]
     xn = rms_norm(hr, lw["input_norm"], eps)
     q = rope(rms_norm((xn @ f64(lw["wq"]).T).reshape(len(rows), nh, hd), lw["q_norm"], eps), (pos0 + rows)[:, None], inv)
-    o = attention(q, K, V, pos0 + rows, W if sliding else None)
+    if bidirectional:
+        o = attention_bidirectional(q, K, V, pos0 + rows, pos0, pos0 + T, W if sliding else None)
+    else:
+        o = attention(q, K, V, pos0 + rows, W if sliding else None)
     hr = hr + rms_norm(o.reshape(len(rows), nh * hd) @ f64(lw["wo"]).T, lw["post_attn_norm"], eps)
     xn2 = rms_norm(hr, lw["pre_ffn_norm"], eps)
     act = gelu_tanh(xn2 @ f64(lw["w_gate"]).T) * (xn2 @ f64(lw["w_up"]).T)
@@ -368,11 +412,12 @@ def entry(cfg, glob, ids):
     return e, ple
 
 
-def forward(cfg, layers, h0, ple_in, pos, caches, srcs=None, layer_range=None, per_layer=None):
+def forward(cfg, layers, h0, ple_in, pos, caches, srcs=None, layer_range=None, per_layer=None, bidirectional=False):
     """Run layers over h0 [B, T, H] with per-layer inputs ple_in [B, T, L, d] at positions pos [B, T].
 
     Returns the hidden state before the final norm (page 1: the caller applies the final norm, lm_head
     and softcap). `layers` is a list (or a callable layer -> weights dict, for lazy loading).
+    `bidirectional`: every layer attends like page 4's encoder (see `layer_forward`).
     """
     srcs = srcs if srcs is not None else kv_sources(cfg["layer_types"], cfg["n_shared"])
     h = f64(h0)
@@ -380,7 +425,7 @@ def forward(cfg, layers, h0, ple_in, pos, caches, srcs=None, layer_range=None, p
     rng = layer_range if layer_range is not None else range(cfg["n_layers"])
     for l in rng:
         lw = layers(l) if callable(layers) else layers[l]
-        h = layer_forward(cfg, lw, l, srcs[l], h, ple_in[:, :, l, :], pos, caches)
+        h = layer_forward(cfg, lw, l, srcs[l], h, ple_in[:, :, l, :], pos, caches, bidirectional=bidirectional)
         if per_layer is not None:
             per_layer.append(h)
     return h

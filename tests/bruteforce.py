@@ -49,9 +49,11 @@ def attend(qh, keys, vals):
     return [sum(e[j] * vals[j][d] for j in range(len(keys))) / z for d in range(len(vals[0]))]
 
 
-def layer(cfg, lw, layer_idx, own_kv, h_rows, ple_rows, positions, cache):
+def layer(cfg, lw, layer_idx, own_kv, h_rows, ple_rows, positions, cache, bidirectional=False):
     """One layer for one sequence. h_rows: list of T lists (H); cache: dict with 'k','v' lists
-    indexed [g][pos] -> list(hd) (mutated when own_kv). Returns the new list of rows."""
+    indexed [g][pos] -> list(hd) (mutated when own_kv). Returns the new list of rows.
+    bidirectional: the encoder's mask, every key of the call within W positions on either side (sliding)
+    or every key of the call (full)."""
     eps, nh = cfg["eps"], cfg["n_heads"]
     sliding = cfg["layer_types"][layer_idx] == "S"
     # variants: a full layer may have its own KV head count, and with K=V its V comes from the K weight
@@ -83,12 +85,15 @@ def layer(cfg, lw, layer_idx, own_kv, h_rows, ple_rows, positions, cache):
                 cache["v"][g][positions[t]] = rms(v[g * hd:(g + 1) * hd], None, eps)
     for t in range(T):
         i = positions[t]
-        lo = max(0, i - W + 1) if sliding else 0
+        if bidirectional:
+            sel = [j for j in positions if not sliding or abs(i - j) <= W]
+        else:
+            sel = list(range(max(0, i - W + 1) if sliding else 0, i + 1))
         o = []
         for hh in range(nh):
             g = hh // grp
-            keys = [cache["k"][g][j] for j in range(lo, i + 1)]
-            vals = [cache["v"][g][j] for j in range(lo, i + 1)]
+            keys = [cache["k"][g][j] for j in sel]
+            vals = [cache["v"][g][j] for j in sel]
             o.extend(attend(qs[t][hh], keys, vals))
         a = matvec(lw["wo"], o)
         an = rms(a, lw["post_attn_norm"], eps)

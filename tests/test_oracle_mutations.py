@@ -28,6 +28,12 @@ MUTATIONS = {
                                   'v = rms_norm(k, None, eps) if cfg.get("k_eq_v") and not sliding else '
                                   'rms_norm((xn @ f64(value_weight(cfg, lw, layer)).T).reshape(B, T, nkv, hd), None, eps)'),
     "full_kv_heads_ignored": ('return cfg.get("n_kv_heads_full") or cfg["n_kv_heads"]', 'return cfg["n_kv_heads"]'),
+    "bidir_band_one_sided": ("vis &= np.abs(j[None, :] - p[:, None]) <= window",
+                             "vis &= (j[None, :] - p[:, None] <= 0) & (p[:, None] - j[None, :] <= window)"),
+    "bidir_band_strict": ("vis &= np.abs(j[None, :] - p[:, None]) <= window",
+                          "vis &= np.abs(j[None, :] - p[:, None]) < window"),
+    "bidir_flag_dropped": ("h = layer_forward(cfg, lw, l, srcs[l], h, ple_in[:, :, l, :], pos, caches, bidirectional=bidirectional)",
+                           "h = layer_forward(cfg, lw, l, srcs[l], h, ple_in[:, :, l, :], pos, caches)"),
     "eps_outside_mean": ("y = x * (ms + eps) ** -0.5", "y = x * (ms ** -0.5 + eps)"),
     "partial_rotary_denominator": ("inv = float(theta) ** (-2.0 * j / hd)",
                                    "inv = float(theta) ** (-2.0 * j / (2 * max(n_rot, 1)))"),

@@ -160,6 +160,33 @@ def test_attention_matches_torch_sdpa_with_mask_and_repeated_kv():
         np.testing.assert_allclose(got, ref.transpose(0, 1).numpy(), rtol=1e-11, atol=1e-12)
 
 
+def test_bidirectional_attention_matches_torch_sdpa():
+    """Page 4 `text_attention`: no causal mask; sliding keys within |i - j| <= W (a band of 2W + 1);
+    the call's keys only (rows outside [k0, k1) of the cache hold junk that must not be seen)."""
+    T, nh, nkv, hd, W = 29, 8, 2, 16, 4
+    q, K, V = _rand_qkv(T, nh, nkv, hd)
+    k0 = 3  # the sequence occupies cache rows 3 .. 3 + T - 1 of a longer cache
+    Kc = np.concatenate([rng.normal(size=(nkv, 3, hd)) * 50, K, rng.normal(size=(nkv, 4, hd)) * 50], axis=1)
+    Vc = np.concatenate([rng.normal(size=(nkv, 3, hd)) * 50, V, rng.normal(size=(nkv, 4, hd)) * 50], axis=1)
+    for window in (None, W):
+        got = O.attention_bidirectional(q, Kc, Vc, k0 + np.arange(T), k0, k0 + T, window, chunk=8)
+        i, j = np.arange(T)[:, None], np.arange(T)[None, :]
+        mask = np.ones((T, T), bool) if window is None else (np.abs(i - j) <= window)
+        Kr = torch.from_numpy(K).repeat_interleave(nh // nkv, dim=0)
+        Vr = torch.from_numpy(V).repeat_interleave(nh // nkv, dim=0)
+        ref = F.scaled_dot_product_attention(torch.from_numpy(q).transpose(0, 1), Kr, Vr,
+                                             attn_mask=torch.from_numpy(mask), scale=1.0)
+        np.testing.assert_allclose(got, ref.transpose(0, 1).numpy(), rtol=1e-11, atol=1e-12)
+    # band edges: the first query sees keys 0..W, a middle one 2W + 1 keys; a window of T - 1 is full
+    full = O.attention_bidirectional(q, K, V, np.arange(T), 0, T, None)
+    np.testing.assert_allclose(O.attention_bidirectional(q, K, V, np.arange(T), 0, T, T - 1), full, rtol=1e-13)
+    assert not np.allclose(O.attention_bidirectional(q, K, V, np.arange(T), 0, T, T - 2), full)
+    # the last query of a full layer sees every key either way: causal and bidirectional rows agree
+    causal = O.attention(q, K, V, np.arange(T), None)
+    np.testing.assert_allclose(full[-1], causal[-1], rtol=1e-12)
+    assert not np.allclose(full[0], causal[0])
+
+
 def test_attention_special_cases():
     T, nh, nkv, hd = 9, 4, 1, 8
     q, K, V = _rand_qkv(T, nh, nkv, hd)
@@ -251,9 +278,11 @@ def _run_oracle_stack(cfg, layers, h0, ple, pos, srcs, cap):
 VARIANT = dict(n_kv_heads_full=4, k_eq_v=True, ffn_dims=[48, 40, 56, 32, 24])
 
 
-@pytest.mark.parametrize("types,n_shared,extra", [("SSF", 0, {}), ("SFSSF", 2, {}), ("SFSSF", 2, VARIANT),
-                                                  ("SFSFF", 0, dict(VARIANT, n_kv_heads_full=1))])
-def test_stack_brute_force(types, n_shared, extra):
+@pytest.mark.parametrize("types,n_shared,extra,bidir", [("SSF", 0, {}, False), ("SFSSF", 2, {}, False),
+                                                        ("SFSSF", 2, VARIANT, False),
+                                                        ("SFSFF", 0, dict(VARIANT, n_kv_heads_full=1), False),
+                                                        ("SFSSF", 0, {}, True), ("SSFSF", 2, {"window": 2}, True)])
+def test_stack_brute_force(types, n_shared, extra, bidir):
     cfg = configs.tiny(layer_types=types, n_shared=n_shared, T=6, **extra)
     glob, layers = _tiny_model(cfg)
     for lw in layers:
@@ -262,7 +291,8 @@ def test_stack_brute_force(types, n_shared, extra):
     h0, ple = O.entry(cfg, glob, ids)
     srcs = O.kv_sources(types, n_shared)
     pos = O.prefill_positions([0], cfg["T"])
-    got, _ = _run_oracle_stack(cfg, layers, h0, ple, pos, srcs, cfg["T"])
+    caches = O.new_caches(cfg, 1, cfg["T"], srcs)
+    got = O.forward(cfg, layers, h0, ple, pos, caches, srcs, bidirectional=bidir)
     rows = h0[0].tolist()
     bcache = {}
     for l in range(cfg["n_layers"]):
@@ -273,7 +303,7 @@ def test_stack_brute_force(types, n_shared, extra):
                          "v": [[None] * cfg["T"] for _ in range(nkv)]}
         lw = {k: (f64l(v) if isinstance(v, torch.Tensor) else v) for k, v in layers[l].items()}
         rows = bf.layer(cfg, lw, l, srcs[l] == l, rows, ple[0, :, l, :].tolist(), list(range(cfg["T"])),
-                        bcache[srcs[l]])
+                        bcache[srcs[l]], bidirectional=bidir)
         assert len(rows[0]) == cfg["hidden"] and hd > 0
     np.testing.assert_allclose(got[0], np.array(rows), rtol=1e-10, atol=1e-11)
 
@@ -407,14 +437,15 @@ def test_batch_rows_are_independent():
     np.testing.assert_allclose(one[0], out[1], rtol=1e-13, atol=1e-13)
 
 
-@pytest.mark.parametrize("types", ["SSF", "FSS"])
-def test_layer_rows_equal_whole_layer_rows(types):
+@pytest.mark.parametrize("types,bidir", [("SSF", False), ("FSS", False), ("SSF", True), ("FSS", True)])
+def test_layer_rows_equal_whole_layer_rows(types, bidir):
     cfg = configs.tiny(layer_types=types, T=13, window=4)
     _, layers = _tiny_model(cfg)
     h = rng.normal(size=(1, 13, cfg["hidden"]))
     ple = rng.normal(size=(1, 13, cfg["ple_dim"]))
-    whole = O.layer_forward(cfg, layers[0], 0, 0, h, ple, O.prefill_positions([3], 13), O.new_caches(cfg, 1, 16))
-    rows, part = O.layer_forward_rows(cfg, layers[0], 0, h[0], ple[0], 3, [12, 0, 5, 9])
+    whole = O.layer_forward(cfg, layers[0], 0, 0, h, ple, O.prefill_positions([3], 13), O.new_caches(cfg, 1, 16),
+                            bidirectional=bidir)
+    rows, part = O.layer_forward_rows(cfg, layers[0], 0, h[0], ple[0], 3, [12, 0, 5, 9], bidirectional=bidir)
     np.testing.assert_allclose(part, whole[0, rows], rtol=1e-13, atol=1e-13)
 
 
