@@ -56,12 +56,17 @@ def gemm_flops(cfg, M):
 
 
 def attn_flops(cfg, T):
-    """4 * nh * hd * (visible query-key pairs) over all layers of a prefill from position 0."""
+    """4 * nh * hd * (visible query-key pairs) over all layers of a prefill from position 0 (the
+    encoder: every pair on full layers, |i - j| <= W on sliding layers)."""
     tot = 0
     W = cfg["window"]
+    enc = cfg["mode"] == "encode"
     for t in cfg["layer_types"]:
         hd = cfg["head_dim_swa"] if t == "S" else cfg["head_dim_full"]
-        pairs = T * (T + 1) // 2 if t == "F" else sum(min(i + 1, W) for i in range(T))
+        if enc:
+            pairs = T * T if t == "F" else sum(min(i + W, T - 1) - max(i - W, 0) + 1 for i in range(T))
+        else:
+            pairs = T * (T + 1) // 2 if t == "F" else sum(min(i + 1, W) for i in range(T))
         tot += 4 * cfg["n_heads"] * hd * pairs * cfg["B"]
     return tot
 
@@ -151,7 +156,7 @@ def run_gpu(cfg, steps, warmup, breakdown, use_graph=True):
     else:
         cap = T
         _, table = model.new_caches(B, cap)
-        mode = bd.G4_PREFILL
+        mode = bd.G4_ENCODE if cfg["mode"] == "encode" else bd.G4_PREFILL
     H = cfg["hidden"]
     h = torch.empty((B, T, H), dtype=torch.float32, device="cuda")
     ple = None if cfg["embed"] else acts["ple_in"]
@@ -255,7 +260,7 @@ def cpu_baseline(cfg, budget_s):
         t0 = time.perf_counter()
         if cfg["embed"]:
             h0, ple = O.entry(sub2, gh, idl)
-        O.forward(sub, layers, h0, ple, pos, caches, srcs)
+        O.forward(sub, layers, h0, ple, pos, caches, srcs, bidirectional=cfg["mode"] == "encode")
         return time.perf_counter() - t0
 
     if cfg["mode"] == "decode":
@@ -320,7 +325,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5, 6])
+    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5, 6, 7])
     ap.add_argument("--batch", type=int, default=64, help="decode batch (workload 4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
@@ -346,7 +351,8 @@ def main():
     dom_avg_s = r["dom_ms"] / max(r["dom_n"], 1) / 1e3
     names = {2: "e4b-layer-pair prefill", 3: "e4b-42-layer prefill from token ids", 4: "e4b-42-layer decode",
              5: "e4b-12-layer long-context prefill",
-             6: "e4b-width 6-layer prefill with the variants (full-layer kv heads, K=V, per-layer FFN widths)"}
+             6: "e4b-width 6-layer prefill with the variants (full-layer kv heads, K=V, per-layer FFN widths)",
+             7: "e4b-width 6-layer bidirectional encoder"}
     wname = f"{names[args.workload]}: B={B} T={T}" + (f" ctx={cfg['ctx']}" if decode else "")
     traffic = counted_traffic(wname, "gate_up_gemm")
     if decode:
@@ -371,7 +377,7 @@ def main():
         extra["breakdown_ms_per_step"] = r["breakdown_ms_per_step"]
         extra["class_rates"] = class_rates(cfg, tokens, decode, r["breakdown_ms_per_step"])
     line = dict(
-        metric="prefill tokens/s" if not decode else "decode tokens/s",
+        metric="decode tokens/s" if decode else ("encoder tokens/s" if cfg["mode"] == "encode" else "prefill tokens/s"),
         value=round(tokens / (ms / 1e3), 2), unit="tokens/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
         ms_per_step=round(ms, 4), higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16",
         data="synthetic (seeded N(0,0.02) weights, N(0,1) activations / uniform token ids)",

@@ -11,7 +11,7 @@ LIB_PATH = os.path.join(HERE, "libg4.so")
 
 G4_OK, G4_EINVAL, G4_EGEOM, G4_ERANGE, G4_EHIP, G4_EUNSUP = range(6)
 G4_F32, G4_BF16 = 0, 1
-G4_PREFILL, G4_DECODE = 0, 1
+G4_PREFILL, G4_DECODE, G4_ENCODE = 0, 1, 2
 
 i32, i64, f32, vp, sz = C.c_int32, C.c_int64, C.c_float, C.c_void_p, C.c_size_t
 
@@ -45,6 +45,8 @@ _SIGS = {
     "g4_qk_norm_rope": (C.c_int, [vp, i64, vp, vp, i64, i64, vp, i64, i64, i64, i64, f32, i64, f32, i32, vp]),
     "g4_attn_prefill": (C.c_int, [vp, i64, vp, i32, i32, i32, i32, i64, vp, i64, i64, i64, i64, i64, f32, vp, i64,
                                   i32, vp]),
+    "g4_attn_encode": (C.c_int, [vp, i64, vp, i32, i32, i32, i32, i64, vp, i64, i64, i64, i64, i64, f32, vp, i64,
+                                 i32, vp]),
     "g4_attn_decode": (C.c_int, [vp, i64, vp, i32, i32, i32, i32, i64, vp, i64, i64, i64, i64, f32, vp, i64, vp, sz,
                                  i32, vp]),
     "g4_attn_decode_ws": (sz, [i64, i64, i64, i64]),
@@ -124,6 +126,12 @@ def g4_qk_norm_rope(x, x_ld, w, y, y_ld, y_cap, pos, B, T, heads, hd, theta, rot
 def g4_attn_prefill(q, q_ld, kv, n_kv, layer, kv_src, sliding, window, pos0, B, T, nh, nkv, hd, scale, out, out_ld,
                     dtype, stream=None):
     return _call("g4_attn_prefill", q, q_ld, kv, n_kv, layer, kv_src, sliding, window, pos0, B, T, nh, nkv, hd, scale,
+                 out, out_ld, dtype, stream)
+
+
+def g4_attn_encode(q, q_ld, kv, n_kv, layer, kv_src, sliding, window, pos0, B, T, nh, nkv, hd, scale, out, out_ld,
+                   dtype, stream=None):
+    return _call("g4_attn_encode", q, q_ld, kv, n_kv, layer, kv_src, sliding, window, pos0, B, T, nh, nkv, hd, scale,
                  out, out_ld, dtype, stream)
 
 

@@ -126,7 +126,9 @@ static g4_status check_kv(const g4_kv_entry* kv, int32_t n_kv, int32_t layer, in
   } else {
     G4_REQ(T <= e.cap, G4_ERANGE, "T %lld exceeds cache capacity %lld", (long long)T, (long long)e.cap);
   }
-  G4_REQ(mode == G4_PREFILL || T == 1, G4_EINVAL, "decode takes T == 1");
+  G4_REQ(mode != G4_DECODE || T == 1, G4_EINVAL, "decode takes T == 1");
+  G4_REQ(mode != G4_ENCODE || !e.ring, G4_EINVAL, "kv entry %d: the encoder's attention needs a linear cache",
+         kv_src);
   return G4_OK;
 }
 
@@ -158,7 +160,7 @@ static Plan plan(const g4_model_desc* m, int64_t B, int64_t T, int64_t cap, int3
   if (mode == G4_DECODE) o += al(attn_decode_ws(B, m->n_heads, hdm, cap > 0 ? cap : 1));
   p.aws = o;  // key-split partials of a short prefill's attention
   p.aws_bytes = 0;
-  if (mode == G4_PREFILL) {
+  if (mode != G4_DECODE) {
     const size_t s0 = attn_prefill_ws(B, T, m->n_heads, kv_heads(m, 1), m->head_dim_swa);
     const size_t s1 = attn_prefill_ws(B, T, m->n_heads, kv_heads(m, 0), m->head_dim_full);
     p.aws_bytes = s0 > s1 ? s0 : s1;
@@ -390,7 +392,7 @@ static g4_status few_row_layer(const LayerCtx& c) {
     AttnArgs aa{};
     aa.q = qkv; aa.q_ld = qld; aa.k = src.k; aa.v = src.v; aa.cap = src.cap; aa.pos0 = c.pos;
     aa.B = c.B; aa.T = c.T; aa.nh = nh; aa.nkv = nkv; aa.hd = hd; aa.sliding = sliding; aa.window = m->window;
-    aa.scale = 1.f; aa.out = ao; aa.out_ld = nh * hd; aa.ring = src.ring;
+    aa.scale = 1.f; aa.out = ao; aa.out_ld = nh * hd; aa.ring = src.ring; aa.bidir = c.mode == G4_ENCODE;
     TimedScope ts(G4_KC_ATTENTION, c.s);
     if (c.mode == G4_DECODE) G4_TRY(attn_decode(aa, c.ws + c.p->dec, c.p->fx - c.p->dec, dt, c.s));
     else G4_TRY(attn_prefill(aa, dt, c.s));
@@ -544,7 +546,7 @@ static g4_status layer_impl(const LayerCtx& c) {
   AttnArgs aa{};
   aa.q = qkv; aa.q_ld = qld; aa.k = src.k; aa.v = src.v; aa.cap = src.cap; aa.pos0 = c.pos;
   aa.B = c.B; aa.T = c.T; aa.nh = nh; aa.nkv = nkv; aa.hd = hd; aa.sliding = sliding; aa.window = m->window;
-  aa.scale = 1.f; aa.out = ao; aa.out_ld = nh * hd; aa.ring = src.ring;
+  aa.scale = 1.f; aa.out = ao; aa.out_ld = nh * hd; aa.ring = src.ring; aa.bidir = c.mode == G4_ENCODE;
   aa.ws = (float*)(c.ws + c.p->aws); aa.ws_bytes = c.p->aws_bytes;
   {
     TimedScope ts(G4_KC_ATTENTION, c.s);
@@ -616,7 +618,7 @@ const char* g4_status_str(int status) {
 
 const char* g4_last_error(void) { return g_last_error.c_str(); }
 
-int g4_version(void) { return 200; }
+int g4_version(void) { return 300; }
 
 g4_status g4_kv_sources(const int32_t* sliding, int32_t n_layers, int32_t n_shared, int32_t* kv_src) {
   G4_REQ(sliding && kv_src, G4_EINVAL, "sliding or kv_src is NULL");
@@ -689,19 +691,35 @@ static g4_status check_attn(const void* q, int64_t q_ld, const g4_kv_entry* kv, 
   return check_kv(kv, n_kv, layer, kv_src, sliding, hd, T, mode, window);
 }
 
-g4_status g4_attn_prefill(const void* q, int64_t q_ld, const g4_kv_entry* kv, int32_t n_kv, int32_t layer,
-                          int32_t kv_src, int32_t sliding, int64_t window, const int32_t* pos0, int64_t B,
-                          int64_t T, int64_t nh, int64_t nkv, int64_t hd, float scale, void* out, int64_t out_ld,
-                          int32_t dtype, void* stream) {
+static g4_status attn_prefill_entry(const void* q, int64_t q_ld, const g4_kv_entry* kv, int32_t n_kv, int32_t layer,
+                                    int32_t kv_src, int32_t sliding, int64_t window, const int32_t* pos0, int64_t B,
+                                    int64_t T, int64_t nh, int64_t nkv, int64_t hd, float scale, void* out,
+                                    int64_t out_ld, int32_t dtype, void* stream, int32_t mode) {
   g4_status st = check_attn(q, q_ld, kv, n_kv, layer, kv_src, sliding, window, pos0, B, T, nh, nkv, hd, out,
-                            out_ld, dtype, G4_PREFILL);
+                            out_ld, dtype, mode);
   if (st != G4_OK) return st;
   AttnArgs a{};
   a.q = q; a.q_ld = q_ld; a.k = kv[kv_src].k; a.v = kv[kv_src].v; a.cap = kv[kv_src].cap; a.pos0 = pos0;
   a.B = B; a.T = T; a.nh = nh; a.nkv = nkv; a.hd = hd; a.sliding = sliding; a.window = window; a.scale = scale;
-  a.out = out; a.out_ld = out_ld; a.ring = kv[kv_src].ring;
+  a.out = out; a.out_ld = out_ld; a.ring = kv[kv_src].ring; a.bidir = mode == G4_ENCODE;
   if (B * T == 0) return G4_OK;
   return attn_prefill(a, dtype, (hipStream_t)stream);
+}
+
+g4_status g4_attn_prefill(const void* q, int64_t q_ld, const g4_kv_entry* kv, int32_t n_kv, int32_t layer,
+                          int32_t kv_src, int32_t sliding, int64_t window, const int32_t* pos0, int64_t B,
+                          int64_t T, int64_t nh, int64_t nkv, int64_t hd, float scale, void* out, int64_t out_ld,
+                          int32_t dtype, void* stream) {
+  return attn_prefill_entry(q, q_ld, kv, n_kv, layer, kv_src, sliding, window, pos0, B, T, nh, nkv, hd, scale, out,
+                            out_ld, dtype, stream, G4_PREFILL);
+}
+
+g4_status g4_attn_encode(const void* q, int64_t q_ld, const g4_kv_entry* kv, int32_t n_kv, int32_t layer,
+                         int32_t kv_src, int32_t sliding, int64_t window, const int32_t* pos0, int64_t B,
+                         int64_t T, int64_t nh, int64_t nkv, int64_t hd, float scale, void* out, int64_t out_ld,
+                         int32_t dtype, void* stream) {
+  return attn_prefill_entry(q, q_ld, kv, n_kv, layer, kv_src, sliding, window, pos0, B, T, nh, nkv, hd, scale, out,
+                            out_ld, dtype, stream, G4_ENCODE);
 }
 
 size_t g4_attn_decode_ws(int64_t B, int64_t nh, int64_t hd, int64_t cap) { return attn_decode_ws(B, nh, hd, cap); }
@@ -909,7 +927,7 @@ g4_status g4_layer_forward(const g4_model_desc* model, const g4_layer_desc* ld, 
                            int64_t T, int32_t mode, void* ws, size_t ws_bytes, void* stream) {
   g4_status st = check_model(model);
   if (st != G4_OK) return st;
-  G4_REQ(mode == G4_PREFILL || mode == G4_DECODE, G4_EINVAL, "mode %d", mode);
+  G4_REQ(mode == G4_PREFILL || mode == G4_DECODE || mode == G4_ENCODE, G4_EINVAL, "mode %d", mode);
   G4_REQ(h && ple_in && pos, G4_EINVAL, "h, ple_in or pos is NULL");
   G4_REQ(B >= 0 && T >= 0, G4_EINVAL, "B, T");
   if ((st = check_layer(model, ld, layer, kv, n_kv, T, mode)) != G4_OK) return st;
@@ -922,7 +940,7 @@ g4_status g4_stack_forward(const g4_model_desc* model, const g4_layer_desc* laye
   g4_status st = check_model(model);
   if (st != G4_OK) return st;
   G4_REQ(layers, G4_EINVAL, "layers is NULL");
-  G4_REQ(mode == G4_PREFILL || mode == G4_DECODE, G4_EINVAL, "mode %d", mode);
+  G4_REQ(mode == G4_PREFILL || mode == G4_DECODE || mode == G4_ENCODE, G4_EINVAL, "mode %d", mode);
   G4_REQ(h && ple_in && pos, G4_EINVAL, "h, ple_in or pos is NULL");
   G4_REQ(B >= 0 && T >= 0, G4_EINVAL, "B, T");
   for (int32_t l = 0; l < model->n_layers; ++l)

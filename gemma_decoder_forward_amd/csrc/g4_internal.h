@@ -155,6 +155,7 @@ struct AttnArgs {
   float scale;
   void* out; int64_t out_ld;
   int32_t ring;  // the cache is a ring of cap rows: key j lives in row j mod cap
+  int32_t bidir; // prefill only: the encoder's non-causal mask over the call's own keys
   // Prefill only, optional: float32 scratch of attn_prefill_ws() bytes for key-split partial results
   // (used when a short prefill gives too few query blocks to fill the device); null = no key split.
   float* ws; size_t ws_bytes;
@@ -169,6 +170,33 @@ __device__ __forceinline__ int64_t kv_row(int64_t j, int64_t cap, int32_t ring) 
 }
 __device__ __forceinline__ int64_t kv_last(int64_t i, int64_t cap, int32_t ring) {
   return ring || i < cap - 1 ? i : cap - 1;
+}
+
+// Keys a query at position i sees, as [max(i - back, kmin), min(i + fwd, kmax)].
+//   causal (decoder): back = W - 1 on sliding layers (W keys, itself included), unbounded on full
+//     layers; fwd = 0; kmin = 0; kmax = the last row of a linear cache.
+//   bidir (encoder, taconite-embeddinggemma2 `text_attention`): the call's keys p0 .. p0 + T - 1 only,
+//     with back = fwd = W on sliding layers (|i - j| <= W) and unbounded on full layers.
+struct KeySpan {
+  int64_t back, fwd, kmin, kmax;
+};
+__device__ __forceinline__ KeySpan key_span(int32_t bidir, int32_t sliding, int64_t window, int64_t cap,
+                                            int32_t ring, int64_t p0, int64_t T) {
+  const int64_t big = (int64_t)1 << 48;  // "unbounded": i +- big cannot overflow for any real position
+  const int64_t w = window < big ? window : big;
+  KeySpan s;
+  if (bidir) {
+    s.back = sliding ? w : big;
+    s.fwd = s.back;
+    s.kmin = p0 > 0 ? p0 : 0;  // rows below 0 do not exist, whatever pos0 holds
+    s.kmax = p0 + T - 1 < cap - 1 ? p0 + T - 1 : cap - 1;
+  } else {
+    s.back = sliding ? w - 1 : big;
+    s.fwd = 0;
+    s.kmin = 0;
+    s.kmax = ring ? big : cap - 1;
+  }
+  return s;
 }
 g4_status attn_prefill(const AttnArgs& a, int32_t dtype, hipStream_t s);
 g4_status attn_decode(const AttnArgs& a, void* ws, size_t ws_bytes, int32_t dtype, hipStream_t s);

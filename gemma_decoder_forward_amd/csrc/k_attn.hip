@@ -1,7 +1,9 @@
 // Causal GQA attention over a layer's KV cache (cortiq-engine `attend_all_heads` with scale 1.0 and the
 // sliding window; ferrox `causal_gqa_attention(_windowed)`; turbospark `encode_attention_any` over
 // [kv_start, seq_len)). Query at absolute position i sees cache rows lo <= j <= i with lo = 0 on full
-// layers and i - W + 1 on sliding layers. Head h reads kv head h / (nh / nkv).
+// layers and i - W + 1 on sliding layers. Head h reads kv head h / (nh / nkv). A prefill may instead
+// take the encoder's mask (taconite-embeddinggemma2 `text_attention`): the call's own keys, within
+// |i - j| <= W on sliding layers (key_span).
 //
 // This file holds the vector-ALU kernels:
 //   * k_attn_rowwise: one wave per (query, head), online softmax; any head width <= 512, any dtype.
@@ -11,11 +13,14 @@
 
 namespace g4 {
 
-__device__ __forceinline__ void key_range(int64_t i, int sliding, int64_t window, int64_t cap, int32_t ring,
-                                          int64_t& lo, int64_t& hi) {
-  lo = sliding ? i - window + 1 : 0;
-  if (lo < 0) lo = 0;
-  hi = kv_last(i, cap, ring);  // keys beyond a linear cache do not exist
+// [lo, hi]: the keys query position i sees (causal, or the encoder's mask; see key_span). Keys beyond
+// a linear cache do not exist.
+__device__ __forceinline__ void key_range(const AttnArgs& a, int64_t p0, int64_t i, int64_t& lo, int64_t& hi) {
+  const KeySpan ks = key_span(a.bidir, a.sliding, a.window, a.cap, a.ring, p0, a.T);
+  lo = i - ks.back;
+  if (lo < ks.kmin) lo = ks.kmin;
+  hi = i + ks.fwd;
+  if (hi > ks.kmax) hi = ks.kmax;
 }
 
 // --------------------------------------------------------------------------------------------
@@ -27,9 +32,9 @@ __global__ __launch_bounds__(256) void k_attn_rowwise(AttnArgs a) {
   if (t >= a.T) return;
   const int64_t grp = a.nh / a.nkv, g = h / grp;
   const int hd = (int)a.hd;
-  const int64_t i = (int64_t)a.pos0[b] + t;
+  const int64_t p0 = a.pos0[b], i = p0 + t;
   int64_t lo, hi;
-  key_range(i, a.sliding, a.window, a.cap, a.ring, lo, hi);
+  key_range(a, p0, i, lo, hi);
   const T* qr = (const T*)a.q + (b * a.T + t) * a.q_ld + h * hd;
   const T* Kb = (const T*)a.k + (b * a.nkv + g) * a.cap * hd;
   const T* Vb = (const T*)a.v + (b * a.nkv + g) * a.cap * hd;
@@ -102,7 +107,7 @@ __global__ __launch_bounds__(256) void k_attn_dec_part(AttnArgs a, int chunk, in
   const int hd = (int)a.hd;
   const int64_t i = a.pos0[b];
   int64_t lo, hi;
-  key_range(i, a.sliding, a.window, a.cap, a.ring, lo, hi);
+  key_range(a, i, i, lo, hi);  // decode is always causal
   const int64_t k0 = lo + (int64_t)c * chunk;
   int64_t k1 = k0 + chunk - 1;
   if (k1 > hi) k1 = hi;

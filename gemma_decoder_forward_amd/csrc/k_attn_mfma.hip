@@ -1,5 +1,6 @@
 // Flash-style prefill attention on the CDNA4 matrix cores (bf16 operands, float32 softmax and
-// accumulation), causal with an optional sliding window, GQA groups sharing every K/V tile.
+// accumulation), causal with an optional sliding window or with the encoder's non-causal mask (key_span),
+// GQA groups sharing every K/V tile.
 // Two kernels: k_attn_w16 (16-query waves, head dims 256 and 512, described before it) and
 // k_attn_mfma (32-query waves, head dim 128), described here.
 //
@@ -116,24 +117,26 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
   int64_t tlast = (int64_t)(g_last / G) * 32 + 31;
   if (tlast > a.T - 1) tlast = a.T - 1;
   const int64_t imin = p0 + (int64_t)(g_first / G) * 32, imax = p0 + tlast;
-  int64_t lob = a.sliding ? imin - a.window + 1 : 0;
-  if (lob < 0) lob = 0;
-  int64_t hib = kv_last(imax, a.cap, a.ring);
+  const KeySpan ksp = key_span(a.bidir, a.sliding, a.window, a.cap, a.ring, p0, a.T);
+  int64_t lob = imin - ksp.back;
+  if (lob < ksp.kmin) lob = ksp.kmin;
+  int64_t hib = imax + ksp.fwd;
+  if (hib > ksp.kmax) hib = ksp.kmax;
   const int64_t kstart = lob & ~(int64_t)(AT_KB - 1);
   const int ntiles = hib >= lob ? (int)((hib - kstart) / AT_KB + 1) : 0;
   const int half_tiles = (ntiles + 1) / 2;
   const int it0 = nparts == 2 && part == 1 ? half_tiles : 0;
   const int it1 = nparts == 2 && part == 0 ? half_tiles : ntiles;
-  int64_t qlo = a.sliding ? qi - a.window + 1 : 0;
-  if (qlo < 0) qlo = 0;
-  const int64_t qhi = qi < hib ? qi : hib;  // this query's last visible key
+  int64_t qlo = qi - ksp.back;
+  if (qlo < ksp.kmin) qlo = ksp.kmin;
+  const int64_t qhi = qi + ksp.fwd < hib ? qi + ksp.fwd : hib;  // this query's last visible key
   // keys visible to every query of the wave: [wlo_all, whi_all] (empty for a wave with invalid queries)
   int64_t wlo_all, whi_all;
   {
     const int64_t first = p0 + (int64_t)run * 32, last = p0 + (int64_t)run * 32 + 31;
-    wlo_all = a.sliding ? last - a.window + 1 : 0;
+    wlo_all = last - ksp.back;
     if (wlo_all < lob) wlo_all = lob;
-    whi_all = first < hib ? first : hib;
+    whi_all = first + ksp.fwd < hib ? first + ksp.fwd : hib;
     if (!(gi < ngroups && (int64_t)run * 32 + 31 < a.T)) { wlo_all = 1; whi_all = 0; }
   }
 
@@ -410,26 +413,27 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl
   int64_t tlast = (int64_t)(g_last / G) * 32 + 31;
   if (tlast > a.T - 1) tlast = a.T - 1;
   const int64_t imin = p0 + (int64_t)(g_first / G) * 32, imax = p0 + tlast;
-  int64_t lob = a.sliding ? imin - a.window + 1 : 0;
-  if (lob < 0) lob = 0;
-  const int64_t hib = kv_last(imax, a.cap, a.ring);
+  const KeySpan ksp = key_span(a.bidir, a.sliding, a.window, a.cap, a.ring, p0, a.T);
+  int64_t lob = imin - ksp.back;
+  if (lob < ksp.kmin) lob = ksp.kmin;
+  const int64_t hib = imax + ksp.fwd < ksp.kmax ? imax + ksp.fwd : ksp.kmax;
   const int64_t kstart = lob & ~(int64_t)(AT_KB - 1);
   const int ntiles = hib >= lob ? (int)((hib - kstart) / AT_KB + 1) : 0;
   const int half_tiles = (ntiles + 1) / 2;
   const int it0 = nparts == 2 && part == 1 ? half_tiles : 0;
   const int it1 = nparts == 2 && part == 0 ? half_tiles : ntiles;
-  int64_t qlo = a.sliding ? qi - a.window + 1 : 0;
-  if (qlo < 0) qlo = 0;
-  const int64_t qhi = qi < hib ? qi : hib;
+  int64_t qlo = qi - ksp.back;
+  if (qlo < ksp.kmin) qlo = ksp.kmin;
+  const int64_t qhi = qi + ksp.fwd < hib ? qi + ksp.fwd : hib;
   // the lane's visible keys relative to the first tile, in 32 bits (none for an invalid query)
   const int vlo = qvalid ? (int)(qlo - kstart) : 0x7fffffff, vhi = qvalid ? (int)(qhi - kstart) : -1;
   // keys visible to every query of the wave (empty when some query of the wave is invalid)
   int64_t wlo_all, whi_all;
   {
     const int64_t first = p0 + tq0, last = p0 + tq0 + 15;
-    wlo_all = a.sliding ? last - a.window + 1 : 0;
+    wlo_all = last - ksp.back;
     if (wlo_all < lob) wlo_all = lob;
-    whi_all = first < hib ? first : hib;
+    whi_all = first + ksp.fwd < hib ? first + ksp.fwd : hib;
     if (!(gi < ngroups && tq0 + 15 < a.T)) { wlo_all = 1; whi_all = 0; }
   }
   // per-tile range tests in 32 bits, relative to the first tile's first key
@@ -669,8 +673,8 @@ __global__ __launch_bounds__(64) void k_attn_merge_split(AttnArgs a, int64_t tq_
 // sliding-window launch (every block's key range about the same) with fewer blocks than CUs splits
 // all of its blocks. split_from is a multiple of the blocks per 32-token
 // run so that the split rows start at a run boundary. Returns false if the shape is not the MFMA path's.
-static bool attn_plan(int64_t B, int64_t T, int64_t nh, int64_t nkv, int64_t hd, int32_t sliding, int* nblk,
-                      int* split_from, int64_t* tq_lo) {
+static bool attn_plan(int64_t B, int64_t T, int64_t nh, int64_t nkv, int64_t hd, int32_t sliding, int32_t bidir,
+                      int* nblk, int* split_from, int64_t* tq_lo) {
   if (nkv <= 0 || nh % nkv) return false;
   const int64_t G = nh / nkv;
   if (!(G == 1 || G == 2 || G == 4) || !(hd == 128 || hd == 256 || hd == 512)) return false;
@@ -682,7 +686,9 @@ static bool attn_plan(int64_t B, int64_t T, int64_t nh, int64_t nkv, int64_t hd,
   const int64_t blocks = (int64_t)*nblk * nkv * B;
   if (sliding ? blocks < cus : blocks < 2 * cus) {
     const int step = G > QG ? (int)(G / QG) : 1;
-    *split_from = sliding ? 0 : (*nblk / 2) / step * step;
+    // causal full layers: the later half of the blocks holds the longer key ranges; with a window or the
+    // encoder's mask every block's range is about as long, so every block is split
+    *split_from = (sliding || bidir) ? 0 : (*nblk / 2) / step * step;
   }
   *tq_lo = ((int64_t)*split_from * QG / G) * 32;
   return true;
@@ -693,7 +699,7 @@ size_t attn_prefill_ws(int64_t B, int64_t T, int64_t nh, int64_t nkv, int64_t hd
   int64_t tq_lo = 0;
   size_t need = 0;
   for (int sl = 0; sl < 2; ++sl)
-    if (attn_plan(B, T, nh, nkv, hd, sl, &nblk, &sf, &tq_lo) && sf < nblk) need = (size_t)2 * B * T * nh * (hd + 2) * 4;
+    if (attn_plan(B, T, nh, nkv, hd, sl, 0, &nblk, &sf, &tq_lo) && sf < nblk) need = (size_t)2 * B * T * nh * (hd + 2) * 4;
   return need;
 }
 
@@ -703,7 +709,7 @@ bool attn_mfma(const AttnArgs& a, hipStream_t s, g4_status* st) {
   if (((uintptr_t)a.q | (uintptr_t)a.k | (uintptr_t)a.v | (uintptr_t)a.out) & 15) return false;
   int nblk = 0, split_from = 0;
   int64_t tq_lo = 0;
-  if (!attn_plan(a.B, a.T, a.nh, a.nkv, a.hd, a.sliding, &nblk, &split_from, &tq_lo)) return false;
+  if (!attn_plan(a.B, a.T, a.nh, a.nkv, a.hd, a.sliding, a.bidir, &nblk, &split_from, &tq_lo)) return false;
   const size_t need = (size_t)2 * a.B * a.T * a.nh * (a.hd + 2) * 4;
   if (!a.ws || a.ws_bytes < need || ((uintptr_t)a.ws & 15)) split_from = nblk;  // no scratch: no split
   const int64_t G = a.nh / a.nkv;

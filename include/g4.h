@@ -42,7 +42,9 @@ typedef enum g4_status {
 
 typedef enum g4_dtype { G4_F32 = 0, G4_BF16 = 1 } g4_dtype;
 
-typedef enum g4_mode { G4_PREFILL = 0, G4_DECODE = 1 } g4_mode;
+/* G4_ENCODE: a prefill whose attention is the encoder's non-causal mask (taconite-embeddinggemma2
+ * model.rs, `text_attention`); see g4_attn_encode. */
+typedef enum g4_mode { G4_PREFILL = 0, G4_DECODE = 1, G4_ENCODE = 2 } g4_mode;
 
 /* Model hyper-parameters (cortiq-engine `G4eGlobals`; ferrox-models `Gemma4Hparams`). */
 typedef struct g4_model_desc {
@@ -172,6 +174,18 @@ g4_status g4_attn_prefill(const void* q, int64_t q_ld, const g4_kv_entry* kv, in
                           int64_t hd, float scale, void* out, int64_t out_ld, int32_t dtype,
                           void* stream);
 
+/* The encoder's non-causal attention (taconite-embeddinggemma2 model.rs, `text_attention`: every key
+ * of the sequence, a sliding layer's keys within |i - j| <= window). Arguments as g4_attn_prefill; the
+ * sequence is this call: query i = pos0[b]+t sees the cache rows j of the call's own tokens,
+ * pos0[b] <= j <= pos0[b]+T-1, all of them (sliding == 0) or those with |i - j| <= window
+ * (sliding == 1), so rows before pos0[b] are never read. The call's K/V rows must already be in the
+ * cache. The cache must be linear (ring == 0), else G4_EINVAL. */
+g4_status g4_attn_encode(const void* q, int64_t q_ld, const g4_kv_entry* kv, int32_t n_kv,
+                         int32_t layer, int32_t kv_src, int32_t sliding, int64_t window,
+                         const int32_t* pos0, int64_t B, int64_t T, int64_t nh, int64_t nkv,
+                         int64_t hd, float scale, void* out, int64_t out_ld, int32_t dtype,
+                         void* stream);
+
 /* Decode attention: one query per sequence at position pos[b] (turbospark `encode_attention_any`
  * over [kv_start, seq_len)). Same semantics as g4_attn_prefill with T = 1. Split over key chunks;
  * the workspace holds per-chunk partial results (size from g4_attn_decode_ws). */
@@ -236,6 +250,8 @@ g4_status g4_embed_ple(const int32_t* ids, int64_t M, const void* E, const void*
  *   d-wide slice); kv the per-layer cache table (n_kv == model->n_layers); pos int32 [B].
  *   mode G4_PREFILL: T tokens per sequence at pos[b] .. pos[b]+T-1.
  *   mode G4_DECODE:  T must be 1.
+ *   mode G4_ENCODE:  as G4_PREFILL, with the encoder's attention (g4_attn_encode) over the call's
+ *                    tokens; linear caches only.
  * A layer that owns its cache (kv_src == layer) writes its K/V rows before attending. */
 g4_status g4_layer_forward(const g4_model_desc* model, const g4_layer_desc* layer_desc,
                            int32_t layer, float* h, const float* ple_in, const g4_kv_entry* kv,

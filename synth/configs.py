@@ -41,6 +41,10 @@ CONFIGS = {
     6: dict(E4B, name="e4b-variants-6L", dtype="bf16", mode="prefill", B=1, T=2048, layer_types="SSFSSF",
             n_shared=2, embed=False, n_kv_heads_full=4, k_eq_v=True,
             ffn_dims=[10240, 6144, 8192, 10240, 4096, 8192]),
+    # The encoder at E4B widths (taconite-embeddinggemma2 `text`/`text_attention`): the same layers with
+    # the non-causal mask, every layer computing its own K/V (no shared tail), given h0 and ple_in.
+    7: dict(E4B, name="e4b-encoder-6L", dtype="bf16", mode="encode", B=1, T=2048, layer_types="SSSSSF",
+            n_shared=0, embed=False),
 }
 
 

@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported_and_bound():
 
 
 def test_version_and_status_strings():
-    assert bd.lib().g4_version() >= 200
+    assert bd.lib().g4_version() >= 300
     assert bd.lib().g4_status_str(bd.G4_EGEOM) == b"G4_EGEOM"
 
 
@@ -87,6 +87,31 @@ def test_attention_validation_errors():
     assert _attn(t, 2, 0, 1, 256, q=None) == bd.G4_EINVAL
     assert _attn(t, 7, 0, 1, 256) == bd.G4_EINVAL     # layer outside the table
     assert b"head_dim" in bd.lib().g4_last_error() or bd.lib().g4_last_error()
+
+
+def test_encode_validation_errors():
+    """The encoder's attention takes the prefill checks, and a ring cache is refused (its call's keys could
+    have been overwritten); the layer forward accepts G4_ENCODE and refuses unknown modes."""
+    t = _table([(640, 256, 1, 1), (64, 256, 1)])
+    L = bd.lib()
+
+    def enc(table, layer, kv_src, T=8, window=512):
+        return L.g4_attn_encode(FAKE, 8 * 256, table, len(table), layer, kv_src, 1, window, FAKE, 1, T, 8, 2, 256, 1.0,
+                                FAKE, 8 * 256, bd.G4_BF16, None)
+
+    assert enc(t, 0, 0) == bd.G4_EINVAL and b"linear" in L.g4_last_error()
+    assert enc(t, 1, 1, T=65) == bd.G4_ERANGE
+    assert enc(t, 1, 1, window=0) == bd.G4_ERANGE
+    m = _model()
+    ld = bd.LayerDesc(sliding=1, kv_src=0, layer_scalar=1.0)
+    for n in bd.LAYER_PTRS:
+        setattr(ld, n, FAKE)
+    lt = _table([(64, 256, 1), (64, 512, 0)])
+    for mode, want in ((3, bd.G4_EINVAL), (bd.G4_ENCODE, bd.G4_EINVAL)):
+        # mode 3 is unknown; G4_ENCODE passes validation and stops at the (too small) workspace
+        assert L.g4_layer_forward(C.byref(m), C.byref(ld), 0, FAKE, FAKE, lt, 2, FAKE, 1, 8, mode, FAKE, 1,
+                                  None) == want
+    assert b"workspace" in L.g4_last_error()
 
 
 def test_ring_cache_validation_errors():
