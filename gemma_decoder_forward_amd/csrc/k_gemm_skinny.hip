@@ -11,6 +11,14 @@
 //
 // B may be the concatenation of up to three matrices (q/k/v projections, or gate then up) so that one
 // launch covers them; the output columns follow the concatenation.
+//
+// For at most 4 token rows (k_gemv) the products are formed on the vector ALUs instead: a wave reads
+// its weight rows as contiguous 1 KB runs (64 lanes x 16 bytes), the pattern that keeps HBM streaming
+// (the MFMA operand layout makes each load instruction touch 64 bytes of 16 different rows, which caps
+// a pure read of the gate/up weights near 4.4 TB/s against 5.6 TB/s row by row on the same device).
+// Each lane takes 8 consecutive k of a row per 512-k chunk, the 16-byte A pieces at the same k from LDS,
+// and accumulates with v_dot2c_f32_bf16; a wave sum per (row, token row) finishes. Same partial-slice
+// output and epilogues as k_gemm_skinny.
 #include "g4_internal.h"
 
 namespace g4 {
@@ -71,6 +79,21 @@ __device__ __forceinline__ uint4 sk_a_from_parts(const SkA& sa, int64_t m, int64
 // columns 16b .. 16b+15; waves 0, 1 take those gate rows and waves 2, 3 the same up rows, each pair
 // splitting K in halves. The four sums meet in LDS and wave 0 stores bf16(gelu_tanh(gate) * up) to
 // C[m][16b + ...] (ldc = Nt).
+// Stages A[0:M, k0:k0+kn] in LDS as bf16 rows of stride ald, plus zero rows up to nrow.
+template <int AK>
+__device__ __forceinline__ void sk_stage_a(const SkA& sa, int64_t M, int64_t k0, int kn, int nrow, int ald, bf16* As) {
+  const int cpr = kn / 8;
+  for (int idx = threadIdx.x; idx < nrow * cpr; idx += 256) {
+    const int m = idx / cpr, c = idx - m * cpr;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (m < M) {
+      if (AK == SKA_BF16) v = *(const uint4*)((const bf16*)sa.a + m * sa.lda + k0 + 8 * c);
+      else v = sk_a_from_parts<AK>(sa, m, k0 + 8 * c);
+    }
+    *(uint4*)(As + m * ald + 8 * c) = v;
+  }
+}
+
 template <int MB, int AK, int RW, bool GATED = false>
 __global__ __launch_bounds__(256) void k_gemm_skinny(SkA sa, int64_t M, SkSeg sg, int64_t K, int kc,
                                                      float* __restrict__ part, int64_t Nt) {
@@ -117,16 +140,7 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(SkA sa, int64_t M, SkSeg sg
   // stage A[0:M, k0:k0+kn] while the first weights arrive, plus one zero row that stands in for every
   // MFMA row >= M (so the LDS slice and its staging scale with M, not with the 16-row MFMA blocks)
   const int nrow = sk_lds_rows(MB, M);
-  const int cpr = kn / 8;
-  for (int idx = tid; idx < nrow * cpr; idx += 256) {
-    const int m = idx / cpr, c = idx - m * cpr;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (m < M) {
-      if (AK == SKA_BF16) v = *(const uint4*)((const bf16*)sa.a + m * sa.lda + k0 + 8 * c);
-      else v = sk_a_from_parts<AK>(sa, m, k0 + 8 * c);
-    }
-    *(uint4*)(As + m * ald + 8 * c) = v;
-  }
+  sk_stage_a<AK>(sa, M, k0, kn, nrow, ald, As);
   __syncthreads();
 
   int aoff[MB];
@@ -205,6 +219,117 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(SkA sa, int64_t M, SkSeg sg
     }
 }
 
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_v;
+// Token rows taken by k_gemv, from timings of both kernels on the decode shapes (gate+up 20480 x 2560,
+// down 2560 x 10240, q/k/v 3072 x 2560, o 2560 x 2048): the vector-ALU path is faster on every shape
+// up to 2 rows (by 1.6-4.2 us), on all but gate+up at 3-4 rows, and slower from 6 rows on, where each
+// 16-row block re-staging M x K activations costs more than the better weight stream saves.
+constexpr int GV_MAX = 4;        // split-K products
+constexpr int GV_MAX_GATED = 2;  // the one-pass gate/up product
+constexpr int GV_CH = 5;   // 512-k chunks of each weight row loaded per round trip
+
+// 16 bytes of a weight row dotted with 16 bytes of an A row: four bf16 pairs, float32 accumulation.
+__device__ __forceinline__ float gv_dot8(const uint4& w, const uint4& a, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, w.x), __builtin_bit_cast(bf16x2_v, a.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, w.y), __builtin_bit_cast(bf16x2_v, a.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, w.z), __builtin_bit_cast(bf16x2_v, a.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, w.w), __builtin_bit_cast(bf16x2_v, a.w), acc, false);
+  return acc;
+}
+
+// MM: compile-time bound on the token rows (M <= MM). Block = 4 waves, each wave four weight rows over
+// the block's K range [k0, k0 + kc): rows 16 b + 4 w .. +3 of the concatenation (partial slices out), or
+// (GATED, one K range) the gate and up rows of output columns 8 b + 2 w and 8 b + 2 w + 1, written as
+// bf16(gelu_tanh(gate) * up) to C[m][col] (row stride Nt).
+template <int MM, int AK, bool GATED>
+__global__ __launch_bounds__(256) void k_gemv(SkA sa, int64_t M, SkSeg sg, int64_t K, int kc,
+                                              float* __restrict__ part, int64_t Nt) {
+  extern __shared__ __attribute__((aligned(16))) bf16 As[];
+  const int ald = kc + 8;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t k0 = (int64_t)blockIdx.y * kc;
+  const int kn = (int)((K - k0) < kc ? (K - k0) : kc);
+  const int nch = (kn + 511) >> 9;
+
+  // The wave's four rows, each through a buffer descriptor of exactly its kn elements: a chunk's lanes
+  // past the row's end read zero and cost no traffic. (Segments are multiples of 64 rows, so the four
+  // rows of a wave lie in one matrix.)
+  const bf16* wr[4];
+  if (GATED) {
+    const int64_t c0 = (int64_t)blockIdx.x * 8 + 2 * wave;
+    wr[0] = sg.b[0] + c0 * sg.ldb + k0;
+    wr[2] = sg.b[1] + c0 * sg.ldb + k0;
+    wr[1] = wr[0] + sg.ldb;
+    wr[3] = wr[2] + sg.ldb;
+  } else {
+    wr[0] = sk_row(sg, (int64_t)blockIdx.x * 16 + 4 * wave) + k0;
+    wr[1] = wr[0] + sg.ldb;
+    wr[2] = wr[1] + sg.ldb;
+    wr[3] = wr[2] + sg.ldb;
+  }
+  __amdgpu_buffer_rsrc_t rs[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) rs[j] = __builtin_amdgcn_make_buffer_rsrc((void*)wr[j], (short)0, kn * 2, 0x00020000);
+
+  // first round trip of weights in flight while A is staged
+  uint4 w[4][GV_CH];
+  auto load = [&](int cg) {
+#pragma unroll
+    for (int c = 0; c < GV_CH; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs[j], 16 * lane + 1024 * (cg + c), 0, 0);
+        w[j][c] = *(const uint4*)&v;
+      }
+  };
+  load(0);
+  const int nrow = sk_lds_rows(1, M);
+  sk_stage_a<AK>(sa, M, k0, kn, nrow, ald, As);
+  __syncthreads();
+
+  float acc[4][MM];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int m = 0; m < MM; ++m) acc[j][m] = 0.f;
+  for (int cg = 0; cg < nch; cg += GV_CH) {
+    if (cg > 0) load(cg);
+#pragma unroll
+    for (int c = 0; c < GV_CH; ++c) {
+      const int kk = 8 * lane + 512 * (cg + c);
+      if (cg + c < nch) {  // uniform
+#pragma unroll
+        for (int m = 0; m < MM; ++m) {
+          const uint4 a = (m < M && kk < kn) ? *(const uint4*)(As + m * ald + kk) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[j][m] = gv_dot8(w[j][c], a, acc[j][m]);
+        }
+      }
+    }
+  }
+  if (GATED) {
+    bf16* C = (bf16*)part;
+    const int64_t c0 = (int64_t)blockIdx.x * 8 + 2 * wave;
+#pragma unroll
+    for (int m = 0; m < MM; ++m)
+      if (m < M) {
+        const float g0 = wave_sum(acc[0][m]), g1 = wave_sum(acc[1][m]);
+        const float u0 = wave_sum(acc[2][m]), u1 = wave_sum(acc[3][m]);
+        if (lane < 2) C[m * Nt + c0 + lane] = f2bf(lane == 0 ? gelu_tanh(g0) * u0 : gelu_tanh(g1) * u1);
+      }
+    return;
+  }
+  float* pb = part + (int64_t)blockIdx.y * M * Nt + (int64_t)blockIdx.x * 16 + 4 * wave;
+#pragma unroll
+  for (int m = 0; m < MM; ++m)
+    if (m < M) {
+      const float s0 = wave_sum(acc[0][m]), s1 = wave_sum(acc[1][m]);
+      const float s2 = wave_sum(acc[2][m]), s3 = wave_sum(acc[3][m]);
+      if (lane < 4) pb[m * Nt + lane] = lane == 0 ? s0 : (lane == 1 ? s1 : (lane == 2 ? s2 : s3));
+    }
+}
+
 // Sums the split partials and applies the epilogue. GEGLU: part columns [0, N) are gate, [N, 2N) up.
 template <int EPI, bool CF32>
 __global__ __launch_bounds__(256) void k_gemm_finish(GemmArgs a, const float* __restrict__ part, int splits,
@@ -249,10 +374,29 @@ static void sk_plan(int mb, int64_t K, int64_t Nt, int& rw, int& kc, int& splits
   splits = (int)((steps + per - 1) / per);
 }
 
+// k_gemv: 16-row blocks, K split so that about four blocks per CU stream (blocks of one K range each), the
+// K range a multiple of 128 and its A slice within 64 KB of LDS.
+static void gv_plan(int64_t M, int64_t K, int64_t Nt, int& kc, int& splits) {
+  const int64_t rowblocks = Nt / 16;
+  const int64_t steps = K / 128;
+  const int64_t max_steps = ((65536 / (2 * sk_lds_rows(1, M))) - 8) / 128;
+  int64_t s = (1024 + rowblocks - 1) / rowblocks;
+  const int64_t smin = (steps + max_steps - 1) / max_steps;
+  if (s < smin) s = smin;
+  if (s > steps) s = steps;
+  if (s < 1) s = 1;
+  const int64_t per = (steps + s - 1) / s;
+  kc = (int)(per * 128);
+  splits = (int)((steps + per - 1) / per);
+}
+
 size_t gemm_skinny_ws(int64_t M, int64_t Nt, int64_t K) {
-  const int mb = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   int rw, kc, splits;
-  sk_plan(mb, K, Nt, rw, kc, splits);
+  if (M <= GV_MAX) {
+    gv_plan(M, K, Nt, kc, splits);
+  } else {
+    sk_plan(M <= 16 ? 1 : (M <= 32 ? 2 : 4), K, Nt, rw, kc, splits);
+  }
   return (size_t)splits * M * Nt * sizeof(float);
 }
 
@@ -281,6 +425,24 @@ static void sk_launch(const SkA& sa, dim3 g, size_t lds, hipStream_t s, int64_t 
     hipLaunchKernelGGL((k_gemm_skinny<MB, SKA_BF16, RW>), g, dim3(256), lds, s, sa, M, sg, K, kc, part, Nt);
 }
 
+template <bool GATED>
+static void gv_launch(const SkA& sa, dim3 g, hipStream_t s, int64_t M, const SkSeg& sg, int64_t K, int kc, float* part,
+                      int64_t Nt) {
+  const size_t lds = (size_t)sk_lds_rows(1, M) * (kc + 8) * sizeof(bf16);  // <= 64 KB (gv_plan)
+#define G4_GV(MM, AKV) hipLaunchKernelGGL((k_gemv<MM, AKV, GATED>), g, dim3(256), lds, s, sa, M, sg, K, kc, part, Nt)
+#define G4_GV_M(AKV) \
+  do { if (M <= 1) G4_GV(1, AKV); else if (M <= 2) G4_GV(2, AKV); else G4_GV(4, AKV); } while (0)
+  if constexpr (GATED) {
+    G4_GV_M(SKA_BF16);
+  } else {
+    if (sa.kind == SKA_BF16) G4_GV_M(SKA_BF16);
+    else if (sa.kind == SKA_GEGLU) G4_GV_M(SKA_GEGLU);
+    else G4_GV_M(SKA_GELU_MUL);
+  }
+#undef G4_GV_M
+#undef G4_GV
+}
+
 g4_status gemm_skinny_part(const SkA& sa, int64_t M, int64_t K, const void* const* segs, const int64_t* seg_rows,
                            int nseg, int64_t ldb, float* part, size_t part_bytes, int* splits_out, hipStream_t s) {
   if (!skinny_ok(M, K, segs, seg_rows, nseg, ldb))
@@ -301,6 +463,15 @@ g4_status gemm_skinny_part(const SkA& sa, int64_t M, int64_t K, const void* cons
     sg.end[i] = Nt;
   }
   sg.ldb = ldb;
+  if (M <= GV_MAX) {
+    int kc, splits;
+    gv_plan(M, K, Nt, kc, splits);
+    if ((size_t)splits * M * Nt * sizeof(float) > part_bytes)
+      return fail(G4_EINVAL, "few-row GEMM: partial buffer too small");
+    gv_launch<false>(sa, dim3((unsigned)(Nt / 16), (unsigned)splits), s, M, sg, K, kc, part, Nt);
+    *splits_out = splits;
+    return check_launch("gemv");
+  }
   const int mb = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   int rw, kc, splits;
   sk_plan(mb, K, Nt, rw, kc, splits);
@@ -322,6 +493,11 @@ g4_status gemm_skinny_part(const SkA& sa, int64_t M, int64_t K, const void* cons
 }
 
 void skinny_plan(int64_t M, int64_t K, int64_t Nt, int* rows_per_block, int* kc, int* splits) {
+  if (M <= GV_MAX) {
+    gv_plan(M, K, Nt, *kc, *splits);
+    *rows_per_block = 16;
+    return;
+  }
   int rw = 0;
   sk_plan(M <= 16 ? 1 : (M <= 32 ? 2 : 4), K, Nt, rw, *kc, *splits);
   *rows_per_block = 16 * rw;
@@ -355,6 +531,10 @@ g4_status gemm_skinny_gated(const SkA& sa, int64_t M, int64_t K, const void* w_g
   sg.ldb = ldb;
   const int kc = (int)K;
   const size_t lds = (size_t)sk_lds_rows(1, M) * (kc + 8) * sizeof(bf16);
+  if (M <= GV_MAX_GATED && lds <= 65536) {
+    gv_launch<true>(sa, dim3((unsigned)(F / 8), 1), s, M, sg, K, kc, (float*)C, ldc);
+    return check_launch("gemv_gated");
+  }
   static bool lds_set = false;
   if (!lds_set) {
     (void)hipFuncSetAttribute((const void*)k_gemm_skinny<1, SKA_BF16, 4, true>, hipFuncAttributeMaxDynamicSharedMemorySize,

@@ -287,7 +287,11 @@ def test_linear_large_tiles_pipeline_depths(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 256, 2560), (8, 3072, 2560), (33, 512, 10240), (64, 2560, 10240),
-                                   (17, 20480, 2560)])
+                                   (17, 20480, 2560),
+                                   # the vector-ALU path (M <= 4): several 512-k chunk groups per row, a part-filled
+                                   # last chunk, every token-row bound (1, 2, 4) and odd M; then M = 5, 7 either side
+                                   (1, 16384, 4096), (2, 16384, 6400), (3, 640, 384), (4, 128, 256), (3, 16384, 5248),
+                                   (5, 2560, 10240), (7, 2048, 2688)])
 def test_linear_few_rows_weight_streaming(M, N, K):
     """Decode-shaped projections (M = batch): the weight-streaming split-K path, given a workspace."""
     log(f"linear few rows {M}x{N}x{K}")
