@@ -30,8 +30,10 @@
 // n = 8 (r / 4) + 4 (l / 32) + r % 4: four consecutive output columns per register group.
 //
 // Epilogues: float32 or bf16 store, split-K float32 slices, the gelu-tanh gated product of two weight
-// matrices (gate and up rows interleaved in 32-row blocks of the B tile, so a lane holds matching gate
-// and up accumulators), and gelu_tanh(acc) * aux.
+// matrices, and gelu_tanh(acc) * aux. Gated product: gate and up rows alternate in blocks of RPI rows
+// (one load instruction's rows: 8 for BK = 64, 16 for BK = 32) down the B tile. A 32-column MFMA block
+// then holds 16 gate and 16 up columns, and by the register layout above the up partner of gate
+// register r is register r + RPI/2 of the same lane, so every block finishes its own 16 outputs.
 #include "g4_internal.h"
 
 namespace g4 {
@@ -120,7 +122,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a, int tiles_
   constexpr int AJ = BM / (RPI * NW), BJ = BN / (RPI * NW);  // load instructions per wave per step
   constexpr int LG = AJ + BJ;
   constexpr int ASZ = BM * BK, STAGE = (BM + BN) * BK;  // in bf16 elements
-  static_assert(EPI != EPI_GEGLU || (FN % 2) == 0, "gate/up pairs must sit in one wave");
+  static_assert(EPI != EPI_GEGLU || RPI == 8 || RPI == 16, "gate/up blocks of one load instruction's rows");
   static_assert((NW == 4 || NW == 8) && AJ * RPI * NW == BM && BJ * RPI * NW == BN, "loader covers the tile");
   static_assert(KS % 2 == 0 && MF_KMIN % BK == 0, "k-slices alternate two register sets");
   static_assert(NRD <= NMF && LG <= NMF, "every read and load rides behind an MFMA");
@@ -175,8 +177,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a, int tiles_
 
   // Loader geometry. Load instruction q covers the RPI LDS rows of group g = wave + NW q (A rows for
   // q < AJ, B rows after): lane i fills LDS row RPI g + i / CPR, chunk i % CPR, from global chunk
-  // (i % CPR) ^ swz(row). GEGLU: B tile row block b = RPI g / 32 (32 rows) holds gate rows (b even) or
-  // up rows (b odd) 32 (b / 2) + (RPI g) % 32 + ...; every row of one instruction sits in one block.
+  // (i % CPR) ^ swz(row). GEGLU: B group g holds gate rows (g even) or up rows (g odd)
+  // RPI (g / 2) + i / CPR of the tile's output columns.
   const int lr = lane / CPR, lcp = lane % CPR;
   uint32_t voff[LG];
   bool use_up[LG];
@@ -189,9 +191,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a, int tiles_
     int src = row;
     use_up[q] = false;
     if (!isa && EPI == EPI_GEGLU) {
-      const int b = (RPI * g) / 32;
-      use_up[q] = b & 1;
-      src = 32 * (b >> 1) + (RPI * g) % 32 + lr;
+      use_up[q] = g & 1;
+      src = RPI * (g >> 1) + lr;
     }
     voff[q] = (uint32_t)(((int64_t)src * (isa ? a.lda : a.ldb) + 8 * chunk) * 2);
   }
@@ -218,30 +219,35 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a, int tiles_
     }
   };
 
-  // fragment addresses (elements within a stage): row r, k chunk 2ks + h at chunk (2ks + h) ^ swz(r)
+  // fragment addresses (elements within a stage): row r, k chunk 2ks + h at chunk (2ks + h) ^ swz(r).
+  // Row r + 64 has the swizzle of row r (BK = 64 reads row bits 0-5, and bits 3-5 move by 8 mod 8;
+  // BK = 32 reads bits 1-3 only), so fragment j sits a constant 32 (j - j % 2) rows after fragment
+  // j % 2: two offsets per k-slice stay in registers and the rest fold into the read's immediate.
   const int frow = lane & 31, fh = lane >> 5;
-  int aoff[KS][FM], boff[KS][FN];
+  int aoff[KS][2], boff[KS][2];
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+  for (int i = 0; i < 2; ++i) {
     const int row = wm * WM + 32 * i + frow;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) aoff[ks][i] = row * BK + (((2 * ks + fh) ^ swz<BK>(row)) << 3);
   }
 #pragma unroll
-  for (int j = 0; j < FN; ++j) {
+  for (int j = 0; j < 2; ++j) {
     const int row = wn * WN + 32 * j + frow;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) boff[ks][j] = ASZ + row * BK + (((2 * ks + fh) ^ swz<BK>(row)) << 3);
   }
+  auto aof = [&](int ks, int i) { return aoff[ks][i & 1] + 32 * (i & ~1) * BK; };
+  auto bof = [&](int ks, int j) { return boff[ks][j & 1] + 32 * (j & ~1) * BK; };
 
   // Two fragment sets. Read q of a k-slice comes in the order the MFMAs consume them: A0, B0..B(FN-1),
   // A1..A(FM-1); MFMA q multiplies A fragment q / FN with B fragment q % FN.
   f32x16_t acc[FM][FN];
   bf16x8_t fa[2][FM], fb[2][FN];
   auto rd = [&](int set, int ks, const bf16* st, int q) {
-    if (q == 0) fa[set][0] = *(const bf16x8_t*)(st + aoff[ks][0]);
-    else if (q <= FN) fb[set][q - 1] = *(const bf16x8_t*)(st + boff[ks][q - 1]);
-    else fa[set][q - FN] = *(const bf16x8_t*)(st + aoff[ks][q - FN]);
+    if (q == 0) fa[set][0] = *(const bf16x8_t*)(st + aof(ks, 0));
+    else if (q <= FN) fb[set][q - 1] = *(const bf16x8_t*)(st + bof(ks, q - 1));
+    else fa[set][q - FN] = *(const bf16x8_t*)(st + aof(ks, q - FN));
   };
   auto mf = [&](int set, int q) {
     const int i = q / FN, j = q % FN;
@@ -257,14 +263,18 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a, int tiles_
       const int64_t m = m0 + wm * WM + i * 32 + em;
       if (m >= a.M) continue;
       if (EPI == EPI_GEGLU) {
+        // block j: columns c = 8 g + en of register group g are gate when (c / RPI) is even; the up
+        // partner is group g + RPI / 8; output column n0 + 16 (wn FN + j) + the gate column's rank
 #pragma unroll
-        for (int p = 0; p < FN / 2; ++p) {
+        for (int j = 0; j < FN; ++j) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int64_t n = n0 + (wn * (FN / 2) + p) * 32 + 8 * g + en;
+            if (((8 * g) / RPI) & 1) continue;  // an up group
+            const int c = 8 * g + en;
+            const int64_t n = n0 + 16 * (wn * FN + j) + RPI * (c / (2 * RPI)) + c % RPI;
             float v[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = gelu_tanh(acc[i][2 * p][4 * g + e]) * acc[i][2 * p + 1][4 * g + e];
+            for (int e = 0; e < 4; ++e) v[e] = gelu_tanh(acc[i][j][4 * g + e]) * acc[i][j][4 * (g + RPI / 8) + e];
             *(uint2*)((bf16*)a.C + m * a.ldc + n) = pack_bf16x4(v);
           }
         }
@@ -422,8 +432,23 @@ static g4_status launch_mfma(const GemmArgs& a, hipStream_t s) {
 }
 
 // Picks a tile that gives enough blocks for 256 CUs; false if the shape does not suit the MFMA path.
+// The gated product may take 256 x 320 tiles (160 outputs each) where they need fewer passes over the
+// CUs, counting a 320-wide tile as 1.25 of a 256-wide one: at 2048 token rows and 10240 outputs, 640
+// tiles of 256 x 256 take three passes of 256 CUs (the last half empty), 512 of 256 x 320 take two.
 bool gemm_mfma(const GemmArgs& a, hipStream_t s, g4_status* st) {
   const int64_t tiles256 = ((a.M + 255) / 256) * (a.N / (a.epi == EPI_GEGLU ? 128 : 256)) * a.splits;
+  if (a.epi == EPI_GEGLU && a.splits == 1 && mfma_ok(a, 320) && tiles256 >= 192) {
+    const int64_t cus = device_cus();
+    const int64_t tiles320 = ((a.M + 255) / 256) * (a.N / 160);
+    const double p256 = (double)((tiles256 + cus - 1) / cus), p320 = 1.25 * (double)((tiles320 + cus - 1) / cus);
+    if (p320 < p256 - 1e-9) {
+      const int tm = (int)((a.M + 255) / 256), tn = (int)(a.N / 160);
+      const bool persist = a.K >= 2 * 64;
+      launch_one<256, 320, 8, 64, 2, EPI_GEGLU, false>(a, tm, tn, tm * tn, persist, s);
+      *st = check_launch("gemm_mfma_320");
+      return true;
+    }
+  }
   if (mfma_ok(a, 256) && tiles256 >= 192) {
     *st = launch_mfma<256, 256, G4_GEMM_NW, G4_GEMM_BK, G4_GEMM_NS>(a, s);
     return true;
