@@ -19,6 +19,11 @@
 //   * V stays row-major in LDS and the V^T operand comes from the LDS transpose read; K and V rows are
 //     padded (strides of 16 and 32 bytes mod 256) so both operand reads are free of bank conflicts.
 // The O accumulator (HD/32 32x32 blocks per wave) lives in the accumulation registers.
+#include <functional>
+#include <queue>
+#include <utility>
+#include <vector>
+
 #include "g4_internal.h"
 
 namespace g4 {
@@ -28,6 +33,24 @@ typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 
 constexpr int AT_KB = 32;        // keys per tile
+constexpr int AT_PS = 4;         // most key parts one query block is split into
+
+// Key split of a launch's query blocks: block b takes 1 + (b >= th1) + (b >= th2) + (b >= th3) parts
+// (th1 <= th2 <= th3 <= nblk), each part a contiguous share of the block's key tiles. Work items run
+// heaviest first: the 4-part blocks from the last one down, then the 3-part, 2-part and whole ones.
+struct AtSplit {
+  int th1, th2, th3;
+};
+__device__ __forceinline__ void at_item(int v, int nblk, const AtSplit& sp, int& blk, int& part, int& nparts) {
+  const int c4 = nblk - sp.th3, c3 = sp.th3 - sp.th2, c2 = sp.th2 - sp.th1;
+  if (v < 4 * c4) { blk = nblk - 1 - v / 4; part = v % 4; nparts = 4; return; }
+  v -= 4 * c4;
+  if (v < 3 * c3) { blk = sp.th3 - 1 - v / 3; part = v % 3; nparts = 3; return; }
+  v -= 3 * c3;
+  if (v < 2 * c2) { blk = sp.th2 - 1 - v / 2; part = v & 1; nparts = 2; return; }
+  v -= 2 * c2;
+  blk = sp.th1 - 1 - v; part = 0; nparts = 1;
+}
 
 typedef __attribute__((address_space(3))) void at_lds_void;
 typedef short at_v4s __attribute__((ext_vector_type(4)));
@@ -81,7 +104,7 @@ template <int HD> struct AttnStages { static constexpr int NS = HD == 512 ? 2 : 
 #define G4_ATT_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
 
 template <int HD>
-__global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float sl2, int split_from) {
+__global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float sl2, AtSplit sp) {
   using L = AttnLds<HD>;
   constexpr int NB = HD / 32;      // O blocks per wave
   constexpr int KS = HD / 16;      // MFMA k-steps for S
@@ -97,14 +120,12 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
   const int nruns = (int)((a.T + 31) / 32);
   const int ngroups = nruns * G;
   const int nblk = (ngroups + QG - 1) / QG;
-  // Work items, heaviest first: blocks split_from .. nblk-1 (the latest queries, whose key ranges are
-  // longest) come as two items each, one per half of the block's key tiles; the others whole.
-  const int nsplit = nblk - split_from;
-  const int v = (int)blockIdx.x;
-  const int blk = v < 2 * nsplit ? nblk - 1 - v / 2 : nblk - 1 - nsplit - (v - 2 * nsplit);
-  const int part = v < 2 * nsplit ? (v & 1) : 0, nparts = v < 2 * nsplit ? 2 : 1;
+  // Work items, heaviest first (AtSplit): a split block comes as one item per share of its key tiles;
+  // consecutive blocks of the grid take the same item of each kv head and sequence.
+  int blk, part, nparts;
+  const int64_t g = (int64_t)blockIdx.x % a.nkv, b = ((int64_t)blockIdx.x / a.nkv) % a.B;
+  at_item((int)((int64_t)blockIdx.x / (a.nkv * a.B)), nblk, sp, blk, part, nparts);
   const int gi = blk * QG + wave;
-  const int64_t g = blockIdx.y, b = blockIdx.z;
   const int run = gi / G;
   const int64_t head = g * G + gi % G;
   const int64_t tq = (int64_t)run * 32 + col;  // this lane's query token
@@ -124,9 +145,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
   if (hib > ksp.kmax) hib = ksp.kmax;
   const int64_t kstart = lob & ~(int64_t)(AT_KB - 1);
   const int ntiles = hib >= lob ? (int)((hib - kstart) / AT_KB + 1) : 0;
-  const int half_tiles = (ntiles + 1) / 2;
-  const int it0 = nparts == 2 && part == 1 ? half_tiles : 0;
-  const int it1 = nparts == 2 && part == 0 ? half_tiles : ntiles;
+  const int it0 = part * ntiles / nparts, it1 = (part + 1) * ntiles / nparts;
   int64_t qlo = qi - ksp.back;
   if (qlo < ksp.kmin) qlo = ksp.kmin;
   const int64_t qhi = qi + ksp.fwd < hib ? qi + ksp.fwd : hib;  // this query's last visible key
@@ -328,7 +347,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (!qvalid) return;
-  if (nparts == 2) {  // unnormalised partial O with its reference and normaliser, merged afterwards
+  if (nparts > 1) {  // unnormalised partial O with its reference and normaliser, merged afterwards
     const int64_t row = ((part * a.B + b) * a.T + tq) * a.nh + head;
     float* po = a.ws + row * HD;
 #pragma unroll
@@ -338,7 +357,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
         *(float4*)(po + 32 * d + 8 * r4 + 4 * h) =
             make_float4(o[d][4 * r4], o[d][4 * r4 + 1], o[d][4 * r4 + 2], o[d][4 * r4 + 3]);
     if (h == 0) {
-      float* ml = a.ws + 2 * a.B * a.T * a.nh * HD + 2 * row;
+      float* ml = a.ws + AT_PS * a.B * a.T * a.nh * HD + 2 * row;
       ml[0] = m_run;
       ml[1] = l_tot;
     }
@@ -377,7 +396,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
 //     cross-lane steps; the normaliser is summed per lane and across the four lanes at the end.
 // --------------------------------------------------------------------------------------------
 template <int HD>
-__global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl2, int split_from) {
+__global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl2, AtSplit sp) {
   using L = AttnLdsW<HD>;
   typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
   constexpr int NO = HD / 16;      // O blocks (16 head elements each) per wave
@@ -394,12 +413,10 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl
   const int nruns = (int)((a.T + 31) / 32);
   const int ngroups = nruns * G;
   const int nblk = (ngroups + QG - 1) / QG;
-  const int nsplit = nblk - split_from;
-  const int v = (int)blockIdx.x;
-  const int blk = v < 2 * nsplit ? nblk - 1 - v / 2 : nblk - 1 - nsplit - (v - 2 * nsplit);
-  const int part = v < 2 * nsplit ? (v & 1) : 0, nparts = v < 2 * nsplit ? 2 : 1;
+  int blk, part, nparts;
+  const int64_t g = (int64_t)blockIdx.x % a.nkv, b = ((int64_t)blockIdx.x / a.nkv) % a.B;
+  at_item((int)((int64_t)blockIdx.x / (a.nkv * a.B)), nblk, sp, blk, part, nparts);
   const int gi = blk * QG + (wave >> 1);
-  const int64_t g = blockIdx.y, b = blockIdx.z;
   const int run = gi / G;
   const int64_t head = g * G + gi % G;
   const int64_t tq0 = (int64_t)run * 32 + 16 * (wave & 1);  // the wave's first query token
@@ -419,9 +436,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl
   const int64_t hib = imax + ksp.fwd < ksp.kmax ? imax + ksp.fwd : ksp.kmax;
   const int64_t kstart = lob & ~(int64_t)(AT_KB - 1);
   const int ntiles = hib >= lob ? (int)((hib - kstart) / AT_KB + 1) : 0;
-  const int half_tiles = (ntiles + 1) / 2;
-  const int it0 = nparts == 2 && part == 1 ? half_tiles : 0;
-  const int it1 = nparts == 2 && part == 0 ? half_tiles : ntiles;
+  const int it0 = part * ntiles / nparts, it1 = (part + 1) * ntiles / nparts;
   int64_t qlo = qi - ksp.back;
   if (qlo < ksp.kmin) qlo = ksp.kmin;
   const int64_t qhi = qi + ksp.fwd < hib ? qi + ksp.fwd : hib;
@@ -619,13 +634,13 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl
   l_tot += __shfl_xor(l_tot, 32, 64);
   if (!qvalid) return;
   // lane holds head elements 16 d + 4 qq + 0..3 of query tq
-  if (nparts == 2) {
+  if (nparts > 1) {
     const int64_t row = ((part * a.B + b) * a.T + tq) * a.nh + head;
     float* po = a.ws + row * HD;
 #pragma unroll
     for (int d = 0; d < NO; ++d) *(float4*)(po + 16 * d + 4 * qq) = make_float4(o[d][0], o[d][1], o[d][2], o[d][3]);
     if (qq == 0) {
-      float* ml = a.ws + 2 * a.B * a.T * a.nh * HD + 2 * row;
+      float* ml = a.ws + AT_PS * a.B * a.T * a.nh * HD + 2 * row;
       ml[0] = m_run;
       ml[1] = l_tot;
     }
@@ -642,39 +657,130 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl
   }
 }
 
-// Merges the two key-half partials of each split query row: O = (O0 2^(m0-m) + O1 2^(m1-m)) /
-// (l0 2^(m0-m) + l1 2^(m1-m)) with m = max(m0, m1) (exp2 domain); a row that saw no key stays zero.
-// One wave per (sequence, query token >= tq_lo, head).
+// Merges the key-share partials of each split query row: O = sum_p O_p 2^(m_p - m) / sum_p l_p 2^(m_p - m)
+// with m = max_p m_p (exp2 domain), parts in order; a row that saw no key stays zero. One wave per
+// (sequence, query token >= tq_lo, head); the row's part count comes from its query block (AtSplit).
 template <int HD>
-__global__ __launch_bounds__(64) void k_attn_merge_split(AttnArgs a, int64_t tq_lo) {
+__global__ __launch_bounds__(64) void k_attn_merge_split(AttnArgs a, int64_t tq_lo, int G, int QG, AtSplit sp) {
   constexpr int EPL = HD / 64;
   const int64_t tq = tq_lo + blockIdx.x, head = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x;
-  const int64_t row0 = ((0 * a.B + b) * a.T + tq) * a.nh + head, row1 = ((1 * a.B + b) * a.T + tq) * a.nh + head;
-  const float* ml = a.ws + 2 * a.B * a.T * a.nh * HD;
-  const float m0 = ml[2 * row0], l0 = ml[2 * row0 + 1], m1 = ml[2 * row1], l1 = ml[2 * row1 + 1];
-  const float m = fmaxf(m0, m1);
-  const float a0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - m);
-  const float a1 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
-  const float den = l0 * a0 + l1 * a1;
+  const int blk = (int)(((tq / 32) * G + head % G) / QG);
+  const int np = 1 + (blk >= sp.th1) + (blk >= sp.th2) + (blk >= sp.th3);
+  const float* ml = a.ws + AT_PS * a.B * a.T * a.nh * HD;
+  float mp[AT_PS], lp[AT_PS], m = -INFINITY;
+#pragma unroll
+  for (int p = 0; p < AT_PS; ++p) {
+    const int64_t row = ((p * a.B + b) * a.T + tq) * a.nh + head;
+    mp[p] = p < np ? ml[2 * row] : -INFINITY;
+    lp[p] = p < np ? ml[2 * row + 1] : 0.f;
+    m = fmaxf(m, mp[p]);
+  }
+  float w[AT_PS], den = 0.f;
+#pragma unroll
+  for (int p = 0; p < AT_PS; ++p) {
+    w[p] = (p < np && m != -INFINITY) ? __builtin_amdgcn_exp2f(mp[p] - m) : 0.f;
+    den += lp[p] * w[p];
+  }
   const float inv = den > 0.f ? 1.f / den : 0.f;
-  const float* p0 = a.ws + row0 * HD + lane * EPL;
-  const float* p1 = a.ws + row1 * HD + lane * EPL;
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int p = 0; p < AT_PS; ++p)
+    if (p < np) {
+      const float* pp = a.ws + (((p * a.B + b) * a.T + tq) * a.nh + head) * HD + lane * EPL;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] += pp[e] * w[p];
+    }
   bf16* out = (bf16*)a.out + (b * a.T + tq) * a.out_ld + head * HD + lane * EPL;
 #pragma unroll
-  for (int e = 0; e < EPL; e += 2) {
-    const float x = (p0[e] * a0 + p1[e] * a1) * inv, y = (p0[e + 1] * a0 + p1[e + 1] * a1) * inv;
-    *(uint32_t*)(out + e) = (uint32_t)f2bf(x) | ((uint32_t)f2bf(y) << 16);
-  }
+  for (int e = 0; e < EPL; e += 2)
+    *(uint32_t*)(out + e) = (uint32_t)f2bf(acc[e] * inv) | ((uint32_t)f2bf(acc[e + 1] * inv) << 16);
 }
 
-// Query blocks of one launch and the first block to split. A causal launch with fewer blocks than
-// twice the CUs splits its heaviest half (the latest queries, whose key ranges are longest); a
-// sliding-window launch (every block's key range about the same) with fewer blocks than CUs splits
-// all of its blocks. split_from is a multiple of the blocks per 32-token
-// run so that the split rows start at a run boundary. Returns false if the shape is not the MFMA path's.
+// Query blocks of one launch and their key split (AtSplit). Only a launch with fewer blocks than the
+// device keeps busy splits (twice the CUs for causal full layers, whose blocks differ in length; the
+// CUs otherwise). Candidate splits give block b min(AT_PS, ceil(tiles_b / t)) parts for a tile target
+// t, made non-decreasing in the block index (the latest causal queries have the longest key ranges),
+// so three thresholds describe each. The plan keeps the candidate (or no split) whose items, dispatched
+// in the kernels' order onto the earliest free CU, finish first, counting each part of a split block
+// HD/512 of a tile more for its partial and the merge. Tile counts assume the call starts at position
+// 0 (positions live on the device): any split gives the same result, this one balances the usual
+// case. Plans are cached per shape. Returns false if the shape is not the MFMA path's.
+struct AtPlanKey {
+  int64_t B, T, nh, nkv, hd, window, cus;
+  int32_t sliding, bidir;
+  bool operator==(const AtPlanKey& o) const {
+    return B == o.B && T == o.T && nh == o.nh && nkv == o.nkv && hd == o.hd && window == o.window && cus == o.cus &&
+           sliding == o.sliding && bidir == o.bidir;
+  }
+};
+
+static AtSplit at_choose_split(const AtPlanKey& k, int nblk, int64_t G, int64_t ngroups, int QG) {
+  std::vector<int64_t> tl(nblk);
+  int64_t maxt = 1;
+  for (int b = 0; b < nblk; ++b) {  // key tiles of block b for a call from position 0
+    const int64_t g0 = (int64_t)b * QG, g1 = (g0 + QG < ngroups ? g0 + QG : ngroups) - 1;
+    const int64_t imin = (g0 / G) * 32, imax = (g1 / G) * 32 + 31 < k.T - 1 ? (g1 / G) * 32 + 31 : k.T - 1;
+    int64_t lo = 0, hi = imax;
+    if (k.bidir) {
+      if (k.sliding) { lo = imin - k.window; hi = imax + k.window < k.T - 1 ? imax + k.window : k.T - 1; }
+      else hi = k.T - 1;
+    } else if (k.sliding) {
+      lo = imin - k.window + 1;
+    }
+    if (lo < 0) lo = 0;
+    tl[b] = (hi - (lo & ~(int64_t)(AT_KB - 1))) / AT_KB + 1;
+    if (tl[b] > maxt) maxt = tl[b];
+  }
+  const int64_t copies = k.nkv * k.B;
+  const double part_cost = (double)k.hd / 512.0;
+  auto split_for = [&](int64_t t) {
+    AtSplit sp{nblk, nblk, nblk};
+    int prev = 1;
+    for (int b = 0; b < nblk; ++b) {
+      int64_t p = (tl[b] + t - 1) / t;
+      if (p > AT_PS) p = AT_PS;
+      if (p < prev) p = prev;
+      prev = (int)p;
+      if (p >= 2 && sp.th1 == nblk) sp.th1 = b;
+      if (p >= 3 && sp.th2 == nblk) sp.th2 = b;
+      if (p >= 4 && sp.th3 == nblk) sp.th3 = b;
+    }
+    return sp;
+  };
+  auto makespan = [&](const AtSplit& sp) {
+    std::priority_queue<double, std::vector<double>, std::greater<double>> cu;
+    for (int64_t c = 0; c < k.cus; ++c) cu.push(0.0);
+    const int th[5] = {0, sp.th1, sp.th2, sp.th3, nblk};
+    double end = 0.0;
+    for (int np = AT_PS; np >= 1; --np)  // the kernels' item order: 4-part blocks from the last down, ...
+      for (int b = th[np] - 1; b >= th[np - 1]; --b)
+        for (int p = 0; p < np; ++p) {
+          const double dur = (double)((p + 1) * tl[b] / np - p * tl[b] / np) + (np > 1 ? part_cost : 0.0);
+          for (int64_t c = 0; c < copies; ++c) {
+            const double t0 = cu.top();
+            cu.pop();
+            cu.push(t0 + dur);
+            if (t0 + dur > end) end = t0 + dur;
+          }
+        }
+    return end;
+  };
+  AtSplit best{nblk, nblk, nblk};
+  double best_ms = makespan(best);
+  const int64_t tmin = (maxt + AT_PS - 1) / AT_PS, stride = (maxt - tmin) / 48 + 1;
+  for (int64_t t = tmin; t < maxt; t += stride) {
+    const AtSplit sp = split_for(t);
+    const double ms = makespan(sp);
+    if (ms < best_ms - 1e-9) { best_ms = ms; best = sp; }
+  }
+  return best;
+}
+
 static bool attn_plan(int64_t B, int64_t T, int64_t nh, int64_t nkv, int64_t hd, int32_t sliding, int32_t bidir,
-                      int* nblk, int* split_from, int64_t* tq_lo) {
+                      int64_t window, int* nblk, AtSplit* sp, int64_t* tq_lo) {
   if (nkv <= 0 || nh % nkv) return false;
   const int64_t G = nh / nkv;
   if (!(G == 1 || G == 2 || G == 4) || !(hd == 128 || hd == 256 || hd == 512)) return false;
@@ -682,47 +788,60 @@ static bool attn_plan(int64_t B, int64_t T, int64_t nh, int64_t nkv, int64_t hd,
   const int QG = 4;  // query groups (head x 32 tokens) per block
   const int64_t ngroups = runs * G;
   *nblk = (int)((ngroups + QG - 1) / QG);
-  *split_from = *nblk;
+  *sp = AtSplit{*nblk, *nblk, *nblk};
   const int64_t blocks = (int64_t)*nblk * nkv * B;
-  if (sliding ? blocks < cus : blocks < 2 * cus) {
-    const int step = G > QG ? (int)(G / QG) : 1;
-    // causal full layers: the later half of the blocks holds the longer key ranges; with a window or the
-    // encoder's mask every block's range is about as long, so every block is split
-    *split_from = (sliding || bidir) ? 0 : (*nblk / 2) / step * step;
+  if ((sliding || bidir) ? blocks < cus : blocks < 2 * cus) {
+    static thread_local std::vector<std::pair<AtPlanKey, AtSplit>> cache;
+    const AtPlanKey key{B, T, nh, nkv, hd, (sliding || bidir) ? window : 0, cus, sliding, bidir};
+    bool hit = false;
+    for (const auto& e : cache)
+      if (e.first == key) { *sp = e.second; hit = true; break; }
+    if (!hit) {
+      *sp = at_choose_split(key, *nblk, G, ngroups, QG);
+      if (cache.size() >= 64) cache.erase(cache.begin());
+      cache.emplace_back(key, *sp);
+    }
   }
-  *tq_lo = ((int64_t)*split_from * QG / G) * 32;
+  *tq_lo = ((int64_t)sp->th1 * QG / G) * 32;
   return true;
 }
 
+static size_t attn_split_bytes(int64_t B, int64_t T, int64_t nh, int64_t hd) {
+  return (size_t)AT_PS * B * T * nh * (hd + 2) * 4;
+}
+
+// Scratch for the key-split partials of any launch attn_mfma may make for these shapes (the largest
+// split trigger is the causal full layer's).
 size_t attn_prefill_ws(int64_t B, int64_t T, int64_t nh, int64_t nkv, int64_t hd) {
-  int nblk = 0, sf = 0;
-  int64_t tq_lo = 0;
-  size_t need = 0;
-  for (int sl = 0; sl < 2; ++sl)
-    if (attn_plan(B, T, nh, nkv, hd, sl, 0, &nblk, &sf, &tq_lo) && sf < nblk) need = (size_t)2 * B * T * nh * (hd + 2) * 4;
-  return need;
+  if (nkv <= 0 || nh % nkv) return 0;
+  const int64_t nblk = ((T + 31) / 32 * (nh / nkv) + 3) / 4;
+  return nblk * nkv * B < 2 * device_cus() ? attn_split_bytes(B, T, nh, hd) : 0;
 }
 
 // bf16, head_dim 128/256/512, groups of 1, 2 or 4 query heads per kv head, 16-byte aligned rows.
 bool attn_mfma(const AttnArgs& a, hipStream_t s, g4_status* st) {
   if ((a.q_ld | a.out_ld) & 7) return false;
   if (((uintptr_t)a.q | (uintptr_t)a.k | (uintptr_t)a.v | (uintptr_t)a.out) & 15) return false;
-  int nblk = 0, split_from = 0;
+  int nblk = 0;
+  AtSplit sp{};
   int64_t tq_lo = 0;
-  if (!attn_plan(a.B, a.T, a.nh, a.nkv, a.hd, a.sliding, a.bidir, &nblk, &split_from, &tq_lo)) return false;
-  const size_t need = (size_t)2 * a.B * a.T * a.nh * (a.hd + 2) * 4;
-  if (!a.ws || a.ws_bytes < need || ((uintptr_t)a.ws & 15)) split_from = nblk;  // no scratch: no split
+  if (!attn_plan(a.B, a.T, a.nh, a.nkv, a.hd, a.sliding, a.bidir, a.window, &nblk, &sp, &tq_lo)) return false;
+  if (!a.ws || a.ws_bytes < attn_split_bytes(a.B, a.T, a.nh, a.hd) || ((uintptr_t)a.ws & 15)) {
+    sp.th1 = sp.th2 = sp.th3 = nblk;  // no scratch: no split
+    tq_lo = a.T;
+  }
   const int64_t G = a.nh / a.nkv;
-  dim3 grid((unsigned)(2 * (nblk - split_from) + split_from), (unsigned)a.nkv, (unsigned)a.B);
+  const int items = nblk + (nblk - sp.th1) + (nblk - sp.th2) + (nblk - sp.th3);
+  dim3 grid((unsigned)((int64_t)items * a.nkv * a.B));
   const float sl2 = a.scale * 1.4426950408889634f;
-  if (a.hd == 128) hipLaunchKernelGGL((k_attn_mfma<128>), grid, dim3(256), 0, s, a, (int)G, sl2, split_from);
-  else if (a.hd == 256) hipLaunchKernelGGL((k_attn_w16<256>), grid, dim3(512), 0, s, a, (int)G, sl2, split_from);
-  else hipLaunchKernelGGL((k_attn_w16<512>), grid, dim3(512), 0, s, a, (int)G, sl2, split_from);
-  if ((*st = check_launch("attn_mfma")) != G4_OK || split_from == nblk || tq_lo >= a.T) return true;
+  if (a.hd == 128) hipLaunchKernelGGL((k_attn_mfma<128>), grid, dim3(256), 0, s, a, (int)G, sl2, sp);
+  else if (a.hd == 256) hipLaunchKernelGGL((k_attn_w16<256>), grid, dim3(512), 0, s, a, (int)G, sl2, sp);
+  else hipLaunchKernelGGL((k_attn_w16<512>), grid, dim3(512), 0, s, a, (int)G, sl2, sp);
+  if ((*st = check_launch("attn_mfma")) != G4_OK || sp.th1 == nblk || tq_lo >= a.T) return true;
   dim3 gm((unsigned)(a.T - tq_lo), (unsigned)a.nh, (unsigned)a.B);
-  if (a.hd == 128) hipLaunchKernelGGL((k_attn_merge_split<128>), gm, dim3(64), 0, s, a, tq_lo);
-  else if (a.hd == 256) hipLaunchKernelGGL((k_attn_merge_split<256>), gm, dim3(64), 0, s, a, tq_lo);
-  else hipLaunchKernelGGL((k_attn_merge_split<512>), gm, dim3(64), 0, s, a, tq_lo);
+  if (a.hd == 128) hipLaunchKernelGGL((k_attn_merge_split<128>), gm, dim3(64), 0, s, a, tq_lo, (int)G, 4, sp);
+  else if (a.hd == 256) hipLaunchKernelGGL((k_attn_merge_split<256>), gm, dim3(64), 0, s, a, tq_lo, (int)G, 4, sp);
+  else hipLaunchKernelGGL((k_attn_merge_split<512>), gm, dim3(64), 0, s, a, tq_lo, (int)G, 4, sp);
   *st = check_launch("attn_merge_split");
   return true;
 }
