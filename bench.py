@@ -276,7 +276,15 @@ def cpu_baseline(cfg, budget_s):
             Tp = target
             t = run(Tp, 1)
         tokens = Tp
-        sample = f"prefill of the first {Tp} of {cfg['T']} tokens (batch 1) through all {L} layers"
+        reps = 1
+        # a sample shorter than the budget (the whole workload fits) is repeated until about 2/3 of it is
+        # spent, so that the rate is not one short run's
+        while t < budget_s * 2 / 3:
+            t += run(Tp, 1)
+            reps += 1
+        tokens = Tp * reps
+        sample = (f"prefill of the first {Tp} of {cfg['T']} tokens (batch 1) through all {L} layers"
+                  + (f", {reps} runs" if reps > 1 else ""))
     cores = sum(p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas") or 1
     return dict(value=round(tokens / t, 3), unit="tokens/s", cores=cores, kind="oracle", sample=sample,
                 seconds=round(t, 2))
