@@ -173,3 +173,30 @@ def test_encoder_full_size_layer_sampled_rows(layer):
     e = rel_l2(h[0, rr], ref)
     log(f"encoder layer {layer} T={T}: sampled rows rel L2 {e:.3e}")
     assert e <= TOL_BF16_RELL2
+
+
+def test_bf16_encoder_batch_at_offsets_ignores_earlier_rows():
+    """Two sequences encoded at cache offsets 0 and 37 of a 160-row cache whose other rows hold junk
+    (x 50): every layer, from the oracle's input, matches the oracle's encoder over each call's own keys."""
+    cfg = configs.get(7, T=100, B=2, layer_types="SSF")
+    T, cap, offs = 100, 160, [0, 37]
+    model, layers, _ = build_model(cfg)
+    acts = gen.activations(cfg, "cuda")
+    pos = torch.tensor(offs, dtype=torch.int32, device="cuda")
+    caches, table = model.new_caches(2, cap)
+    for l, (k, v) in caches.items():
+        k.copy_(randn(k.shape, 150 + l, k.dtype, 50.0))
+        v.copy_(randn(v.shape, 160 + l, v.dtype, 50.0))
+    h0, ple = O.f64(acts["h0"]), O.f64(acts["ple_in"])
+    hs = [h0]
+    O.forward(cfg, host_layer(layers), h0, ple, O.prefill_positions(offs, T), O.new_caches(cfg, 2, cap),
+              per_layer=hs, bidirectional=True)
+    ple_d = _dev(ple)
+    errs = []
+    for l in range(model.L):
+        x = _dev(hs[l])
+        model.forward(x, ple_d, pos, table, cap, bd.G4_ENCODE, layer=l)
+        torch.cuda.synchronize()
+        errs.append(max(rel_l2(x[b], hs[l + 1][b]) for b in range(2)))
+    log("encoder at offsets, per-layer rel L2 (worst sequence): " + " ".join(f"{e:.1e}" for e in errs))
+    assert max(errs) <= TOL_BF16_RELL2
