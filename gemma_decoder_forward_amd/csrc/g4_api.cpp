@@ -333,6 +333,33 @@ static bool stage_from_parts(int64_t M, int64_t Kc, int64_t Nc, int parts, int r
   return bytes <= 16e6;
 }
 
+// A few-row product above 16 rows on the tiled kernel, K split into float32 slices [slice][M][N] of the
+// stacked matrices' rows: about 256 (128-wide tile, K slice) pairs, and no more slices than `out` holds.
+// The few-row kernel re-stages the activations for every 16 or 64 weight rows, as many bytes as it
+// streams at 64 rows; with a single K range the tiled kernel would have only N / 128 tiles. Returns false,
+// with nothing launched, when the tiled kernel does not take the shape.
+static bool tiled_slices(const void* A, int64_t lda, const void* const* segs, const int64_t* rows, int nseg,
+                         int64_t ldb, int64_t M, int64_t K, float* out, size_t out_bytes, int* slices,
+                         hipStream_t s, g4_status* st) {
+  int64_t N = 0;
+  for (int i = 0; i < nseg; ++i) N += rows[i];
+  const int64_t tiles = (N + 127) / 128;
+  int64_t sd = 256 / tiles < K / 256 ? 256 / tiles : K / 256;
+  if (sd < 1) sd = 1;
+  while (sd > 1 && (size_t)sd * M * N * 4 > out_bytes) --sd;
+  if ((size_t)sd * M * N * 4 > out_bytes) return false;
+  GemmArgs ga{};
+  ga.A = A; ga.lda = lda; ga.B = segs[0]; ga.ldb = ldb; ga.C = out; ga.ldc = N; ga.c_dtype = G4_F32;
+  ga.M = M; ga.N = N; ga.K = K; ga.epi = EPI_STORE; ga.splits = (int32_t)sd; ga.split_stride = M * N;
+  if (nseg > 1) {
+    ga.nseg = nseg;
+    for (int i = 0; i < nseg; ++i) { ga.segB[i] = segs[i]; ga.seg_rows[i] = rows[i]; }
+  }
+  if (!gemm_mfma(ga, s, st)) return false;
+  *slices = (int)sd;
+  return true;
+}
+
 static g4_status few_row_layer(const LayerCtx& c) {
   const g4_model_desc* m = c.m;
   const g4_layer_desc* l = c.l;
@@ -370,9 +397,14 @@ static g4_status few_row_layer(const LayerCtx& c) {
     TimedScope ts(G4_KC_QKV_GEMM, c.s);
     const void* segs[3] = {l->wq, l->wk, l->wv};
     const int64_t rows[3] = {nh * hd, nkv * hd, nkv * hd};
-    SkA sa{};
-    sa.a = xn; sa.lda = H; sa.kind = SKA_BF16;
-    G4_TRY(gemm_skinny_part(sa, M, H, segs, rows, nseg, H, X, XB, &s1, c.s));
+    g4_status mst = G4_OK;
+    if (M > 16 && tiled_slices(xn, H, segs, rows, nseg, H, M, H, X, XB, &s1, c.s, &mst)) {
+      G4_TRY(mst);
+    } else {
+      SkA sa{};
+      sa.a = xn; sa.lda = H; sa.kind = SKA_BF16;
+      G4_TRY(gemm_skinny_part(sa, M, H, segs, rows, nseg, H, X, XB, &s1, c.s));
+    }
   }
   {
     TimedScope ts(G4_KC_QK_NORM_ROPE, c.s);
@@ -406,35 +438,44 @@ static g4_status few_row_layer(const LayerCtx& c) {
   int s2 = 0;
   {
     TimedScope ts(G4_KC_O_GEMM, c.s);
-    SkA sa{};
-    sa.a = ao; sa.lda = nh * hd; sa.kind = SKA_BF16;
-    G4_TRY(gemm_skinny_part(sa, M, nh * hd, wo, rH, 1, nh * hd, Y, YB, &s2, c.s));
+    g4_status mst = G4_OK;
+    if (M > 16 && tiled_slices(ao, nh * hd, wo, rH, 1, nh * hd, M, nh * hd, Y, YB, &s2, c.s, &mst)) {
+      G4_TRY(mst);
+    } else {
+      SkA sa{};
+      sa.a = ao; sa.lda = nh * hd; sa.kind = SKA_BF16;
+      G4_TRY(gemm_skinny_part(sa, M, nh * hd, wo, rH, 1, nh * hd, Y, YB, &s2, c.s));
+    }
   }
   {
     TimedScope ts(G4_KC_ROW_TAIL, c.s);
     G4_TRY(rownorm(Y, G4_F32, s2, M * H, l->post_attn_norm, nullptr, c.h, 1.f, l->pre_ffn_norm, xn, M, H, m->eps,
                    dt, c.s));
   }
-  // gate/up: up to 16 rows one weight-streaming pass writes the bf16 product; above that the tiled
-  // gated-product kernel does (measured at 20480 x 2560 weights: 23.5 vs 32.4 us at 32 rows, 24.5 vs
-  // 68.5 at 64, where each few-row block re-stages as many activation bytes as it streams weights);
-  // failing both, partials, whose gelu_tanh(gate) * up the down projection forms while staging its A
+  // gate/up: up to 12 rows one weight-streaming pass writes the bf16 product; above that the tiled
+  // gated-product kernel does. Decode steps, 42 layers (gate/up ms per step, one pass / tiled): 1.18 /
+  // 1.58 at 4 rows, 1.23 / 1.59 at 8, 1.98 / 1.62 at 16; at 64 rows the split-K few-row form took 2.83
+  // against the tiled 1.77 (each few-row block re-stages as many activation bytes as it streams
+  // weights). Failing both, partials, whose gelu_tanh(gate) * up the down projection forms in its A.
   int s3 = 0, s4 = 0;
   bool gated = false;  // act holds the bf16 product
   {
     TimedScope ts(G4_KC_GATE_UP_GEMM, c.s);
     SkA sa{};
     sa.a = xn; sa.lda = H; sa.kind = SKA_BF16;
-    if (skinny_gated_ok(M, H, F)) {
+    if (M <= 12 && skinny_gated_ok(M, H, F)) {
       G4_TRY(gemm_skinny_gated(sa, M, H, l->w_gate, l->w_up, F, H, act, F, c.s));
       gated = true;
-    } else if (M > 16) {
+    } else {
       GemmArgs ga{};
       ga.A = xn; ga.lda = H; ga.B = l->w_gate; ga.B2 = l->w_up; ga.ldb = H; ga.C = act; ga.ldc = F; ga.c_dtype = dt;
       ga.M = M; ga.N = F; ga.K = H; ga.epi = EPI_GEGLU; ga.splits = 1;
       g4_status mst = G4_OK;
       if (gemm_mfma(ga, c.s, &mst)) {
         G4_TRY(mst);
+        gated = true;
+      } else if (skinny_gated_ok(M, H, F)) {
+        G4_TRY(gemm_skinny_gated(sa, M, H, l->w_gate, l->w_up, F, H, act, F, c.s));
         gated = true;
       }
     }
@@ -446,18 +487,27 @@ static g4_status few_row_layer(const LayerCtx& c) {
   }
   {
     TimedScope ts(G4_KC_DOWN_GEMM, c.s);
-    SkA sa{};
-    if (gated) {
-      sa.a = act; sa.lda = F; sa.kind = SKA_BF16;
-    } else if (stage_from_parts(M, F, H, s3, 2)) {
-      sa.a = X; sa.lda = 2 * F; sa.kind = SKA_GEGLU; sa.parts = s3; sa.part_stride = M * 2 * F; sa.up_off = F;
-    } else {
-      GemmArgs ga{};
-      ga.M = M; ga.N = F; ga.C = act; ga.ldc = F; ga.c_dtype = dt; ga.epi = EPI_GEGLU;
-      G4_TRY(gemm_skinny_finish(ga, X, s3, 2 * F, c.s));
-      sa.a = act; sa.lda = F; sa.kind = SKA_BF16;
+    // above 16 rows with the product in act: the tiled kernel, K split into slices the row tail sums
+    bool down_done = false;
+    if (gated && M > 16) {
+      g4_status mst = G4_OK;
+      down_done = tiled_slices(act, F, wd, rH, 1, F, M, F, Y, YB, &s4, c.s, &mst);
+      if (down_done) G4_TRY(mst);
     }
-    G4_TRY(gemm_skinny_part(sa, M, F, wd, rH, 1, F, Y, YB, &s4, c.s));
+    if (!down_done) {
+      SkA sa{};
+      if (gated) {
+        sa.a = act; sa.lda = F; sa.kind = SKA_BF16;
+      } else if (stage_from_parts(M, F, H, s3, 2)) {
+        sa.a = X; sa.lda = 2 * F; sa.kind = SKA_GEGLU; sa.parts = s3; sa.part_stride = M * 2 * F; sa.up_off = F;
+      } else {
+        GemmArgs ga{};
+        ga.M = M; ga.N = F; ga.C = act; ga.ldc = F; ga.c_dtype = dt; ga.epi = EPI_GEGLU;
+        G4_TRY(gemm_skinny_finish(ga, X, s3, 2 * F, c.s));
+        sa.a = act; sa.lda = F; sa.kind = SKA_BF16;
+      }
+      G4_TRY(gemm_skinny_part(sa, M, F, wd, rH, 1, F, Y, YB, &s4, c.s));
+    }
   }
   {
     TimedScope ts(G4_KC_ROW_TAIL, c.s);
