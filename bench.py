@@ -4,8 +4,10 @@
 Default workload: the E4B-shaped layer pair (one sliding layer, hd 256, W 512; one full layer, hd 512,
 25% proportional RoPE; H 2560, 8/2 heads, FFN 10240, PLE 256), bf16 weights, prefill of T = 2048
 tokens, batch 1. A step is one pass of the whole layer forward over that batch, inputs resident in HBM.
-Other workloads (--workload 3/4/5): the 42-layer prefill from token ids, decode at context 8192, and
-the 12-layer T = 32768 slice.
+Other workloads (--workload 3/4/5/6/7): the 42-layer prefill from token ids at T = 4096, decode at
+context 8192 (--batch B), the 12-layer T = 32768 slice, a 6-layer E4B-width model with the variants
+(own full-layer KV heads, K=V, per-layer FFN widths) at T = 2048, and the 6-layer E4B-width
+bidirectional encoder at T = 2048.
 
 Prints one JSON line. The dominant kernel's launches are timed inside the timed region with HIP events
 recorded by the library on its launch stream (g4_timer_*); `roofline` divides its algorithmic work per

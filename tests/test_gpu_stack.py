@@ -80,7 +80,7 @@ def test_config1_fp32_stack_full_parity():
     rc = O.new_caches(cfg, 1, cfg["T"])
     ref = O.forward(cfg, host_layer(layers), h0, ple, O.prefill_positions([0], cfg["T"]), rc)
     e = assert_close(h, ref, "f32", "final hidden")
-    log(f"config 1 max rel err {e:.2e}")
+    log(f"tiny fp32 4-layer stack: max rel err {e:.2e}")
     for l, (k, v) in caches.items():
         assert_close(k, rc[l][0], "f32", f"K cache {l}")
         assert_close(v, rc[l][1], "f32", f"V cache {l}")
@@ -128,7 +128,7 @@ def test_fp32_e4b_layer_pair_end_to_end():
     h0, ple = _oracle_inputs(cfg, glob, acts, cfg["T"])
     ref = O.forward(cfg, host_layer(layers), h0, ple, O.prefill_positions([0], cfg["T"]), O.new_caches(cfg, 1, cfg["T"]))
     e = assert_close(h, ref, "f32", "final hidden")
-    log(f"fp32 config 2 T=700: max rel err {e:.2e}")
+    log(f"fp32 E4B layer pair T=700: max rel err {e:.2e}")
 
 
 def test_fp32_e4b_12_layer_stack_per_layer():
@@ -163,7 +163,7 @@ def test_bf16_stack_per_layer_parity(cid, T):
     cfg = configs.get(cid, T=T)
     model, layers, glob = build_model(cfg)
     acts = gen.activations(cfg, "cuda")
-    log(f"config {cid} T={T}: GPU end to end")
+    log(f"{cfg['name']} T={T}: GPU end to end")
     h_gpu, _ = _gpu_stack(cfg, model, acts)
     if cid == 2:
         h_again, _ = _gpu_stack(cfg, model, acts)
@@ -236,7 +236,7 @@ def test_config4_decode_per_layer_sampled_sequences(B):
     model, layers, glob = build_model(cfg)
     acts = gen.activations(cfg, "cuda")
     ctx = cfg["ctx"]
-    log(f"config 4 B={B}: caches")
+    log(f"42-layer decode B={B}: caches")
     fills = {l: gen.decode_cache(cfg, l, "cuda") for l in range(cfg["n_layers"]) if model.kv_src[l] == l}
     sample = sorted({0, B - 1})
     ocache = {l: (O.f64(k[sample]), O.f64(v[sample])) for l, (k, v) in fills.items()}
@@ -246,7 +246,7 @@ def test_config4_decode_per_layer_sampled_sequences(B):
     model.forward(h, ple, acts["pos"], table, ctx, bd.G4_DECODE)
     torch.cuda.synchronize()
     assert torch.isfinite(h).all()
-    log(f"config 4 B={B}: oracle on sequences {sample}")
+    log(f"42-layer decode B={B}: oracle on sequences {sample}")
     sub = dict(cfg, B=len(sample))
     e0, p0 = _oracle_entry(sub, glob, acts["ids"][sample])
     hs = [e0]
