@@ -1,13 +1,15 @@
 #!/usr/bin/env python3
 """Throughput of the Gemma-4 E-series decoder forward on one MI355X.
 
-Default workload: the E4B-shaped layer pair (one sliding layer, hd 256, W 512; one full layer, hd 512,
-25% proportional RoPE; H 2560, 8/2 heads, FFN 10240, PLE 256), bf16 weights, prefill of T = 2048
-tokens, batch 1. A step is one pass of the whole layer forward over that batch, inputs resident in HBM.
-Other workloads (--workload 3/4/5/6/7): the 42-layer prefill from token ids at T = 4096, decode at
-context 8192 (--batch B), the 12-layer T = 32768 slice, a 6-layer E4B-width model with the variants
-(own full-layer KV heads, K=V, per-layer FFN widths) at T = 2048, and the 6-layer E4B-width
-bidirectional encoder at T = 2048.
+Default workload: the full E4B-like 42-layer stack (5 sliding + 1 full layer, repeated; the last 18
+layers share KV), bf16 weights, prefill of T = 4096 tokens of batch 1 from token ids: the embedding and
+per-layer inputs, then every layer. A step is one pass of that whole forward over the batch, inputs
+resident in HBM. In the same process, on the same weights, `extra.decode` times one decode step at
+context 8192 for batch 1 and 64 (the 42-layer model, caches filled to position 8190), and `extra.long`
+the 12-layer T = 32768 slice. Other workloads (--workload 2/4/5/6/7): the E4B layer pair at T = 2048,
+decode alone (--batch B), the 12-layer slice alone, a 6-layer E4B-width model with the variants (own
+full-layer KV heads, K=V, per-layer FFN widths) at T = 2048, and the 6-layer E4B-width bidirectional
+encoder at T = 2048.
 
 Prints one JSON line. The dominant kernel's launches are timed inside the timed region with HIP events
 recorded by the library on its launch stream (g4_timer_*); `roofline` divides its algorithmic work per
@@ -137,7 +139,41 @@ def gate_up_weight_bytes(cfg):
     return 2 * mean_ffn(cfg) * cfg["hidden"] * 2
 
 
-def run_gpu(cfg, steps, warmup, breakdown, use_graph=True):
+def decode_step_bytes(cfg):
+    """Algorithmic HBM bytes of one decode step of B sequences: every weight the step reads once (the layer
+    projections and norms by routing, the PLE model projection), the embedding and PLE table rows of the B
+    tokens, each attention layer's K and V over its visible keys (shared layers count their re-read of the
+    source cache), and the new K/V rows the owning layers write."""
+    E = 2 if cfg["dtype"] == "bf16" else 4
+    H, nh, d, L, B = cfg["hidden"], cfg["n_heads"], cfg["ple_dim"], cfg["n_layers"], cfg["B"]
+    from gemma_decoder_forward_amd import binding as bd
+    srcs = bd.g4_kv_sources([1 if t == "S" else 0 for t in cfg["layer_types"]], cfg["n_shared"])
+    w = 0
+    kv = 0
+    for l, t in enumerate(cfg["layer_types"]):
+        hd, nkv, F, has_v = layer_shape(cfg, l)
+        own = srcs[l] == l
+        w += (nh * hd * H + (nkv * hd * H * (2 if has_v else 1) if own else 0) + H * nh * hd + 3 * F * H
+              + 2 * d * H) * E
+        w += (5 * H + hd * (2 if own else 1)) * E  # norm weights
+        keys = min(cfg["ctx"], cfg["window"]) if t == "S" else cfg["ctx"]
+        kv += B * 2 * nkv * keys * hd * E
+        if own:
+            kv += B * 2 * nkv * hd * E
+    w += (L * d * H + d) * E  # PLE model projection and its norm
+    gathers = B * (H + L * d) * E
+    return dict(weights=w, kv=kv, gathers=gathers, total=w + kv + gathers)
+
+
+def build_weights(cfg):
+    """Device weights of a workload (layers, and the embedding/PLE tables for configs built from ids)."""
+    from synth import gen
+    layers = [gen.layer_weights(cfg, l, "cuda") for l in range(cfg["n_layers"])]
+    glob = gen.model_globals(cfg, "cuda") if cfg["embed"] else None
+    return layers, glob
+
+
+def run_gpu(cfg, layers, glob, steps, warmup, breakdown, use_graph=True):
     import torch
     from gemma_decoder_forward_amd import binding as bd
     from gemma_decoder_forward_amd.model import G4Model
@@ -145,8 +181,6 @@ def run_gpu(cfg, steps, warmup, breakdown, use_graph=True):
 
     torch.cuda.set_device(0)
     B, T = cfg["B"], cfg["T"]
-    layers = [gen.layer_weights(cfg, l, "cuda") for l in range(cfg["n_layers"])]
-    glob = gen.model_globals(cfg, "cuda") if cfg["embed"] else None
     model = G4Model(cfg, layers, glob)
     acts = gen.activations(cfg, "cuda")
     decode = cfg["mode"] == "decode"
@@ -212,29 +246,109 @@ def run_gpu(cfg, steps, warmup, breakdown, use_graph=True):
             per[name] = round(ms / 2, 4)
         res["breakdown_ms_per_step"] = per
     assert torch.isfinite(h).all().item(), "non-finite output"
+    del model, table, h, acts
+    if decode:
+        del fills
+    torch.cuda.empty_cache()
     return res
 
 
-def cpu_baseline(cfg, budget_s):
-    """The float64 oracle, as it stands, on a bounded sample of the workload (host cores)."""
+WORKLOAD_NAMES = {2: "e4b-layer-pair prefill", 3: "e4b-42-layer prefill from token ids", 4: "e4b-42-layer decode",
+                  5: "e4b-12-layer long-context prefill",
+                  6: "e4b-width 6-layer prefill with the variants (full-layer kv heads, K=V, per-layer FFN widths)",
+                  7: "e4b-width 6-layer bidirectional encoder"}
+
+
+def workload_name(cfg):
+    decode = cfg["mode"] == "decode"
+    return f"{WORKLOAD_NAMES[cfg['id']]}: B={cfg['B']} T={cfg['T']}" + (f" ctx={cfg['ctx']}" if decode else "")
+
+
+def summarize(cfg, r):
+    """Throughput, the dominant kernel's roofline and (decode) the step's HBM fraction of one GPU run."""
+    B, T = cfg["B"], cfg["T"]
+    tokens = B * T
+    ms = r["ms_per_step"]
+    decode = cfg["mode"] == "decode"
+    dom_avg_s = r["dom_ms"] / max(r["dom_n"], 1) / 1e3
+    out = dict(workload=workload_name(cfg), tokens_per_s=round(tokens / (ms / 1e3), 2), ms_per_step=round(ms, 4),
+               hip_graph=r["graph"])
+    if decode:
+        per_launch = gate_up_weight_bytes(cfg) + 2 * B * cfg["hidden"] + 2 * B * mean_ffn(cfg)
+        achieved = per_launch / dom_avg_s / 1e9
+        out["roofline"] = dict(bound="hbm", kernel="gate_up_gemm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS,
+                               unit="GB/s", frac=round(achieved / PEAK_HBM_GBS, 4), bytes_per_launch=per_launch,
+                               avg_launch_us=round(dom_avg_s * 1e6, 2))
+        sb = decode_step_bytes(cfg)
+        gbs = sb["total"] / (ms / 1e3) / 1e9
+        out["step_bytes"] = sb
+        out["step_GB_s"] = round(gbs, 1)
+        out["frac_hbm"] = round(gbs / PEAK_HBM_GBS, 4)
+    else:
+        per_launch = 2 * tokens * 2 * mean_ffn(cfg) * cfg["hidden"]
+        achieved = per_launch / dom_avg_s / 1e12
+        out["roofline"] = dict(bound="mfma", kernel="gate_up_gemm", achieved=round(achieved, 2),
+                               peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", frac=round(achieved / PEAK_BF16_TFLOPS, 4),
+                               flops_per_launch=per_launch, avg_launch_us=round(dom_avg_s * 1e6, 2))
+        gf = gemm_flops(cfg, tokens)
+        af = attn_flops(cfg, T)
+        out["gemm_tflop_per_step"] = round(sum(gf.values()) / 1e12, 4)
+        out["attn_tflop_per_step"] = round(af / 1e12, 4)
+        out["model_tflops"] = round((sum(gf.values()) + af) / (ms / 1e3) / 1e12, 2)
+        out["frac_mfma"] = round(out["model_tflops"] / PEAK_BF16_TFLOPS, 4)
+    if "breakdown_ms_per_step" in r:
+        out["breakdown_ms_per_step"] = r["breakdown_ms_per_step"]
+        out["class_rates"] = class_rates(cfg, tokens, decode, r["breakdown_ms_per_step"])
+    return out
+
+
+def host_cores():
+    """Threads the oracle's BLAS may use: the CPUs this process may run on, capped by the cgroup CPU quota
+    when one is set (a container's share can be smaller than its affinity mask)."""
+    aff = len(os.sched_getaffinity(0))
+    quota = None
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            q, per = f.read().split()[:2]
+        if q != "max":
+            quota = max(1, -(-int(q) // int(per)))
+    except (OSError, ValueError):
+        pass
+    return (min(aff, quota) if quota else aff), aff, quota
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, layers_dev, glob_dev, budget_s):
+    """The float64 oracle, as it stands, on a bounded sample of the workload (host cores, BLAS threads
+    pinned to the cores this process may use). Only the oracle's forward is timed; each layer's weights
+    are copied to the host and widened to float64 before its timed call, one layer at a time."""
     import numpy as np
     import torch
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_limits
 
     import oracle as O
     from synth import gen
 
+    cores, aff, quota = host_cores()
     L = cfg["n_layers"]
-    layers = [{k: (O.f64(v) if isinstance(v, torch.Tensor) else v) for k, v in gen.layer_weights(cfg, l, "cuda").items()}
-              for l in range(L)]
     acts = gen.activations(cfg, "cuda")
-    glob = None
-    if cfg["embed"]:
-        g = gen.model_globals(cfg, "cuda")
-        glob = g
     srcs = O.kv_sources(cfg["layer_types"], cfg["n_shared"])
 
+    def host_layer(l):
+        return {k: (O.f64(v) if isinstance(v, torch.Tensor) else v) for k, v in layers_dev[l].items()}
+
     def run(Tp, nseq):
+        """Seconds of oracle compute for a prefill of Tp tokens (or one decode step of nseq sequences)."""
         if cfg["mode"] == "decode":
             sub = dict(cfg, B=nseq)
             ids = acts["ids"][:nseq].cpu().numpy()
@@ -249,47 +363,53 @@ def cpu_baseline(cfg, budget_s):
             ids = acts["ids"][:, :Tp].cpu().numpy() if cfg["embed"] else None
             caches = O.new_caches(cfg, 1, Tp, srcs)
             pos = O.prefill_positions([0], Tp)
+        t = 0.0
         if cfg["embed"]:
             uniq, inv = np.unique(ids, return_inverse=True)
             idx = torch.from_numpy(uniq).cuda()
-            gh = dict(embed=glob["embed"][idx].cpu(), ple_embed=glob["ple_embed"][idx].cpu(),
-                      ple_model_proj=O.f64(glob["ple_model_proj"]), ple_norm=glob["ple_norm"].cpu())
+            gh = dict(embed=glob_dev["embed"][idx].cpu(), ple_embed=glob_dev["ple_embed"][idx].cpu(),
+                      ple_model_proj=O.f64(glob_dev["ple_model_proj"]), ple_norm=glob_dev["ple_norm"].cpu())
             sub2 = dict(sub, vocab=len(uniq), ple_vocab=len(uniq))
-            idl = inv.reshape(ids.shape)
+            t0 = time.perf_counter()
+            h, ple = O.entry(sub2, gh, inv.reshape(ids.shape))
+            t += time.perf_counter() - t0
         else:
-            h0 = O.f64(acts["h0"][:, :Tp])
+            h = O.f64(acts["h0"][:, :Tp])
             ple = O.f64(acts["ple_in"][:, :Tp])
-        t0 = time.perf_counter()
-        if cfg["embed"]:
-            h0, ple = O.entry(sub2, gh, idl)
-        O.forward(sub, layers, h0, ple, pos, caches, srcs, bidirectional=cfg["mode"] == "encode")
-        return time.perf_counter() - t0
+        for l in range(L):
+            lw = host_layer(l)
+            t0 = time.perf_counter()
+            h = O.forward(sub, {l: lw}, h, ple, pos, caches, srcs, layer_range=[l],
+                          bidirectional=cfg["mode"] == "encode")
+            t += time.perf_counter() - t0
+        return t
 
-    if cfg["mode"] == "decode":
-        n = 1
-        t = run(0, n)
-        tokens, sample = n, f"decode step of {n} sequence at context {cfg['ctx']}"
-    else:
-        Tp = 128
-        t = run(Tp, 1)
-        target = int(Tp * budget_s / max(t, 1e-3)) // 64 * 64
-        target = min(cfg["T"], target)
-        if target > Tp:
-            Tp = target
+    with threadpool_limits(limits=cores, user_api="blas"):
+        if cfg["mode"] == "decode":
+            n = 1
+            t = run(0, n)
+            tokens, sample = n, f"decode step of {n} sequence at context {cfg['ctx']} through all {L} layers"
+        else:
+            Tp = 64
             t = run(Tp, 1)
-        tokens = Tp
-        reps = 1
-        # a sample shorter than the budget (the whole workload fits) is repeated until about 2/3 of it is
-        # spent, so that the rate is not one short run's
-        while t < budget_s * 2 / 3:
-            t += run(Tp, 1)
-            reps += 1
-        tokens = Tp * reps
-        sample = (f"prefill of the first {Tp} of {cfg['T']} tokens (batch 1) through all {L} layers"
-                  + (f", {reps} runs" if reps > 1 else ""))
-    cores = sum(p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas") or 1
+            target = int(Tp * budget_s / max(t, 1e-3)) // 64 * 64
+            target = min(cfg["T"], target)
+            if target > Tp:
+                Tp = target
+                t = run(Tp, 1)
+            reps = 1
+            # a sample shorter than the budget (the whole workload fits) is repeated until about 2/3 of it
+            # is spent, so that the rate is not one short run's
+            while t < budget_s * 2 / 3:
+                t += run(Tp, 1)
+                reps += 1
+            tokens = Tp * reps
+            sample = (f"prefill of the first {Tp} of {cfg['T']} tokens (batch 1) through all {L} layers"
+                      + (" from token ids (embedding and per-layer inputs included)" if cfg["embed"] else "")
+                      + (f", {reps} runs" if reps > 1 else ""))
     return dict(value=round(tokens / t, 3), unit="tokens/s", cores=cores, kind="oracle", sample=sample,
-                seconds=round(t, 2))
+                seconds=round(t, 2), cpu_model=cpu_model(), affinity_cpus=aff, cgroup_cpu_quota=quota,
+                blas_threads=cores)
 
 
 def counted_traffic(workload_name, kernel_class):
@@ -335,8 +455,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5, 6, 7])
+    ap.add_argument("--workload", type=int, default=3, choices=[2, 3, 4, 5, 6, 7])
     ap.add_argument("--batch", type=int, default=64, help="decode batch (workload 4)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="workload 3: skip the decode (B=1, 64) and T=32768 lines of `extra`")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -352,44 +474,46 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): this build "
               "measures the single-GPU forward; sharding is a design note, not implemented.", file=sys.stderr)
         sys.exit(2)
+    from synth import configs
     cfg = workload(args.workload, args.batch)
-    r = run_gpu(cfg, args.steps, args.warmup, not args.no_breakdown, not args.no_graph)
-    B, T = cfg["B"], cfg["T"]
-    tokens = B * T
-    ms = r["ms_per_step"]
+    breakdown = not args.no_breakdown
+    print(f"[bench] {workload_name(cfg)}: building weights", file=sys.stderr, flush=True)
+    layers, glob = build_weights(cfg)
+    r = run_gpu(cfg, layers, glob, args.steps, args.warmup, breakdown, not args.no_graph)
+    main_sum = summarize(cfg, r)
+    print(f"[bench] {main_sum['workload']}: {main_sum['tokens_per_s']} tokens/s", file=sys.stderr, flush=True)
     decode = cfg["mode"] == "decode"
-    dom_avg_s = r["dom_ms"] / max(r["dom_n"], 1) / 1e3
-    names = {2: "e4b-layer-pair prefill", 3: "e4b-42-layer prefill from token ids", 4: "e4b-42-layer decode",
-             5: "e4b-12-layer long-context prefill",
-             6: "e4b-width 6-layer prefill with the variants (full-layer kv heads, K=V, per-layer FFN widths)",
-             7: "e4b-width 6-layer bidirectional encoder"}
-    wname = f"{names[args.workload]}: B={B} T={T}" + (f" ctx={cfg['ctx']}" if decode else "")
-    traffic = counted_traffic(wname, "gate_up_gemm")
-    if decode:
-        per_launch = gate_up_weight_bytes(cfg) + 2 * B * cfg["hidden"] + 2 * B * mean_ffn(cfg)
-        achieved = per_launch / dom_avg_s / 1e9
-        roof = dict(bound="hbm", kernel="gate_up_gemm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=round(achieved / PEAK_HBM_GBS, 4), traffic=traffic, bytes_per_launch=per_launch,
-                    avg_launch_us=round(dom_avg_s * 1e6, 2))
-    else:
-        per_launch = 2 * tokens * 2 * mean_ffn(cfg) * cfg["hidden"]
-        achieved = per_launch / dom_avg_s / 1e12
-        roof = dict(bound="mfma", kernel="gate_up_gemm", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS,
-                    unit="TFLOP/s", frac=round(achieved / PEAK_BF16_TFLOPS, 4), traffic=traffic,
-                    flops_per_launch=per_launch, avg_launch_us=round(dom_avg_s * 1e6, 2))
-    gf = gemm_flops(cfg, tokens)
-    extra = dict(gemm_tflop_per_step=round(sum(gf.values()) / 1e12, 4), hip_graph=r["graph"])
-    if not decode:
-        af = attn_flops(cfg, T)
-        extra["attn_tflop_per_step"] = round(af / 1e12, 4)
-        extra["model_tflops"] = round((sum(gf.values()) + af) / (ms / 1e3) / 1e12, 2)
-    if "breakdown_ms_per_step" in r:
-        extra["breakdown_ms_per_step"] = r["breakdown_ms_per_step"]
-        extra["class_rates"] = class_rates(cfg, tokens, decode, r["breakdown_ms_per_step"])
+    wname = main_sum["workload"]
+    roof = dict(main_sum["roofline"], traffic=counted_traffic(wname, "gate_up_gemm"))
+    extra = {k: v for k, v in main_sum.items() if k not in ("workload", "tokens_per_s", "ms_per_step", "roofline")}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, layers, glob, args.cpu_seconds)
+        print(f"[bench] oracle on the host: {cpu['value']} tokens/s", file=sys.stderr, flush=True)
+    if args.workload == 3 and not args.no_extra:
+        # decode on the same model (config 4's weights are config 3's), then the long-context slice
+        extra["decode"] = {}
+        for B in (1, 64):
+            c4 = configs.get(4, B=B)
+            r4 = run_gpu(c4, layers, glob, args.steps, args.warmup, breakdown, not args.no_graph)
+            extra["decode"][f"B{B}"] = summarize(c4, r4)
+            print(f"[bench] {extra['decode'][f'B{B}']['workload']}: {extra['decode'][f'B{B}']['tokens_per_s']} "
+                  "tokens/s", file=sys.stderr, flush=True)
+        del layers, glob
+        import torch
+        torch.cuda.empty_cache()
+        c5 = configs.get(5)
+        l5, _ = build_weights(c5)
+        r5 = run_gpu(c5, l5, None, args.steps, args.warmup, breakdown)
+        extra["long"] = summarize(c5, r5)
+        print(f"[bench] {extra['long']['workload']}: {extra['long']['tokens_per_s']} tokens/s", file=sys.stderr,
+              flush=True)
+        del l5
+    B, T = cfg["B"], cfg["T"]
     line = dict(
         metric="decode tokens/s" if decode else ("encoder tokens/s" if cfg["mode"] == "encode" else "prefill tokens/s"),
-        value=round(tokens / (ms / 1e3), 2), unit="tokens/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
-        ms_per_step=round(ms, 4), higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16",
+        value=main_sum["tokens_per_s"], unit="tokens/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+        ms_per_step=main_sum["ms_per_step"], higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16",
         data="synthetic (seeded N(0,0.02) weights, N(0,1) activations / uniform token ids)",
         config=dict(workload=wname,
                     layers=cfg["n_layers"], layer_types=cfg["layer_types"], hidden=cfg["hidden"],
@@ -401,8 +525,8 @@ def main():
                     global_batch=B, seq_len=T, parallelism="none (1 GPU)"),
         roofline=roof, extra=extra,
     )
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 

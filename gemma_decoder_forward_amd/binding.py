@@ -43,10 +43,11 @@ _SIGS = {
     "g4_kv_sources": (C.c_int, [C.POINTER(i32), i32, i32, C.POINTER(i32)]),
     "g4_rmsnorm": (C.c_int, [vp, i32, i32, vp, vp, vp, f32, vp, vp, i64, i64, f32, i32, vp]),
     "g4_qk_norm_rope": (C.c_int, [vp, i64, vp, vp, i64, i64, vp, i64, i64, i64, i64, f32, i64, f32, i32, vp]),
+    "g4_attn_prefill_ws": (sz, [i64, i64, i64, i64, i64]),
     "g4_attn_prefill": (C.c_int, [vp, i64, vp, i32, i32, i32, i32, i64, vp, i64, i64, i64, i64, i64, f32, vp, i64,
-                                  i32, vp]),
+                                  vp, sz, i32, vp]),
     "g4_attn_encode": (C.c_int, [vp, i64, vp, i32, i32, i32, i32, i64, vp, i64, i64, i64, i64, i64, f32, vp, i64,
-                                 i32, vp]),
+                                 vp, sz, i32, vp]),
     "g4_attn_decode": (C.c_int, [vp, i64, vp, i32, i32, i32, i32, i64, vp, i64, i64, i64, i64, f32, vp, i64, vp, sz,
                                  i32, vp]),
     "g4_attn_decode_ws": (sz, [i64, i64, i64, i64]),
@@ -123,16 +124,20 @@ def g4_qk_norm_rope(x, x_ld, w, y, y_ld, y_cap, pos, B, T, heads, hd, theta, rot
                  stream)
 
 
+def g4_attn_prefill_ws(B, T, nh, nkv, hd):
+    return lib().g4_attn_prefill_ws(B, T, nh, nkv, hd)
+
+
 def g4_attn_prefill(q, q_ld, kv, n_kv, layer, kv_src, sliding, window, pos0, B, T, nh, nkv, hd, scale, out, out_ld,
-                    dtype, stream=None):
+                    ws, ws_bytes, dtype, stream=None):
     return _call("g4_attn_prefill", q, q_ld, kv, n_kv, layer, kv_src, sliding, window, pos0, B, T, nh, nkv, hd, scale,
-                 out, out_ld, dtype, stream)
+                 out, out_ld, ws, ws_bytes, dtype, stream)
 
 
 def g4_attn_encode(q, q_ld, kv, n_kv, layer, kv_src, sliding, window, pos0, B, T, nh, nkv, hd, scale, out, out_ld,
-                   dtype, stream=None):
+                   ws, ws_bytes, dtype, stream=None):
     return _call("g4_attn_encode", q, q_ld, kv, n_kv, layer, kv_src, sliding, window, pos0, B, T, nh, nkv, hd, scale,
-                 out, out_ld, dtype, stream)
+                 out, out_ld, ws, ws_bytes, dtype, stream)
 
 
 def g4_attn_decode(q, q_ld, kv, n_kv, layer, kv_src, sliding, window, pos, B, nh, nkv, hd, scale, out, out_ld, ws,

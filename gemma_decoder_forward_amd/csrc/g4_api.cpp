@@ -293,6 +293,10 @@ static g4_status check_layer(const g4_model_desc* m, const g4_layer_desc* l, int
            "layer %d owns its cache but wk/wv/k_norm is NULL", layer);
   else G4_REQ(l->kv_src < layer, G4_EGEOM, "layer %d: kv_src %d is not an earlier layer", layer, l->kv_src);
   const int64_t hd = l->sliding ? m->head_dim_swa : m->head_dim_full;
+  // decode attention groups at most 8 query heads per kv head (checked here, before anything launches)
+  G4_REQ(mode != G4_DECODE || m->n_heads / kv_heads(m, l->sliding) <= 8, G4_EUNSUP,
+         "layer %d: decode attention takes at most 8 query heads per kv head (%lld)", layer,
+         (long long)(m->n_heads / kv_heads(m, l->sliding)));
   return check_kv(kv, n_kv, layer, l->kv_src, l->sliding, hd, T, mode, m->window);
 }
 
@@ -755,14 +759,26 @@ static g4_status check_attn(const void* q, int64_t q_ld, const g4_kv_entry* kv, 
   return check_kv(kv, n_kv, layer, kv_src, sliding, hd, T, mode, window);
 }
 
+size_t g4_attn_prefill_ws(int64_t B, int64_t T, int64_t nh, int64_t nkv, int64_t hd) {
+  if (B <= 0 || T <= 0 || nh <= 0 || nkv <= 0 || hd <= 0 || nh % nkv) return 0;
+  return attn_prefill_ws(B, T, nh, nkv, hd);
+}
+
 static g4_status attn_prefill_entry(const void* q, int64_t q_ld, const g4_kv_entry* kv, int32_t n_kv, int32_t layer,
                                     int32_t kv_src, int32_t sliding, int64_t window, const int32_t* pos0, int64_t B,
                                     int64_t T, int64_t nh, int64_t nkv, int64_t hd, float scale, void* out,
-                                    int64_t out_ld, int32_t dtype, void* stream, int32_t mode) {
+                                    int64_t out_ld, void* ws, size_t ws_bytes, int32_t dtype, void* stream,
+                                    int32_t mode) {
   g4_status st = check_attn(q, q_ld, kv, n_kv, layer, kv_src, sliding, window, pos0, B, T, nh, nkv, hd, out,
                             out_ld, dtype, mode);
   if (st != G4_OK) return st;
+  if (ws) {
+    const size_t need = g4_attn_prefill_ws(B, T, nh, nkv, hd);
+    G4_REQ(ws_bytes >= need, G4_EINVAL, "attention workspace too small (%zu < %zu)", ws_bytes, need);
+    G4_REQ(((uintptr_t)ws & 15) == 0, G4_EINVAL, "attention workspace is not 16-byte aligned");
+  }
   AttnArgs a{};
+  a.ws = (float*)ws; a.ws_bytes = ws ? ws_bytes : 0;
   a.q = q; a.q_ld = q_ld; a.k = kv[kv_src].k; a.v = kv[kv_src].v; a.cap = kv[kv_src].cap; a.pos0 = pos0;
   a.B = B; a.T = T; a.nh = nh; a.nkv = nkv; a.hd = hd; a.sliding = sliding; a.window = window; a.scale = scale;
   a.out = out; a.out_ld = out_ld; a.ring = kv[kv_src].ring; a.bidir = mode == G4_ENCODE;
@@ -773,17 +789,17 @@ static g4_status attn_prefill_entry(const void* q, int64_t q_ld, const g4_kv_ent
 g4_status g4_attn_prefill(const void* q, int64_t q_ld, const g4_kv_entry* kv, int32_t n_kv, int32_t layer,
                           int32_t kv_src, int32_t sliding, int64_t window, const int32_t* pos0, int64_t B,
                           int64_t T, int64_t nh, int64_t nkv, int64_t hd, float scale, void* out, int64_t out_ld,
-                          int32_t dtype, void* stream) {
+                          void* ws, size_t ws_bytes, int32_t dtype, void* stream) {
   return attn_prefill_entry(q, q_ld, kv, n_kv, layer, kv_src, sliding, window, pos0, B, T, nh, nkv, hd, scale, out,
-                            out_ld, dtype, stream, G4_PREFILL);
+                            out_ld, ws, ws_bytes, dtype, stream, G4_PREFILL);
 }
 
 g4_status g4_attn_encode(const void* q, int64_t q_ld, const g4_kv_entry* kv, int32_t n_kv, int32_t layer,
                          int32_t kv_src, int32_t sliding, int64_t window, const int32_t* pos0, int64_t B,
                          int64_t T, int64_t nh, int64_t nkv, int64_t hd, float scale, void* out, int64_t out_ld,
-                         int32_t dtype, void* stream) {
+                         void* ws, size_t ws_bytes, int32_t dtype, void* stream) {
   return attn_prefill_entry(q, q_ld, kv, n_kv, layer, kv_src, sliding, window, pos0, B, T, nh, nkv, hd, scale, out,
-                            out_ld, dtype, stream, G4_ENCODE);
+                            out_ld, ws, ws_bytes, dtype, stream, G4_ENCODE);
 }
 
 size_t g4_attn_decode_ws(int64_t B, int64_t nh, int64_t hd, int64_t cap) { return attn_decode_ws(B, nh, hd, cap); }
@@ -974,47 +990,82 @@ size_t g4_workspace_size(const g4_model_desc* model, int64_t B, int64_t T, int64
   return plan(model, B, T, cap, mode).total;
 }
 
+// Plan of a layer-forward call over the caches its layers read: decode partials are sized by the largest
+// capacity among them, so one plan (and one workspace check) covers every layer of the call.
+static Plan call_plan(const g4_model_desc* model, const g4_layer_desc* layers, int32_t n_layers, const g4_kv_entry* kv,
+                      int64_t B, int64_t T, int32_t mode) {
+  int64_t cap = 1;
+  for (int32_t i = 0; i < n_layers; ++i) cap = std::max(cap, kv[layers[i].kv_src].cap);
+  return plan(model, B, T, cap, mode);
+}
+
+static g4_status check_ws(const Plan& p, const void* ws, size_t ws_bytes) {
+  G4_REQ(ws && ws_bytes >= p.total, G4_EINVAL, "workspace too small (%zu < %zu)", ws_bytes, p.total);
+  G4_REQ(((uintptr_t)ws & 255) == 0, G4_EINVAL, "workspace is not 256-byte aligned");
+  return G4_OK;
+}
+
 static g4_status layer_entry(const g4_model_desc* model, const g4_layer_desc* ld, int32_t layer, float* h,
                              const float* ple_in, const g4_kv_entry* kv, int32_t n_kv, const int32_t* pos, int64_t B,
-                             int64_t T, int32_t mode, void* ws, size_t ws_bytes, void* stream, bool xn_ready,
+                             int64_t T, int32_t mode, void* ws, const Plan& p, void* stream, bool xn_ready,
                              const void* next_norm) {
-  const int64_t cap = kv[ld->kv_src].cap;
-  Plan p = plan(model, B, T, cap, mode);
-  G4_REQ(ws && ws_bytes >= p.total, G4_EINVAL, "workspace too small (%zu < %zu)", ws_bytes, p.total);
   LayerCtx c{model, ld, layer, h, ple_in, kv, n_kv, pos, B, T, mode, (char*)ws, &p, (hipStream_t)stream, xn_ready,
              next_norm};
   return layer_impl(c);
 }
 
-g4_status g4_layer_forward(const g4_model_desc* model, const g4_layer_desc* ld, int32_t layer, float* h,
-                           const float* ple_in, const g4_kv_entry* kv, int32_t n_kv, const int32_t* pos, int64_t B,
-                           int64_t T, int32_t mode, void* ws, size_t ws_bytes, void* stream) {
+static g4_status check_call(const g4_model_desc* model, const float* h, const float* ple_in, const int32_t* pos,
+                            int64_t B, int64_t T, int32_t mode) {
   g4_status st = check_model(model);
   if (st != G4_OK) return st;
   G4_REQ(mode == G4_PREFILL || mode == G4_DECODE || mode == G4_ENCODE, G4_EINVAL, "mode %d", mode);
   G4_REQ(h && ple_in && pos, G4_EINVAL, "h, ple_in or pos is NULL");
   G4_REQ(B >= 0 && T >= 0, G4_EINVAL, "B, T");
+  return G4_OK;
+}
+
+g4_status g4_layer_forward(const g4_model_desc* model, const g4_layer_desc* ld, int32_t layer, float* h,
+                           const float* ple_in, const g4_kv_entry* kv, int32_t n_kv, const int32_t* pos, int64_t B,
+                           int64_t T, int32_t mode, void* ws, size_t ws_bytes, void* stream) {
+  g4_status st = check_call(model, h, ple_in, pos, B, T, mode);
+  if (st != G4_OK) return st;
   if ((st = check_layer(model, ld, layer, kv, n_kv, T, mode)) != G4_OK) return st;
-  return layer_entry(model, ld, layer, h, ple_in, kv, n_kv, pos, B, T, mode, ws, ws_bytes, stream, false, nullptr);
+  const Plan p = call_plan(model, ld, 1, kv, B, T, mode);
+  if ((st = check_ws(p, ws, ws_bytes)) != G4_OK) return st;
+  return layer_entry(model, ld, layer, h, ple_in, kv, n_kv, pos, B, T, mode, ws, p, stream, false, nullptr);
+}
+
+// Every check of a stack call (model, each layer, workspace) happens before the first launch.
+static g4_status stack_run(const g4_model_desc* model, const g4_layer_desc* layers, float* h, const float* ple_in,
+                           const g4_kv_entry* kv, int32_t n_kv, const int32_t* pos, int64_t B, int64_t T, int32_t mode,
+                           void* ws, const Plan& p, void* stream) {
+  for (int32_t l = 0; l < model->n_layers; ++l) {
+    const void* nn = l + 1 < model->n_layers ? layers[l + 1].input_norm : nullptr;
+    const g4_status st = layer_entry(model, &layers[l], l, h, ple_in, kv, n_kv, pos, B, T, mode, ws, p, stream, l > 0, nn);
+    if (st != G4_OK) return st;
+  }
+  return G4_OK;
+}
+
+static g4_status check_stack(const g4_model_desc* model, const g4_layer_desc* layers, const float* h,
+                             const float* ple_in, const g4_kv_entry* kv, int32_t n_kv, const int32_t* pos, int64_t B,
+                             int64_t T, int32_t mode) {
+  g4_status st = check_call(model, h, ple_in, pos, B, T, mode);
+  if (st != G4_OK) return st;
+  G4_REQ(layers, G4_EINVAL, "layers is NULL");
+  for (int32_t l = 0; l < model->n_layers; ++l)
+    if ((st = check_layer(model, &layers[l], l, kv, n_kv, T, mode)) != G4_OK) return st;
+  return G4_OK;
 }
 
 g4_status g4_stack_forward(const g4_model_desc* model, const g4_layer_desc* layers, float* h, const float* ple_in,
                            const g4_kv_entry* kv, int32_t n_kv, const int32_t* pos, int64_t B, int64_t T, int32_t mode,
                            void* ws, size_t ws_bytes, void* stream) {
-  g4_status st = check_model(model);
+  g4_status st = check_stack(model, layers, h, ple_in, kv, n_kv, pos, B, T, mode);
   if (st != G4_OK) return st;
-  G4_REQ(layers, G4_EINVAL, "layers is NULL");
-  G4_REQ(mode == G4_PREFILL || mode == G4_DECODE || mode == G4_ENCODE, G4_EINVAL, "mode %d", mode);
-  G4_REQ(h && ple_in && pos, G4_EINVAL, "h, ple_in or pos is NULL");
-  G4_REQ(B >= 0 && T >= 0, G4_EINVAL, "B, T");
-  for (int32_t l = 0; l < model->n_layers; ++l)
-    if ((st = check_layer(model, &layers[l], l, kv, n_kv, T, mode)) != G4_OK) return st;
-  for (int32_t l = 0; l < model->n_layers; ++l) {
-    const void* nn = l + 1 < model->n_layers ? layers[l + 1].input_norm : nullptr;
-    st = layer_entry(model, &layers[l], l, h, ple_in, kv, n_kv, pos, B, T, mode, ws, ws_bytes, stream, l > 0, nn);
-    if (st != G4_OK) return st;
-  }
-  return G4_OK;
+  const Plan p = call_plan(model, layers, (int32_t)model->n_layers, kv, B, T, mode);
+  if ((st = check_ws(p, ws, ws_bytes)) != G4_OK) return st;
+  return stack_run(model, layers, h, ple_in, kv, n_kv, pos, B, T, mode, ws, p, stream);
 }
 
 }  // extern "C"

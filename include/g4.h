@@ -167,24 +167,30 @@ g4_status g4_qk_norm_rope(const void* x, int64_t x_ld, const void* w, void* y, i
  *   lo = 0 (sliding == 0) or i - window + 1 (sliding == 1). Those rows must already hold this call's
  *   K/V (written by g4_qk_norm_rope) and earlier tokens.
  *   out[b*T+t, h*hd:(h+1)*hd] = softmax_j(scale * q.k_j) v_j, leading dimension out_ld.
+ *   ws, ws_bytes: optional scratch (16-byte aligned) for the key split of a short prefill, whose few query
+ *   blocks would leave most compute units idle: the blocks then split their key ranges and a merge pass
+ *   combines the partial softmax sums. ws == NULL: no split (same result, fewer blocks in flight);
+ *   otherwise ws_bytes >= g4_attn_prefill_ws(B, T, nh, nkv, hd), else G4_EINVAL.
  * Validation: kv_src <= layer, kv[kv_src] present with hd and attention type equal to this call's. */
+size_t g4_attn_prefill_ws(int64_t B, int64_t T, int64_t nh, int64_t nkv, int64_t hd);
 g4_status g4_attn_prefill(const void* q, int64_t q_ld, const g4_kv_entry* kv, int32_t n_kv,
                           int32_t layer, int32_t kv_src, int32_t sliding, int64_t window,
                           const int32_t* pos0, int64_t B, int64_t T, int64_t nh, int64_t nkv,
-                          int64_t hd, float scale, void* out, int64_t out_ld, int32_t dtype,
-                          void* stream);
+                          int64_t hd, float scale, void* out, int64_t out_ld, void* ws,
+                          size_t ws_bytes, int32_t dtype, void* stream);
 
 /* The encoder's non-causal attention (taconite-embeddinggemma2 model.rs, `text_attention`: every key
  * of the sequence, a sliding layer's keys within |i - j| <= window). Arguments as g4_attn_prefill; the
  * sequence is this call: query i = pos0[b]+t sees the cache rows j of the call's own tokens,
  * pos0[b] <= j <= pos0[b]+T-1, all of them (sliding == 0) or those with |i - j| <= window
  * (sliding == 1), so rows before pos0[b] are never read. The call's K/V rows must already be in the
- * cache. The cache must be linear (ring == 0), else G4_EINVAL. */
+ * cache. The cache must be linear (ring == 0), else G4_EINVAL. The workspace is g4_attn_prefill's
+ * (same size query, NULL allowed). */
 g4_status g4_attn_encode(const void* q, int64_t q_ld, const g4_kv_entry* kv, int32_t n_kv,
                          int32_t layer, int32_t kv_src, int32_t sliding, int64_t window,
                          const int32_t* pos0, int64_t B, int64_t T, int64_t nh, int64_t nkv,
-                         int64_t hd, float scale, void* out, int64_t out_ld, int32_t dtype,
-                         void* stream);
+                         int64_t hd, float scale, void* out, int64_t out_ld, void* ws,
+                         size_t ws_bytes, int32_t dtype, void* stream);
 
 /* Decode attention: one query per sequence at position pos[b] (turbospark `encode_attention_any`
  * over [kv_start, seq_len)). Same semantics as g4_attn_prefill with T = 1. Split over key chunks;
@@ -252,14 +258,18 @@ g4_status g4_embed_ple(const int32_t* ids, int64_t M, const void* E, const void*
  *   mode G4_DECODE:  T must be 1.
  *   mode G4_ENCODE:  as G4_PREFILL, with the encoder's attention (g4_attn_encode) over the call's
  *                    tokens; linear caches only.
- * A layer that owns its cache (kv_src == layer) writes its K/V rows before attending. */
+ * A layer that owns its cache (kv_src == layer) writes its K/V rows before attending.
+ * ws: 256-byte aligned device scratch of at least g4_workspace_size(model, B, T, cap, mode) bytes, cap the
+ * capacity of the cache this layer reads. */
 g4_status g4_layer_forward(const g4_model_desc* model, const g4_layer_desc* layer_desc,
                            int32_t layer, float* h, const float* ple_in, const g4_kv_entry* kv,
                            int32_t n_kv, const int32_t* pos, int64_t B, int64_t T, int32_t mode,
                            void* ws, size_t ws_bytes, void* stream);
 
 /* All n_layers layers in order; layers is an array of n_layers descriptors. Returns the hidden state
- * before the final norm, in h. */
+ * before the final norm, in h. ws as for g4_layer_forward, with cap the largest capacity among the caches
+ * the layers read. Every layer and the workspace are validated before the first launch, so a failing
+ * call leaves h and the caches untouched. */
 g4_status g4_stack_forward(const g4_model_desc* model, const g4_layer_desc* layers, float* h,
                            const float* ple_in, const g4_kv_entry* kv, int32_t n_kv,
                            const int32_t* pos, int64_t B, int64_t T, int32_t mode, void* ws,

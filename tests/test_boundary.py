@@ -70,9 +70,9 @@ def _table(entries):
     return t
 
 
-def _attn(table, layer, kv_src, sliding, hd, T=8, window=512, nh=8, nkv=2, q=FAKE):
+def _attn(table, layer, kv_src, sliding, hd, T=8, window=512, nh=8, nkv=2, q=FAKE, ws=None, ws_bytes=0):
     return bd.lib().g4_attn_prefill(q, nh * hd, table, len(table), layer, kv_src, sliding, window, FAKE, 1, T, nh,
-                                    nkv, hd, 1.0, FAKE, nh * hd, bd.G4_BF16, None)
+                                    nkv, hd, 1.0, FAKE, nh * hd, ws, ws_bytes, bd.G4_BF16, None)
 
 
 def test_attention_validation_errors():
@@ -86,6 +86,11 @@ def test_attention_validation_errors():
     assert _attn(t, 2, 0, 1, 256, nh=6, nkv=4) == bd.G4_EGEOM
     assert _attn(t, 2, 0, 1, 256, q=None) == bd.G4_EINVAL
     assert _attn(t, 7, 0, 1, 256) == bd.G4_EINVAL     # layer outside the table
+    need = bd.g4_attn_prefill_ws(1, 8, 8, 2, 256)
+    assert need > 0                                   # a short prefill splits its keys when given scratch
+    assert _attn(t, 2, 0, 1, 256, ws=FAKE, ws_bytes=need - 1) == bd.G4_EINVAL  # scratch too small
+    assert b"workspace" in bd.lib().g4_last_error()
+    assert _attn(t, 2, 0, 1, 256, ws=FAKE + 8, ws_bytes=need) == bd.G4_EINVAL  # misaligned scratch
     assert b"head_dim" in bd.lib().g4_last_error() or bd.lib().g4_last_error()
 
 
@@ -97,7 +102,7 @@ def test_encode_validation_errors():
 
     def enc(table, layer, kv_src, T=8, window=512):
         return L.g4_attn_encode(FAKE, 8 * 256, table, len(table), layer, kv_src, 1, window, FAKE, 1, T, 8, 2, 256, 1.0,
-                                FAKE, 8 * 256, bd.G4_BF16, None)
+                                FAKE, 8 * 256, None, 0, bd.G4_BF16, None)
 
     assert enc(t, 0, 0) == bd.G4_EINVAL and b"linear" in L.g4_last_error()
     assert enc(t, 1, 1, T=65) == bd.G4_ERANGE
@@ -248,3 +253,57 @@ def test_logits_validation_errors():
     assert L.g4_logits(FAKE, 4, 64, None, FAKE, 128, 1e-6, 30.0, FAKE, FAKE, ws, 1, None) == bd.G4_EINVAL
     assert L.g4_logits(FAKE, 4, 64, FAKE, FAKE, 0, 1e-6, 30.0, FAKE, FAKE, ws, 1, None) == bd.G4_EINVAL
     assert L.g4_logits(FAKE, 4, 64, FAKE, FAKE, 128, 1e-6, 30.0, FAKE, FAKE, ws, 5, None) == bd.G4_EINVAL
+
+
+def _stack_descs(pattern, n_shared):
+    """Layer descriptors of a stack with fake weight pointers and the library's own routing."""
+    srcs = bd.g4_kv_sources([1 if t == "S" else 0 for t in pattern], n_shared)
+    descs = (bd.LayerDesc * len(pattern))()
+    for l, t in enumerate(pattern):
+        descs[l].sliding = 1 if t == "S" else 0
+        descs[l].kv_src = srcs[l]
+        descs[l].layer_scalar = 1.0
+        for n in bd.LAYER_PTRS:
+            setattr(descs[l], n, FAKE)
+    return descs, srcs
+
+
+def test_stack_workspace_checked_once_for_the_largest_cache():
+    """Mixed ring (sliding) and linear (full) caches: a workspace sized for the ring's capacity is too small
+    for the full layers' decode partials. The stack call must refuse it before the first layer launches
+    (the message names the workspace), and accept the size planned for the largest capacity."""
+    pattern = "SSSSSF"
+    m = _model(n_layers=len(pattern))
+    m.n_layers = len(pattern)
+    descs, srcs = _stack_descs(pattern, 0)
+    t = _table([(1024, 256, 1, 1) if c == "S" else (8192, 512, 0, 0) for c in pattern])
+    L = bd.lib()
+    B = 4
+    small = bd.g4_workspace_size(m, B, 1, 1024, bd.G4_DECODE)
+    big = bd.g4_workspace_size(m, B, 1, 8192, bd.G4_DECODE)
+    assert 0 < small < big
+
+    def stack(ws_bytes, model=m):
+        return L.g4_stack_forward(C.byref(model), descs, FAKE, FAKE, t, len(t), FAKE, B, 1, bd.G4_DECODE, FAKE,
+                                  ws_bytes, None)
+
+    assert stack(small) == bd.G4_EINVAL and b"workspace" in L.g4_last_error()
+    assert stack(big - 1) == bd.G4_EINVAL
+    assert L.g4_stack_forward(C.byref(m), descs, FAKE, FAKE, t, len(t), FAKE, B, 1, bd.G4_DECODE, FAKE + 16, big,
+                              None) == bd.G4_EINVAL
+    assert b"aligned" in L.g4_last_error()
+
+
+def test_stack_unsupported_decode_group_refused_before_launch():
+    """Decode attention groups at most 8 query heads per kv head: 16 query heads over one kv head is
+    refused by the layer checks (G4_EUNSUP), with nothing launched and the workspace never consulted."""
+    pattern = "SF"
+    m = _model(n_layers=2, n_heads=16, n_kv_heads=1)
+    descs, _ = _stack_descs(pattern, 0)
+    t = _table([(64, 256, 1), (64, 512, 0)])
+    L = bd.lib()
+    st = L.g4_stack_forward(C.byref(m), descs, FAKE, FAKE, t, 2, FAKE, 1, 1, bd.G4_DECODE, FAKE, 1 << 40, None)
+    assert st == bd.G4_EUNSUP and b"8 query heads" in L.g4_last_error()
+    # the same model prefills (the prefill kernels take any group size)
+    st = L.g4_stack_forward(C.byref(m), descs, FAKE, FAKE, t, 2, FAKE, 1, 8, bd.G4_PREFILL, FAKE, 1, None)
+    assert st == bd.G4_EINVAL and b"workspace" in L.g4_last_error()

@@ -28,7 +28,7 @@ def _encode(q, K, V, sliding, window, pos0, B, T, nh, nkv, hd, gdt):
     out = torch.empty((B * T, nh * hd), dtype=q.dtype, device="cuda")
     t = _kv_table([(K, V, sliding)])
     bd.g4_attn_encode(q.data_ptr(), nh * hd, t, 1, 0, 0, sliding, window, pos0.data_ptr(), B, T, nh, nkv, hd, 1.0,
-                      out.data_ptr(), nh * hd, gdt, stream())
+                      out.data_ptr(), nh * hd, None, 0, gdt, stream())
     torch.cuda.synchronize()
     return out
 

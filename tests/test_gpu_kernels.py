@@ -128,7 +128,7 @@ def test_attention_prefill_vs_oracle(dt, hd, sliding, window, nh, nkv):
     out = torch.empty((B * T, nh * hd), dtype=tdt, device="cuda")
     t = _kv_table([(K, V, sliding)])
     bd.g4_attn_prefill(q.data_ptr(), nh * hd, t, 1, 0, 0, sliding, window, pos0.data_ptr(), B, T, nh, nkv, hd, 1.0,
-                       out.data_ptr(), nh * hd, gdt, stream())
+                       out.data_ptr(), nh * hd, None, 0, gdt, stream())
     torch.cuda.synchronize()
     qv = O.f64(q).reshape(B, T, nh, hd)
     pos = O.prefill_positions(pos0_l, T)
@@ -151,7 +151,7 @@ def test_attention_mask_probe_bit_exact(hd, sliding, window):
     out = torch.empty_like(q)
     t = _kv_table([(K, V, sliding)])
     bd.g4_attn_prefill(q.data_ptr(), nh * hd, t, 1, 0, 0, sliding, window, pos0.data_ptr(), 1, T, nh, nkv, hd, 1.0,
-                       out.data_ptr(), nh * hd, bd.G4_BF16, stream())
+                       out.data_ptr(), nh * hd, None, 0, bd.G4_BF16, stream())
     torch.cuda.synchronize()
     o = O.f64(out).reshape(T, nh, hd)
     for i in range(T):
@@ -179,15 +179,18 @@ def test_attention_reads_kv_src_cache_without_copy():
     for src in (0, 1, 3):
         out = torch.empty_like(q)
         bd.g4_attn_prefill(q.data_ptr(), nh * hd, t, 4, 3, src, 0, 0, pos0.data_ptr(), 1, T, nh, nkv, hd, 1.0,
-                           out.data_ptr(), nh * hd, bd.G4_BF16, stream())
+                           out.data_ptr(), nh * hd, None, 0, bd.G4_BF16, stream())
         torch.cuda.synchronize()
         assert torch.all(out == float(src + 1))
 
 
+@pytest.mark.parametrize("with_ws", [False, True])
 @pytest.mark.parametrize("hd,sliding,W", [(256, 1, 512), (512, 0, 0)])
-def test_attention_prefill_long_e4b_shapes(hd, sliding, W):
-    """E4B heads (8 q / 2 kv) over T = 2048 from position 0, the layer pair's attention call."""
-    log(f"attn_prefill long hd={hd}")
+def test_attention_prefill_long_e4b_shapes(hd, sliding, W, with_ws):
+    """E4B heads (8 q / 2 kv) over T = 2048 from position 0, the layer pair's attention call. With a
+    workspace the export takes the key split (128 query blocks for 256 compute units), without one it
+    does not; both must match the oracle."""
+    log(f"attn_prefill long hd={hd} ws={with_ws}")
     B, T, nh, nkv = 1, 2048, 8, 2
     q = randn((T, nh * hd), 35 + hd, torch.bfloat16)
     K = randn((1, nkv, T, hd), 36, torch.bfloat16)
@@ -195,8 +198,12 @@ def test_attention_prefill_long_e4b_shapes(hd, sliding, W):
     out = torch.empty_like(q)
     pos0 = torch.zeros(1, dtype=torch.int32, device="cuda")
     t = _kv_table([(K, V, sliding)])
+    nws = bd.g4_attn_prefill_ws(B, T, nh, nkv, hd)
+    assert nws > 0  # this shape splits its keys when given scratch
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda") if with_ws else None
     bd.g4_attn_prefill(q.data_ptr(), nh * hd, t, 1, 0, 0, sliding, W, pos0.data_ptr(), B, T, nh, nkv, hd, 1.0,
-                       out.data_ptr(), nh * hd, bd.G4_BF16, stream())
+                       out.data_ptr(), nh * hd, None if ws is None else ws.data_ptr(), nws if with_ws else 0,
+                       bd.G4_BF16, stream())
     torch.cuda.synchronize()
     ref = O.attention(O.f64(q).reshape(T, nh, hd), O.f64(K[0]), O.f64(V[0]), np.arange(T), W if sliding else None)
     assert_close(out.reshape(T, nh, hd), ref, "bf16", "long")
