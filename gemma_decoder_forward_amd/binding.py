@@ -63,6 +63,8 @@ _SIGS = {
                                    vp, i64, i64, i32, vp, sz, vp]),
     "g4_stack_forward": (C.c_int, [C.POINTER(ModelDesc), C.POINTER(LayerDesc), vp, vp, C.POINTER(KvEntry), i32, vp,
                                    i64, i64, i32, vp, sz, vp]),
+    "g4_stack_forward_noalloc": (C.c_int, [C.POINTER(ModelDesc), C.POINTER(LayerDesc), vp, vp, C.POINTER(KvEntry),
+                                           i32, vp, i64, i64, i32, vp]),
     "g4_timer_enable": (C.c_int, [i32, i32]),
     "g4_timer_read": (C.c_int, [C.POINTER(C.c_double), C.POINTER(i32)]),
     "g4_workspace_size": (sz, [C.POINTER(ModelDesc), i64, i64, i64, i32]),
@@ -190,6 +192,13 @@ def g4_layer_forward(model, layer_desc, layer, h, ple_in, kv, n_kv, pos, B, T, m
 
 def g4_stack_forward(model, layers, h, ple_in, kv, n_kv, pos, B, T, mode, ws, ws_bytes, stream=None):
     return _call("g4_stack_forward", C.byref(model), layers, h, ple_in, kv, n_kv, pos, B, T, mode, ws, ws_bytes, stream)
+
+
+def g4_stack_forward_noalloc(model, layers, h, ple_in, kv, n_kv, pos, B, T, mode, stream=None):
+    return _call("g4_stack_forward_noalloc", C.byref(model), layers, h, ple_in, kv, n_kv, pos, B, T, mode, stream)
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 def g4_workspace_size(model, B, T, cap, mode):

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "g4_internal.h"
@@ -1056,6 +1057,47 @@ static g4_status check_stack(const g4_model_desc* model, const g4_layer_desc* la
   for (int32_t l = 0; l < model->n_layers; ++l)
     if ((st = check_layer(model, &layers[l], l, kv, n_kv, T, mode)) != G4_OK) return st;
   return G4_OK;
+}
+
+// ---- the stack forward without a caller workspace --------------------------------------------------
+// Scratch of g4_stack_forward_noalloc: one static array per GPU the library runs on, held until the
+// process ends. Host code never passes `scratch` itself to a kernel (on the host that name is only a
+// stand-in): its device address is resolved once per device with hipGetSymbolAddress, with that device
+// current, and kept in g_scratch_dev.
+static __device__ __align__(256) unsigned char scratch[G4_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_dev[kMaxDevices];
+
+static g4_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(G4_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  G4_REQ(dev >= 0 && dev < kMaxDevices, G4_EUNSUP, "device ordinal %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(G4_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return G4_OK;
+}
+
+g4_status g4_stack_forward_noalloc(const g4_model_desc* model, const g4_layer_desc* layers, float* h,
+                                   const float* ple_in, const g4_kv_entry* kv, int32_t n_kv, const int32_t* pos,
+                                   int64_t B, int64_t T, int32_t mode, void* stream) {
+  g4_status st = check_stack(model, layers, h, ple_in, kv, n_kv, pos, B, T, mode);
+  if (st != G4_OK) return st;
+  const Plan p = call_plan(model, layers, (int32_t)model->n_layers, kv, B, T, mode);
+  G4_REQ(p.total <= G4_NOALLOC_SCRATCH_BYTES, G4_ERANGE,
+         "this call needs %zu bytes of scratch; the static buffer holds %zu (use g4_stack_forward with a workspace)",
+         p.total, (size_t)G4_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != G4_OK) return st;
+  return stack_run(model, layers, h, ple_in, kv, n_kv, pos, B, T, mode, ws, p, stream);
 }
 
 g4_status g4_stack_forward(const g4_model_desc* model, const g4_layer_desc* layers, float* h, const float* ple_in,

@@ -275,6 +275,21 @@ g4_status g4_stack_forward(const g4_model_desc* model, const g4_layer_desc* laye
                            const int32_t* pos, int64_t B, int64_t T, int32_t mode, void* ws,
                            size_t ws_bytes, void* stream);
 
+/* g4_stack_forward for callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. Same arguments and results as g4_stack_forward, without
+ * the workspace: scratch is a static device array of G4_NOALLOC_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on until the process ends. No call allocates or frees device memory; the first call
+ * on a device resolves the array's address there (hipGetSymbolAddress, with the stream's device current).
+ * A call needing more scratch than that (g4_workspace_size with cap the largest cache capacity the layers
+ * read: e.g. decode of up to 64 sequences over caches of 8192 rows fits, a prefill of 2048 tokens does
+ * not) returns G4_ERANGE with nothing launched. Every call on one GPU shares that GPU's array, which keeps
+ * the last call's contents (no kernel reads scratch it has not written in the same call); calls that
+ * overlap on one GPU, on different streams or threads, race on it and must be serialized by the caller. */
+#define G4_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+g4_status g4_stack_forward_noalloc(const g4_model_desc* model, const g4_layer_desc* layers, float* h,
+                                   const float* ple_in, const g4_kv_entry* kv, int32_t n_kv,
+                                   const int32_t* pos, int64_t B, int64_t T, int32_t mode, void* stream);
+
 /* ---- timing instrumentation ------------------------------------------------------------------ */
 
 /* Kernel classes of the layer forward, for g4_timer_enable. */

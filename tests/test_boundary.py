@@ -307,3 +307,29 @@ def test_stack_unsupported_decode_group_refused_before_launch():
     # the same model prefills (the prefill kernels take any group size)
     st = L.g4_stack_forward(C.byref(m), descs, FAKE, FAKE, t, 2, FAKE, 1, 8, bd.G4_PREFILL, FAKE, 1, None)
     assert st == bd.G4_EINVAL and b"workspace" in L.g4_last_error()
+
+
+def test_noalloc_stack_validation_on_the_host():
+    """g4_stack_forward_noalloc takes g4_stack_forward's checks, and refuses a call whose workspace plan
+    exceeds its static buffer (G4_ERANGE) before resolving the buffer or launching anything."""
+    pattern = "SF"
+    m = _model(n_layers=2)
+    descs, _ = _stack_descs(pattern, 0)
+    L = bd.lib()
+    t = _table([(8192, 256, 1), (8192, 512, 0)])
+    assert bd.g4_workspace_size(m, 1, 4096, 8192, bd.G4_PREFILL) > bd.NOALLOC_SCRATCH_BYTES
+    assert L.g4_stack_forward_noalloc(C.byref(m), descs, FAKE, FAKE, t, 2, FAKE, 1, 4096, bd.G4_PREFILL,
+                                      None) == bd.G4_ERANGE
+    assert b"static buffer" in L.g4_last_error()
+    assert bd.g4_workspace_size(m, 64, 1, 8192, bd.G4_DECODE) <= bd.NOALLOC_SCRATCH_BYTES
+    assert L.g4_stack_forward_noalloc(C.byref(m), descs, FAKE, FAKE, t, 2, FAKE, 1, 9000, bd.G4_PREFILL,
+                                      None) == bd.G4_ERANGE  # T beyond the caches
+    assert L.g4_stack_forward_noalloc(C.byref(m), descs, None, FAKE, t, 2, FAKE, 1, 8, bd.G4_PREFILL,
+                                      None) == bd.G4_EINVAL
+    assert L.g4_stack_forward_noalloc(C.byref(m), descs, FAKE, FAKE, t, 2, FAKE, 1, 8, 5, None) == bd.G4_EINVAL
+
+
+def test_noalloc_limit_matches_the_header():
+    src = open(os.path.join(ROOT, "include", "g4.h")).read()
+    m = re.search(r"#define G4_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == bd.NOALLOC_SCRATCH_BYTES
