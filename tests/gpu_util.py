@@ -64,3 +64,14 @@ def host_layer(layers):
 
 def log(msg):
     print(msg, flush=True)
+
+
+def assert_layers_within_floor(errs, floors, what=""):
+    """Each layer's relative L2 from the oracle within max(1.5 x its bf16 floor, 5e-3), and within the
+    2e-2 outer bar. The floor (tests/bf16_floor.py) is what storing the bf16 path's intermediates in bf16
+    costs by itself on the same inputs; a kernel adding error of its own would exceed it."""
+    assert len(errs) == len(floors)
+    log(f"{what} per-layer rel L2 / floor: " + " ".join(f"{e:.1e}/{f:.1e}" for e, f in zip(errs, floors)))
+    for l, (e, f) in enumerate(zip(errs, floors)):
+        bound = min(TOL_BF16_RELL2, max(1.5 * f, 5e-3))
+        assert e <= bound, f"{what} layer {l}: rel L2 {e:.3e} > {bound:.3e} (floor {f:.3e})"

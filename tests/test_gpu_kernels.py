@@ -414,6 +414,37 @@ def test_embed_ple_vs_oracle(dt):
     assert torch.all(h[0, 4:7] == 0)
 
 
+def test_embed_ple_e4b_widths_vs_oracle():
+    """The entry at the 42-layer model's widths: H = 2560, 42 layers of 256 per-layer inputs, vocabulary
+    262144 (5.6 GB PLE table), 300 token ids including out-of-range ones, bf16."""
+    from gemma_decoder_forward_amd.model import G4Model
+    from synth import configs, gen
+    cfg = configs.get(3)
+    glob = gen.model_globals(cfg, "cuda")
+    g = torch.Generator(device="cuda").manual_seed(77)
+    ids = torch.randint(0, cfg["vocab"], (300,), generator=g, device="cuda", dtype=torch.int64).to(torch.int32)
+    ids[[3, 100, 299]] = torch.tensor([cfg["vocab"], -1, 2 ** 30], dtype=torch.int32, device="cuda")
+    ids[7] = cfg["vocab"] - 1
+    lw = gen.layer_weights(cfg, 0, "cuda")
+    model = G4Model(cfg, [lw] * cfg["n_layers"], glob)  # the entry reads only the tables
+    h, ple = model.embed(ids.view(1, -1))
+    torch.cuda.synchronize()
+    m_ids = ids.cpu().numpy()
+    valid = (m_ids >= 0) & (m_ids < cfg["vocab"])
+    uniq, inv = np.unique(np.where(valid, m_ids, 0), return_inverse=True)
+    idx = torch.from_numpy(uniq).cuda()
+    sub = dict(cfg, vocab=len(uniq), ple_vocab=len(uniq))
+    gh = dict(embed=glob["embed"][idx].cpu(), ple_embed=glob["ple_embed"][idx].cpu(),
+              ple_model_proj=glob["ple_model_proj"].cpu(), ple_norm=glob["ple_norm"].cpu())
+    local = np.where(valid, inv, len(uniq)).reshape(1, -1)  # out-of-range ids stay out of range
+    e_ref, p_ref = O.entry(sub, gh, local)
+    assert_close(h, e_ref, "f32", "h0")
+    e = assert_close(ple, p_ref, "bf16", "ple_in")
+    log(f"entry at E4B widths: ple_in rel L2 {e:.2e}")
+    # an out-of-range id: zero embedding row, so a zero projection, and no table term
+    assert torch.all(h[0, [3, 100, 299]] == 0) and torch.all(ple[0, [3, 100, 299]] == 0)
+
+
 # ------------------------------------------------------------------------------- output head
 @pytest.mark.parametrize("dt,M,H,V,cap", [("f32", 5, 256, 512, 30.0), ("f32", 70, 64, 200, 0.0),
                                           ("bf16", 1, 2560, 262144, 30.0), ("bf16", 7, 2560, 262144, 30.0),

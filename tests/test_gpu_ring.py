@@ -131,3 +131,87 @@ def test_ring_bf16_e4b_layer_pair_chunked_per_layer():
         dec = rel_l2(torch.cat(outs[l][-nd:], 1), ref[:, T - nd:])
         log(f"layer {l}: prefill chunks rel L2 " + " ".join(f"{e:.1e}" for e in errs) + f"; decode rows {dec:.1e}")
         assert max(errs) <= TOL_BF16_RELL2 and dec <= TOL_BF16_RELL2, f"layer {l}"
+
+
+def _seq_view(table, b, caches, L):
+    """A kv table over sequence b's slabs only (its [nkv, rows, hd] block of every cache), for B = 1 calls."""
+    t = (bd.KvEntry * L)()
+    for l, (k, v) in caches.items():
+        e = table[l]
+        off = b * k.shape[1] * k.shape[2] * k.shape[3] * k.element_size()
+        t[l] = bd.KvEntry(k=e.k + off, v=e.v + off, cap=e.cap, hd=e.hd, sliding=e.sliding, ring=e.ring)
+    return t
+
+
+def _per_sequence_schedule(model, h0, ple, prompts, n_decode, caches, table, cap, chunk):
+    """Each sequence's prompt prefilled alone (B = 1 over its own cache slabs, chunks of at most `chunk`),
+    then n_decode joint steps in which sequence b sits at position prompts[b] + i. Returns each sequence's
+    hidden states of the decode steps [B, n_decode, H]."""
+    B = len(prompts)
+    for b, P in enumerate(prompts):
+        view = _seq_view(table, b, caches, model.L)
+        for s in range(0, P, chunk):
+            n = min(chunk, P - s)
+            h = h0[b:b + 1, s:s + n].clone()
+            model.forward(h, ple[b:b + 1, s:s + n].contiguous(), _pos(1, s), view, cap, bd.G4_PREFILL)
+    outs = []
+    for i in range(n_decode):
+        pos = torch.tensor([P + i for P in prompts], dtype=torch.int32, device="cuda")
+        h = torch.stack([h0[b, P + i] for b, P in enumerate(prompts)])[:, None].contiguous()
+        p = torch.stack([ple[b, P + i] for b, P in enumerate(prompts)])[:, None].contiguous()
+        model.forward(h, p, pos, table, cap, bd.G4_DECODE)
+        outs.append(h)
+    torch.cuda.synchronize()
+    return torch.cat(outs, 1)
+
+
+def test_ring_fp32_per_sequence_positions():
+    """Three sequences with prompts of 20, 50 and 33 tokens over 45-row sliding rings (window 32), then 25
+    joint decode steps: every step's batch holds three different positions, and the sequences wrap their
+    rings at different steps. The result equals the same schedule over linear caches bit for bit, and
+    each sequence's decode rows match the oracle's one-shot prefill of that sequence within 1e-3."""
+    prompts, n_dec, R = [20, 50, 33], 25, 45
+    Tmax = max(prompts) + n_dec
+    cfg = configs.get(1, T=Tmax, B=3)
+    model, layers, glob = build_model(cfg)
+    acts = gen.activations(cfg, "cuda")
+    h0, ple = model.embed(acts["ids"])
+    ring_caches, ring_table = model.new_caches(3, Tmax, ring=R)
+    lin_caches, lin_table = model.new_caches(3, Tmax)
+    hr = _per_sequence_schedule(model, h0, ple, prompts, n_dec, ring_caches, ring_table, Tmax, R - 32 + 1)
+    hl = _per_sequence_schedule(model, h0, ple, prompts, n_dec, lin_caches, lin_table, Tmax, R - 32 + 1)
+    assert torch.equal(hr, hl), "ring and linear caches give different results"
+    worst = 0.0
+    for b, P in enumerate(prompts):
+        n = P + n_dec
+        ids = acts["ids"][b:b + 1, :n].cpu().numpy()
+        uniq, inv = np.unique(ids, return_inverse=True)
+        idx = torch.from_numpy(uniq).cuda()
+        sub = dict(cfg, B=1, T=n, vocab=len(uniq), ple_vocab=len(uniq))
+        g_host = dict(embed=glob["embed"][idx].cpu(), ple_embed=glob["ple_embed"][idx].cpu(),
+                      ple_model_proj=glob["ple_model_proj"].cpu(), ple_norm=glob["ple_norm"].cpu())
+        oh0, ople = O.entry(sub, g_host, inv.reshape(ids.shape))
+        ref = O.forward(sub, host_layer(layers), oh0, ople, O.prefill_positions([0], n), O.new_caches(sub, 1, n))
+        e = max_rel(hr[b], ref[0, P:])
+        worst = max(worst, e)
+        assert e <= 1e-3, f"sequence {b}: max rel {e:.2e}"
+    log(f"ring fp32, per-sequence positions {prompts} + {n_dec} decode steps: max rel {worst:.2e}")
+
+
+def test_ring_bf16_e4b_per_sequence_positions_bit_equal_to_linear():
+    """The E4B layer pair (window 512) over 700-row sliding rings: prompts of 100, 530 and 777 tokens
+    (chunks of at most 189), then 6 joint decode steps at three different positions, bit-identical to the
+    same schedule over linear caches (the ring changes only where rows live)."""
+    prompts, n_dec, R = [100, 530, 777], 6, 700
+    Tmax = max(prompts) + n_dec
+    cfg = configs.get(2, T=Tmax, B=3)
+    model, layers, glob = build_model(cfg)
+    acts = gen.activations(cfg, "cuda")
+    ring_caches, ring_table = model.new_caches(3, Tmax, ring=R)
+    lin_caches, lin_table = model.new_caches(3, Tmax)
+    args = (acts["h0"], acts["ple_in"], prompts, n_dec)
+    hr = _per_sequence_schedule(model, *args, ring_caches, ring_table, Tmax, R - 512 + 1)
+    hl = _per_sequence_schedule(model, *args, lin_caches, lin_table, Tmax, R - 512 + 1)
+    assert torch.isfinite(hr).all()
+    assert torch.equal(hr, hl), "ring and linear caches give different results"
+    log(f"ring bf16 E4B pair, per-sequence positions {prompts} + {n_dec} decode steps: bit-equal to linear")

@@ -4,9 +4,11 @@ How the stacks are checked (the reasoning and measurements are in the design not
   * float32 stacks end to end: the final hidden state within max relative error 1e-3.
   * bf16 stacks layer by layer: every layer runs on the GPU from the oracle's input for that layer (and
     from caches written by the GPU in that same layer-by-layer pass), and its output must be within
-    relative L2 2e-2 of the oracle's. End to end, a random-weight stack with score scale 1.0 is chaotic:
-    any bf16-sized perturbation grows 2-3x per layer, so the end-to-end bf16 deviation is logged, not
-    asserted.
+    max(1.5 x the layer's bf16 floor, 5e-3) of the oracle's, and within relative L2 2e-2. The floor is the
+    oracle's layer replayed with the bf16 path's stored intermediates rounded to bf16 (tests/bf16_floor.py)
+    on the same inputs. End to end, a random-weight stack with score scale 1.0 is chaotic: any
+    bf16-sized perturbation grows 2-3x per layer (tests/test_bf16_sensitivity.py), so the end-to-end bf16
+    deviation is logged, not asserted.
   * full lengths the oracle cannot run whole: single layers at full size on sampled rows
     (`layer_forward_rows`), decode batches on sampled sequences.
 """
@@ -17,7 +19,9 @@ import torch
 import oracle as O
 from gemma_decoder_forward_amd import binding as bd
 from synth import configs, gen
-from tests.gpu_util import TOL_BF16_RELL2, assert_close, build_model, host_layer, log, max_rel, rel_l2
+from tests import bf16_floor as F
+from tests.gpu_util import (TOL_BF16_RELL2, assert_close, assert_layers_within_floor, build_model, host_layer, log,
+                            max_rel, rel_l2)
 
 pytestmark = pytest.mark.gpu
 
@@ -176,8 +180,9 @@ def test_bf16_stack_per_layer_parity(cid, T):
     log(f"end-to-end bf16 deviation after {cfg['n_layers']} layers: rel L2 {rel_l2(h_gpu, hs[-1]):.3e}")
     caches, table = model.new_caches(1, T)
     errs = _per_layer(model, hs, ple, acts["pos"], table, T, bd.G4_PREFILL)
-    log("per-layer rel L2: " + " ".join(f"{e:.1e}" for e in errs))
-    assert max(errs) <= TOL_BF16_RELL2, f"layer {int(np.argmax(errs))}: {max(errs):.3e}"
+    floors = F.layer_floors(cfg, host_layer(layers), hs, ple, O.prefill_positions([0], T), O.new_caches(cfg, 1, T),
+                            "bf16_prefill")
+    assert_layers_within_floor(errs, floors, f"{cfg['name']} T={T}")
 
 
 @pytest.mark.parametrize("T", [1, 24, 48])
@@ -191,8 +196,9 @@ def test_bf16_few_row_prefill_per_layer(T):
     O.forward(cfg, host_layer(layers), h0, ple, O.prefill_positions([0], T), O.new_caches(cfg, 1, T), per_layer=hs)
     caches, table = model.new_caches(1, T)
     errs = _per_layer(model, hs, ple, acts["pos"], table, T, bd.G4_PREFILL)
-    log(f"T={T} per-layer rel L2: " + " ".join(f"{e:.1e}" for e in errs))
-    assert max(errs) <= TOL_BF16_RELL2
+    floors = F.layer_floors(cfg, host_layer(layers), hs, ple, O.prefill_positions([0], T), O.new_caches(cfg, 1, T),
+                            "bf16_few_rows")
+    assert_layers_within_floor(errs, floors, f"few-row T={T}")
 
 
 # ------------------------------------------------------------------------------- full sizes, sampled rows
@@ -229,8 +235,43 @@ def test_config3_full_length_first_layer_sampled_rows():
     _rows_case(cfg, 0, h0, ple, model, cfg["T"], [700, 2047])
 
 
+def test_config3_full_length_shared_full_layer():
+    """The last layer of the 42-layer stack (41: full, shared) at T = 4096 reads layer 23's cache in place.
+    The GPU runs layer 23 (which writes that cache) and then layer 41, each from its own input, in the
+    stack's launch configuration; the oracle does the same in float64, and all 4096 rows of layer 41's
+    output are compared (bf16 bound: layer 41's error includes that of the bf16 cache layer 23 wrote)."""
+    cfg = configs.get(3)
+    T = cfg["T"]
+    from gemma_decoder_forward_amd.model import G4Model
+    lw23, lw41 = gen.layer_weights(cfg, 23, "cuda"), gen.layer_weights(cfg, 41, "cuda")
+    slots = [lw23] * cfg["n_layers"]
+    slots[41] = lw41  # only layers 23 and 41 run; the other slots are never used
+    model = G4Model(cfg, slots)
+    assert model.kv_src[41] == 23 and model.kv_src[23] == 23 and not model.sliding[41]
+    L, H, d = cfg["n_layers"], cfg["hidden"], cfg["ple_dim"]
+    gin = torch.Generator(device="cuda").manual_seed(4141)
+    h23 = torch.randn((1, T, H), generator=gin, device="cuda")
+    h41 = torch.randn((1, T, H), generator=gin, device="cuda")
+    ple = torch.randn((1, T, L, d), generator=gin, device="cuda")
+    pos = torch.zeros(1, dtype=torch.int32, device="cuda")
+    caches, table = model.new_caches(1, T)
+    x23, x41 = h23.clone(), h41.clone()
+    model.forward(x23, ple, pos, table, T, bd.G4_PREFILL, layer=23)
+    model.forward(x41, ple, pos, table, T, bd.G4_PREFILL, layer=41)
+    torch.cuda.synchronize()
+    log("oracle: layers 23 and 41 at T=4096")
+    oc = O.new_caches(cfg, 1, T)
+    opos = O.prefill_positions([0], T)
+    get = host_layer(model.layers)
+    r23 = O.layer_forward(cfg, get(23), 23, 23, O.f64(h23), O.f64(ple)[:, :, 23], opos, oc)
+    r41 = O.layer_forward(cfg, get(41), 41, 23, O.f64(h41), O.f64(ple)[:, :, 41], opos, oc)
+    e23, e41 = rel_l2(x23, r23), rel_l2(x41, r41)
+    log(f"layer 23 (full, owns its cache) rel L2 {e23:.3e}; layer 41 (full, reads 23) rel L2 {e41:.3e}")
+    assert e23 <= TOL_BF16_RELL2 and e41 <= TOL_BF16_RELL2
+
+
 # ------------------------------------------------------------------------------- decode
-@pytest.mark.parametrize("B", [1, 8, 64])
+@pytest.mark.parametrize("B", [1, 8, 32, 64])
 def test_config4_decode_per_layer_sampled_sequences(B):
     cfg = configs.get(4, B=B)
     model, layers, glob = build_model(cfg)
@@ -249,15 +290,17 @@ def test_config4_decode_per_layer_sampled_sequences(B):
     log(f"42-layer decode B={B}: oracle on sequences {sample}")
     sub = dict(cfg, B=len(sample))
     e0, p0 = _oracle_entry(sub, glob, acts["ids"][sample])
+    c0 = {l: (k.copy(), v.copy()) for l, (k, v) in ocache.items()}
     hs = [e0]
-    O.forward(sub, host_layer(layers), e0, p0, np.full((len(sample), 1), ctx - 1), ocache, per_layer=hs)
+    opos = np.full((len(sample), 1), ctx - 1)
+    O.forward(sub, host_layer(layers), e0, p0, opos, ocache, per_layer=hs)
     log(f"end-to-end bf16 deviation: rel L2 {rel_l2(h[sample], hs[-1]):.3e}")
     # layer by layer: sampled sequences get the oracle's inputs, the others a copy of sequence 0's
     owner = [sample.index(b) if b in sample else 0 for b in range(B)]
     hs_b = [x[owner] for x in hs]
     errs = _per_layer(model, hs_b, p0[owner], acts["pos"], table, ctx, bd.G4_DECODE, rows=sample)
-    log("per-layer rel L2: " + " ".join(f"{e:.1e}" for e in errs))
-    assert max(errs) <= TOL_BF16_RELL2, f"layer {int(np.argmax(errs))}: {max(errs):.3e}"
+    floors = F.layer_floors(sub, host_layer(layers), hs, p0, opos, c0, "bf16_decode")
+    assert_layers_within_floor(errs, floors, f"decode B={B}")
 
 
 # ------------------------------------------------------------------------------- HIP graph replay
