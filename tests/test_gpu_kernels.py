@@ -396,6 +396,30 @@ def test_ple_inject_vs_oracle(dt, scalar):
     assert_close(h, ref, "f32" if dt == "f32" else "bf16", "h")
 
 
+@pytest.mark.parametrize("M,scalar", [(1000, 1.0), (70, 0.5), (4096, 1.0)])
+def test_ple_inject_e4b_widths_vs_oracle(M, scalar):
+    """The PLE block at E4B widths (H 2560, d 256), bf16, at prefill row counts (the fused one-launch
+    kernel: 16-row blocks, the last one ragged for M = 1000 and 70). The branch itself, h_out / scalar - h,
+    is compared at the bf16 bound, and h within it."""
+    H, d, L = 2560, 256, 4
+    h = randn((M, H), 95)
+    h0 = h.clone()
+    ple = randn((M, L * d), 96)
+    wg, wp = randn((d, H), 97, torch.bfloat16, 0.02), randn((H, d), 98, torch.bfloat16, 0.02)
+    wpost = randn((H,), 99, torch.bfloat16, 0.1, 1.0)
+    wsb = bd.g4_ple_inject_ws(M, H, d, bd.G4_BF16)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    bd.g4_ple_inject(h.data_ptr(), wg.data_ptr(), ple[:, 2 * d:].data_ptr(), L * d, wp.data_ptr(), wpost.data_ptr(),
+                     scalar, M, H, d, 1e-6, ws.data_ptr(), wsb, bd.G4_BF16, stream())
+    torch.cuda.synchronize()
+    hv = O.f64(h0)
+    gmix = O.gelu_tanh(hv @ O.f64(wg).T) * O.f64(ple)[:, 2 * d:3 * d]
+    branch = O.rms_norm(gmix @ O.f64(wp).T, wpost, 1e-6)
+    e = assert_close(O.f64(h) / scalar - hv, branch, "bf16", "PLE branch")
+    assert_close(h, (hv + branch) * scalar, "bf16", "h")
+    log(f"PLE block M={M}: branch rel L2 {e:.2e}")
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_embed_ple_vs_oracle(dt):
     from synth import configs, gen
