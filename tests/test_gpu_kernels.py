@@ -398,9 +398,9 @@ def test_ple_inject_vs_oracle(dt, scalar):
 
 @pytest.mark.parametrize("M,scalar", [(1000, 1.0), (70, 0.5), (4096, 1.0)])
 def test_ple_inject_e4b_widths_vs_oracle(M, scalar):
-    """The PLE block at E4B widths (H 2560, d 256), bf16, at prefill row counts (the fused one-launch
-    kernel: 16-row blocks, the last one ragged for M = 1000 and 70). The branch itself, h_out / scalar - h,
-    is compared at the bf16 bound, and h within it."""
+    """The PLE block at E4B widths (H 2560, d 256), bf16, at prefill row counts (the split-K gate GEMM and
+    its finishing pass, the projection GEMM and the row tail; M = 1000 and 70 leave ragged tiles). The
+    branch itself, h_out / scalar - h, is compared at the bf16 bound, and h within it."""
     H, d, L = 2560, 256, 4
     h = randn((M, H), 95)
     h0 = h.clone()
