@@ -223,22 +223,6 @@ static g4_status run_gemm(const void* A, int64_t lda, const void* B, const void*
   return gemm(a, dt, s);
 }
 
-// Split-K slices for a float32-output projection whose consumer (the row tail) sums the slices:
-// minimise rounds-of-256x256-tiles / splits over 1..4.
-static int32_t pick_splits(int64_t M, int64_t N, int64_t K) {
-  if (M < 128 || N % 256 || K % 256) return 1;
-  const int64_t tiles = ((M + 255) / 256) * (N / 256);
-  int32_t best = 1;
-  double best_cost = 1e30;
-  for (int32_t s = 1; s <= 4; ++s) {
-    if (K / s < 512) break;
-    const double rounds = (double)((tiles * s + 255) / 256);
-    const double cost = rounds / s * (1.0 + 0.03 * (s - 1));  // extra slices cost a little traffic
-    if (cost < best_cost - 1e-9) { best_cost = cost; best = s; }
-  }
-  return best;
-}
-
 // gelu_tanh(A W^T) * aux into C (dtype). The PLE gate has few output columns (the PLE width), so at
 // prefill sizes it has too few output tiles to fill the device: K is then split over float32 slices in
 // `part` ([splits][M][N]) and a finisher sums them in a fixed order and applies the epilogue.
@@ -623,7 +607,7 @@ static g4_status layer_impl(const LayerCtx& c) {
     else G4_TRY(attn_prefill(aa, dt, c.s));
   }
   // 5-6. o projection, then h += rms(a) * w_pa and xn2 = rms(h) * w_pf
-  const int32_t so = pick_splits(M, H, nh * hd);
+  const int32_t so = gemm_pick_splits(M, H, nh * hd, (int32_t)c.p->splits);
   {
   TimedScope ts(G4_KC_O_GEMM, c.s);
   G4_TRY(run_gemm(ao, nh * hd, l->wo, nullptr, nh * hd, fb, H, G4_F32, M, H, nh * hd, EPI_STORE, nullptr, 0, so,
@@ -640,7 +624,7 @@ static g4_status layer_impl(const LayerCtx& c) {
     G4_TRY(run_gemm(xn, H, l->w_gate, l->w_up, H, act, F, dt, M, F, H, EPI_GEGLU, nullptr, 0, 1, 0, dt, c.s));
   }
   // 8-9. down projection, then h += rms(ffn) * w_pff; hb = h in dtype for the PLE gate
-  const int32_t sd = pick_splits(M, H, F);
+  const int32_t sd = gemm_pick_splits(M, H, F, (int32_t)c.p->splits);
   {
   TimedScope ts(G4_KC_DOWN_GEMM, c.s);
   G4_TRY(run_gemm(act, F, l->w_down, nullptr, F, fb, H, G4_F32, M, H, F, EPI_STORE, nullptr, 0, sd, M * H, dt, c.s));

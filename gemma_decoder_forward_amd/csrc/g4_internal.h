@@ -212,6 +212,9 @@ g4_status cast_rows(const float* x, void* y, int64_t n, int32_t dtype, hipStream
 g4_status softcap_inplace(float* x, int64_t n, float cap, hipStream_t s);
 g4_status gemm_simt(const GemmArgs& a, int32_t dtype, hipStream_t s);
 bool gemm_mfma(const GemmArgs& a, hipStream_t s, g4_status* st);
+// Split-K slices (1..max_splits) for a float32-output product whose consumer sums the slices: the
+// count whose MFMA tiling (tile width and slices together) takes the fewest tile-passes.
+int32_t gemm_pick_splits(int64_t M, int64_t N, int64_t K, int32_t max_splits);
 bool gemm_skinny(const GemmArgs& a, const void* const* segs, const int64_t* seg_rows, int nseg, void* ws,
                  size_t ws_bytes, hipStream_t s, g4_status* st);
 size_t gemm_skinny_ws(int64_t M, int64_t Nt, int64_t K);

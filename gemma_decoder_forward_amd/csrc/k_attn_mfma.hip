@@ -89,13 +89,21 @@ __device__ __forceinline__ void at_dma16(const at_rsrc& r, uint32_t voff, uint32
 // K/V stages in the LDS ring: the loads of a tile are issued NS - 1 tiles ahead of its use. A tile of
 // 32 keys at head dim 256 or less is a short stretch of matrix work, shorter than a trip to memory, so
 // those dims keep four stages in flight (137 KB of LDS at 256); head dim 512 fits two (134 KB).
-// The 16-query kernel's staging: K rows padded by 32 bytes (see k_attn_w16), V rows as above.
+// The 16-query kernel's staging: K rows padded by 32 bytes (see k_attn_w16), V rows as above; tiles
+// of KB keys. Head dim 256 takes 64-key tiles, so the per-tile costs that do not scale with the
+// tile's matrix work (block barrier, stage wait, load addressing, softmax bookkeeping) are paid once
+// per 64 keys; a 64-key stage is 70 KB, two fit. Head dim 512 keeps 32-key tiles (two 68 KB stages).
+template <int HD> struct AttnTileW {
+  static constexpr int KB = HD == 256 ? 64 : 32;
+  static constexpr int NS = 2;
+};
 template <int HD>
 struct AttnLdsW {
+  static constexpr int KB = AttnTileW<HD>::KB;
   static constexpr int KLD = HD + 16;
   static constexpr int VROW = HD + 16;
-  static constexpr int KSZ = AT_KB * KLD;
-  static constexpr int VSZ = AT_KB * VROW;
+  static constexpr int KSZ = KB * KLD;
+  static constexpr int VSZ = KB * VROW;
   static constexpr int STAGE = KSZ + VSZ;
 };
 
@@ -395,15 +403,18 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
 //   * A query's 32 scores of a tile sit in the four lanes l % 16 + 16j: its maximum takes two
 //     cross-lane steps; the normaliser is summed per lane and across the four lanes at the end.
 // --------------------------------------------------------------------------------------------
-template <int HD>
+template <int HD, bool RING>
 __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl2, AtSplit sp) {
   using L = AttnLdsW<HD>;
   typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+  constexpr int KB = L::KB;        // keys per tile
+  constexpr int NKB = KB / 16;     // 16-key blocks of S per tile
+  constexpr int NPV = KB / 32;     // 32-key steps of P V per tile
   constexpr int NO = HD / 16;      // O blocks (16 head elements each) per wave
   constexpr int KS = HD / 32;      // k-steps of S (32 head elements each)
   constexpr int QG = 4;            // query groups per block, two waves each
-  constexpr int NS = AttnStages<HD>::NS;
-  constexpr int RPW = AT_KB / 8;   // tile rows staged by each wave
+  constexpr int NS = AttnTileW<HD>::NS;
+  constexpr int RPW = KB / 8;      // tile rows staged by each wave
   constexpr int LPT = 2 * RPW;     // direct-to-LDS load instructions per wave per tile (K and V rows)
   static_assert((NS - 2) * LPT <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(16))) bf16 lds[NS * L::STAGE];
@@ -430,12 +441,12 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl
   int64_t tlast = (int64_t)(g_last / G) * 32 + 31;
   if (tlast > a.T - 1) tlast = a.T - 1;
   const int64_t imin = p0 + (int64_t)(g_first / G) * 32, imax = p0 + tlast;
-  const KeySpan ksp = key_span(a.bidir, a.sliding, a.window, a.cap, a.ring, p0, a.T);
+  const KeySpan ksp = key_span(a.bidir, a.sliding, a.window, a.cap, RING ? 1 : 0, p0, a.T);
   int64_t lob = imin - ksp.back;
   if (lob < ksp.kmin) lob = ksp.kmin;
   const int64_t hib = imax + ksp.fwd < ksp.kmax ? imax + ksp.fwd : ksp.kmax;
-  const int64_t kstart = lob & ~(int64_t)(AT_KB - 1);
-  const int ntiles = hib >= lob ? (int)((hib - kstart) / AT_KB + 1) : 0;
+  const int64_t kstart = lob & ~(int64_t)(KB - 1);
+  const int ntiles = hib >= lob ? (int)((hib - kstart) / KB + 1) : 0;
   const int it0 = part * ntiles / nparts, it1 = (part + 1) * ntiles / nparts;
   int64_t qlo = qi - ksp.back;
   if (qlo < ksp.kmin) qlo = ksp.kmin;
@@ -483,8 +494,8 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl
   auto dma = [&](int it) {
     const bool live = it < it1;
     const uint32_t so = (uint32_t)(it % NS) * L::STAGE * 2;
-    const int64_t kb = kstart + (int64_t)it * AT_KB + RPW * wv;  // the wave's first key of the tile
-    const int rb = a.ring ? (int)kv_row(kb, a.cap, a.ring) : (int)(kb < a.cap ? kb : a.cap - 1);
+    const int64_t kb = kstart + (int64_t)it * KB + RPW * wv;  // the wave's first key of the tile
+    const int rb = RING ? (int)kv_row(kb, a.cap, 1) : (int)(kb < a.cap ? kb : a.cap - 1);
     // The row's byte offset rides in the per-lane offset, so no scalar register written by a vector
     // instruction feeds the load (the compiler's hazard checks do not see into the assembly); the
     // scalar offset only marks a tile past the range.
@@ -492,9 +503,9 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       int cr;
-      if (!a.ring) cr = rb + r < cap32 - 1 ? rb + r : cap32 - 1;  // keys past the cache clamp to its last row
+      if (!RING) cr = rb + r < cap32 - 1 ? rb + r : cap32 - 1;  // keys past the cache clamp to its last row
       else if (cap32 >= RPW) cr = rb + r >= cap32 ? rb + r - cap32 : rb + r;
-      else cr = (int)kv_row(kb + r, a.cap, a.ring);
+      else cr = (int)kv_row(kb + r, a.cap, 1);
       const uint32_t voff = (uint32_t)cr * (HD * 2) + (uint32_t)lane * 16;
       if (lane < HD / 8) {
         at_dma16(rks, voff, oob, lds_k + so + (uint32_t)(r * L::KLD * 2));
@@ -503,13 +514,13 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl
     }
   };
   auto edge_tile = [&](int it) {
-    const int kt = it * AT_KB;
-    return !(kt >= lob_r && kt + AT_KB - 1 <= hib_r);
+    const int kt = it * KB;
+    return !(kt >= lob_r && kt + KB - 1 <= hib_r);
   };
   auto vclean = [&](int it, int buf) {
-    const int kt = it * AT_KB;
+    const int kt = it * KB;
     bf16* vs = lds + buf * L::STAGE + L::KSZ;
-    for (int u = tid; u < AT_KB * (HD / 8); u += 512) {
+    for (int u = tid; u < KB * (HD / 8); u += 512) {
       const int row = u / (HD / 8);
       const int key = kt + row;
       if (key < lob_r || key > hib_r) *(uint4*)(vs + row * L::VROW + 8 * (u % (HD / 8))) = make_uint4(0, 0, 0, 0);
@@ -539,42 +550,45 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl
     dma(it + NS - 1);
     const bf16* ks = lds + cur * L::STAGE;
     const bf16* vs = ks + L::KSZ;
-    const int kt = it * AT_KB;  // the tile's first key relative to kstart
-    // S^T for key blocks 0 and 1 (two independent accumulation chains). K fragments are read PK steps
-    // ahead in a rolling window (pinned by scheduling barriers: hoisted further, the reads would need
-    // more registers than two waves per SIMD leave); the SIMD's other wave covers the rest of the
+    const int kt = it * KB;  // the tile's first key relative to kstart
+    // S^T for the tile's NKB key blocks (independent accumulation chains). K fragments are read PK
+    // steps ahead in a rolling window (pinned by scheduling barriers: hoisted further, the reads would
+    // need more registers than two waves per SIMD leave); the SIMD's other wave covers the rest of the
     // read latency.
     constexpr int PK = 2;
-    f32x4_t s0 = (f32x4_t){0.f, 0.f, 0.f, 0.f}, s1 = s0;
-    bf16x8_t kw0[PK], kw1[PK];
+    f32x4_t sacc[NKB];
+    bf16x8_t kw[NKB][PK];
 #pragma unroll
-    for (int j = 0; j < PK; ++j) {
-      kw0[j] = *(const bf16x8_t*)(ks + kfo + 32 * j);
-      kw1[j] = *(const bf16x8_t*)(ks + kfo + 16 * L::KLD + 32 * j);
+    for (int k = 0; k < NKB; ++k) {
+      sacc[k] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < PK; ++j) kw[k][j] = *(const bf16x8_t*)(ks + kfo + 16 * k * L::KLD + 32 * j);
     }
 #pragma unroll
     for (int st = 0; st < KS; ++st) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kw0[st % PK], qf[st], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kw1[st % PK], qf[st], s1, 0, 0, 0);
-      if (st + PK < KS) {
-        kw0[st % PK] = *(const bf16x8_t*)(ks + kfo + 32 * (st + PK));
-        kw1[st % PK] = *(const bf16x8_t*)(ks + kfo + 16 * L::KLD + 32 * (st + PK));
+#pragma unroll
+      for (int k = 0; k < NKB; ++k) {
+        sacc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kw[k][st % PK], qf[st], sacc[k], 0, 0, 0);
+        if (st + PK < KS) kw[k][st % PK] = *(const bf16x8_t*)(ks + kfo + 16 * k * L::KLD + 32 * (st + PK));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    float sc[8];
+    // lane holds keys 16 k + 4 qq + (r & 3) of key block k = r / 4, in sc[r]
+    float sc[4 * NKB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { sc[i] = s0[i]; sc[4 + i] = s1[i]; }
+    for (int k = 0; k < NKB; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[4 * k + i] = sacc[k][i];
     float mt = -INFINITY;
-    if (kt >= wlo_r && kt + AT_KB - 1 <= whi_r) {
+    if (kt >= wlo_r && kt + KB - 1 <= whi_r) {
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
+      for (int r = 0; r < 4 * NKB; ++r) {
         sc[r] *= sl2;
         mt = fmaxf(mt, sc[r]);
       }
     } else {
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
+      for (int r = 0; r < 4 * NKB; ++r) {
         const int kk = kt + 16 * (r >> 2) + 4 * qq + (r & 3);
         const bool vis = kk >= vlo && kk <= vhi;
         const float x = vis ? sc[r] * sl2 : -INFINITY;
@@ -589,12 +603,13 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl
     const float m_new = raise ? mt : m_run;
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     float psum = 0.f;
-    bf16x8_t pb;
+    // P operand of the 32-key step h: the lane's keys {32 h + 4 qq + 0..3, 32 h + 16 + 4 qq + 0..3}
+    bf16x8_t pb[NPV];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
+    for (int r = 0; r < 4 * NKB; ++r) {
       const float pr = __builtin_amdgcn_exp2f(sc[r] - m_use);
       psum += pr;
-      pb[r] = (__bf16)pr;
+      pb[r / 8][r % 8] = (__bf16)pr;
     }
     if (__builtin_amdgcn_ballot_w64(raise) != 0) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
@@ -604,10 +619,13 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl
     }
     l_run += psum;
     m_run = m_new;
-    // O^T += V^T P^T, 16 head elements per MFMA; V^T fragments read PV blocks ahead
+    // O^T += V^T P^T, 16 head elements per MFMA, for each 32-key step h; V^T fragments read PV MFMAs
+    // ahead
     constexpr int PV = 4;
-    auto vread = [&](int d) {
-      const bf16* va = vs + vfo + 16 * d;
+    constexpr int NM = NPV * NO;
+    auto vread = [&](int j) {
+      const int h = j / NO, d = j % NO;
+      const bf16* va = vs + vfo + 32 * h * L::VROW + 16 * d;
       const bf16x4_t lo = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((at_lds_v4s*)(at_lds_void*)va));
       const bf16x4_t hi = __builtin_bit_cast(
           bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((at_lds_v4s*)(at_lds_void*)(va + 16 * L::VROW)));
@@ -617,9 +635,9 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl
 #pragma unroll
     for (int j = 0; j < PV; ++j) vw[j] = vread(j);
 #pragma unroll
-    for (int d = 0; d < NO; ++d) {
-      o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vw[d % PV], pb, o[d], 0, 0, 0);
-      if (d + PV < NO) vw[d % PV] = vread(d + PV);
+    for (int j = 0; j < NM; ++j) {
+      o[j % NO] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vw[j % PV], pb[j / NO], o[j % NO], 0, 0, 0);
+      if (j + PV < NM) vw[j % PV] = vread(j + PV);
       __builtin_amdgcn_sched_barrier(0);
     }
     G4_ATT_WAIT_VMCNT((NS - 2) * LPT);  // tile it + 1 landed
@@ -718,6 +736,8 @@ struct AtPlanKey {
 };
 
 static AtSplit at_choose_split(const AtPlanKey& k, int nblk, int64_t G, int64_t ngroups, int QG) {
+  // the kernel's tile: 32 keys, 64 for the 16-query kernel at head dim 256
+  const int64_t kb = k.hd == 256 ? AttnTileW<256>::KB : AT_KB;
   std::vector<int64_t> tl(nblk);
   int64_t maxt = 1;
   for (int b = 0; b < nblk; ++b) {  // key tiles of block b for a call from position 0
@@ -731,11 +751,11 @@ static AtSplit at_choose_split(const AtPlanKey& k, int nblk, int64_t G, int64_t 
       lo = imin - k.window + 1;
     }
     if (lo < 0) lo = 0;
-    tl[b] = (hi - (lo & ~(int64_t)(AT_KB - 1))) / AT_KB + 1;
+    tl[b] = (hi - (lo & ~(int64_t)(kb - 1))) / kb + 1;
     if (tl[b] > maxt) maxt = tl[b];
   }
   const int64_t copies = k.nkv * k.B;
-  const double part_cost = (double)k.hd / 512.0;
+  const double part_cost = (double)k.hd / 512.0 * (double)AT_KB / (double)kb;
   auto split_for = [&](int64_t t) {
     AtSplit sp{nblk, nblk, nblk};
     int prev = 1;
@@ -835,8 +855,10 @@ bool attn_mfma(const AttnArgs& a, hipStream_t s, g4_status* st) {
   dim3 grid((unsigned)((int64_t)items * a.nkv * a.B));
   const float sl2 = a.scale * 1.4426950408889634f;
   if (a.hd == 128) hipLaunchKernelGGL((k_attn_mfma<128>), grid, dim3(256), 0, s, a, (int)G, sl2, sp);
-  else if (a.hd == 256) hipLaunchKernelGGL((k_attn_w16<256>), grid, dim3(512), 0, s, a, (int)G, sl2, sp);
-  else hipLaunchKernelGGL((k_attn_w16<512>), grid, dim3(512), 0, s, a, (int)G, sl2, sp);
+  else if (a.hd == 256 && a.ring) hipLaunchKernelGGL((k_attn_w16<256, true>), grid, dim3(512), 0, s, a, (int)G, sl2, sp);
+  else if (a.hd == 256) hipLaunchKernelGGL((k_attn_w16<256, false>), grid, dim3(512), 0, s, a, (int)G, sl2, sp);
+  else if (a.ring) hipLaunchKernelGGL((k_attn_w16<512, true>), grid, dim3(512), 0, s, a, (int)G, sl2, sp);
+  else hipLaunchKernelGGL((k_attn_w16<512, false>), grid, dim3(512), 0, s, a, (int)G, sl2, sp);
   if ((*st = check_launch("attn_mfma")) != G4_OK || sp.th1 == nblk || tq_lo >= a.T) return true;
   dim3 gm((unsigned)(a.T - tq_lo), (unsigned)a.nh, (unsigned)a.B);
   if (a.hd == 128) hipLaunchKernelGGL((k_attn_merge_split<128>), gm, dim3(64), 0, s, a, tq_lo, (int)G, 4, sp);

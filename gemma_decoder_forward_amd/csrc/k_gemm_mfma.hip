@@ -111,7 +111,9 @@ __device__ __forceinline__ void lds_dma16(const rsrc_t& r, uint32_t voff, uint32
 // vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt[3:0] and [15:14]).
 #define G4_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
 
-template <int BM, int BN, int NW, int BK, int NS, int EPI, bool CF32>
+// SEGB: every B load group (RPI rows) gets its own descriptor at its first row, so a tile may straddle
+// the boundary between two stacked B matrices (segments a multiple of RPI rows long).
+template <int BM, int BN, int NW, int BK, int NS, int EPI, bool CF32, bool SEGB = false>
 __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a, int tiles_m, int tiles_n) {
   constexpr int WM = BM / (NW / 2), WN = BN / 2;  // waves in a (NW/2) x 2 grid
   constexpr int FM = WM / 32, FN = WN / 32;
@@ -125,7 +127,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a, int tiles_
   static_assert(EPI != EPI_GEGLU || RPI == 8 || RPI == 16, "gate/up blocks of one load instruction's rows");
   static_assert((NW == 4 || NW == 8) && AJ * RPI * NW == BM && BJ * RPI * NW == BN, "loader covers the tile");
   static_assert(KS % 2 == 0 && MF_KMIN % BK == 0, "k-slices alternate two register sets");
-  static_assert(NRD <= NMF && LG <= NMF, "every read and load rides behind an MFMA");
+  static_assert(NRD <= NMF, "every fragment read rides behind an MFMA");
+  static_assert(!SEGB || EPI == EPI_STORE, "segmented B rows: plain store epilogue");
   static_assert((NS - 1) * LG <= 63 && NS >= 2, "vmcnt range");
   static_assert(NS * STAGE * 2 <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(1024))) bf16 lds[NS * STAGE];
@@ -141,6 +144,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a, int tiles_
     int64_t m0, n0;
     int z, nk;
     rsrc_t ra, rg, ru;
+    rsrc_t rq[SEGB ? BJ : 1];  // SEGB: B load group q's rows
   };
   auto tile_at = [&](int t) {
     Tile c;
@@ -172,6 +176,22 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a, int tiles_
     }
     c.rg = make_rsrc(bbase + nloc * a.ldb + kb, (nrows - nloc) * a.ldb * 2 - kb * 2);
     c.ru = EPI == EPI_GEGLU ? make_rsrc((const bf16*)a.B2 + c.n0 * a.ldb + kb, (a.N - c.n0) * a.ldb * 2 - kb * 2) : c.rg;
+    if (SEGB) {
+#pragma unroll
+      for (int q = 0; q < (SEGB ? BJ : 1); ++q) {
+        const int64_t r = c.n0 + RPI * (wave + NW * q);  // the group's first B row (wave-uniform)
+        const bf16* base = (const bf16*)a.B;
+        int64_t loc = r, len = a.N;
+        if (a.nseg > 1) {
+          const int64_t r0 = a.seg_rows[0], r1 = a.seg_rows[1];
+          const int sg = r < r0 ? 0 : (r < r0 + r1 ? 1 : 2);
+          base = (const bf16*)(sg == 0 ? a.segB[0] : (sg == 1 ? a.segB[1] : a.segB[2]));
+          loc = r - (sg == 0 ? 0 : (sg == 1 ? r0 : r0 + r1));
+          len = sg == 0 ? r0 : (sg == 1 ? r1 : a.seg_rows[2]);
+        }
+        c.rq[q] = make_rsrc(base + loc * a.ldb + kb, (len - loc) * a.ldb * 2 - kb * 2);
+      }
+    }
     return c;
   };
 
@@ -194,6 +214,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a, int tiles_
       use_up[q] = g & 1;
       src = RPI * (g >> 1) + lr;
     }
+    if (!isa && SEGB) src = lr;  // relative to the group's own descriptor
     voff[q] = (uint32_t)(((int64_t)src * (isa ? a.lda : a.ldb) + 8 * chunk) * 2);
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)lds;
@@ -213,6 +234,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a, int tiles_
     // value selects (a reference to one of the two tiles would put them in scratch memory)
     if (q < AJ) {
       lds_dma16(in_nxt ? nxt.ra : cur.ra, voff[q], koff, lbase + (wave + NW * q) * 1024);
+    } else if (SEGB) {
+      const int qb = SEGB ? q - AJ : 0;
+      lds_dma16(in_nxt ? nxt.rq[qb] : cur.rq[qb], voff[q], koff, lbase + ASZ * 2 + (wave + NW * (q - AJ)) * 1024);
     } else {
       const rsrc_t rc = use_up[q] ? (in_nxt ? nxt.ru : cur.ru) : (in_nxt ? nxt.rg : cur.rg);
       lds_dma16(rc, voff[q], koff, lbase + ASZ * 2 + (wave + NW * (q - AJ)) * 1024);
@@ -350,12 +374,18 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a, int tiles_
       G4_WAIT_VMCNT((NS - 2) * LG);
       __syncthreads();
       // last k-slice; behind its MFMAs the next step's first fragments (the next tile's, after the last
-      // step), then the loads that refill the stage just released with step kt + NS
+      // step), then the loads that refill the stage just released with step kt + NS (behind the last
+      // LG MFMAs, or spread over all of them when there are more loads than MFMAs)
 #pragma unroll
       for (int q = 0; q < NMF; ++q) {
         mf(1, q);
         if (q < NRD) rd(0, 0, st1, q);
-        if (q >= NMF - LG) dma(kt + NS, q - (NMF - LG));
+        if (LG <= NMF) {
+          if (q >= NMF - LG) dma(kt + NS, q - (NMF - LG));
+        } else {
+#pragma unroll
+          for (int l = q * LG / NMF; l < (q + 1) * LG / NMF; ++l) dma(kt + NS, l);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -370,8 +400,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a, int tiles_
 
 // Shapes the MFMA kernel takes: bf16, K a multiple of 64, output columns a multiple of the tile,
 // 16-byte aligned rows, operands small enough for 32-bit buffer offsets, and outputs (and the
-// GELU_MUL factor) whose rows take 4-column vector stores.
-static bool mfma_ok(const GemmArgs& a, int BN) {
+// GELU_MUL factor) whose rows take 4-column vector stores. Stacked B matrices must each be a whole
+// number of tiles, or (seg, the segmented loader) a whole number of 8-row load groups.
+static bool mfma_ok(const GemmArgs& a, int BN, bool seg = false) {
   const int ncols = a.epi == EPI_GEGLU ? BN / 2 : BN;
   if (a.K % MF_KMIN || a.N % ncols) return false;
   if ((a.lda | a.ldb) & 7) return false;
@@ -381,11 +412,13 @@ static bool mfma_ok(const GemmArgs& a, int BN) {
   if ((a.ldc & 3) || ((uintptr_t)a.C & (f32 ? 15 : 7))) return false;
   if (f32 && a.splits > 1 && (a.split_stride & 3)) return false;
   if (a.epi == EPI_GELU_MUL && ((a.aux_ld & 3) || ((uintptr_t)a.aux & 15))) return false;
-  if (a.nseg > 1) {  // stacked B matrices: each a whole number of tiles, aligned, 32-bit offsets
+  if (seg && a.epi != EPI_STORE) return false;
+  if (a.nseg > 1) {  // stacked B matrices: aligned, 32-bit offsets, whole tiles (or load groups)
     if (a.epi != EPI_STORE || a.nseg > 3) return false;
     int64_t rows = 0;
     for (int i = 0; i < a.nseg; ++i) {
-      if (a.seg_rows[i] % ncols || ((uintptr_t)a.segB[i] & 15) || a.seg_rows[i] * a.ldb * 2 > 0x7fffffffLL) return false;
+      if (a.seg_rows[i] % (seg ? 8 : ncols) || ((uintptr_t)a.segB[i] & 15) || a.seg_rows[i] * a.ldb * 2 > 0x7fffffffLL)
+        return false;
       rows += a.seg_rows[i];
     }
     if (rows != a.N) return false;
@@ -402,21 +435,22 @@ static int resident_blocks(const void* k, int threads) {
   return cus * per_cu;
 }
 
-template <int BM, int BN, int NW, int BK, int NS, int EPI, bool CF32>
+template <int BM, int BN, int NW, int BK, int NS, int EPI, bool CF32, bool SEGB = false>
 static void launch_one(const GemmArgs& a, int tm, int tn, int total, bool persist, hipStream_t s) {
-  const void* k = (const void*)k_gemm_mfma<BM, BN, NW, BK, NS, EPI, CF32>;
+  const void* k = (const void*)k_gemm_mfma<BM, BN, NW, BK, NS, EPI, CF32, SEGB>;
   int grid = total;
   if (persist) {
     const int res = resident_blocks(k, NW * 64);
     if (res > 0 && res < total) grid = res;
   }
-  hipLaunchKernelGGL((k_gemm_mfma<BM, BN, NW, BK, NS, EPI, CF32>), dim3((unsigned)grid), dim3(NW * 64), 0, s, a, tm, tn);
+  hipLaunchKernelGGL((k_gemm_mfma<BM, BN, NW, BK, NS, EPI, CF32, SEGB>), dim3((unsigned)grid), dim3(NW * 64), 0, s, a,
+                     tm, tn);
 }
 
 // One launch walks every (split, tile) pair. When every split spans at least NS K-steps, the grid is
 // what fits on the device at once and each block walks several tiles, prefetching the next tile's
 // first steps under the current tile's last ones; otherwise each block takes one tile.
-template <int BM, int BN, int NW, int BK, int NS>
+template <int BM, int BN, int NW, int BK, int NS, bool SEGB = false>
 static g4_status launch_mfma(const GemmArgs& a, hipStream_t s) {
   const int ncols = a.epi == EPI_GEGLU ? BN / 2 : BN;
   const int tm = (int)((a.M + BM - 1) / BM), tn = (int)(a.N / ncols);
@@ -424,32 +458,91 @@ static g4_status launch_mfma(const GemmArgs& a, hipStream_t s) {
   const int64_t kper = ((a.K + a.splits - 1) / a.splits + BK - 1) / BK * BK;
   const int64_t last = a.K - (int64_t)(a.splits - 1) * kper;
   const bool persist = (last < kper ? last : kper) >= (int64_t)NS * BK;
-  if (a.epi == EPI_GEGLU) launch_one<BM, BN, NW, BK, NS, EPI_GEGLU, false>(a, tm, tn, total, persist, s);
+  if (SEGB && a.c_dtype == G4_F32) launch_one<BM, BN, NW, BK, NS, EPI_STORE, true, true>(a, tm, tn, total, persist, s);
+  else if (SEGB) launch_one<BM, BN, NW, BK, NS, EPI_STORE, false, true>(a, tm, tn, total, persist, s);
+  else if (a.epi == EPI_GEGLU) launch_one<BM, BN, NW, BK, NS, EPI_GEGLU, false>(a, tm, tn, total, persist, s);
   else if (a.epi == EPI_GELU_MUL) launch_one<BM, BN, NW, BK, NS, EPI_GELU_MUL, false>(a, tm, tn, total, persist, s);
   else if (a.c_dtype == G4_F32) launch_one<BM, BN, NW, BK, NS, EPI_STORE, true>(a, tm, tn, total, persist, s);
   else launch_one<BM, BN, NW, BK, NS, EPI_STORE, false>(a, tm, tn, total, persist, s);
   return check_launch("gemm_mfma");
 }
 
+// Cost of a 256-row tiling in tile-passes over the CUs, weighted by the tile's width and its split's
+// K length (each extra split-K slice also costs its float32 traffic, counted as 3%). 0 when the
+// tiling leaves more than a quarter of the CUs idle in its only pass (the 128 x 128 kernel then does
+// better).
+static double tiling_cost(int64_t M, int64_t N, int64_t K, int bn, int splits, int64_t cus) {
+  const int64_t items = ((M + 255) / 256) * (N / bn) * splits;
+  if (items * 4 < cus * 3) return 0.0;
+  const int64_t kper = ((K + splits - 1) / splits + 63) / 64 * 64;
+  const int64_t passes = (items + cus - 1) / cus;
+  return (double)passes * bn / 256.0 * (double)kper * (1.0 + 0.03 * (splits - 1));
+}
+
+// The plain-store widths: 256, 320 (five 32-column blocks per wave), 192 through the segmented loader
+// (stacked B matrices need not be whole tiles), and 128. Ties go to the wider tile.
+static int pick_width(const GemmArgs& a, int64_t cus, double* cost) {
+  int best = 0;
+  double bc = 0.0;
+  const int widths[4] = {256, 320, 192, 128};
+  for (int w : widths) {
+    if (!mfma_ok(a, w, w == 192)) continue;
+    const double c = tiling_cost(a.M, a.N, a.K, w, a.splits, cus);
+    if (c > 0.0 && (best == 0 || c < bc - 1e-9)) { best = w; bc = c; }
+  }
+  if (cost) *cost = bc;
+  return best;
+}
+
+int32_t gemm_pick_splits(int64_t M, int64_t N, int64_t K, int32_t max_splits) {
+  if (M < 128 || K % 256) return 1;
+  const int64_t cus = device_cus();
+  GemmArgs a{};
+  a.M = M; a.N = N; a.K = K; a.lda = a.ldb = K; a.ldc = N; a.c_dtype = G4_F32; a.epi = EPI_STORE;
+  a.split_stride = M * N;
+  int32_t best = 1;
+  double bc = 0.0;
+  for (int32_t s = 1; s <= max_splits; ++s) {
+    if (K / s < 512) break;
+    a.splits = s;
+    double c = 0.0;
+    if (pick_width(a, cus, &c) == 0) continue;
+    if (bc == 0.0 || c < bc - 1e-9) { bc = c; best = s; }
+  }
+  return best;
+}
+
 // Picks a tile that gives enough blocks for 256 CUs; false if the shape does not suit the MFMA path.
 // The gated product may take 256 x 320 tiles (160 outputs each) where they need fewer passes over the
 // CUs, counting a 320-wide tile as 1.25 of a 256-wide one: at 2048 token rows and 10240 outputs, 640
 // tiles of 256 x 256 take three passes of 256 CUs (the last half empty), 512 of 256 x 320 take two.
+// Plain stores choose among 256, 320, 192 and 128 wide tiles by the same count (tiling_cost).
 bool gemm_mfma(const GemmArgs& a, hipStream_t s, g4_status* st) {
-  const int64_t tiles256 = ((a.M + 255) / 256) * (a.N / (a.epi == EPI_GEGLU ? 128 : 256)) * a.splits;
-  if (a.epi == EPI_GEGLU && a.splits == 1 && mfma_ok(a, 320) && tiles256 >= 192) {
-    const int64_t cus = device_cus();
-    const int64_t tiles320 = ((a.M + 255) / 256) * (a.N / 160);
-    const double p256 = (double)((tiles256 + cus - 1) / cus), p320 = 1.25 * (double)((tiles320 + cus - 1) / cus);
-    if (p320 < p256 - 1e-9) {
-      const int tm = (int)((a.M + 255) / 256), tn = (int)(a.N / 160);
-      const bool persist = a.K >= 2 * 64;
-      launch_one<256, 320, 8, 64, 2, EPI_GEGLU, false>(a, tm, tn, tm * tn, persist, s);
-      *st = check_launch("gemm_mfma_320");
+  const int64_t cus = device_cus();
+  if (a.epi == EPI_GEGLU) {
+    const int64_t tiles256 = ((a.M + 255) / 256) * (a.N / 128) * a.splits;
+    if (a.splits == 1 && mfma_ok(a, 320) && tiles256 >= 192) {
+      const int64_t tiles320 = ((a.M + 255) / 256) * (a.N / 160);
+      const double p256 = (double)((tiles256 + cus - 1) / cus), p320 = 1.25 * (double)((tiles320 + cus - 1) / cus);
+      if (p320 < p256 - 1e-9) {
+        const int tm = (int)((a.M + 255) / 256), tn = (int)(a.N / 160);
+        const bool persist = a.K >= 2 * 64;
+        launch_one<256, 320, 8, 64, 2, EPI_GEGLU, false>(a, tm, tn, tm * tn, persist, s);
+        *st = check_launch("gemm_mfma_320");
+        return true;
+      }
+    }
+    if (mfma_ok(a, 256) && tiles256 >= 192) {
+      *st = launch_mfma<256, 256, G4_GEMM_NW, G4_GEMM_BK, G4_GEMM_NS>(a, s);
       return true;
     }
-  }
-  if (mfma_ok(a, 256) && tiles256 >= 192) {
+  } else if (a.epi == EPI_STORE) {
+    const int w = pick_width(a, cus, nullptr);
+    if (w == 256) { *st = launch_mfma<256, 256, G4_GEMM_NW, G4_GEMM_BK, G4_GEMM_NS>(a, s); return true; }
+    if (w == 320) { *st = launch_mfma<256, 320, 8, 64, 2>(a, s); return true; }
+    if (w == 192) { *st = launch_mfma<256, 192, 8, 64, 2, true>(a, s); return true; }
+    if (w == 128) { *st = launch_mfma<256, 128, 8, 64, 2>(a, s); return true; }
+  } else if (mfma_ok(a, 256) && ((a.M + 255) / 256) * (a.N / 256) * a.splits >= 192) {
     *st = launch_mfma<256, 256, G4_GEMM_NW, G4_GEMM_BK, G4_GEMM_NS>(a, s);
     return true;
   }
