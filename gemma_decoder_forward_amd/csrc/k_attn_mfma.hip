@@ -21,6 +21,7 @@
 // The O accumulator (HD/32 32x32 blocks per wave) lives in the accumulation registers.
 #include <functional>
 #include <queue>
+#include <type_traits>
 #include <utility>
 #include <vector>
 
@@ -385,6 +386,18 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
     }
 }
 
+// Maximum of x over lanes l and l ^ 16 (l ^ 32): the permlane swaps exchange 16-lane rows (32-lane
+// halves) between two registers in the vector unit, so the pair meets in every lane without an LDS
+// round trip.
+__device__ __forceinline__ float at_max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float at_max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // --------------------------------------------------------------------------------------------
 // The same attention with 16-query waves on v_mfma_f32_16x16x32_bf16, eight waves per block.
 //
@@ -400,8 +413,14 @@ __global__ __launch_bounds__(256, 1) void k_attn_mfma(AttnArgs a, int G, float s
 //   * O^T += V^T P^T: the B operand's 32 k-slots of lane group q = l / 16 are keys {4q + 0..3,
 //     16 + 4q + 0..3}, exactly the lane's eight probabilities; the A operand reads V^T at those keys
 //     with two LDS transpose reads (four consecutive key rows of 16 head elements each).
-//   * A query's 32 scores of a tile sit in the four lanes l % 16 + 16j: its maximum takes two
+//   * A query's scores of a tile sit in the four lanes l % 16 + 16j: its maximum takes two
 //     cross-lane steps; the normaliser is summed per lane and across the four lanes at the end.
+//   * Tiles of KB keys (64 at head dim 256, 32 at 512; the P V operand above repeats per 32 keys).
+//     Software pipeline: while a wave takes the softmax of tile t, the S MFMAs of tile t + 1 issue
+//     between its vector instructions (the matrix unit and the vector unit work side by side), then
+//     come the P V MFMAs of tile t. Two LDS stages hold K of tiles t + 1 and t + 2 and V of tiles t and
+//     t + 1: the K rows of t + 2 and the V rows of t + 1 load during tile t into the halves whose
+//     previous contents every wave finished before the last barrier.
 // --------------------------------------------------------------------------------------------
 template <int HD, bool RING>
 __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl2, AtSplit sp) {
@@ -414,9 +433,10 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl
   constexpr int KS = HD / 32;      // k-steps of S (32 head elements each)
   constexpr int QG = 4;            // query groups per block, two waves each
   constexpr int NS = AttnTileW<HD>::NS;
+  constexpr int NE = 4 * NKB;      // scores per lane per tile
   constexpr int RPW = KB / 8;      // tile rows staged by each wave
-  constexpr int LPT = 2 * RPW;     // direct-to-LDS load instructions per wave per tile (K and V rows)
-  static_assert((NS - 2) * LPT <= 63, "vmcnt range");
+  static_assert(NS == 2, "K and V tiles alternate between two stages");
+  static_assert(KS >= 8, "the softmax steps ride behind the S steps");
   __shared__ __attribute__((aligned(16))) bf16 lds[NS * L::STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -491,7 +511,9 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl
   const int cap32 = (int)a.cap;
   const uint32_t lds_k = (uint32_t)(uintptr_t)(at_lds_void*)lds + (uint32_t)(RPW * wv * L::KLD * 2);
   const uint32_t lds_v = (uint32_t)(uintptr_t)(at_lds_void*)lds + L::KSZ * 2 + (uint32_t)(RPW * wv * L::VROW * 2);
-  auto dma = [&](int it) {
+  // K (isv false) or V rows of tile it into stage it % 2: rows RPW w .. RPW w + RPW - 1 from wave w
+  // (see k_attn_mfma for the out-of-range tiles and the clamped rows).
+  auto dma = [&](int it, bool isv) {
     const bool live = it < it1;
     const uint32_t so = (uint32_t)(it % NS) * L::STAGE * 2;
     const int64_t kb = kstart + (int64_t)it * KB + RPW * wv;  // the wave's first key of the tile
@@ -508,8 +530,8 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl
       else cr = (int)kv_row(kb + r, a.cap, 1);
       const uint32_t voff = (uint32_t)cr * (HD * 2) + (uint32_t)lane * 16;
       if (lane < HD / 8) {
-        at_dma16(rks, voff, oob, lds_k + so + (uint32_t)(r * L::KLD * 2));
-        at_dma16(rvs, voff, oob, lds_v + so + (uint32_t)(r * L::VROW * 2));
+        if (isv) at_dma16(rvs, voff, oob, lds_v + so + (uint32_t)(r * L::VROW * 2));
+        else at_dma16(rks, voff, oob, lds_k + so + (uint32_t)(r * L::KLD * 2));
       }
     }
   };
@@ -531,36 +553,20 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl
 #pragma unroll
   for (int d = 0; d < NO; ++d) o[d] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
-
-  if (it1 > it0) {
-#pragma unroll
-    for (int j = 0; j < NS - 1; ++j) dma(it0 + j);
-    G4_ATT_WAIT_VMCNT((NS - 2) * LPT);
-    __syncthreads();
-    if (edge_tile(it0)) {
-      vclean(it0, it0 % NS);
-      __syncthreads();
-    }
-  }
   // operand addresses within a stage (bf16 elements)
   const int kfo = ql * L::KLD + 8 * qq;                                   // K: key row ql, chunk qq
   const int vfo = (4 * qq + (ql >> 2)) * L::VROW + 4 * (ql & 3);          // V^T: rows 4qq + ql/4
-  for (int it = it0; it < it1; ++it) {
-    const int cur = it % NS;
-    dma(it + NS - 1);
-    const bf16* ks = lds + cur * L::STAGE;
-    const bf16* vs = ks + L::KSZ;
-    const int kt = it * KB;  // the tile's first key relative to kstart
-    // S^T for the tile's NKB key blocks (independent accumulation chains). K fragments are read PK
-    // steps ahead in a rolling window (pinned by scheduling barriers: hoisted further, the reads would
-    // need more registers than two waves per SIMD leave); the SIMD's other wave covers the rest of the
-    // read latency.
-    constexpr int PK = 2;
-    f32x4_t sacc[NKB];
+
+  // S^T of one tile for the tile's NKB key blocks (independent accumulation chains). K fragments are
+  // read PK steps ahead in a rolling window, pinned by scheduling barriers (at head dim 512 the two
+  // waves per SIMD leave registers for two steps only). step(st) runs after the MFMAs of k-step st,
+  // inside the same scheduling region, so its vector work issues between them.
+  constexpr int PK = HD == 256 ? 3 : 2;
+  auto s_tile = [&](const bf16* ks, f32x4_t (&acc)[NKB], auto&& step) {
     bf16x8_t kw[NKB][PK];
 #pragma unroll
     for (int k = 0; k < NKB; ++k) {
-      sacc[k] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+      acc[k] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < PK; ++j) kw[k][j] = *(const bf16x8_t*)(ks + kfo + 16 * k * L::KLD + 32 * j);
     }
@@ -568,48 +574,90 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl
     for (int st = 0; st < KS; ++st) {
 #pragma unroll
       for (int k = 0; k < NKB; ++k) {
-        sacc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kw[k][st % PK], qf[st], sacc[k], 0, 0, 0);
+        acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kw[k][st % PK], qf[st], acc[k], 0, 0, 0);
         if (st + PK < KS) kw[k][st % PK] = *(const bf16x8_t*)(ks + kfo + 16 * k * L::KLD + 32 * (st + PK));
       }
+      step(st);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // lane holds keys 16 k + 4 qq + (r & 3) of key block k = r / 4, in sc[r]
-    float sc[4 * NKB];
+  };
+
+  // The online softmax of one tile, cut into KS steps that ride behind the next tile's S MFMAs:
+  // step 0 scales (and on edge tiles masks) the lane's NE scores and takes their maximum, steps 1 and
+  // 2 complete the maximum over the four lanes of each query (permlane swaps: no LDS round trip),
+  // step 2 also sets the reference, and steps 3 .. KS-1 take the exponentials. The lane holds keys
+  // 16 k + 4 qq + (r & 3) of key block k = r / 4 in sc[r]; the P operand of the 32-key step h is the
+  // lane's keys {32 h + 4 qq + 0..3, 32 h + 16 + 4 qq + 0..3}, sc[8 h .. 8 h + 7].
+  float sc[NE];
+  float mt = -INFINITY, m_new = -INFINITY, m_use = 0.f, psum = 0.f;
+  bool raise = false, full = false;
+  int kt = 0;
+  bf16x8_t pb[NPV];
+  auto smax_step = [&](int st) {
+    if (st == 0) {
+      mt = -INFINITY;
+      if (full) {
+#pragma unroll
+        for (int r = 0; r < NE; ++r) {
+          sc[r] *= sl2;
+          mt = fmaxf(mt, sc[r]);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < NE; ++r) {
+          const int kk = kt + 16 * (r >> 2) + 4 * qq + (r & 3);
+          const bool vis = kk >= vlo && kk <= vhi;
+          const float x = vis ? sc[r] * sl2 : -INFINITY;
+          sc[r] = x;
+          mt = fmaxf(mt, x);
+        }
+      }
+    } else if (st == 1) {
+      mt = at_max_xor16(mt);
+    } else if (st == 2) {
+      mt = at_max_xor32(mt);
+      // lazy reference, as in k_attn_mfma: raised only when the tile exceeds it by more than 32 (log2)
+      raise = mt > m_run + 32.f;
+      m_new = raise ? mt : m_run;
+      m_use = m_new == -INFINITY ? 0.f : m_new;
+      psum = 0.f;
+    } else {
+#pragma unroll
+      for (int r = 0; r < NE; ++r)
+        if (3 + r * (KS - 3) / NE == st) {
+          const float pr = __builtin_amdgcn_exp2f(sc[r] - m_use);
+          psum += pr;
+          pb[r / 8][r % 8] = (__bf16)pr;
+        }
+    }
+  };
+
+  // One tile: the softmax of tile it (S already in sacc) behind the S MFMAs of tile it + 1 (MORE),
+  // then O^T += V^T P^T. Tile it + 2's K rows and tile it + 1's V rows load meanwhile: each into the
+  // half of the stage whose previous tile every wave finished before the last barrier.
+  f32x4_t sacc[NKB], snext[NKB];
+  auto iter = [&](int it, auto more_t) {
+    constexpr bool MORE = decltype(more_t)::value;
+    const int cur = it % NS, nx = (it + 1) % NS;
+    if (MORE) {
+      dma(it + 2, false);
+      dma(it + 1, true);
+    }
+    kt = it * KB;  // the tile's first key relative to kstart
+    full = kt >= wlo_r && kt + KB - 1 <= whi_r;
 #pragma unroll
     for (int k = 0; k < NKB; ++k)
 #pragma unroll
       for (int i = 0; i < 4; ++i) sc[4 * k + i] = sacc[k][i];
-    float mt = -INFINITY;
-    if (kt >= wlo_r && kt + KB - 1 <= whi_r) {
-#pragma unroll
-      for (int r = 0; r < 4 * NKB; ++r) {
-        sc[r] *= sl2;
-        mt = fmaxf(mt, sc[r]);
-      }
+    if constexpr (MORE) {
+      // the wave in this phase issues first: its matrix and vector work overlap each other, and the
+      // SIMD's other wave, whose P V MFMAs have no vector work beside them, fills the gaps
+      __builtin_amdgcn_s_setprio(1);
+      s_tile(lds + nx * L::STAGE, snext, smax_step);
+      __builtin_amdgcn_s_setprio(0);
     } else {
 #pragma unroll
-      for (int r = 0; r < 4 * NKB; ++r) {
-        const int kk = kt + 16 * (r >> 2) + 4 * qq + (r & 3);
-        const bool vis = kk >= vlo && kk <= vhi;
-        const float x = vis ? sc[r] * sl2 : -INFINITY;
-        sc[r] = x;
-        mt = fmaxf(mt, x);
-      }
-    }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    // lazy reference, as in k_attn_mfma: raised only when the tile exceeds it by more than 32 (log2)
-    const bool raise = mt > m_run + 32.f;
-    const float m_new = raise ? mt : m_run;
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    float psum = 0.f;
-    // P operand of the 32-key step h: the lane's keys {32 h + 4 qq + 0..3, 32 h + 16 + 4 qq + 0..3}
-    bf16x8_t pb[NPV];
-#pragma unroll
-    for (int r = 0; r < 4 * NKB; ++r) {
-      const float pr = __builtin_amdgcn_exp2f(sc[r] - m_use);
-      psum += pr;
-      pb[r / 8][r % 8] = (__bf16)pr;
+      for (int st = 0; st < KS; ++st) smax_step(st);
     }
     if (__builtin_amdgcn_ballot_w64(raise) != 0) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
@@ -621,7 +669,8 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl
     m_run = m_new;
     // O^T += V^T P^T, 16 head elements per MFMA, for each 32-key step h; V^T fragments read PV MFMAs
     // ahead
-    constexpr int PV = 4;
+    const bf16* vs = lds + cur * L::STAGE + L::KSZ;
+    constexpr int PV = HD == 256 ? 8 : 4;
     constexpr int NM = NPV * NO;
     auto vread = [&](int j) {
       const int h = j / NO, d = j % NO;
@@ -640,12 +689,30 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl
       if (j + PV < NM) vw[j % PV] = vread(j + PV);
       __builtin_amdgcn_sched_barrier(0);
     }
-    G4_ATT_WAIT_VMCNT((NS - 2) * LPT);  // tile it + 1 landed
-    __syncthreads();
-    if (it + 1 < it1 && edge_tile(it + 1)) {
-      vclean(it + 1, (it + 1) % NS);
+    if (MORE) {
+      G4_ATT_WAIT_VMCNT(0);  // tile it + 2's K and tile it + 1's V landed
       __syncthreads();
+      if (edge_tile(it + 1)) {
+        vclean(it + 1, nx);
+        __syncthreads();
+      }
+#pragma unroll
+      for (int k = 0; k < NKB; ++k) sacc[k] = snext[k];
     }
+  };
+
+  if (it1 > it0) {
+    dma(it0, false);
+    dma(it0, true);
+    dma(it0 + 1, false);
+    G4_ATT_WAIT_VMCNT(0);
+    __syncthreads();
+    if (edge_tile(it0)) vclean(it0, it0 % NS);
+    s_tile(lds + (it0 % NS) * L::STAGE, sacc, [](int) {});
+    __syncthreads();  // every wave is done with tile it0's K rows (refilled by the first iteration)
+    int it = it0;
+    for (; it + 1 < it1; ++it) iter(it, std::true_type{});
+    iter(it, std::false_type{});
   }
 
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);

@@ -280,13 +280,13 @@ def test_linear_vs_oracle(dt, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1000, 12288, 576), (520, 24576, 128), (600, 24576, 64), (300, 24576, 2560),
-                                   (1024, 16384, 576), (4096, 2560, 2048), (7168, 2560, 256)])
+                                   (1024, 16384, 576), (4096, 2048, 1024), (7168, 2560, 256)])
 def test_linear_large_tiles_pipeline_depths(M, N, K):
     """The 256-row-tile MFMA paths (at least 192 tiles): ragged M, and K steps fewer than, equal to and
     more than the LDS stages (K = 64, 128, 576, 2560 in steps of 64). On 256 CUs the tile widths are
     192 (the first four shapes: the segmented loader over one matrix), 256 (1024 x 16384), 128
-    (4096 x 2560 x 2048: more loads than MFMAs per k-slice) and 320 (7168 x 2560). Large outputs are
-    checked on every 7th row and the last rows."""
+    (4096 x 2048: more loads than MFMAs per k-slice) and 320 (7168 x 2560). Large outputs are checked
+    on every 7th row and the last rows."""
     log(f"linear large tiles {M}x{N}x{K}")
     A = randn((M, K), 74, torch.bfloat16)
     W = randn((N, K), 75, torch.bfloat16, 0.02)
