@@ -43,20 +43,37 @@ constexpr int SK_D = 4;  // 128-k steps per batch of weight loads
 // LDS rows of the staged A slice: the M token rows, plus a zero row when the MFMA blocks have more rows.
 __host__ __device__ inline int sk_lds_rows(int mb, int64_t M) { return M < 16 * mb ? (int)M + 1 : 16 * mb; }
 
-// 8 consecutive A values formed from float32 partial slices (see SkAKind), rounded to bf16.
+// 8 consecutive A values formed from float32 partial slices (see SkAKind), rounded to bf16. The slices'
+// loads go out four at a time (one memory round trip per four slices), and are added in slice order.
 template <int AK>
 __device__ __forceinline__ uint4 sk_a_from_parts(const SkA& sa, int64_t m, int64_t k) {
   const float* pr = (const float*)sa.a + m * sa.lda + k;
+  constexpr int PB = 4;
   float g[8], u[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) g[e] = u[e] = 0.f;
-  for (int p = 0; p < sa.parts; ++p) {
-    const float4 x0 = *(const float4*)(pr + p * sa.part_stride), x1 = *(const float4*)(pr + p * sa.part_stride + 4);
-    g[0] += x0.x; g[1] += x0.y; g[2] += x0.z; g[3] += x0.w; g[4] += x1.x; g[5] += x1.y; g[6] += x1.z; g[7] += x1.w;
-    if (AK == SKA_GEGLU) {
-      const float* ur = pr + p * sa.part_stride + sa.up_off;
-      const float4 y0 = *(const float4*)ur, y1 = *(const float4*)(ur + 4);
-      u[0] += y0.x; u[1] += y0.y; u[2] += y0.z; u[3] += y0.w; u[4] += y1.x; u[5] += y1.y; u[6] += y1.z; u[7] += y1.w;
+  for (int p0 = 0; p0 < sa.parts; p0 += PB) {
+    float4 x0[PB], x1[PB], y0[PB], y1[PB];
+#pragma unroll
+    for (int q = 0; q < PB; ++q) {
+      const int p = p0 + q < sa.parts ? p0 + q : sa.parts - 1;  // past the last slice: re-read it (unused)
+      const float* ps = pr + p * sa.part_stride;
+      x0[q] = *(const float4*)ps;
+      x1[q] = *(const float4*)(ps + 4);
+      if (AK == SKA_GEGLU) {
+        y0[q] = *(const float4*)(ps + sa.up_off);
+        y1[q] = *(const float4*)(ps + sa.up_off + 4);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < PB; ++q) {
+      if (p0 + q >= sa.parts) break;
+      g[0] += x0[q].x; g[1] += x0[q].y; g[2] += x0[q].z; g[3] += x0[q].w;
+      g[4] += x1[q].x; g[5] += x1[q].y; g[6] += x1[q].z; g[7] += x1[q].w;
+      if (AK == SKA_GEGLU) {
+        u[0] += y0[q].x; u[1] += y0[q].y; u[2] += y0[q].z; u[3] += y0[q].w;
+        u[4] += y1[q].x; u[5] += y1[q].y; u[6] += y1[q].z; u[7] += y1[q].w;
+      }
     }
   }
   if (AK == SKA_GELU_MUL) {

@@ -20,7 +20,7 @@ import oracle as O
 from gemma_decoder_forward_amd import binding as bd
 from synth import configs, gen
 from tests import bf16_floor as F
-from tests.gpu_util import (TOL_BF16_RELL2, assert_close, assert_layers_within_floor, build_model, host_layer, log,
+from tests.gpu_util import (G4Model, TOL_BF16_RELL2, assert_close, assert_layers_within_floor, build_model, host_layer, log,
                             max_rel, rel_l2)
 
 pytestmark = pytest.mark.gpu
@@ -301,6 +301,52 @@ def test_config4_decode_per_layer_sampled_sequences(B):
     errs = _per_layer(model, hs_b, p0[owner], acts["pos"], table, ctx, bd.G4_DECODE, rows=sample)
     floors = F.layer_floors(sub, host_layer(layers), hs, p0, opos, c0, "bf16_decode")
     assert_layers_within_floor(errs, floors, f"decode B={B}")
+
+
+@pytest.mark.parametrize("B", [1, 3, 8])
+def test_decode_stack_matches_layer_by_layer(B):
+    """A 3-layer E4B decode step (sliding, sliding, full; layer scalars 0.8, 0.9, 0.7) as one stack
+    call and as one g4_layer_forward call per layer. In a stack each layer's last residual tail also
+    writes the next layer's normed input (one launch less per layer); single-layer calls norm their
+    input themselves. Both compute the same float32 expressions in the same order, up to the compiler's
+    fused multiply-adds. The keys (cached and new) are scaled by 0.05 so the attention stays smooth: with
+    unit-RMS queries and keys the softmax sits near a few keys and one bf16 rounding tipped the other way
+    moves a row by ~1e-3 through the following layers. A mistake in the handover -- a missing scale, a
+    wrong norm weight or row -- moves the result by more than 0.1."""
+    cfg = configs.get(4, B=B, layer_types="SSF", n_shared=0)
+    layers = [gen.layer_weights(cfg, l, "cuda") for l in range(cfg["n_layers"])]
+    for lw, sc in zip(layers, (0.8, 0.9, 0.7)):
+        lw["k_norm"].mul_(0.05)
+        lw["layer_scalar"] = sc
+    glob = gen.model_globals(cfg, "cuda")
+    model = G4Model(cfg, layers, glob)
+    acts = gen.activations(cfg, "cuda")
+    ctx = cfg["ctx"]
+    fills = {}
+    for l in range(cfg["n_layers"]):
+        if model.kv_src[l] == l:
+            k, v = gen.decode_cache(cfg, l, "cuda")
+            fills[l] = ((k.float() * 0.05).to(k.dtype), v)
+    h0, ple = model.embed(acts["ids"])
+    outs = []
+    for per_layer in (False, True):
+        caches, table = model.new_caches(B, ctx, fill=lambda l: tuple(x.clone() for x in fills[l]))
+        h = h0.clone()
+        if per_layer:
+            for l in range(model.L):
+                model.forward(h, ple, acts["pos"], table, ctx, bd.G4_DECODE, layer=l)
+        else:
+            model.forward(h, ple, acts["pos"], table, ctx, bd.G4_DECODE)
+        torch.cuda.synchronize()
+        outs.append((h.clone(), caches))
+    assert torch.isfinite(outs[0][0]).all()
+    d = [rel_l2(outs[0][0][b], outs[1][0][b]) for b in range(B)]
+    log(f"decode B={B}, 3 layers: stack vs layer by layer, rel L2 per sequence " + " ".join(f"{x:.1e}" for x in d))
+    assert max(d) <= 1e-2, f"B={B}: stack and layer-by-layer decode differ (rel L2 {max(d):.3e})"
+    for l in outs[0][1]:
+        for a, b in zip(outs[0][1][l], outs[1][1][l]):
+            a, b = a.float(), b.float()
+            assert float((a - b).norm() / b.norm()) <= 1e-2, f"B={B}: cache of layer {l} differs"
 
 
 # ------------------------------------------------------------------------------- HIP graph replay
