@@ -653,6 +653,49 @@ __global__ __launch_bounds__(256) void k_ple_combine(const int32_t* __restrict__
   }
 }
 
+// The same with four consecutive values per lane (d a multiple of 4, 16-byte aligned rows): every load
+// of the chunk (projection, table row, norm weight) is issued before the reduction, in 16-byte pieces.
+template <typename T, int PER4>
+__global__ __launch_bounds__(256) void k_ple_combine4(const int32_t* __restrict__ ids, const float* __restrict__ P,
+                                                      const T* __restrict__ Tab, int64_t ple_vocab,
+                                                      const T* __restrict__ norm, int64_t L, int d,
+                                                      float pscale, float eps, float* __restrict__ out) {
+  const int64_t m = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t l = blockIdx.y * 4 + wave;
+  if (l >= L) return;
+  const int64_t id = ids[m];
+  const bool ok = id >= 0 && id < ple_vocab;
+  const float tscale = sqrtf((float)d);
+  const float half = 0.70710678118654752f;
+  const float* pr = P + (m * L + l) * d;
+  const T* tr = Tab + (ok ? id : 0) * (L * d) + l * d;
+  float4 v[PER4], tv[PER4], nw[PER4];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER4; ++i) {
+    const int j = 4 * lane + 256 * i;
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+    v[i] = j < d ? *(const float4*)(pr + j) : z;
+    tv[i] = (ok && j < d) ? ld4(tr + j) : z;
+    nw[i] = j < d ? ld4(norm + j) : z;
+  }
+#pragma unroll
+  for (int i = 0; i < PER4; ++i) {
+    v[i] = v[i] * pscale;
+    ss += dot4(v[i]);
+  }
+  ss = wave_sum(ss);
+  const float inv = 1.f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+  for (int i = 0; i < PER4; ++i) {
+    const int j = 4 * lane + 256 * i;
+    if (j >= d) continue;
+    const float4 r = (v[i] * inv * nw[i] + tv[i] * tscale) * half;
+    *(float4*)(out + (m * L + l) * d + j) = r;
+  }
+}
+
 g4_status ple_combine(const int32_t* ids, int64_t M, const float* P, const void* Tab, int64_t ple_vocab,
                       const void* ple_norm, int64_t H, int64_t L, int64_t d, float eps, float* ple_out,
                       int32_t dtype, hipStream_t s) {
@@ -661,6 +704,21 @@ g4_status ple_combine(const int32_t* ids, int64_t M, const float* P, const void*
   const float pscale = 1.f / sqrtf((float)H);
   dim3 g((unsigned)M, (unsigned)((L + 3) / 4));
   const int per = (int)((d + 63) / 64);
+  const size_t tsz = dtype == G4_BF16 ? 2 : 4;
+  if (d % 4 == 0 && ((uintptr_t)P & 15) == 0 && ((uintptr_t)ple_out & 15) == 0 && ((uintptr_t)Tab % (4 * tsz)) == 0 &&
+      ((uintptr_t)ple_norm % (4 * tsz)) == 0) {
+    const int per4 = (int)((d + 255) / 256);
+#define G4_PC4(TT, P4)                                                                                     \
+  hipLaunchKernelGGL((k_ple_combine4<TT, P4>), g, dim3(256), 0, s, ids, P, (const TT*)Tab, ple_vocab, \
+                     (const TT*)ple_norm, L, (int)d, pscale, eps, ple_out)
+    if (dtype == G4_BF16) {
+      if (per4 <= 1) G4_PC4(bf16, 1); else G4_PC4(bf16, 2);
+    } else {
+      if (per4 <= 1) G4_PC4(float, 1); else G4_PC4(float, 2);
+    }
+#undef G4_PC4
+    return check_launch("ple_combine");
+  }
 #define G4_PC(TT, P) hipLaunchKernelGGL((k_ple_combine<TT, P>), g, dim3(256), 0, s, ids, P_, (const TT*)Tab, ple_vocab, (const TT*)ple_norm, L, (int)d, pscale, eps, ple_out)
   const float* P_ = P;
   if (dtype == G4_BF16) {
