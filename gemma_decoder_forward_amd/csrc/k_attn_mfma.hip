@@ -742,6 +742,347 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl
   }
 }
 
+template <int HD, bool RING>
+__global__ __launch_bounds__(512, 1) void k_attn_w16p(AttnArgs a, int G, float sl2, AtSplit sp) {
+  using L = AttnLdsW<HD>;
+  typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+  constexpr int KB = L::KB;        // keys per tile
+  constexpr int NKB = KB / 16;     // 16-key blocks of S per tile
+  constexpr int NPV = KB / 32;     // 32-key steps of P V per tile
+  constexpr int NOH = HD / 32;     // O blocks (16 head elements each) per query block in the wave's half
+  constexpr int KS = HD / 32;      // k-steps of S (32 head elements each)
+  constexpr int QG = 4;            // query groups per block, two waves each
+  constexpr int NS = AttnTileW<HD>::NS;
+  constexpr int NE = 4 * NKB;      // scores per lane per tile
+  constexpr int RPW = KB / 8;      // tile rows staged by each wave
+  static_assert(NS == 2, "K and V tiles alternate between two stages");
+  static_assert(KS >= 8, "the softmax steps ride behind the S steps");
+  __shared__ __attribute__((aligned(16))) bf16 lds[NS * L::STAGE];
+  // the pair's exchange: P of each wave (two buffers), its queries' rescale factors and whether any
+  // was raised, and at the end their normalisers
+  __shared__ bf16x8_t px[2][8][NPV][64];
+  __shared__ float ax[2][8][64];
+  __shared__ int fx[2][8];
+  __shared__ float lx[8][64];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ql = lane & 15, qq = lane >> 4;  // query of the lane within the wave; lane group
+  const int nruns = (int)((a.T + 31) / 32);
+  const int ngroups = nruns * G;
+  const int nblk = (ngroups + QG - 1) / QG;
+  int blk, part, nparts;
+  const int64_t g = (int64_t)blockIdx.x % a.nkv, b = ((int64_t)blockIdx.x / a.nkv) % a.B;
+  at_item((int)((int64_t)blockIdx.x / (a.nkv * a.B)), nblk, sp, blk, part, nparts);
+  const int gi = blk * QG + (wave >> 1);
+  const int run = gi / G;
+  const int64_t head = g * G + gi % G;
+  const int hf = wave & 1;                                    // which 16 queries; which half of O
+  const int64_t tq0 = (int64_t)run * 32 + 16 * hf;            // the wave's first query token
+  const int64_t tq = tq0 + ql;                                // this lane's query token
+  const int64_t ptq = (int64_t)run * 32 + 16 * (1 - hf) + ql; // the partner wave's query in this lane
+  const int64_t p0 = a.pos0[b];
+  const bool qvalid = gi < ngroups && tq < a.T;
+  const bool pvalid = gi < ngroups && ptq < a.T;
+  const int64_t qi = p0 + tq;
+
+  // block key range (union over its groups), as in k_attn_mfma
+  const int g_first = blk * QG, g_last = (blk * QG + QG - 1) < ngroups - 1 ? blk * QG + QG - 1 : ngroups - 1;
+  int64_t tlast = (int64_t)(g_last / G) * 32 + 31;
+  if (tlast > a.T - 1) tlast = a.T - 1;
+  const int64_t imin = p0 + (int64_t)(g_first / G) * 32, imax = p0 + tlast;
+  const KeySpan ksp = key_span(a.bidir, a.sliding, a.window, a.cap, RING ? 1 : 0, p0, a.T);
+  int64_t lob = imin - ksp.back;
+  if (lob < ksp.kmin) lob = ksp.kmin;
+  const int64_t hib = imax + ksp.fwd < ksp.kmax ? imax + ksp.fwd : ksp.kmax;
+  const int64_t kstart = lob & ~(int64_t)(KB - 1);
+  const int ntiles = hib >= lob ? (int)((hib - kstart) / KB + 1) : 0;
+  const int it0 = part * ntiles / nparts, it1 = (part + 1) * ntiles / nparts;
+  int64_t qlo = qi - ksp.back;
+  if (qlo < ksp.kmin) qlo = ksp.kmin;
+  const int64_t qhi = qi + ksp.fwd < hib ? qi + ksp.fwd : hib;
+  // the lane's visible keys relative to the first tile, in 32 bits (none for an invalid query)
+  const int vlo = qvalid ? (int)(qlo - kstart) : 0x7fffffff, vhi = qvalid ? (int)(qhi - kstart) : -1;
+  // keys visible to every query of the wave (empty when some query of the wave is invalid)
+  int64_t wlo_all, whi_all;
+  {
+    const int64_t first = p0 + tq0, last = p0 + tq0 + 15;
+    wlo_all = last - ksp.back;
+    if (wlo_all < lob) wlo_all = lob;
+    whi_all = first + ksp.fwd < hib ? first + ksp.fwd : hib;
+    if (!(gi < ngroups && tq0 + 15 < a.T)) { wlo_all = 1; whi_all = 0; }
+  }
+  // per-tile range tests in 32 bits, relative to the first tile's first key
+  const int lob_r = (int)(lob - kstart), hib_r = (int)(hib - kstart);
+  const int wlo_r = (int)(wlo_all - kstart), whi_r = wlo_all > whi_all ? -1 : (int)(whi_all - kstart);
+
+  // Q fragments (B operand of S^T): query ql, head elements 32 s + 8 qq .. +7
+  bf16x8_t qf[KS];
+  {
+    const bf16* qrow = (const bf16*)a.q + (b * a.T + (qvalid ? tq : 0)) * a.q_ld + (qvalid ? head : 0) * HD + 8 * qq;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      uint4 u = qvalid ? *(const uint4*)(qrow + 32 * s) : make_uint4(0, 0, 0, 0);
+      qf[s] = *(bf16x8_t*)&u;
+    }
+  }
+  // Q lands before the first tile load (see k_attn_mfma)
+#pragma unroll
+  for (int s = 0; s < KS; ++s) asm volatile("" : : "v"(qf[s]));
+
+  const bf16* Kb = (const bf16*)a.k + (b * a.nkv + g) * a.cap * HD;
+  const bf16* Vb = (const bf16*)a.v + (b * a.nkv + g) * a.cap * HD;
+  const at_rsrc rks = at_make_rsrc(Kb, a.cap * HD * 2), rvs = at_make_rsrc(Vb, a.cap * HD * 2);
+  // Tile it into ring slot it % NS; rows RPW w .. RPW w + RPW - 1 from wave w (see k_attn_mfma for the
+  // out-of-range tiles and the clamped rows).
+  // Cache rows in 32 bits: the byte offsets of a cache fit the 31-bit buffer range (the descriptor's
+  // size saturates there), so every row index that reaches a load does too.
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int cap32 = (int)a.cap;
+  const uint32_t lds_k = (uint32_t)(uintptr_t)(at_lds_void*)lds + (uint32_t)(RPW * wv * L::KLD * 2);
+  const uint32_t lds_v = (uint32_t)(uintptr_t)(at_lds_void*)lds + L::KSZ * 2 + (uint32_t)(RPW * wv * L::VROW * 2);
+  // K (isv false) or V rows of tile it into stage it % 2: rows RPW w .. RPW w + RPW - 1 from wave w
+  // (see k_attn_mfma for the out-of-range tiles and the clamped rows).
+  auto dma = [&](int it, bool isv) {
+    const bool live = it < it1;
+    const uint32_t so = (uint32_t)(it % NS) * L::STAGE * 2;
+    const int64_t kb = kstart + (int64_t)it * KB + RPW * wv;  // the wave's first key of the tile
+    const int rb = RING ? (int)kv_row(kb, a.cap, 1) : (int)(kb < a.cap ? kb : a.cap - 1);
+    // The row's byte offset rides in the per-lane offset, so no scalar register written by a vector
+    // instruction feeds the load (the compiler's hazard checks do not see into the assembly); the
+    // scalar offset only marks a tile past the range.
+    const uint32_t oob = live ? 0u : 0x80000000u;
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      int cr;
+      if (!RING) cr = rb + r < cap32 - 1 ? rb + r : cap32 - 1;  // keys past the cache clamp to its last row
+      else if (cap32 >= RPW) cr = rb + r >= cap32 ? rb + r - cap32 : rb + r;
+      else cr = (int)kv_row(kb + r, a.cap, 1);
+      const uint32_t voff = (uint32_t)cr * (HD * 2) + (uint32_t)lane * 16;
+      if (lane < HD / 8) {
+        if (isv) at_dma16(rvs, voff, oob, lds_v + so + (uint32_t)(r * L::VROW * 2));
+        else at_dma16(rks, voff, oob, lds_k + so + (uint32_t)(r * L::KLD * 2));
+      }
+    }
+  };
+  auto edge_tile = [&](int it) {
+    const int kt = it * KB;
+    return !(kt >= lob_r && kt + KB - 1 <= hib_r);
+  };
+  auto vclean = [&](int it, int buf) {
+    const int kt = it * KB;
+    bf16* vs = lds + buf * L::STAGE + L::KSZ;
+    for (int u = tid; u < KB * (HD / 8); u += 512) {
+      const int row = u / (HD / 8);
+      const int key = kt + row;
+      if (key < lob_r || key > hib_r) *(uint4*)(vs + row * L::VROW + 8 * (u % (HD / 8))) = make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  // O^T of the wave's half of the head elements (hf HD/2 + 16 d + 4 qq + 0..3 in lane (ql, qq)) for its
+  // own 16 queries and for the partner wave's 16
+  f32x4_t oo[NOH], op[NOH];
+#pragma unroll
+  for (int d = 0; d < NOH; ++d) oo[d] = op[d] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  const int kfo = ql * L::KLD + 8 * qq;                                   // K: key row ql, chunk qq
+  const int vfo = (4 * qq + (ql >> 2)) * L::VROW + 4 * (ql & 3) + hf * (HD / 2);  // V^T: rows 4qq + ql/4
+
+  constexpr int PK = 2;
+  auto s_tile = [&](const bf16* ks, f32x4_t (&acc)[NKB], auto&& step) {
+    bf16x8_t kw[NKB][PK];
+#pragma unroll
+    for (int k = 0; k < NKB; ++k) {
+      acc[k] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < PK; ++j) kw[k][j] = *(const bf16x8_t*)(ks + kfo + 16 * k * L::KLD + 32 * j);
+    }
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+#pragma unroll
+      for (int k = 0; k < NKB; ++k) {
+        acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kw[k][st % PK], qf[st], acc[k], 0, 0, 0);
+        if (st + PK < KS) kw[k][st % PK] = *(const bf16x8_t*)(ks + kfo + 16 * k * L::KLD + 32 * (st + PK));
+      }
+      step(st);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  float sc[NE];
+  float mt = -INFINITY, m_new = -INFINITY, m_use = 0.f, psum = 0.f;
+  bool raise = false, full = false;
+  int kt = 0;
+  bf16x8_t pb[NPV];
+  auto smax_step = [&](int st) {
+    if (st == 0) {
+      mt = -INFINITY;
+      if (full) {
+#pragma unroll
+        for (int r = 0; r < NE; ++r) {
+          sc[r] *= sl2;
+          mt = fmaxf(mt, sc[r]);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < NE; ++r) {
+          const int kk = kt + 16 * (r >> 2) + 4 * qq + (r & 3);
+          const bool vis = kk >= vlo && kk <= vhi;
+          const float x = vis ? sc[r] * sl2 : -INFINITY;
+          sc[r] = x;
+          mt = fmaxf(mt, x);
+        }
+      }
+    } else if (st == 1) {
+      mt = at_max_xor16(mt);
+    } else if (st == 2) {
+      mt = at_max_xor32(mt);
+      raise = mt > m_run + 32.f;
+      m_new = raise ? mt : m_run;
+      m_use = m_new == -INFINITY ? 0.f : m_new;
+      psum = 0.f;
+    } else {
+#pragma unroll
+      for (int r = 0; r < NE; ++r)
+        if (3 + r * (KS - 3) / NE == st) {
+          const float pr = __builtin_amdgcn_exp2f(sc[r] - m_use);
+          psum += pr;
+          pb[r / 8][r % 8] = (__bf16)pr;
+        }
+    }
+  };
+
+  // Tile it, in this order: the softmax of tile it behind the S MFMAs of tile it + 1 (MORE); P and the
+  // rescale factors to the pair's exchange; the block barrier (tile it's V, tile it + 2's K and the
+  // partner's P all in place; every wave past the last tile's reads); the loads of tile it + 3's K and
+  // tile it + 1's V into the halves those reads freed; then O^T += V^T P^T for both waves' queries,
+  // each V^T fragment feeding two MFMAs.
+  f32x4_t sacc[NKB], snext[NKB];
+  auto iter = [&](int it, auto more_t) {
+    constexpr bool MORE = decltype(more_t)::value;
+    const int cur = it % NS, nx = (it + 1) % NS;
+    kt = it * KB;
+    full = kt >= wlo_r && kt + KB - 1 <= whi_r;
+#pragma unroll
+    for (int k = 0; k < NKB; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[4 * k + i] = sacc[k][i];
+    if constexpr (MORE) {
+      __builtin_amdgcn_s_setprio(1);
+      s_tile(lds + nx * L::STAGE, snext, smax_step);
+      __builtin_amdgcn_s_setprio(0);
+    } else {
+#pragma unroll
+      for (int st = 0; st < KS; ++st) smax_step(st);
+    }
+    const bool rs = __builtin_amdgcn_ballot_w64(raise) != 0;
+    float alpha = 1.f;
+    if (rs) {
+      alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < NOH; ++d) oo[d] *= alpha;
+    }
+    l_run += psum;
+    m_run = m_new;
+    const int xb = it & 1;
+#pragma unroll
+    for (int h = 0; h < NPV; ++h) px[xb][wave][h][lane] = pb[h];
+    ax[xb][wave][lane] = alpha;
+    if (lane == 0) fx[xb][wave] = rs ? 1 : 0;
+    G4_ATT_WAIT_VMCNT(0);
+    __syncthreads();
+    if (MORE) {
+      dma(it + 3, false);
+      dma(it + 1, true);
+    }
+    if (it > it0 && edge_tile(it)) {
+      vclean(it, cur);
+      __syncthreads();
+    }
+    if (MORE) {
+#pragma unroll
+      for (int k = 0; k < NKB; ++k) sacc[k] = snext[k];
+    }
+    bf16x8_t pp[NPV];
+#pragma unroll
+    for (int h = 0; h < NPV; ++h) pp[h] = px[xb][wave ^ 1][h][lane];
+    if (fx[xb][wave ^ 1]) {
+      const float pa = ax[xb][wave ^ 1][lane];
+#pragma unroll
+      for (int d = 0; d < NOH; ++d) op[d] *= pa;
+    }
+    const bf16* vs = lds + cur * L::STAGE + L::KSZ;
+    constexpr int PV = 4;
+    constexpr int NM = NPV * NOH;
+    auto vread = [&](int j) {
+      const int h = j / NOH, d = j % NOH;
+      const bf16* va = vs + vfo + 32 * h * L::VROW + 16 * d;
+      const bf16x4_t lo = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((at_lds_v4s*)(at_lds_void*)va));
+      const bf16x4_t hi = __builtin_bit_cast(
+          bf16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((at_lds_v4s*)(at_lds_void*)(va + 16 * L::VROW)));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    bf16x8_t vw[PV];
+#pragma unroll
+    for (int j = 0; j < PV; ++j) vw[j] = vread(j);
+#pragma unroll
+    for (int j = 0; j < NM; ++j) {
+      oo[j % NOH] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vw[j % PV], pb[j / NOH], oo[j % NOH], 0, 0, 0);
+      op[j % NOH] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vw[j % PV], pp[j / NOH], op[j % NOH], 0, 0, 0);
+      if (j + PV < NM) vw[j % PV] = vread(j + PV);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  if (it1 > it0) {
+    dma(it0, false);
+    dma(it0, true);
+    dma(it0 + 1, false);
+    G4_ATT_WAIT_VMCNT(0);
+    __syncthreads();
+    if (edge_tile(it0)) vclean(it0, it0 % NS);
+    s_tile(lds + (it0 % NS) * L::STAGE, sacc, [](int) {});
+    __syncthreads();  // tile it0's K rows are read: its half takes tile it0 + 2's
+    dma(it0 + 2, false);
+    int it = it0;
+    for (; it + 1 < it1; ++it) iter(it, std::true_type{});
+    iter(it, std::false_type{});
+  }
+
+  // normalisers of the pair's queries (lane (ql, qq) holds its query's sum after the two steps)
+  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  lx[wave][lane] = l_tot;
+  __syncthreads();
+  const float l_par = lx[wave ^ 1][lane];
+  // lane holds head elements hf HD/2 + 16 d + 4 qq + 0..3 of queries tq (own) and ptq (partner)
+  auto emit = [&](const f32x4_t (&o)[NOH], int64_t q, float lt, float m, bool owner) {
+    if (nparts > 1) {
+      const int64_t row = ((part * a.B + b) * a.T + q) * a.nh + head;
+      float* po = a.ws + row * HD + hf * (HD / 2);
+#pragma unroll
+      for (int d = 0; d < NOH; ++d) *(float4*)(po + 16 * d + 4 * qq) = make_float4(o[d][0], o[d][1], o[d][2], o[d][3]);
+      if (owner && qq == 0) {
+        float* ml = a.ws + AT_PS * a.B * a.T * a.nh * HD + 2 * row;
+        ml[0] = m;
+        ml[1] = lt;
+      }
+      return;
+    }
+    const float il = lt > 0.f ? 1.f / lt : 0.f;
+    bf16* orow = (bf16*)a.out + (b * a.T + q) * a.out_ld + head * HD + hf * (HD / 2);
+#pragma unroll
+    for (int d = 0; d < NOH; ++d) {
+      uint2 pk;
+      pk.x = (uint32_t)f2bf(o[d][0] * il) | ((uint32_t)f2bf(o[d][1] * il) << 16);
+      pk.y = (uint32_t)f2bf(o[d][2] * il) | ((uint32_t)f2bf(o[d][3] * il) << 16);
+      *(uint2*)(orow + 16 * d + 4 * qq) = pk;
+    }
+  };
+  if (qvalid) emit(oo, tq, l_tot, m_run, true);
+  if (pvalid) emit(op, ptq, l_par, 0.f, false);
+}
+
 // Merges the key-share partials of each split query row: O = sum_p O_p 2^(m_p - m) / sum_p l_p 2^(m_p - m)
 // with m = max_p m_p (exp2 domain), parts in order; a row that saw no key stays zero. One wave per
 // (sequence, query token >= tq_lo, head); the row's part count comes from its query block (AtSplit).
@@ -924,8 +1265,8 @@ bool attn_mfma(const AttnArgs& a, hipStream_t s, g4_status* st) {
   if (a.hd == 128) hipLaunchKernelGGL((k_attn_mfma<128>), grid, dim3(256), 0, s, a, (int)G, sl2, sp);
   else if (a.hd == 256 && a.ring) hipLaunchKernelGGL((k_attn_w16<256, true>), grid, dim3(512), 0, s, a, (int)G, sl2, sp);
   else if (a.hd == 256) hipLaunchKernelGGL((k_attn_w16<256, false>), grid, dim3(512), 0, s, a, (int)G, sl2, sp);
-  else if (a.ring) hipLaunchKernelGGL((k_attn_w16<512, true>), grid, dim3(512), 0, s, a, (int)G, sl2, sp);
-  else hipLaunchKernelGGL((k_attn_w16<512, false>), grid, dim3(512), 0, s, a, (int)G, sl2, sp);
+  else if (a.ring) hipLaunchKernelGGL((k_attn_w16p<512, true>), grid, dim3(512), 0, s, a, (int)G, sl2, sp);
+  else hipLaunchKernelGGL((k_attn_w16p<512, false>), grid, dim3(512), 0, s, a, (int)G, sl2, sp);
   if ((*st = check_launch("attn_mfma")) != G4_OK || sp.th1 == nblk || tq_lo >= a.T) return true;
   dim3 gm((unsigned)(a.T - tq_lo), (unsigned)a.nh, (unsigned)a.B);
   if (a.hd == 128) hipLaunchKernelGGL((k_attn_merge_split<128>), gm, dim3(64), 0, s, a, tq_lo, (int)G, 4, sp);
