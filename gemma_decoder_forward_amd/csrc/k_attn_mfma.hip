@@ -496,9 +496,8 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl
       qf[s] = *(bf16x8_t*)&u;
     }
   }
-  // Q lands before the first tile load (see k_attn_mfma)
-#pragma unroll
-  for (int s = 0; s < KS; ++s) asm volatile("" : : "v"(qf[s]));
+  // Q is in flight together with the first tiles: the prologue waits for both at once, before the key
+  // loop (see k_attn_mfma for why the wait must not be left to the compiler)
 
   const bf16* Kb = (const bf16*)a.k + (b * a.nkv + g) * a.cap * HD;
   const bf16* Vb = (const bf16*)a.v + (b * a.nkv + g) * a.cap * HD;
@@ -705,6 +704,8 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl
     dma(it0, false);
     dma(it0, true);
     dma(it0 + 1, false);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) asm volatile("" : : "v"(qf[s]));
     G4_ATT_WAIT_VMCNT(0);
     __syncthreads();
     if (edge_tile(it0)) vclean(it0, it0 % NS);
@@ -825,9 +826,8 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16p(AttnArgs a, int G, float s
       qf[s] = *(bf16x8_t*)&u;
     }
   }
-  // Q lands before the first tile load (see k_attn_mfma)
-#pragma unroll
-  for (int s = 0; s < KS; ++s) asm volatile("" : : "v"(qf[s]));
+  // Q is in flight together with the first tiles: the prologue waits for both at once, before the key
+  // loop (see k_attn_mfma for why the wait must not be left to the compiler)
 
   const bf16* Kb = (const bf16*)a.k + (b * a.nkv + g) * a.cap * HD;
   const bf16* Vb = (const bf16*)a.v + (b * a.nkv + g) * a.cap * HD;
@@ -1038,6 +1038,8 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16p(AttnArgs a, int G, float s
     dma(it0, false);
     dma(it0, true);
     dma(it0 + 1, false);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) asm volatile("" : : "v"(qf[s]));
     G4_ATT_WAIT_VMCNT(0);
     __syncthreads();
     if (edge_tile(it0)) vclean(it0, it0 % NS);
