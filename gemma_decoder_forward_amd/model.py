@@ -3,6 +3,7 @@
 PyTorch supplies device memory and the stream; every step of the forward runs in the library.
 """
 import ctypes as C
+import os
 
 import torch
 
@@ -115,9 +116,20 @@ class G4Model:
                         ple.data_ptr(), ws.data_ptr(), ws.numel(), _stream())
         return h, ple
 
-    def forward(self, h, ple_in, pos, table, cap, mode=bd.G4_PREFILL, layer=None):
-        """Run all layers (or one, if `layer` is given) in place on h [B, T, H] float32."""
+    def forward(self, h, ple_in, pos, table, cap, mode=bd.G4_PREFILL, layer=None, dump=None, caches=None):
+        """Run all layers (or one, if `layer` is given) in place on h [B, T, H] float32.
+
+        dump: a directory (default: the G4_DUMP environment variable, if set) for a per-layer dump to diff
+        against an oracle, as cortiq-engine `g4e_forward` writes one (`CMF_LAYER_DUMP`: the hidden state
+        after every block). The layers then run one library call each, and the
+        hidden state goes to `l_in.f32` before the first layer and `lNN.f32` after layer NN, float32
+        little-endian [B, T, H]. With `caches` (from new_caches) every owning layer's K and V rows at the
+        call's positions go to `lNN_k.f32` / `lNN_v.f32`, [B, nkv, T, hd] upcast to float32."""
         B, T = h.shape[0], h.shape[1]
+        if dump is None:
+            dump = os.environ.get("G4_DUMP") or None
+        if dump is not None and layer is None:
+            return self._forward_dump(h, ple_in, pos, table, cap, mode, dump, caches)
         ws = self.workspace(B, T, cap, mode)
         if layer is None:
             bd.g4_stack_forward(self.desc, self.descs, h.data_ptr(), ple_in.data_ptr(), table, self.L, pos.data_ptr(),
@@ -125,6 +137,30 @@ class G4Model:
         else:
             bd.g4_layer_forward(self.desc, self.descs[layer], layer, h.data_ptr(), ple_in.data_ptr(), table, self.L,
                                 pos.data_ptr(), B, T, mode, ws.data_ptr(), ws.numel(), _stream())
+        return h
+
+    def _forward_dump(self, h, ple_in, pos, table, cap, mode, path, caches):
+        os.makedirs(path, exist_ok=True)
+        B, T = h.shape[0], h.shape[1]
+
+        def write(name, t):
+            torch.cuda.synchronize()
+            t.detach().to(torch.float32).contiguous().cpu().numpy().astype("<f4").tofile(os.path.join(path, name))
+
+        write("l_in.f32", h)
+        # cache row of token t of sequence b: position pos[b] + t, wrapped on a ring
+        steps = torch.arange(T, device=h.device, dtype=torch.int64)
+        for l in range(self.L):
+            self.forward(h, ple_in, pos, table, cap, mode, layer=l)
+            write(f"l{l:02d}.f32", h)
+            if caches is not None and l in caches:
+                k, v = caches[l]
+                rows = pos.to(torch.int64)[:, None] + steps[None, :]
+                if table[l].ring:
+                    rows = rows % table[l].cap
+                idx = rows[:, None, :, None].expand(B, k.shape[1], T, k.shape[3])
+                write(f"l{l:02d}_k.f32", torch.gather(k, 2, idx))
+                write(f"l{l:02d}_v.f32", torch.gather(v, 2, idx))
         return h
 
 

@@ -349,6 +349,51 @@ def test_decode_stack_matches_layer_by_layer(B):
             assert float((a - b).norm() / b.norm()) <= 1e-2, f"B={B}: cache of layer {l} differs"
 
 
+# ------------------------------------------------------------------------------- per-layer dump
+def test_per_layer_dump(tmp_path, monkeypatch):
+    """The driver's per-layer dump (G4_DUMP): the hidden state before and after every layer and each
+    owning layer's new K/V rows, float32 little-endian. The hidden-state files equal the same layers run
+    one call at a time (bit for bit: the dump makes exactly those calls), the K/V files equal the caches'
+    rows at the call's positions (two sequences at different positions), a layer that reads another
+    layer's cache writes none, and the returned state is the last file."""
+    cfg = configs.get(1, T=40, B=2)
+    model, layers, glob = build_model(cfg)
+    acts = gen.activations(cfg, "cuda")
+    h0, ple = model.embed(acts["ids"])
+    pos = torch.tensor([3, 9], dtype=torch.int32, device="cuda")
+    B, T, H, cap = 2, 40, cfg["hidden"], 64
+    _, table_r = model.new_caches(B, cap)
+    h = h0.clone()
+    ref = [h.clone()]
+    for l in range(model.L):
+        model.forward(h, ple, pos, table_r, cap, bd.G4_PREFILL, layer=l)
+        ref.append(h.clone())
+    torch.cuda.synchronize()
+    caches, table = model.new_caches(B, cap)
+    monkeypatch.setenv("G4_DUMP", str(tmp_path))
+    out = model.forward(h0.clone(), ple, pos, table, cap, bd.G4_PREFILL, caches=caches)
+    torch.cuda.synchronize()
+
+    def rd(name, shape):
+        a = np.fromfile(tmp_path / name, dtype="<f4")
+        assert a.size == int(np.prod(shape)), name
+        return a.reshape(shape)
+
+    assert np.array_equal(rd("l_in.f32", (B, T, H)), ref[0].cpu().numpy())
+    for l in range(model.L):
+        assert np.array_equal(rd(f"l{l:02d}.f32", (B, T, H)), ref[l + 1].cpu().numpy()), f"layer {l}"
+        if l not in caches:
+            assert not (tmp_path / f"l{l:02d}_k.f32").exists()
+            continue
+        for nm, c in zip(("k", "v"), caches[l]):
+            got = rd(f"l{l:02d}_{nm}.f32", (B, c.shape[1], T, c.shape[3]))
+            for b in range(B):
+                p = int(pos[b])
+                assert np.array_equal(got[b], c[b, :, p:p + T].float().cpu().numpy()), f"{nm} rows of layer {l}, seq {b}"
+    assert torch.equal(out, ref[-1])
+    log(f"per-layer dump: {len(list(tmp_path.iterdir()))} files")
+
+
 # ------------------------------------------------------------------------------- HIP graph replay
 def test_decode_step_graph_replays_match_eager():
     """A decode step captured as a HIP graph and replayed (with eager work and syncs between replays)
