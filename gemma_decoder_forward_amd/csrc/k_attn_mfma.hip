@@ -1095,6 +1095,8 @@ __global__ __launch_bounds__(64) void k_attn_merge_split(AttnArgs a, int64_t tq_
   const int lane = threadIdx.x;
   const int blk = (int)(((tq / 32) * G + head % G) / QG);
   const int np = 1 + (blk >= sp.th1) + (blk >= sp.th2) + (blk >= sp.th3);
+  if (np == 1) return;  // an unsplit block wrote this row itself (with 8 heads per kv head a run's heads
+                        // may straddle the first split block)
   const float* ml = a.ws + AT_PS * a.B * a.T * a.nh * HD;
   float mp[AT_PS], lp[AT_PS], m = -INFINITY;
 #pragma unroll
@@ -1213,7 +1215,7 @@ static bool attn_plan(int64_t B, int64_t T, int64_t nh, int64_t nkv, int64_t hd,
                       int64_t window, int* nblk, AtSplit* sp, int64_t* tq_lo) {
   if (nkv <= 0 || nh % nkv) return false;
   const int64_t G = nh / nkv;
-  if (!(G == 1 || G == 2 || G == 4) || !(hd == 128 || hd == 256 || hd == 512)) return false;
+  if (!(G == 1 || G == 2 || G == 4 || G == 8) || !(hd == 128 || hd == 256 || hd == 512)) return false;
   const int64_t runs = (T + 31) / 32, cus = device_cus();
   const int QG = 4;  // query groups (head x 32 tokens) per block
   const int64_t ngroups = runs * G;
@@ -1248,7 +1250,7 @@ size_t attn_prefill_ws(int64_t B, int64_t T, int64_t nh, int64_t nkv, int64_t hd
   return nblk * nkv * B < 2 * device_cus() ? attn_split_bytes(B, T, nh, hd) : 0;
 }
 
-// bf16, head_dim 128/256/512, groups of 1, 2 or 4 query heads per kv head, 16-byte aligned rows.
+// bf16, head_dim 128/256/512, groups of 1, 2, 4 or 8 query heads per kv head, 16-byte aligned rows.
 bool attn_mfma(const AttnArgs& a, hipStream_t s, g4_status* st) {
   if ((a.q_ld | a.out_ld) & 7) return false;
   if (((uintptr_t)a.q | (uintptr_t)a.k | (uintptr_t)a.v | (uintptr_t)a.out) & 15) return false;

@@ -115,7 +115,8 @@ def _kv_table(entries):
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("hd,sliding,window,nh,nkv", [(64, 1, 32, 4, 1), (128, 0, 0, 4, 1), (256, 1, 512, 8, 2),
                                                       (512, 0, 0, 8, 2), (256, 1, 7, 4, 2), (128, 1, 40, 2, 2),
-                                                      (512, 1, 100, 4, 2)])
+                                                      (512, 1, 100, 4, 2), (512, 0, 0, 8, 1), (256, 1, 100, 8, 1),
+                                                      (128, 0, 0, 8, 1)])
 def test_attention_prefill_vs_oracle(dt, hd, sliding, window, nh, nkv):
     log(f"attn_prefill {dt} hd={hd} sliding={sliding} W={window}")
     gdt, tdt = DT[dt]
@@ -185,13 +186,14 @@ def test_attention_reads_kv_src_cache_without_copy():
 
 
 @pytest.mark.parametrize("with_ws", [False, True])
-@pytest.mark.parametrize("hd,sliding,W", [(256, 1, 512), (512, 0, 0)])
-def test_attention_prefill_long_e4b_shapes(hd, sliding, W, with_ws):
-    """E4B heads (8 q / 2 kv) over T = 2048 from position 0, the layer pair's attention call. With a
-    workspace the export takes the key split (128 query blocks for 256 compute units), without one it
-    does not; both must match the oracle."""
-    log(f"attn_prefill long hd={hd} ws={with_ws}")
-    B, T, nh, nkv = 1, 2048, 8, 2
+@pytest.mark.parametrize("hd,sliding,W,nkv", [(256, 1, 512, 2), (512, 0, 0, 2), (512, 0, 0, 1), (256, 1, 512, 1)])
+def test_attention_prefill_long_e4b_shapes(hd, sliding, W, nkv, with_ws):
+    """E4B heads (8 q / 2 kv, or the variant's full layer with one kv head) over T = 2048 from position
+    0, the layer pair's attention call. With a workspace the export takes the key split (128 query blocks
+    for 256 compute units), without one it does not; both must match the oracle. With 8 query heads per
+    kv head a block covers half of a 32-token run's heads, so a split threshold can fall inside a run."""
+    log(f"attn_prefill long hd={hd} nkv={nkv} ws={with_ws}")
+    B, T, nh = 1, 2048, 8
     q = randn((T, nh * hd), 35 + hd, torch.bfloat16)
     K = randn((1, nkv, T, hd), 36, torch.bfloat16)
     V = randn((1, nkv, T, hd), 37, torch.bfloat16)
