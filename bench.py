@@ -215,8 +215,9 @@ def run_gpu(cfg, layers, glob, steps, warmup, breakdown, use_graph=True):
     run = step
     if decode and use_graph:
         # A decode step is hundreds of short kernels: it is captured once as a HIP graph and replayed.
-        # The timer's event pairs (the first 2*steps gate/up launches of the step) are captured with it
-        # and re-recorded on every replay, so after the timed region they hold the last replay's times.
+        # The gate/up launch time comes from capture()'s warm-up step, whose launches are eager (on a side
+        # stream, an event pair around each of the first 2*steps gate/up launches, which fills the timer),
+        # so it includes each launch's dispatch gap; the replayed graph records no events.
         from gemma_decoder_forward_amd.model import capture
         bd.g4_timer_enable(bd.KC[dom], 2 * steps)
         graph = capture(step)
