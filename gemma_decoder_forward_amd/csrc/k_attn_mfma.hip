@@ -594,19 +594,18 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl
   bf16x8_t pb[NPV];
   auto smax_step = [&](int st) {
     if (st == 0) {
+      // the maximum of the unscaled scores (sl2 > 0: the host takes only positive scales here); the
+      // scale rides in the exponential's fused multiply-add
       mt = -INFINITY;
       if (full) {
 #pragma unroll
-        for (int r = 0; r < NE; ++r) {
-          sc[r] *= sl2;
-          mt = fmaxf(mt, sc[r]);
-        }
+        for (int r = 0; r < NE; ++r) mt = fmaxf(mt, sc[r]);
       } else {
 #pragma unroll
         for (int r = 0; r < NE; ++r) {
           const int kk = kt + 16 * (r >> 2) + 4 * qq + (r & 3);
           const bool vis = kk >= vlo && kk <= vhi;
-          const float x = vis ? sc[r] * sl2 : -INFINITY;
+          const float x = vis ? sc[r] : -INFINITY;
           sc[r] = x;
           mt = fmaxf(mt, x);
         }
@@ -614,7 +613,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl
     } else if (st == 1) {
       mt = at_max_xor16(mt);
     } else if (st == 2) {
-      mt = at_max_xor32(mt);
+      mt = at_max_xor32(mt) * sl2;
       // lazy reference, as in k_attn_mfma: raised only when the tile exceeds it by more than 32 (log2)
       raise = mt > m_run + 32.f;
       m_new = raise ? mt : m_run;
@@ -624,7 +623,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl
 #pragma unroll
       for (int r = 0; r < NE; ++r)
         if (3 + r * (KS - 3) / NE == st) {
-          const float pr = __builtin_amdgcn_exp2f(sc[r] - m_use);
+          const float pr = __builtin_amdgcn_exp2f(fmaf(sc[r], sl2, -m_use));
           psum += pr;
           pb[r / 8][r % 8] = (__bf16)pr;
         }
@@ -915,19 +914,18 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16p(AttnArgs a, int G, float s
   bf16x8_t pb[NPV];
   auto smax_step = [&](int st) {
     if (st == 0) {
+      // the maximum of the unscaled scores (sl2 > 0: the host takes only positive scales here); the
+      // scale rides in the exponential's fused multiply-add
       mt = -INFINITY;
       if (full) {
 #pragma unroll
-        for (int r = 0; r < NE; ++r) {
-          sc[r] *= sl2;
-          mt = fmaxf(mt, sc[r]);
-        }
+        for (int r = 0; r < NE; ++r) mt = fmaxf(mt, sc[r]);
       } else {
 #pragma unroll
         for (int r = 0; r < NE; ++r) {
           const int kk = kt + 16 * (r >> 2) + 4 * qq + (r & 3);
           const bool vis = kk >= vlo && kk <= vhi;
-          const float x = vis ? sc[r] * sl2 : -INFINITY;
+          const float x = vis ? sc[r] : -INFINITY;
           sc[r] = x;
           mt = fmaxf(mt, x);
         }
@@ -935,7 +933,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16p(AttnArgs a, int G, float s
     } else if (st == 1) {
       mt = at_max_xor16(mt);
     } else if (st == 2) {
-      mt = at_max_xor32(mt);
+      mt = at_max_xor32(mt) * sl2;
       raise = mt > m_run + 32.f;
       m_new = raise ? mt : m_run;
       m_use = m_new == -INFINITY ? 0.f : m_new;
@@ -944,7 +942,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16p(AttnArgs a, int G, float s
 #pragma unroll
       for (int r = 0; r < NE; ++r)
         if (3 + r * (KS - 3) / NE == st) {
-          const float pr = __builtin_amdgcn_exp2f(sc[r] - m_use);
+          const float pr = __builtin_amdgcn_exp2f(fmaf(sc[r], sl2, -m_use));
           psum += pr;
           pb[r / 8][r % 8] = (__bf16)pr;
         }
@@ -1253,6 +1251,8 @@ size_t attn_prefill_ws(int64_t B, int64_t T, int64_t nh, int64_t nkv, int64_t hd
 // bf16, head_dim 128/256/512, groups of 1, 2, 4 or 8 query heads per kv head, 16-byte aligned rows.
 bool attn_mfma(const AttnArgs& a, hipStream_t s, g4_status* st) {
   if ((a.q_ld | a.out_ld) & 7) return false;
+  // the 16-query kernels take the maximum of the unscaled scores: positive, finite scales only
+  if (a.hd != 128 && !(a.scale > 0.f && a.scale < INFINITY)) return false;
   if (((uintptr_t)a.q | (uintptr_t)a.k | (uintptr_t)a.v | (uintptr_t)a.out) & 15) return false;
   int nblk = 0;
   AtSplit sp{};

@@ -138,6 +138,31 @@ def test_attention_prefill_vs_oracle(dt, hd, sliding, window, nh, nkv):
         assert_close(out.reshape(B, T, nh, hd)[b], ref, dt, f"seq {b}")
 
 
+@pytest.mark.parametrize("scale", [0.0625, 0.0, -0.5])
+@pytest.mark.parametrize("hd,sliding,window,nh,nkv", [(256, 1, 100, 8, 2), (512, 0, 0, 8, 2)])
+def test_attention_prefill_score_scale(hd, sliding, window, nh, nkv, scale):
+    """g4_attn_prefill with a score scale other than the layers' 1.0: the matrix-core kernels fold a
+    positive scale into the exponential (the maximum is taken over the unscaled scores); zero and negative
+    scales go to the generic kernel. Against the oracle with the same scale."""
+    log(f"attn_prefill scale={scale} hd={hd}")
+    B, T, cap = 2, 77, 700
+    pos0_l = [0, 600]
+    pos0 = torch.tensor(pos0_l, dtype=torch.int32, device="cuda")
+    q = randn((B * T, nh * hd), 70 + hd, torch.bfloat16)
+    K = randn((B, nkv, cap, hd), 71, torch.bfloat16)
+    V = randn((B, nkv, cap, hd), 72, torch.bfloat16)
+    out = torch.empty((B * T, nh * hd), dtype=torch.bfloat16, device="cuda")
+    t = _kv_table([(K, V, sliding)])
+    bd.g4_attn_prefill(q.data_ptr(), nh * hd, t, 1, 0, 0, sliding, window, pos0.data_ptr(), B, T, nh, nkv, hd, scale,
+                       out.data_ptr(), nh * hd, None, 0, bd.G4_BF16, stream())
+    torch.cuda.synchronize()
+    qv = O.f64(q).reshape(B, T, nh, hd)
+    pos = O.prefill_positions(pos0_l, T)
+    for b in range(B):
+        ref = O.attention(qv[b], O.f64(K[b]), O.f64(V[b]), pos[b], window if sliding else None, scale=scale)
+        assert_close(out.reshape(B, T, nh, hd)[b], ref, "bf16", f"seq {b}")
+
+
 @pytest.mark.parametrize("hd,sliding,window", [(64, 1, 7), (64, 0, 0), (256, 1, 33), (128, 0, 0), (512, 1, 21)])
 def test_attention_mask_probe_bit_exact(hd, sliding, window):
     """q = 0 gives uniform weights; V_j = onehot(j mod hd) makes round(o * n) the mask row."""
