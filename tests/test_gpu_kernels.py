@@ -238,7 +238,7 @@ def test_attention_prefill_long_e4b_shapes(hd, sliding, W, nkv, with_ws):
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("hd,sliding,window,nh,nkv", [(64, 1, 32, 4, 1), (512, 0, 0, 8, 2), (256, 1, 512, 8, 2),
-                                                      (128, 0, 0, 4, 2)])
+                                                      (128, 0, 0, 4, 2), (512, 0, 0, 8, 1)])
 def test_attention_decode_vs_oracle(dt, hd, sliding, window, nh, nkv):
     log(f"attn_decode {dt} hd={hd} sliding={sliding}")
     gdt, tdt = DT[dt]
