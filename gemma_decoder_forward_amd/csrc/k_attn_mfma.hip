@@ -1,8 +1,9 @@
 // Flash-style prefill attention on the CDNA4 matrix cores (bf16 operands, float32 softmax and
 // accumulation), causal with an optional sliding window or with the encoder's non-causal mask (key_span),
 // GQA groups sharing every K/V tile.
-// Two kernels: k_attn_w16 (16-query waves, head dims 256 and 512, described before it) and
-// k_attn_mfma (32-query waves, head dim 128), described here.
+// Three kernels: k_attn_w16 (16-query waves, head dim 256) and k_attn_w16p (its head-dim-512 form
+// with the two waves of a query group sharing P), each described before it, and k_attn_mfma (32-query
+// waves, head dim 128), described here.
 //
 // Block = 4 waves. A "query group" is one head x 32 consecutive tokens; each wave owns one, and the
 // block's four groups (the heads of one kv group for G = 4) share every K/V tile. For head dim 512 a
@@ -742,6 +743,18 @@ __global__ __launch_bounds__(512, 1) void k_attn_w16(AttnArgs a, int G, float sl
   }
 }
 
+// --------------------------------------------------------------------------------------------
+// k_attn_w16p: k_attn_w16's blocks, tiles and pipeline at head dim 512, with the two waves of a query
+// group (32 tokens x one head, 16 queries each) splitting the head elements of O instead of the
+// queries. Each wave computes S and the softmax of its own 16 queries as in k_attn_w16, publishes its
+// P (bf16), its per-query rescale factors and whether it raised its maximum to a double-buffered
+// exchange in LDS, and after the block barrier reads its partner's. Its O accumulators hold head
+// elements hf HD/2 .. hf HD/2 + HD/2 - 1 (hf = wave & 1) for both waves' queries (HD/32 + HD/32
+// blocks, the same 128 registers as O of 16 queries over the whole head), so every V^T fragment read
+// from LDS feeds two MFMAs (own P, partner's P): half the V reads of k_attn_w16 per MFMA. The partner's
+// O half is rescaled only when the partner raised its maximum. At the end the normalisers are swapped
+// through LDS and each wave writes its half of both queries' rows (the m and l of a split part come
+// from the query's own wave).
 template <int HD, bool RING>
 __global__ __launch_bounds__(512, 1) void k_attn_w16p(AttnArgs a, int G, float sl2, AtSplit sp) {
   using L = AttnLdsW<HD>;
