@@ -472,8 +472,8 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): this build "
-              "measures the single-GPU forward; sharding is a design note, not implemented.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): the library "
+              "implements the single-GPU forward; sharding across GPUs is described, not implemented.", file=sys.stderr)
         sys.exit(2)
     from synth import configs
     cfg = workload(args.workload, args.batch)

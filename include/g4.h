@@ -37,7 +37,7 @@ typedef enum g4_status {
   G4_EGEOM = 2,  /* inconsistent geometry: kv_src routing, head-dim or attention-type mismatch */
   G4_ERANGE = 3, /* a size beyond a capacity: T > cap, window < 1, dims beyond kernel limits */
   G4_EHIP = 4,   /* a HIP runtime call or kernel launch failed (see g4_last_error) */
-  G4_EUNSUP = 5  /* a combination this build does not implement */
+  G4_EUNSUP = 5  /* a combination the library does not implement */
 } g4_status;
 
 typedef enum g4_dtype { G4_F32 = 0, G4_BF16 = 1 } g4_dtype;

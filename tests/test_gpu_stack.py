@@ -351,7 +351,7 @@ def test_decode_stack_matches_layer_by_layer(B):
 
 # ------------------------------------------------------------------------------- per-layer dump
 def test_per_layer_dump(tmp_path, monkeypatch):
-    """The driver's per-layer dump (G4_DUMP): the hidden state before and after every layer and each
+    """The model driver's per-layer dump (G4_DUMP): the hidden state before and after every layer and each
     owning layer's new K/V rows, float32 little-endian. The hidden-state files equal the same layers run
     one call at a time (bit for bit: the dump makes exactly those calls), the K/V files equal the caches'
     rows at the call's positions (two sequences at different positions), a layer that reads another
