@@ -195,15 +195,15 @@ def run_gpu(cfg, layers, glob, steps, warmup, breakdown, use_graph=True):
         mode = bd.G4_ENCODE if cfg["mode"] == "encode" else bd.G4_PREFILL
     H = cfg["hidden"]
     h = torch.empty((B, T, H), dtype=torch.float32, device="cuda")
-    ple = None if cfg["embed"] else acts["ple_in"]
+    if cfg["embed"]:
+        ple = torch.empty((B, T, cfg["n_layers"], cfg["ple_dim"]), dtype=torch.float32, device="cuda")
+    else:
+        ple = acts["ple_in"]
     model.workspace(B, T, cap, mode)
 
     def step():
-        nonlocal ple
         if cfg["embed"]:
-            e, p = model.embed(acts["ids"])
-            h.copy_(e)
-            ple = p
+            model.embed(acts["ids"], h, ple)  # the entry writes h0 and the per-layer inputs in place
         else:
             h.copy_(acts["h0"])
         model.forward(h, ple, acts["pos"], table, cap, mode)

@@ -102,13 +102,19 @@ class G4Model:
             self._ws = torch.empty(need, dtype=torch.uint8, device="cuda")
         return self._ws
 
-    def embed(self, ids):
-        """ids int32 [B, T] (device) -> (h0 float32 [B, T, H], ple_in float32 [B, T, L, d])."""
+    def embed(self, ids, h=None, ple=None):
+        """ids int32 [B, T] (device) -> (h0 float32 [B, T, H], ple_in float32 [B, T, L, d]), written into
+        h and ple when given (contiguous float32 tensors of those shapes), else into new tensors."""
         B, T = ids.shape
         M = B * T
         H, L, d = self.cfg["hidden"], self.L, self.cfg["ple_dim"]
-        h = torch.empty((B, T, H), dtype=torch.float32, device="cuda")
-        ple = torch.empty((B, T, L, d), dtype=torch.float32, device="cuda")
+        if h is None:
+            h = torch.empty((B, T, H), dtype=torch.float32, device="cuda")
+        if ple is None:
+            ple = torch.empty((B, T, L, d), dtype=torch.float32, device="cuda")
+        for t, shape in ((h, (B, T, H)), (ple, (B, T, L, d))):
+            if tuple(t.shape) != shape or t.dtype != torch.float32 or not t.is_contiguous():
+                raise ValueError(f"embed output must be a contiguous float32 tensor of shape {shape}")
         ws = self.workspace(B, T, 1, bd.G4_PREFILL)
         g = self.glob
         bd.g4_embed_ple(ids.data_ptr(), M, g["embed"].data_ptr(), g["ple_embed"].data_ptr(),
