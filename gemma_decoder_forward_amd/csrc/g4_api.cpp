@@ -322,28 +322,33 @@ static bool stage_from_parts(int64_t M, int64_t Kc, int64_t Nc, int parts, int r
   return bytes <= 16e6;
 }
 
-// A few-row product above 16 rows on the tiled kernel, K split into float32 slices [slice][M][N] of the
-// stacked matrices' rows: about 256 (128-wide tile, K slice) pairs, and no more slices than `out` holds.
-// The few-row kernel re-stages the activations for every 16 or 64 weight rows, as many bytes as it
-// streams at 64 rows; with a single K range the tiled kernel would have only N / 128 tiles. Returns false,
+// A few-row product above 16 rows on the tiled kernel (one 64-row tile over the token rows), K split into
+// float32 slices [slice][M][N] of the stacked matrices' rows: about 256 (tile, K slice) pairs, slices of
+// at least 256 k, none empty, and no more slices than `out` holds. The few-row kernel re-stages the
+// activations for every 16 or 64 weight rows, as many bytes as it streams at 64 rows. Returns false,
 // with nothing launched, when the tiled kernel does not take the shape.
 static bool tiled_slices(const void* A, int64_t lda, const void* const* segs, const int64_t* rows, int nseg,
                          int64_t ldb, int64_t M, int64_t K, float* out, size_t out_bytes, int* slices,
                          hipStream_t s, g4_status* st) {
   int64_t N = 0;
   for (int i = 0; i < nseg; ++i) N += rows[i];
-  const int64_t tiles = (N + 127) / 128;
-  int64_t sd = 256 / tiles < K / 256 ? 256 / tiles : K / 256;
-  if (sd < 1) sd = 1;
-  while (sd > 1 && (size_t)sd * M * N * 4 > out_bytes) --sd;
-  if ((size_t)sd * M * N * 4 > out_bytes) return false;
   GemmArgs ga{};
   ga.A = A; ga.lda = lda; ga.B = segs[0]; ga.ldb = ldb; ga.C = out; ga.ldc = N; ga.c_dtype = G4_F32;
-  ga.M = M; ga.N = N; ga.K = K; ga.epi = EPI_STORE; ga.splits = (int32_t)sd; ga.split_stride = M * N;
+  ga.M = M; ga.N = N; ga.K = K; ga.epi = EPI_STORE; ga.splits = 1; ga.split_stride = M * N;
   if (nseg > 1) {
     ga.nseg = nseg;
     for (int i = 0; i < nseg; ++i) { ga.segB[i] = segs[i]; ga.seg_rows[i] = rows[i]; }
   }
+  const int cols = gemm_rows64_cols(ga);
+  if (cols == 0) return false;
+  const int64_t tiles = N / cols;
+  int64_t sd = 256 / tiles < K / 256 ? 256 / tiles : K / 256;
+  if (sd < 1) sd = 1;
+  const int64_t kper = ((K + sd - 1) / sd + 63) / 64 * 64;  // the kernel's slice length
+  sd = (K + kper - 1) / kper;                               // so that no slice is empty
+  while (sd > 1 && (size_t)sd * M * N * 4 > out_bytes) --sd;
+  if ((size_t)sd * M * N * 4 > out_bytes) return false;
+  ga.splits = (int32_t)sd;
   if (!gemm_mfma(ga, s, st)) return false;
   *slices = (int)sd;
   return true;
@@ -502,16 +507,27 @@ static g4_status few_row_layer(const LayerCtx& c) {
     TimedScope ts(G4_KC_ROW_TAIL, c.s);
     G4_TRY(rownorm(Y, G4_F32, s4, M * H, l->post_ffn_norm, nullptr, c.h, 1.f, nullptr, hb, M, H, m->eps, dt, c.s));
   }
-  // PLE: gate partials from the raw residual; the projection forms gelu_tanh(gate) * ple_in while staging
+  // PLE: gate partials from the raw residual; up to 16 rows the projection forms gelu_tanh(gate) * ple_in
+  // while staging. Above 16 rows both products run on the tiled kernel with a finishing pass between
+  // them: each few-row projection block would re-form 64 x 256 activations from every gate slice, ten
+  // times its own weight bytes (64 rows, 42 layers: 0.82 against 1.11 ms per step; no change at 32).
   int s5 = 0, s6 = 0;
   {
     TimedScope ts(G4_KC_PLE_GEMM, c.s);
-    SkA sa{};
-    sa.a = hb; sa.lda = H; sa.kind = SKA_BF16;
-    G4_TRY(gemm_skinny_part(sa, M, H, wpg, rd, 1, H, X, XB, &s5, c.s));
+    bool gate_tiled = false;
+    if (M > 16) {
+      g4_status mst = G4_OK;
+      gate_tiled = tiled_slices(hb, H, wpg, rd, 1, H, M, H, X, XB, &s5, c.s, &mst);
+      if (gate_tiled) G4_TRY(mst);
+    }
+    if (!gate_tiled) {
+      SkA sa{};
+      sa.a = hb; sa.lda = H; sa.kind = SKA_BF16;
+      G4_TRY(gemm_skinny_part(sa, M, H, wpg, rd, 1, H, X, XB, &s5, c.s));
+    }
     const float* ple_l = c.ple_in + (int64_t)c.layer * d;
     SkA sb{};
-    if (stage_from_parts(M, d, H, s5, 1)) {
+    if (M <= 16 && stage_from_parts(M, d, H, s5, 1)) {
       sb.a = X; sb.lda = d; sb.kind = SKA_GELU_MUL; sb.parts = s5; sb.part_stride = M * d;
       sb.aux = ple_l; sb.aux_ld = m->n_layers * d;
     } else {
@@ -521,7 +537,13 @@ static g4_status few_row_layer(const LayerCtx& c) {
       G4_TRY(gemm_skinny_finish(ga, X, s5, d, c.s));
       sb.a = gm; sb.lda = d; sb.kind = SKA_BF16;
     }
-    G4_TRY(gemm_skinny_part(sb, M, d, wpp, rH, 1, d, Y, YB, &s6, c.s));
+    bool proj_tiled = false;
+    if (M > 16) {
+      g4_status mst = G4_OK;
+      proj_tiled = tiled_slices(gm, d, wpp, rH, 1, d, M, d, Y, YB, &s6, c.s, &mst);
+      if (proj_tiled) G4_TRY(mst);
+    }
+    if (!proj_tiled) G4_TRY(gemm_skinny_part(sb, M, d, wpp, rH, 1, d, Y, YB, &s6, c.s));
   }
   {
     TimedScope ts(G4_KC_ROW_TAIL, c.s);

@@ -1,10 +1,11 @@
 // bf16 GEMM on the CDNA4 matrix cores: C = A B^T, A [M,K] and B [N,K] row-major (K contiguous),
 // float32 accumulation with v_mfma_f32_32x32x16_bf16.
 //
-// Block: NW waves in an (NW/2) x 2 grid; a wave owns a (BM/(NW/2)) x (BN/2) sub-tile made of 32x32
-// MFMA blocks. The 256x256 tile runs 8 waves (two per SIMD, 64x128 each), so one wave's MFMAs cover
-// the other's waits; the 128x128 tile runs 4. K advances in steps of BK (one BK*2-byte row segment
-// per tile row, BK/16 MFMA k-slices).
+// Block: NW waves in a WGM x (NW/WGM) grid (by default (NW/2) x 2); a wave owns a (BM/WGM) x
+// (BN/(NW/WGM)) sub-tile made of 32x32 MFMA blocks. The 256x256 tile runs 8 waves (two per SIMD,
+// 64x128 each), so one wave's MFMAs cover the other's waits; the 128x128 tile runs 4. The 64-row tiles
+// serve 17 to 64 token rows (batched decode), where the weight stream, not the MFMAs, sets the pace.
+// K advances in steps of BK (one BK*2-byte row segment per tile row, BK/16 MFMA k-slices).
 //
 // Operand staging: buffer loads write straight into LDS (buffer_load_dwordx4 ... lds), so no registers
 // hold staged data. One wave load instruction fills 1 KB of a stage: 1024 / (2 BK) tile rows. Global
@@ -113,12 +114,14 @@ __device__ __forceinline__ void lds_dma16(const rsrc_t& r, uint32_t voff, uint32
 
 // SEGB: every B load group (RPI rows) gets its own descriptor at its first row, so a tile may straddle
 // the boundary between two stacked B matrices (segments a multiple of RPI rows long).
-template <int BM, int BN, int NW, int BK, int NS, int EPI, bool CF32, bool SEGB = false>
+template <int BM, int BN, int NW, int BK, int NS, int EPI, bool CF32, bool SEGB = false, int WGM = NW / 2>
 __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a, int tiles_m, int tiles_n) {
-  constexpr int WM = BM / (NW / 2), WN = BN / 2;  // waves in a (NW/2) x 2 grid
+  constexpr int WGN = NW / WGM;                  // waves in a WGM x WGN grid
+  constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int FM = WM / 32, FN = WN / 32;
   constexpr int NMF = FM * FN;                  // MFMAs per wave per k-slice
   constexpr int NRD = FM + FN;                  // fragment reads per wave per k-slice
+  constexpr int NQ = NMF > NRD ? NMF : NRD;     // issue slots per k-slice (reads past the MFMAs follow them)
   constexpr int KS = BK / 16;                   // k-slices per step
   constexpr int CPR = BK / 8, RPI = 64 / CPR;   // 16-byte chunks per LDS row, rows per load instruction
   constexpr int AJ = BM / (RPI * NW), BJ = BN / (RPI * NW);  // load instructions per wave per step
@@ -127,7 +130,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a, int tiles_
   static_assert(EPI != EPI_GEGLU || RPI == 8 || RPI == 16, "gate/up blocks of one load instruction's rows");
   static_assert((NW == 4 || NW == 8) && AJ * RPI * NW == BM && BJ * RPI * NW == BN, "loader covers the tile");
   static_assert(KS % 2 == 0 && MF_KMIN % BK == 0, "k-slices alternate two register sets");
-  static_assert(NRD <= NMF, "every fragment read rides behind an MFMA");
+  static_assert(WGM * WGN == NW && FM >= 1 && FN >= 1 && WM == 32 * FM && WN == 32 * FN, "wave grid");
   static_assert(!SEGB || EPI == EPI_STORE, "segmented B rows: plain store epilogue");
   static_assert((NS - 1) * LG <= 63 && NS >= 2, "vmcnt range");
   static_assert(NS * STAGE * 2 <= 160 * 1024, "LDS");
@@ -135,7 +138,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a, int tiles_
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (feeds the LDS base in M0)
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   const int per_split = tiles_m * tiles_n, total = per_split * a.splits;
   const int64_t kper = ((a.K + a.splits - 1) / a.splits + BK - 1) / BK * BK;  // split-K range length
 
@@ -364,8 +367,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a, int tiles_
 #pragma unroll
       for (int ks = 0; ks < KS - 1; ++ks) {
 #pragma unroll
-        for (int q = 0; q < NMF; ++q) {
-          mf(ks & 1, q);
+        for (int q = 0; q < NQ; ++q) {
+          if (q < NMF) mf(ks & 1, q);
           if (q < NRD) rd((ks + 1) & 1, ks + 1, st, q);
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -377,14 +380,16 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a, int tiles_
       // step), then the loads that refill the stage just released with step kt + NS (behind the last
       // LG MFMAs, or spread over all of them when there are more loads than MFMAs)
 #pragma unroll
-      for (int q = 0; q < NMF; ++q) {
-        mf(1, q);
+      for (int q = 0; q < NQ; ++q) {
+        if (q < NMF) mf(1, q);
         if (q < NRD) rd(0, 0, st1, q);
-        if (LG <= NMF) {
-          if (q >= NMF - LG) dma(kt + NS, q - (NMF - LG));
-        } else {
+        if (q < NMF) {
+          if (LG <= NMF) {
+            if (q >= NMF - LG) dma(kt + NS, q - (NMF - LG));
+          } else {
 #pragma unroll
-          for (int l = q * LG / NMF; l < (q + 1) * LG / NMF; ++l) dma(kt + NS, l);
+            for (int l = q * LG / NMF; l < (q + 1) * LG / NMF; ++l) dma(kt + NS, l);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -435,22 +440,22 @@ static int resident_blocks(const void* k, int threads) {
   return cus * per_cu;
 }
 
-template <int BM, int BN, int NW, int BK, int NS, int EPI, bool CF32, bool SEGB = false>
+template <int BM, int BN, int NW, int BK, int NS, int EPI, bool CF32, bool SEGB = false, int WGM = NW / 2>
 static void launch_one(const GemmArgs& a, int tm, int tn, int total, bool persist, hipStream_t s) {
-  const void* k = (const void*)k_gemm_mfma<BM, BN, NW, BK, NS, EPI, CF32, SEGB>;
+  const void* k = (const void*)k_gemm_mfma<BM, BN, NW, BK, NS, EPI, CF32, SEGB, WGM>;
   int grid = total;
   if (persist) {
     const int res = resident_blocks(k, NW * 64);
     if (res > 0 && res < total) grid = res;
   }
-  hipLaunchKernelGGL((k_gemm_mfma<BM, BN, NW, BK, NS, EPI, CF32, SEGB>), dim3((unsigned)grid), dim3(NW * 64), 0, s, a,
-                     tm, tn);
+  hipLaunchKernelGGL((k_gemm_mfma<BM, BN, NW, BK, NS, EPI, CF32, SEGB, WGM>), dim3((unsigned)grid), dim3(NW * 64), 0,
+                     s, a, tm, tn);
 }
 
 // One launch walks every (split, tile) pair. When every split spans at least NS K-steps, the grid is
 // what fits on the device at once and each block walks several tiles, prefetching the next tile's
 // first steps under the current tile's last ones; otherwise each block takes one tile.
-template <int BM, int BN, int NW, int BK, int NS, bool SEGB = false>
+template <int BM, int BN, int NW, int BK, int NS, bool SEGB = false, int WGM = NW / 2>
 static g4_status launch_mfma(const GemmArgs& a, hipStream_t s) {
   const int ncols = a.epi == EPI_GEGLU ? BN / 2 : BN;
   const int tm = (int)((a.M + BM - 1) / BM), tn = (int)(a.N / ncols);
@@ -458,13 +463,39 @@ static g4_status launch_mfma(const GemmArgs& a, hipStream_t s) {
   const int64_t kper = ((a.K + a.splits - 1) / a.splits + BK - 1) / BK * BK;
   const int64_t last = a.K - (int64_t)(a.splits - 1) * kper;
   const bool persist = (last < kper ? last : kper) >= (int64_t)NS * BK;
-  if (SEGB && a.c_dtype == G4_F32) launch_one<BM, BN, NW, BK, NS, EPI_STORE, true, true>(a, tm, tn, total, persist, s);
-  else if (SEGB) launch_one<BM, BN, NW, BK, NS, EPI_STORE, false, true>(a, tm, tn, total, persist, s);
-  else if (a.epi == EPI_GEGLU) launch_one<BM, BN, NW, BK, NS, EPI_GEGLU, false>(a, tm, tn, total, persist, s);
-  else if (a.epi == EPI_GELU_MUL) launch_one<BM, BN, NW, BK, NS, EPI_GELU_MUL, false>(a, tm, tn, total, persist, s);
-  else if (a.c_dtype == G4_F32) launch_one<BM, BN, NW, BK, NS, EPI_STORE, true>(a, tm, tn, total, persist, s);
-  else launch_one<BM, BN, NW, BK, NS, EPI_STORE, false>(a, tm, tn, total, persist, s);
+  if constexpr (SEGB) {
+    if (a.c_dtype == G4_F32) launch_one<BM, BN, NW, BK, NS, EPI_STORE, true, true, WGM>(a, tm, tn, total, persist, s);
+    else launch_one<BM, BN, NW, BK, NS, EPI_STORE, false, true, WGM>(a, tm, tn, total, persist, s);
+  } else {
+    if (a.epi == EPI_GEGLU) launch_one<BM, BN, NW, BK, NS, EPI_GEGLU, false, false, WGM>(a, tm, tn, total, persist, s);
+    else if (a.epi == EPI_GELU_MUL) launch_one<BM, BN, NW, BK, NS, EPI_GELU_MUL, false, false, WGM>(a, tm, tn, total, persist, s);
+    else if (a.c_dtype == G4_F32) launch_one<BM, BN, NW, BK, NS, EPI_STORE, true, false, WGM>(a, tm, tn, total, persist, s);
+    else launch_one<BM, BN, NW, BK, NS, EPI_STORE, false, false, WGM>(a, tm, tn, total, persist, s);
+  }
   return check_launch("gemm_mfma");
+}
+
+// Up to 64 token rows (batched decode): one 64-row tile covers every token row, and the weights stream
+// once in whole 128-byte lines (K steps of 64) through four stages. Plain stores take 64 x 64 tiles
+// (2 x 2 waves of 32 x 32): the most tiles, so the most CUs pulling weights (at 64 rows, 42 decode
+// layers: q/k/v, o and down 1.71 ms per step against 1.77 with 64 x 128 tiles, 2.02 with 64 x 256 and
+// 2.13 with the 256-row tiles). The gated product takes 64 x 128 tiles (64 outputs, 2 x 2 waves of
+// 32 x 64): 1.52 ms against 1.69 with 64 x 64 (twice the activation re-reads) and 1.76 with 128 x 128
+// tiles in K steps of 32. Deeper rings (five to eight stages) measured slower. Returns the output
+// columns per tile, 0 when the shape does not fit.
+int gemm_rows64_cols(const GemmArgs& a) {
+  if (a.M > 64) return 0;
+  if (a.epi == EPI_GEGLU && mfma_ok(a, 128)) return 64;
+  if (mfma_ok(a, 64)) return a.epi == EPI_GEGLU ? 32 : 64;
+  return 0;
+}
+
+static bool gemm_mfma_rows64(const GemmArgs& a, hipStream_t s, g4_status* st) {
+  const int cols = gemm_rows64_cols(a);
+  if (cols == 0) return false;
+  if (a.epi == EPI_GEGLU && cols == 64) *st = launch_mfma<64, 128, 4, 64, 4, false, 2>(a, s);
+  else *st = launch_mfma<64, 64, 4, 64, 4, false, 2>(a, s);
+  return true;
 }
 
 // Cost of a 256-row tiling in tile-passes over the CUs, weighted by the tile's width and its split's
@@ -515,13 +546,15 @@ int32_t gemm_pick_splits(int64_t M, int64_t N, int64_t K, int32_t max_splits) {
   return best;
 }
 
-// Picks a tile that gives enough blocks for 256 CUs; false if the shape does not suit the MFMA path.
+// Picks a tile that gives enough blocks for 256 CUs (up to 64 token rows, the 64-row tiles above); false
+// if the shape does not suit the MFMA path.
 // The gated product may take 256 x 320 tiles (160 outputs each) where they need fewer passes over the
 // CUs, counting a 320-wide tile as 1.25 of a 256-wide one: at 2048 token rows and 10240 outputs, 640
 // tiles of 256 x 256 take three passes of 256 CUs (the last half empty), 512 of 256 x 320 take two.
 // Plain stores choose among 256, 320, 192 and 128 wide tiles by the same count (tiling_cost).
 bool gemm_mfma(const GemmArgs& a, hipStream_t s, g4_status* st) {
   const int64_t cus = device_cus();
+  if (a.M <= 64 && gemm_mfma_rows64(a, s, st)) return true;
   if (a.epi == EPI_GEGLU) {
     const int64_t tiles256 = ((a.M + 255) / 256) * (a.N / 128) * a.splits;
     if (a.splits == 1 && mfma_ok(a, 320) && tiles256 >= 192) {

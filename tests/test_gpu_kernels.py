@@ -349,6 +349,44 @@ def test_linear_few_rows_weight_streaming(M, N, K):
     assert_close(Cb, ref, "bf16", "bf16 out")
 
 
+@pytest.mark.parametrize("M,N,K", [(17, 16384, 2560), (64, 20480, 640), (48, 16512, 512)])
+def test_linear_rows64_tiles(M, N, K):
+    """17 to 64 token rows on wide, short weights (at least 16384 rows, K <= 4096): one 64-row MFMA tile
+    over all token rows, 64 output columns per tile (16512 = 258 x 64 is not a whole number of wider
+    tiles); float32 and bf16 outputs."""
+    log(f"linear 64-row tiles {M}x{N}x{K}")
+    A = randn((M, K), 88, torch.bfloat16)
+    W = randn((N, K), 89, torch.bfloat16, 0.02)
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    Cb = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    bd.g4_linear(A.data_ptr(), W.data_ptr(), C.data_ptr(), M, N, K, bd.G4_F32, bd.G4_BF16, None, 0, stream())
+    bd.g4_linear(A.data_ptr(), W.data_ptr(), Cb.data_ptr(), M, N, K, bd.G4_BF16, bd.G4_BF16, None, 0, stream())
+    torch.cuda.synchronize()
+    ref = O.f64(A) @ O.f64(W).T
+    assert max_rel(C, ref) <= 1e-3
+    assert_close(Cb, ref, "bf16", "bf16 out")
+
+
+@pytest.mark.parametrize("M,H,F", [(40, 2560, 10240), (23, 256, 8224)])
+def test_ffn_geglu_rows64(M, H, F):
+    """17 to 64 token rows: the gate/up product on 64-row tiles with the gated epilogue, 64 outputs per
+    tile (E4B widths: 160 tiles), or 32 when F is not a multiple of 64 (8224 = 257 x 32); then the down
+    projection."""
+    log(f"ffn geglu {M} rows H={H} F={F}")
+    x = randn((M, H), 90, torch.bfloat16)
+    wg, wu = randn((F, H), 91, torch.bfloat16, 0.02), randn((F, H), 92, torch.bfloat16, 0.02)
+    wd = randn((H, F), 93, torch.bfloat16, 0.02)
+    out = torch.empty((M, H), dtype=torch.float32, device="cuda")
+    wsb = bd.g4_ffn_geglu_ws(M, H, F, bd.G4_BF16)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    bd.g4_ffn_geglu(x.data_ptr(), wg.data_ptr(), wu.data_ptr(), wd.data_ptr(), out.data_ptr(), M, H, F, ws.data_ptr(),
+                    wsb, bd.G4_BF16, stream())
+    torch.cuda.synchronize()
+    xv = O.f64(x)
+    ref = (O.gelu_tanh(xv @ O.f64(wg).T) * (xv @ O.f64(wu).T)) @ O.f64(wd).T
+    assert_close(out, ref, "bf16", f"ffn {M} rows")
+
+
 def _sample_rows(M):
     return sorted(set(list(range(24)) + list(range(M // 2 - 8, M // 2 + 8)) + list(range(M - 24, M))))
 
