@@ -322,9 +322,17 @@ static bool stage_from_parts(int64_t M, int64_t Kc, int64_t Nc, int parts, int r
   return bytes <= 16e6;
 }
 
-// A few-row product above 16 rows on the tiled kernel (one 64-row tile over the token rows), K split into
-// float32 slices [slice][M][N] of the stacked matrices' rows: about 256 (tile, K slice) pairs, slices of
-// at least 256 k, none empty, and no more slices than `out` holds. The few-row kernel re-stages the
+// Where the few-row layer leaves the few-row kernels (42-layer decode steps, tokens/s, against 16 rows
+// for the projections and 12 for the one-pass gate/up): q/k/v, o and down take the tiled kernel above
+// kTiledRows token rows (B = 4 944 -> 983, B = 8 1705 -> 1838, B = 12 2224 -> 2586, B = 16 2944 ->
+// 3288; tiling one or two rows was 8% slower), gate/up the one-pass few-row kernel up to kGatedRows
+// (the tiled gated product ties at 8 rows and wins from 12), and the PLE pair the tiled kernel above
+// kTiledPleRows (equal at 32 rows, ahead at 64).
+constexpr int64_t kTiledRows = 2, kGatedRows = 8, kTiledPleRows = 16;
+
+// A few-row product on the tiled kernel (one 64-row tile over the token rows), K split into float32
+// slices [slice][M][N] of the stacked matrices' rows: about 256 (tile, K slice) pairs, slices of at
+// least 256 k, none empty, and no more slices than `out` holds. The few-row kernel re-stages the
 // activations for every 16 or 64 weight rows, as many bytes as it streams at 64 rows. Returns false,
 // with nothing launched, when the tiled kernel does not take the shape.
 static bool tiled_slices(const void* A, int64_t lda, const void* const* segs, const int64_t* rows, int nseg,
@@ -392,7 +400,7 @@ static g4_status few_row_layer(const LayerCtx& c) {
     const void* segs[3] = {l->wq, l->wk, l->wv};
     const int64_t rows[3] = {nh * hd, nkv * hd, nkv * hd};
     g4_status mst = G4_OK;
-    if (M > 16 && tiled_slices(xn, H, segs, rows, nseg, H, M, H, X, XB, &s1, c.s, &mst)) {
+    if (M > kTiledRows && tiled_slices(xn, H, segs, rows, nseg, H, M, H, X, XB, &s1, c.s, &mst)) {
       G4_TRY(mst);
     } else {
       SkA sa{};
@@ -433,7 +441,7 @@ static g4_status few_row_layer(const LayerCtx& c) {
   {
     TimedScope ts(G4_KC_O_GEMM, c.s);
     g4_status mst = G4_OK;
-    if (M > 16 && tiled_slices(ao, nh * hd, wo, rH, 1, nh * hd, M, nh * hd, Y, YB, &s2, c.s, &mst)) {
+    if (M > kTiledRows && tiled_slices(ao, nh * hd, wo, rH, 1, nh * hd, M, nh * hd, Y, YB, &s2, c.s, &mst)) {
       G4_TRY(mst);
     } else {
       SkA sa{};
@@ -446,18 +454,19 @@ static g4_status few_row_layer(const LayerCtx& c) {
     G4_TRY(rownorm(Y, G4_F32, s2, M * H, l->post_attn_norm, nullptr, c.h, 1.f, l->pre_ffn_norm, xn, M, H, m->eps,
                    dt, c.s));
   }
-  // gate/up: up to 12 rows one weight-streaming pass writes the bf16 product; above that the tiled
-  // gated-product kernel does. Decode steps, 42 layers (gate/up ms per step, one pass / tiled): 1.18 /
-  // 1.58 at 4 rows, 1.23 / 1.59 at 8, 1.98 / 1.62 at 16; at 64 rows the split-K few-row form took 2.83
-  // against the tiled 1.77 (each few-row block re-stages as many activation bytes as it streams
-  // weights). Failing both, partials, whose gelu_tanh(gate) * up the down projection forms in its A.
+  // gate/up: up to kGatedRows one weight-streaming pass writes the bf16 product; above that the tiled
+  // gated-product kernel does. Decode steps, 42 layers (gate/up ms per step, one pass / 64-row tiles):
+  // 1.22 / 1.23 at 8 rows, 1.51 / 1.24 at 12; at 64 rows the split-K few-row form took 2.83 against
+  // 1.77 on 128-row tiles and 1.52 on 64-row ones (each few-row block re-stages as many activation
+  // bytes as it streams weights). Failing both, partials, whose gelu_tanh(gate) * up the down
+  // projection forms in its A.
   int s3 = 0, s4 = 0;
   bool gated = false;  // act holds the bf16 product
   {
     TimedScope ts(G4_KC_GATE_UP_GEMM, c.s);
     SkA sa{};
     sa.a = xn; sa.lda = H; sa.kind = SKA_BF16;
-    if (M <= 12 && skinny_gated_ok(M, H, F)) {
+    if (M <= kGatedRows && skinny_gated_ok(M, H, F)) {
       G4_TRY(gemm_skinny_gated(sa, M, H, l->w_gate, l->w_up, F, H, act, F, c.s));
       gated = true;
     } else {
@@ -481,9 +490,9 @@ static g4_status few_row_layer(const LayerCtx& c) {
   }
   {
     TimedScope ts(G4_KC_DOWN_GEMM, c.s);
-    // above 16 rows with the product in act: the tiled kernel, K split into slices the row tail sums
+    // with the product in act: the tiled kernel, K split into slices the row tail sums
     bool down_done = false;
-    if (gated && M > 16) {
+    if (gated && M > kTiledRows) {
       g4_status mst = G4_OK;
       down_done = tiled_slices(act, F, wd, rH, 1, F, M, F, Y, YB, &s4, c.s, &mst);
       if (down_done) G4_TRY(mst);
@@ -507,15 +516,16 @@ static g4_status few_row_layer(const LayerCtx& c) {
     TimedScope ts(G4_KC_ROW_TAIL, c.s);
     G4_TRY(rownorm(Y, G4_F32, s4, M * H, l->post_ffn_norm, nullptr, c.h, 1.f, nullptr, hb, M, H, m->eps, dt, c.s));
   }
-  // PLE: gate partials from the raw residual; up to 16 rows the projection forms gelu_tanh(gate) * ple_in
-  // while staging. Above 16 rows both products run on the tiled kernel with a finishing pass between
-  // them: each few-row projection block would re-form 64 x 256 activations from every gate slice, ten
-  // times its own weight bytes (64 rows, 42 layers: 0.82 against 1.11 ms per step; no change at 32).
+  // PLE: gate partials from the raw residual; up to kTiledPleRows the projection forms
+  // gelu_tanh(gate) * ple_in while staging. Above, both products run on the tiled kernel with a
+  // finishing pass between them: each few-row projection block would re-form 64 x 256 activations from
+  // every gate slice, ten times its own weight bytes (64 rows, 42 layers: 0.82 against 1.11 ms per step;
+  // no change at 32).
   int s5 = 0, s6 = 0;
   {
     TimedScope ts(G4_KC_PLE_GEMM, c.s);
     bool gate_tiled = false;
-    if (M > 16) {
+    if (M > kTiledPleRows) {
       g4_status mst = G4_OK;
       gate_tiled = tiled_slices(hb, H, wpg, rd, 1, H, M, H, X, XB, &s5, c.s, &mst);
       if (gate_tiled) G4_TRY(mst);
@@ -527,7 +537,7 @@ static g4_status few_row_layer(const LayerCtx& c) {
     }
     const float* ple_l = c.ple_in + (int64_t)c.layer * d;
     SkA sb{};
-    if (M <= 16 && stage_from_parts(M, d, H, s5, 1)) {
+    if (M <= kTiledPleRows && stage_from_parts(M, d, H, s5, 1)) {
       sb.a = X; sb.lda = d; sb.kind = SKA_GELU_MUL; sb.parts = s5; sb.part_stride = M * d;
       sb.aux = ple_l; sb.aux_ld = m->n_layers * d;
     } else {
@@ -538,7 +548,7 @@ static g4_status few_row_layer(const LayerCtx& c) {
       sb.a = gm; sb.lda = d; sb.kind = SKA_BF16;
     }
     bool proj_tiled = false;
-    if (M > 16) {
+    if (M > kTiledPleRows) {
       g4_status mst = G4_OK;
       proj_tiled = tiled_slices(gm, d, wpp, rH, 1, d, M, d, Y, YB, &s6, c.s, &mst);
       if (proj_tiled) G4_TRY(mst);

@@ -185,9 +185,11 @@ def test_bf16_stack_per_layer_parity(cid, T):
     assert_layers_within_floor(errs, floors, f"{cfg['name']} T={T}")
 
 
-@pytest.mark.parametrize("T", [1, 24, 48])
+@pytest.mark.parametrize("T", [1, 3, 12, 48])
 def test_bf16_few_row_prefill_per_layer(T):
-    """Prefills of at most 64 token rows take the few-row layer path (fused partial sums); E4B layer pair."""
+    """Prefills of at most 64 token rows take the few-row layer path (fused partial sums); E4B layer pair.
+    T = 1: the vector-ALU products; T = 3: projections on 64-row tiles, the one-pass gate/up; T = 12:
+    the tiled gated product too; T = 48: the tiled PLE pair too."""
     cfg = configs.get(2, T=T)
     model, layers, glob = build_model(cfg)
     acts = gen.activations(cfg, "cuda")
