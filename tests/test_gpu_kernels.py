@@ -83,6 +83,41 @@ def test_qk_norm_rope_token_major_and_cache(dt, hd, theta, nrot):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("hd,theta,nrot", [(256, 1e4, 128), (512, 1e6, 64)])
+def test_qk_norm_rope_long_prefill_rows(dt, hd, theta, nrot):
+    """A long prefill's rows (2 x 1027): against the oracle, bit for bit against one call per sequence,
+    and the cache rows bit for bit against the token-major output (every other cache row untouched)."""
+    log(f"qk_norm_rope long {dt} hd={hd}")
+    gdt, tdt = DT[dt]
+    B, T, heads, cap = 2, 1027, 2, 1100
+    pos_l = [5, 23]
+    pos0 = torch.tensor(pos_l, dtype=torch.int32, device="cuda")
+    x = randn((B * T, heads * hd), 13 + hd, tdt)
+    w = randn((hd,), 14, tdt, 0.1, 1.0)
+    y = torch.empty((B * T, heads * hd), dtype=tdt, device="cuda")
+    bd.g4_qk_norm_rope(x.data_ptr(), heads * hd, w.data_ptr(), y.data_ptr(), heads * hd, 0, pos0.data_ptr(), B, T,
+                       heads, hd, theta, nrot, 1e-6, gdt, stream())
+    y1 = torch.empty_like(y)
+    cache = torch.zeros((B, heads, cap, hd), dtype=tdt, device="cuda")
+    bd.g4_qk_norm_rope(x.data_ptr(), heads * hd, w.data_ptr(), cache.data_ptr(), 0, cap, pos0.data_ptr(), B, T,
+                       heads, hd, theta, nrot, 1e-6, gdt, stream())
+    for b in range(B):
+        xb, yb = x[b * T:(b + 1) * T], y1[b * T:(b + 1) * T]
+        bd.g4_qk_norm_rope(xb.data_ptr(), heads * hd, w.data_ptr(), yb.data_ptr(), heads * hd, 0,
+                           pos0[b:b + 1].data_ptr(), 1, T, heads, hd, theta, nrot, 1e-6, gdt, stream())
+    torch.cuda.synchronize()
+    assert torch.equal(y, y1)
+    xv = O.f64(x).reshape(B, T, heads, hd)
+    pos = O.prefill_positions(pos_l, T)
+    ref = O.rope(O.rms_norm(xv, w, 1e-6), pos[:, :, None], O.inv_freq(hd, theta, nrot))
+    assert_close(y.reshape(B, T, heads, hd), ref, dt, "token-major")
+    c = cache.cpu()
+    for b in range(B):
+        assert torch.equal(c[b, :, pos_l[b]:pos_l[b] + T, :], y.cpu()[b * T:(b + 1) * T].reshape(T, heads, hd).permute(1, 0, 2))
+        assert not c[b, :, :pos_l[b], :].any() and not c[b, :, pos_l[b] + T:, :].any()
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_rope_zero_frequency_tail_is_exact_identity(dt):
     gdt, tdt = DT[dt]
     hd, nrot, heads, T = 512, 64, 8, 33
