@@ -216,10 +216,12 @@ def run_gpu(cfg, layers, glob, steps, warmup, breakdown, use_graph=True):
     if decode and use_graph:
         # A decode step is hundreds of short kernels: it is captured once as a HIP graph and replayed.
         # The gate/up launch time comes from capture()'s warm-up step, whose launches are eager (on a side
-        # stream, an event pair around each of the first 2*steps gate/up launches, which fills the timer),
+        # stream, an event pair around each of its first min(2*steps, layers) gate/up launches),
         # so it includes each launch's dispatch gap; the replayed graph records no events.
         from gemma_decoder_forward_amd.model import capture
-        bd.g4_timer_enable(bd.KC[dom], 2 * steps)
+        # at most one step's gate/up launches, so that the warm-up step fills the timer and no event is
+        # recorded into the graph
+        bd.g4_timer_enable(bd.KC[dom], min(2 * steps, cfg["n_layers"]))
         graph = capture(step)
         run = graph.replay
         for _ in range(warmup):

@@ -408,25 +408,44 @@ static g4_status few_row_layer(const LayerCtx& c) {
       G4_TRY(gemm_skinny_part(sa, M, H, segs, rows, nseg, H, X, XB, &s1, c.s));
     }
   }
-  {
-    TimedScope ts(G4_KC_QK_NORM_ROPE, c.s);
-    HeadSeg segs[3];
-    int ns = 0;
-    segs[ns++] = HeadSeg{X, Nq, l->q_norm, qkv, qld, 0, (int32_t)nh, 1};
-    if (own) {
-      const g4_kv_entry& e = c.kv[c.layer];
-      segs[ns++] = HeadSeg{X + nh * hd, Nq, l->k_norm, e.k, 0, e.cap, (int32_t)nkv, 1, e.ring};
-      segs[ns++] = HeadSeg{X + (vk ? nh : nh + nkv) * hd, Nq, nullptr, e.v, 0, e.cap, (int32_t)nkv, 0, e.ring};
-    }
-    G4_TRY(qk_norm_rope_parts(segs, ns, s1, M * Nq, c.pos, c.B, c.T, hd, sliding ? m->theta_swa : m->theta_full,
-                              rot_pairs(m, sliding), m->eps, dt, c.s));
+  const g4_kv_entry& src = c.kv[l->kv_src];
+  AttnArgs aa{};
+  aa.q = qkv; aa.q_ld = qld; aa.k = src.k; aa.v = src.v; aa.cap = src.cap; aa.pos0 = c.pos;
+  aa.B = c.B; aa.T = c.T; aa.nh = nh; aa.nkv = nkv; aa.hd = hd; aa.sliding = sliding; aa.window = m->window;
+  aa.scale = 1.f; aa.out = ao; aa.out_ld = nh * hd; aa.ring = src.ring; aa.bidir = c.mode == G4_ENCODE;
+  const float theta = sliding ? m->theta_swa : m->theta_full;
+  // decode: the attention launch forms q, and on a layer that owns its cache the new key's k and v, from
+  // the partials itself (one launch fewer per layer); otherwise the head-norm kernel writes q and the
+  // cache rows first
+  bool fused = false;
+  if (c.mode == G4_DECODE && dt == G4_BF16) {
+    DecFuse f{};
+    f.x = X; f.x_ld = Nq; f.part_stride = M * Nq; f.parts = s1;
+    f.q_off = 0;
+    f.k_off = own ? nh * hd : -1;
+    f.v_off = own ? (vk ? nh : nh + nkv) * hd : -1;
+    f.qw = (const bf16*)l->q_norm; f.kw = (const bf16*)l->k_norm;
+    f.n_rot = (int32_t)rot_pairs(m, sliding); f.eps = m->eps;
+    rope_table(f.tab, theta, hd, f.n_rot);
+    TimedScope ts(G4_KC_ATTENTION, c.s);
+    g4_status mst = G4_OK;
+    fused = attn_decode_fused(aa, f, c.ws + c.p->dec, c.p->fx - c.p->dec, c.s, &mst);
+    if (fused) G4_TRY(mst);
   }
-  {
-    const g4_kv_entry& src = c.kv[l->kv_src];
-    AttnArgs aa{};
-    aa.q = qkv; aa.q_ld = qld; aa.k = src.k; aa.v = src.v; aa.cap = src.cap; aa.pos0 = c.pos;
-    aa.B = c.B; aa.T = c.T; aa.nh = nh; aa.nkv = nkv; aa.hd = hd; aa.sliding = sliding; aa.window = m->window;
-    aa.scale = 1.f; aa.out = ao; aa.out_ld = nh * hd; aa.ring = src.ring; aa.bidir = c.mode == G4_ENCODE;
+  if (!fused) {
+    {
+      TimedScope ts(G4_KC_QK_NORM_ROPE, c.s);
+      HeadSeg segs[3];
+      int ns = 0;
+      segs[ns++] = HeadSeg{X, Nq, l->q_norm, qkv, qld, 0, (int32_t)nh, 1};
+      if (own) {
+        const g4_kv_entry& e = c.kv[c.layer];
+        segs[ns++] = HeadSeg{X + nh * hd, Nq, l->k_norm, e.k, 0, e.cap, (int32_t)nkv, 1, e.ring};
+        segs[ns++] = HeadSeg{X + (vk ? nh : nh + nkv) * hd, Nq, nullptr, e.v, 0, e.cap, (int32_t)nkv, 0, e.ring};
+      }
+      G4_TRY(qk_norm_rope_parts(segs, ns, s1, M * Nq, c.pos, c.B, c.T, hd, theta, rot_pairs(m, sliding), m->eps, dt,
+                                c.s));
+    }
     TimedScope ts(G4_KC_ATTENTION, c.s);
     if (c.mode == G4_DECODE) G4_TRY(attn_decode(aa, c.ws + c.p->dec, c.p->fx - c.p->dec, dt, c.s));
     else G4_TRY(attn_prefill(aa, dt, c.s));

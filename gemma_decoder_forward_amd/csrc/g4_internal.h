@@ -208,6 +208,27 @@ size_t attn_prefill_ws(int64_t B, int64_t T, int64_t nh, int64_t nkv, int64_t hd
 bool attn_decode_mfma(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t s, g4_status* st);
 size_t attn_decode_mfma_ws(int64_t B, int64_t nh, int64_t hd, int64_t cap);
 
+// Rotation frequencies of a launch in revolutions per position, inv_j / (2 pi), from the host in f64;
+// zero past the rotated pairs.
+struct RopeTab { double rev[256]; };
+void rope_table(RopeTab& t, float theta, int64_t hd, int64_t n_rot);
+
+// Decode attention that forms its own inputs from the q/k/v projection's split-K partial sums: the
+// per-head RMS norm and RoPE of qk_norm_rope_parts folded into the attention launch (one token per
+// sequence). x holds `parts` float32 slices [B][x_ld], part_stride apart; the q heads start at element
+// q_off of a row, the k and v heads of a layer that owns its cache at k_off and v_off (v: scale-less
+// norm, no rotation). k_off < 0: the layer reads another layer's cache and writes no key.
+struct DecFuse {
+  const float* x; int64_t x_ld; int64_t part_stride; int32_t parts;
+  int64_t q_off, k_off, v_off;
+  const bf16* qw; const bf16* kw;
+  int32_t n_rot; float eps;
+  RopeTab tab;
+};
+// false (nothing launched) when the shape or alignment does not suit the fused kernel.
+bool attn_decode_fused(const AttnArgs& a, const DecFuse& f, void* ws, size_t ws_bytes, hipStream_t s,
+                       g4_status* st);
+
 g4_status cast_rows(const float* x, void* y, int64_t n, int32_t dtype, hipStream_t s);
 g4_status softcap_inplace(float* x, int64_t n, float cap, hipStream_t s);
 g4_status gemm_simt(const GemmArgs& a, int32_t dtype, hipStream_t s);

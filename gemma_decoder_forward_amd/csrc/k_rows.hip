@@ -362,8 +362,6 @@ struct SegDev {
 };
 struct SegPack { SegDev s[3]; int n; int total_heads; int parts; int64_t part_stride; };
 
-// Rotation frequencies of the launch in revolutions per position, inv_j / (2 pi), from the host in f64.
-struct RopeTab { double rev[256]; };
 
 // EPL consecutive values of one row (EPL in {1, 2, 4}) as floats, and back: one vector access when VEC,
 // else element by element, the first n of them.
@@ -518,6 +516,11 @@ __global__ __launch_bounds__(256) void k_qknr(SegPack pk, RopeTab tab, const int
   stv<EPL, VEC>(yh + j0 + half, c, nv);
 }
 
+void rope_table(RopeTab& t, float theta, int64_t hd, int64_t n_rot) {
+  for (int j = 0; j < 256; ++j)
+    t.rev[j] = j < n_rot ? pow((double)theta, -2.0 * j / (double)hd) / 6.283185307179586 : 0.0;
+}
+
 static g4_status qknr_launch(const HeadSeg* segs, int nseg, int parts, int64_t part_stride, bool f32_in,
                              const int32_t* pos, int64_t B, int64_t T, int64_t hd, float theta, int64_t n_rot,
                              float eps, int32_t dtype, hipStream_t s) {
@@ -537,8 +540,7 @@ static g4_status qknr_launch(const HeadSeg* segs, int nseg, int parts, int64_t p
   }
   const int nr = any_rope ? (int)n_rot : 0;
   RopeTab tab;
-  for (int j = 0; j < 256; ++j)
-    tab.rev[j] = j < nr ? pow((double)theta, -2.0 * j / (double)hd) / 6.283185307179586 : 0.0;
+  rope_table(tab, theta, hd, nr);
   // pairs per lane: vector accesses when every row start is aligned to them, else per element
   const int64_t half = hd / 2;
   const size_t isz = f32_in ? 4 : (dtype == G4_BF16 ? 2 : 4), osz = dtype == G4_BF16 ? 2 : 4;
