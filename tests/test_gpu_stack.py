@@ -305,6 +305,38 @@ def test_config4_decode_per_layer_sampled_sequences(B):
     assert_layers_within_floor(errs, floors, f"decode B={B}")
 
 
+def test_decode_cache_rows_per_sequence_positions():
+    """One decode step of a 3-layer E4B stack (sliding, sliding, full, each owning its cache) with three
+    sequences at different positions (the last row, 200 rows earlier, row 7), each layer from the
+    oracle's input: the layer outputs within the bf16 bar, the K and V rows the step writes (at every
+    sequence's own position, for every kv head) within the bf16 bar of the oracle's, and every other
+    cache row bit for bit as filled."""
+    cfg = configs.get(4, B=3, layer_types="SSF", n_shared=0)
+    model, layers, glob = build_model(cfg)
+    acts = gen.activations(cfg, "cuda")
+    ctx = cfg["ctx"]
+    pos_l = [ctx - 1, ctx - 201, 7]
+    pos = torch.tensor(pos_l, dtype=torch.int32, device="cuda")
+    fills = {l: gen.decode_cache(cfg, l, "cuda") for l in range(cfg["n_layers"]) if model.kv_src[l] == l}
+    caches, table = model.new_caches(3, ctx, fill=lambda l: tuple(x.clone() for x in fills[l]))
+    e0, p0 = _oracle_entry(cfg, glob, acts["ids"])
+    oc = {l: (O.f64(k), O.f64(v)) for l, (k, v) in fills.items()}
+    hs = [e0]
+    opos = np.array(pos_l).reshape(3, 1)
+    O.forward(cfg, host_layer(layers), e0, p0, opos, oc, per_layer=hs)
+    errs = _per_layer(model, hs, p0, pos, table, ctx, bd.G4_DECODE)
+    log("decode, per-sequence positions: layer rel L2 " + " ".join(f"{e:.1e}" for e in errs))
+    assert max(errs) <= TOL_BF16_RELL2
+    for l, (k, v) in caches.items():
+        kc, vc, kf, vf = k.cpu(), v.cpu(), fills[l][0].cpu(), fills[l][1].cpu()
+        for b, p in enumerate(pos_l):
+            assert_close(kc[b, :, p], oc[l][0][b, :, p], "bf16", f"layer {l} seq {b} K row {p}")
+            assert_close(vc[b, :, p], oc[l][1][b, :, p], "bf16", f"layer {l} seq {b} V row {p}")
+            keep = torch.ones(ctx, dtype=torch.bool)
+            keep[p] = False
+            assert torch.equal(kc[b, :, keep], kf[b, :, keep]) and torch.equal(vc[b, :, keep], vf[b, :, keep])
+
+
 @pytest.mark.parametrize("B", [1, 3, 8])
 def test_decode_stack_matches_layer_by_layer(B):
     """A 3-layer E4B decode step (sliding, sliding, full; layer scalars 0.8, 0.9, 0.7) as one stack
