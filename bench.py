@@ -5,11 +5,12 @@ Default workload: the full E4B-like 42-layer stack (5 sliding + 1 full layer, re
 layers share KV), bf16 weights, prefill of T = 4096 tokens of batch 1 from token ids: the embedding and
 per-layer inputs, then every layer. A step is one pass of that whole forward over the batch, inputs
 resident in HBM. In the same process, on the same weights, `extra.decode` times one decode step at
-context 8192 for batch 1 and 64 (the 42-layer model, caches filled to position 8190), and `extra.long`
-the 12-layer T = 32768 slice. Other workloads (--workload 2/4/5/6/7): the E4B layer pair at T = 2048,
-decode alone (--batch B), the 12-layer slice alone, a 6-layer E4B-width model with the variants (own
-full-layer KV heads, K=V, per-layer FFN widths) at T = 2048, and the 6-layer E4B-width bidirectional
-encoder at T = 2048.
+context 8192 for batch 1 and 64 (the 42-layer model, caches filled to position 8190), `extra.logits`
+the output head (final norm, projection onto the 262144-token vocabulary, softcap) on 1 and 64 rows,
+and `extra.long` the 12-layer T = 32768 slice. Other workloads (--workload 2/4/5/6/7): the E4B layer
+pair at T = 2048, decode alone (--batch B), the 12-layer slice alone, a 6-layer E4B-width model with
+the variants (own full-layer KV heads, K=V, per-layer FFN widths) at T = 2048, and the 6-layer
+E4B-width bidirectional encoder at T = 2048.
 
 Prints one JSON line. The dominant kernel's launches are timed inside the timed region with HIP events
 recorded by the library on its launch stream (g4_timer_*); `roofline` divides its algorithmic work per
@@ -257,7 +258,47 @@ def run_gpu(cfg, layers, glob, steps, warmup, breakdown, use_graph=True):
     return res
 
 
-WORKLOAD_NAMES = {2: "e4b-layer-pair prefill", 3: "e4b-42-layer prefill from token ids", 4: "e4b-42-layer decode",
+def run_logits(cfg, glob, rows, steps, warmup):
+    """The output head on `rows` rows of the model's width: final RMS norm, the projection onto the vocabulary
+    (the embedding table, [vocab, hidden] bf16, serves as its weights: same shape) and the softcap of 30.
+    Times `steps` calls between two events on the library's stream; returns the summary with the HBM rate of
+    its algorithmic bytes (weights once, the rows in, the float32 logits out)."""
+    import torch
+    from gemma_decoder_forward_amd import binding as bd
+    from synth import gen
+    H, V = cfg["hidden"], cfg["vocab"]
+    s = 7000 + rows
+    h = gen.normal((rows, H), 1.0, 0.0, s, "head_rows", "cuda", torch.float32)
+    wn = gen.normal((H,), 0.1, 1.0, s, "final_norm", "cuda", torch.bfloat16)
+    w = glob["embed"]
+    out = torch.empty((rows, V), dtype=torch.float32, device="cuda")
+    wsb = bd.g4_logits_ws(rows, H, V, bd.G4_BF16)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    st = torch.cuda.current_stream()
+
+    def call():
+        bd.g4_logits(h.data_ptr(), rows, H, wn.data_ptr(), w.data_ptr(), V, cfg["eps"], 30.0, out.data_ptr(),
+                     ws.data_ptr(), wsb, bd.G4_BF16, st.cuda_stream)
+
+    for _ in range(warmup):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(steps):
+        call()
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    assert torch.isfinite(out).all().item() and float(out.abs().max()) <= 30.0, "output head: bad logits"
+    nbytes = 2 * V * H + 2 * H + 4 * rows * H + 4 * rows * V
+    gbs = nbytes / (ms / 1e3) / 1e9
+    del h, out, ws
+    return dict(workload=f"e4b output head (final norm, vocabulary projection, softcap 30): rows={rows} vocab={V}",
+                rows_per_s=round(rows / (ms / 1e3), 2), ms_per_call=round(ms, 4), bytes_per_call=nbytes,
+                GB_s=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4))
+
+
+WORKLOAD_NAMES = {2:"e4b-layer-pair prefill", 3: "e4b-42-layer prefill from token ids", 4: "e4b-42-layer decode",
                   5: "e4b-12-layer long-context prefill",
                   6: "e4b-width 6-layer prefill with the variants (full-layer kv heads, K=V, per-layer FFN widths)",
                   7: "e4b-width 6-layer bidirectional encoder"}
@@ -462,7 +503,9 @@ def main():
     ap.add_argument("--workload", type=int, default=3, choices=[2, 3, 4, 5, 6, 7])
     ap.add_argument("--batch", type=int, default=64, help="decode batch (workload 4)")
     ap.add_argument("--no-extra", action="store_true",
-                    help="workload 3: skip the decode (B=1, 64) and T=32768 lines of `extra`")
+                    help="workload 3: skip the decode (B=1, 64), output head and T=32768 lines of `extra`")
+    ap.add_argument("--only-logits", action="store_true",
+                    help="only the output head lines of `extra` (1 and 64 rows on the E4B vocabulary), as one JSON line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -479,6 +522,14 @@ def main():
               "implements the single-GPU forward; sharding across GPUs is described, not implemented.", file=sys.stderr)
         sys.exit(2)
     from synth import configs
+    if args.only_logits:
+        from synth import gen
+        c3 = configs.get(3)
+        print("[bench] output head: building the embedding table", file=sys.stderr, flush=True)
+        g3 = gen.model_globals(c3, "cuda")
+        lines = {f"rows{rows}": run_logits(c3, g3, rows, args.steps, args.warmup) for rows in (1, 64)}
+        print(json.dumps(dict(logits=lines, steps=args.steps, warmup=args.warmup)), flush=True)
+        return
     cfg = workload(args.workload, args.batch)
     breakdown = not args.no_breakdown
     print(f"[bench] {workload_name(cfg)}: building weights", file=sys.stderr, flush=True)
@@ -503,6 +554,12 @@ def main():
             extra["decode"][f"B{B}"] = summarize(c4, r4)
             print(f"[bench] {extra['decode'][f'B{B}']['workload']}: {extra['decode'][f'B{B}']['tokens_per_s']} "
                   "tokens/s", file=sys.stderr, flush=True)
+        # the output head after the stack: one row per sequence (decode batches 1 and 64)
+        extra["logits"] = {}
+        for rows in (1, 64):
+            extra["logits"][f"rows{rows}"] = lg = run_logits(cfg, glob, rows, args.steps, args.warmup)
+            print(f"[bench] {lg['workload']}: {lg['ms_per_call']} ms per call, {lg['GB_s']} GB/s", file=sys.stderr,
+                  flush=True)
         del layers, glob
         import torch
         torch.cuda.empty_cache()

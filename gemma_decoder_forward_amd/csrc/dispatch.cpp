@@ -11,6 +11,7 @@ static g4_status gemm_one(const GemmArgs& a, int32_t dtype, hipStream_t s) {
 
 g4_status gemm(const GemmArgs& a, int32_t dtype, hipStream_t s) {
   if (a.M == 0) return G4_OK;
+  if (a.epi == EPI_SOFTCAP) return fail(G4_EUNSUP, "gemm: the softcap epilogue is reached through its own routes only");
   g4_status st = G4_OK;
   const int nseg = a.nseg > 0 ? a.nseg : 1;
   // few token rows (decode): stream the weights once, all segments in one launch -- except wide, short

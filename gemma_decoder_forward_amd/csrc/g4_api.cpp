@@ -897,6 +897,21 @@ g4_status g4_logits(const float* h, int64_t M, int64_t H, const void* out_norm, 
   struct ClearGws { ~ClearGws() { g_gws = nullptr; g_gws_bytes = 0; } } clear_gws;
   g4_status st = rownorm(h, G4_F32, 1, 0, out_norm, xn, nullptr, 1.f, nullptr, nullptr, M, H, eps, dtype, s);
   if (st != G4_OK) return st;
+  // up to 64 rows, the softcap in the product's last pass: the finisher of the few-row split-K product
+  // (up to 16 rows) or the store of the 64-row tiles (17 to 64 rows, where wide products take them)
+  if (dtype == G4_BF16 && softcap > 0.f && M <= 64) {
+    GemmArgs ga{};
+    ga.A = xn; ga.lda = H; ga.B = w_out; ga.ldb = H; ga.C = logits; ga.ldc = vocab; ga.c_dtype = G4_F32;
+    ga.M = M; ga.N = vocab; ga.K = H; ga.epi = EPI_SOFTCAP; ga.cap = softcap; ga.splits = 1;
+    ga.split_stride = M * vocab;
+    if (M > 16) {
+      if (gemm_mfma(ga, s, &st)) return st;
+    } else {
+      const void* segs[1] = {w_out};
+      const int64_t rows[1] = {vocab};
+      if (gemm_skinny(ga, segs, rows, 1, g_gws, g_gws_bytes, s, &st)) return st;
+    }
+  }
   st = run_gemm(xn, H, w_out, nullptr, H, logits, vocab, G4_F32, M, vocab, H, EPI_STORE, nullptr, 0, 1, 0, dtype, s);
   if (st != G4_OK) return st;
   return softcap_inplace(logits, M * vocab, softcap, s);

@@ -101,6 +101,7 @@ enum Epi : int {
   EPI_STORE = 0,     // C = acc (C in c_dtype)
   EPI_GEGLU = 1,     // dual B (gate, up): C = gelu_tanh(acc_gate) * acc_up, C in dtype
   EPI_GELU_MUL = 2,  // C = gelu_tanh(acc) * aux[m*aux_ld + n], aux float32, C in dtype
+  EPI_SOFTCAP = 3,   // C = cap * tanh(acc / cap), C float32, no K split (64-row tiles only)
 };
 
 struct GemmArgs {
@@ -118,6 +119,7 @@ struct GemmArgs {
   const void* segB[3];
   int64_t seg_rows[3];
   void* ws; size_t ws_bytes;  // scratch for the few-row kernel's partial sums (may be null)
+  float cap;                  // EPI_SOFTCAP: the cap (> 0)
 };
 
 // Launchers (return G4_OK or a failure with the message set).

@@ -332,6 +332,11 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a, int tiles_
               v[2] = gelu_tanh(v[2]) * x.z; v[3] = gelu_tanh(v[3]) * x.w;
               *(uint2*)((bf16*)a.C + m * a.ldc + n) = pack_bf16x4(v);
             } else if (CF32) {
+              if (EPI == EPI_SOFTCAP) {
+                const float inv = 1.f / a.cap;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = a.cap * tanhf(v[e] * inv);
+              }
               *(float4*)((float*)a.C + (int64_t)z * a.split_stride + m * a.ldc + n) = make_float4(v[0], v[1], v[2], v[3]);
             } else {
               *(uint2*)((bf16*)a.C + m * a.ldc + n) = pack_bf16x4(v);
@@ -413,7 +418,8 @@ static bool mfma_ok(const GemmArgs& a, int BN, bool seg = false) {
   if ((a.lda | a.ldb) & 7) return false;
   if (((uintptr_t)a.A | (uintptr_t)a.B | (uintptr_t)(a.B2 ? a.B2 : a.B)) & 15) return false;
   if (a.M * a.lda * 2 > 0x7fffffffLL || a.N * a.ldb * 2 > 0x7fffffffLL) return false;
-  const bool f32 = a.epi == EPI_STORE && a.c_dtype == G4_F32;
+  if (a.epi == EPI_SOFTCAP && (a.c_dtype != G4_F32 || a.splits > 1 || !(a.cap > 0.f) || a.nseg > 1)) return false;
+  const bool f32 = (a.epi == EPI_STORE || a.epi == EPI_SOFTCAP) && a.c_dtype == G4_F32;
   if ((a.ldc & 3) || ((uintptr_t)a.C & (f32 ? 15 : 7))) return false;
   if (f32 && a.splits > 1 && (a.split_stride & 3)) return false;
   if (a.epi == EPI_GELU_MUL && ((a.aux_ld & 3) || ((uintptr_t)a.aux & 15))) return false;
@@ -469,6 +475,10 @@ static g4_status launch_mfma(const GemmArgs& a, hipStream_t s) {
   } else {
     if (a.epi == EPI_GEGLU) launch_one<BM, BN, NW, BK, NS, EPI_GEGLU, false, false, WGM>(a, tm, tn, total, persist, s);
     else if (a.epi == EPI_GELU_MUL) launch_one<BM, BN, NW, BK, NS, EPI_GELU_MUL, false, false, WGM>(a, tm, tn, total, persist, s);
+    else if (a.epi == EPI_SOFTCAP) {
+      if constexpr (BM == 64) launch_one<BM, BN, NW, BK, NS, EPI_SOFTCAP, true, false, WGM>(a, tm, tn, total, persist, s);
+      else return fail(G4_EUNSUP, "gemm_mfma: the softcap epilogue is built for 64-row tiles only");
+    }
     else if (a.c_dtype == G4_F32) launch_one<BM, BN, NW, BK, NS, EPI_STORE, true, false, WGM>(a, tm, tn, total, persist, s);
     else launch_one<BM, BN, NW, BK, NS, EPI_STORE, false, false, WGM>(a, tm, tn, total, persist, s);
   }
@@ -481,11 +491,16 @@ static g4_status launch_mfma(const GemmArgs& a, hipStream_t s) {
 // layers: q/k/v, o and down 1.71 ms per step against 1.77 with 64 x 128 tiles, 2.02 with 64 x 256 and
 // 2.13 with the 256-row tiles). The gated product takes 64 x 128 tiles (64 outputs, 2 x 2 waves of
 // 32 x 64): 1.52 ms against 1.69 with 64 x 64 (twice the activation re-reads) and 1.76 with 128 x 128
-// tiles in K steps of 32. Deeper rings (five to eight stages) measured slower. Returns the output
-// columns per tile, 0 when the shape does not fit.
+// tiles in K steps of 32. Deeper rings (five to eight stages) measured slower. A plain product so wide
+// that 128-wide tiles still number four per CU (an output head over a vocabulary) takes 64 x 128 tiles:
+// half the activation re-reads of 64-wide ones, which at 64 rows are as many bytes as the weights.
+// Returns the output columns per tile, 0 when the shape does not fit.
 int gemm_rows64_cols(const GemmArgs& a) {
   if (a.M > 64) return 0;
   if (a.epi == EPI_GEGLU && mfma_ok(a, 128)) return 64;
+  const bool plain = a.epi == EPI_STORE || a.epi == EPI_SOFTCAP;
+  if (plain && a.nseg <= 1 && a.N / 256 >= 4 * (int64_t)device_cus() && mfma_ok(a, 256)) return 256;
+  if (plain && a.nseg <= 1 && a.N / 128 >= 4 * (int64_t)device_cus() && mfma_ok(a, 128)) return 128;
   if (mfma_ok(a, 64)) return a.epi == EPI_GEGLU ? 32 : 64;
   return 0;
 }
@@ -493,7 +508,8 @@ int gemm_rows64_cols(const GemmArgs& a) {
 static bool gemm_mfma_rows64(const GemmArgs& a, hipStream_t s, g4_status* st) {
   const int cols = gemm_rows64_cols(a);
   if (cols == 0) return false;
-  if (a.epi == EPI_GEGLU && cols == 64) *st = launch_mfma<64, 128, 4, 64, 4, false, 2>(a, s);
+  if (cols == 256) *st = launch_mfma<64, 256, 4, 64, 3, false, 2>(a, s);
+  else if (cols == 128 || (a.epi == EPI_GEGLU && cols == 64)) *st = launch_mfma<64, 128, 4, 64, 4, false, 2>(a, s);
   else *st = launch_mfma<64, 64, 4, 64, 4, false, 2>(a, s);
   return true;
 }
@@ -555,6 +571,7 @@ int32_t gemm_pick_splits(int64_t M, int64_t N, int64_t K, int32_t max_splits) {
 bool gemm_mfma(const GemmArgs& a, hipStream_t s, g4_status* st) {
   const int64_t cus = device_cus();
   if (a.M <= 64 && gemm_mfma_rows64(a, s, st)) return true;
+  if (a.epi == EPI_SOFTCAP) return false;  // built for the 64-row tiles only
   if (a.epi == EPI_GEGLU) {
     const int64_t tiles256 = ((a.M + 255) / 256) * (a.N / 128) * a.splits;
     if (a.splits == 1 && mfma_ok(a, 320) && tiles256 >= 192) {

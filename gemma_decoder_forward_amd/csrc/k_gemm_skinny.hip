@@ -348,6 +348,7 @@ __global__ __launch_bounds__(256) void k_gemv(SkA sa, int64_t M, SkSeg sg, int64
 }
 
 // Sums the split partials and applies the epilogue. GEGLU: part columns [0, N) are gate, [N, 2N) up.
+// SOFTCAP: float32 C = cap * tanh(sum / cap).
 template <int EPI, bool CF32>
 __global__ __launch_bounds__(256) void k_gemm_finish(GemmArgs a, const float* __restrict__ part, int splits,
                                                      int64_t Nt) {
@@ -363,6 +364,8 @@ __global__ __launch_bounds__(256) void k_gemm_finish(GemmArgs a, const float* __
     ((bf16*)a.C)[m * a.ldc + n] = f2bf(gelu_tanh(v) * u);
   } else if (EPI == EPI_GELU_MUL) {
     ((bf16*)a.C)[m * a.ldc + n] = f2bf(gelu_tanh(v) * a.aux[m * a.aux_ld + n]);
+  } else if (EPI == EPI_SOFTCAP) {
+    ((float*)a.C)[m * a.ldc + n] = a.cap * tanhf(v * (1.f / a.cap));
   } else if (CF32) {
     ((float*)a.C)[m * a.ldc + n] = v;
   } else {
@@ -530,7 +533,10 @@ g4_status gemm_skinny_finish(const GemmArgs& a, const float* part, int splits, i
   dim3 gf((unsigned)((a.M * a.N + 255) / 256));
   if (a.epi == EPI_GEGLU) hipLaunchKernelGGL((k_gemm_finish<EPI_GEGLU, false>), gf, dim3(256), 0, s, a, part, splits, Nt);
   else if (a.epi == EPI_GELU_MUL) hipLaunchKernelGGL((k_gemm_finish<EPI_GELU_MUL, false>), gf, dim3(256), 0, s, a, part, splits, Nt);
-  else if (a.c_dtype == G4_F32) hipLaunchKernelGGL((k_gemm_finish<EPI_STORE, true>), gf, dim3(256), 0, s, a, part, splits, Nt);
+  else if (a.epi == EPI_SOFTCAP) {
+    if (a.c_dtype != G4_F32 || !(a.cap > 0.f)) return fail(G4_EUNSUP, "gemm_finish: softcap needs a float32 C and cap > 0");
+    hipLaunchKernelGGL((k_gemm_finish<EPI_SOFTCAP, true>), gf, dim3(256), 0, s, a, part, splits, Nt);
+  } else if (a.c_dtype == G4_F32) hipLaunchKernelGGL((k_gemm_finish<EPI_STORE, true>), gf, dim3(256), 0, s, a, part, splits, Nt);
   else hipLaunchKernelGGL((k_gemm_finish<EPI_STORE, false>), gf, dim3(256), 0, s, a, part, splits, Nt);
   return check_launch("gemm_finish");
 }

@@ -751,17 +751,30 @@ g4_status cast_rows(const float* x, void* y, int64_t n, int32_t dtype, hipStream
 // Final-logit softcap in place (ferrox-models `forward_token_on_worker`: softcap after the output
 // head): x <- cap * tanh(x / cap).
 // --------------------------------------------------------------------------------------------
+// Four consecutive floats per thread (x 16-byte aligned, n a multiple of 4) when V4, else one.
+template <bool V4>
 __global__ __launch_bounds__(256) void k_softcap(float* __restrict__ x, int64_t n, float cap) {
   const float inv = 1.f / cap;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-    x[i] = cap * tanhf(x[i] * inv);
+  if constexpr (V4) {
+    for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < n; i += (int64_t)gridDim.x * 1024) {
+      float4 v = *(const float4*)(x + i);
+      v.x = cap * tanhf(v.x * inv); v.y = cap * tanhf(v.y * inv);
+      v.z = cap * tanhf(v.z * inv); v.w = cap * tanhf(v.w * inv);
+      *(float4*)(x + i) = v;
+    }
+  } else {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+      x[i] = cap * tanhf(x[i] * inv);
+  }
 }
 
 g4_status softcap_inplace(float* x, int64_t n, float cap, hipStream_t s) {
   if (n == 0 || cap <= 0.f) return G4_OK;
-  int64_t blocks = (n + 255) / 256;
+  const bool v4 = n % 4 == 0 && ((uintptr_t)x & 15) == 0;
+  int64_t blocks = (v4 ? n / 4 + 255 : n + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(k_softcap, dim3((unsigned)blocks), dim3(256), 0, s, x, n, cap);
+  if (v4) hipLaunchKernelGGL(k_softcap<true>, dim3((unsigned)blocks), dim3(256), 0, s, x, n, cap);
+  else hipLaunchKernelGGL(k_softcap<false>, dim3((unsigned)blocks), dim3(256), 0, s, x, n, cap);
   return check_launch("softcap");
 }
 

@@ -577,9 +577,15 @@ def test_embed_ple_e4b_widths_vs_oracle():
 # ------------------------------------------------------------------------------- output head
 @pytest.mark.parametrize("dt,M,H,V,cap", [("f32", 5, 256, 512, 30.0), ("f32", 70, 64, 200, 0.0),
                                           ("bf16", 1, 2560, 262144, 30.0), ("bf16", 7, 2560, 262144, 30.0),
-                                          ("bf16", 300, 256, 4096, 30.0), ("bf16", 33, 256, 960, 0.0)])
+                                          ("bf16", 64, 2560, 262144, 30.0),
+                                          ("bf16", 300, 256, 4096, 30.0), ("bf16", 33, 256, 960, 0.0),
+                                          ("bf16", 33, 256, 960, 30.0), ("bf16", 20, 256, 1000, 30.0),
+                                          ("f32", 5, 256, 510, 30.0)])
 def test_logits_vs_oracle(dt, M, H, V, cap):
-    """Final norm + output projection + softcap; the E4B vocabulary at decode batch sizes (few-row path)."""
+    """Final norm + output projection + softcap; the E4B vocabulary at decode batch sizes. 17 to 64 rows
+    apply the softcap in the 64-row tiles' store (64, 128 or 256 columns wide: vocabularies of 960 and
+    262144); other rows (and a vocabulary that is not whole tiles) take a separate pass, four floats per
+    thread or (a length not a multiple of 4) one."""
     log(f"logits {dt} M={M} H={H} V={V} cap={cap}")
     gdt, tdt = DT[dt]
     h = randn((M, H), 90 + M, torch.float32, 2.0)
