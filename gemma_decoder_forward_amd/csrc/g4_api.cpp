@@ -230,6 +230,13 @@ static g4_status run_gelu_mul(const void* A, int64_t lda, const void* W, int64_t
                               const float* aux, int64_t aux_ld, int64_t M, int64_t N, int64_t K, int32_t dt,
                               float* part, size_t part_bytes, hipStream_t s) {
   int32_t splits = 1;
+  if (dt == G4_BF16 && M > 64 && ((M + 127) / 128) * ((N + 127) / 128) < 256) {
+    GemmArgs ga{};
+    ga.A = A; ga.lda = lda; ga.B = W; ga.ldb = ldb; ga.C = C; ga.ldc = ldc; ga.c_dtype = dt; ga.aux = aux;
+    ga.aux_ld = aux_ld; ga.M = M; ga.N = N; ga.K = K; ga.epi = EPI_GELU_MUL; ga.splits = 1;
+    g4_status st = G4_OK;
+    if (gemm_mfma_tiles64(ga, s, &st)) return st;
+  }
   if (dt == G4_BF16 && M > 64 && part) {
     const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
     while (splits < 8 && tiles * splits * 2 <= 256 && K / (splits * 2) >= 256 &&

@@ -235,6 +235,7 @@ g4_status cast_rows(const float* x, void* y, int64_t n, int32_t dtype, hipStream
 g4_status softcap_inplace(float* x, int64_t n, float cap, hipStream_t s);
 g4_status gemm_simt(const GemmArgs& a, int32_t dtype, hipStream_t s);
 bool gemm_mfma(const GemmArgs& a, hipStream_t s, g4_status* st);
+bool gemm_mfma_tiles64(const GemmArgs& a, hipStream_t s, g4_status* st);
 int gemm_rows64_cols(const GemmArgs& a);  // output columns per 64-row tile (M <= 64), 0 if none fits
 // Split-K slices (1..max_splits) for a float32-output product whose consumer sums the slices: the
 // count whose MFMA tiling (tile width and slices together) takes the fewest tile-passes.

@@ -514,6 +514,15 @@ static bool gemm_mfma_rows64(const GemmArgs& a, hipStream_t s, g4_status* st) {
   return true;
 }
 
+// 64 x 64 tiles at any row count, K whole (plain stores and the gelu-times-factor epilogue): for
+// products with few output columns, where 128-row tiles would need a K split and a finishing pass to
+// fill the CUs.
+bool gemm_mfma_tiles64(const GemmArgs& a, hipStream_t s, g4_status* st) {
+  if (a.splits > 1 || (a.epi != EPI_STORE && a.epi != EPI_GELU_MUL) || a.nseg > 1 || !mfma_ok(a, 64)) return false;
+  *st = launch_mfma<64, 64, 4, 64, 4, false, 2>(a, s);
+  return true;
+}
+
 // Cost of a 256-row tiling in tile-passes over the CUs, weighted by the tile's width and its split's
 // K length (each extra split-K slice also costs its float32 traffic, counted as 3%). 0 when the
 // tiling leaves more than a quarter of the CUs idle in its only pass (the 128 x 128 kernel then does
