@@ -580,12 +580,14 @@ def test_embed_ple_e4b_widths_vs_oracle():
                                           ("bf16", 64, 2560, 262144, 30.0),
                                           ("bf16", 300, 256, 4096, 30.0), ("bf16", 33, 256, 960, 0.0),
                                           ("bf16", 33, 256, 960, 30.0), ("bf16", 20, 256, 1000, 30.0),
-                                          ("f32", 5, 256, 510, 30.0)])
+                                          ("f32", 5, 256, 510, 30.0), ("bf16", 5, 256, 960, 30.0),
+                                          ("bf16", 3, 64, 512, 30.0), ("bf16", 2, 256, 1000, 30.0)])
 def test_logits_vs_oracle(dt, M, H, V, cap):
     """Final norm + output projection + softcap; the E4B vocabulary at decode batch sizes. 17 to 64 rows
     apply the softcap in the 64-row tiles' store (64, 128 or 256 columns wide: vocabularies of 960 and
-    262144); other rows (and a vocabulary that is not whole tiles) take a separate pass, four floats per
-    thread or (a length not a multiple of 4) one."""
+    262144), up to 16 in the few-row product's finishing pass (1, 5 and 7 rows); other rows, and shapes
+    those kernels do not take (K = 64, a vocabulary of 1000), a separate pass, four floats per thread or
+    (a length not a multiple of 4) one."""
     log(f"logits {dt} M={M} H={H} V={V} cap={cap}")
     gdt, tdt = DT[dt]
     h = randn((M, H), 90 + M, torch.float32, 2.0)
