@@ -501,11 +501,12 @@ def test_ple_inject_vs_oracle(dt, scalar):
     assert_close(h, ref, "f32" if dt == "f32" else "bf16", "h")
 
 
-@pytest.mark.parametrize("M,scalar", [(1000, 1.0), (70, 0.5), (4096, 1.0)])
+@pytest.mark.parametrize("M,scalar", [(1000, 1.0), (70, 0.5), (4096, 1.0), (65, 1.0), (129, 0.5)])
 def test_ple_inject_e4b_widths_vs_oracle(M, scalar):
-    """The PLE block at E4B widths (H 2560, d 256), bf16, at prefill row counts (the split-K gate GEMM and
-    its finishing pass, the projection GEMM and the row tail; M = 1000 and 70 leave ragged tiles). The
-    branch itself, h_out / scalar - h, is compared at the bf16 bound, and h within it."""
+    """The PLE block at E4B widths (H 2560, d 256), bf16, at prefill row counts (the gate GEMM on 64 x 64
+    tiles over the whole K with gelu(g) x input in the store, the projection GEMM and the row tail;
+    M = 1000, 70, 65 and 129 leave ragged tiles, 65 a last tile of one row). The branch itself,
+    h_out / scalar - h, is compared at the bf16 bound, and h within it."""
     H, d, L = 2560, 256, 4
     h = randn((M, H), 95)
     h0 = h.clone()
